@@ -1,0 +1,251 @@
+"""ctypes binding of the CPU oracle (oracle/fp4q_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product library does not.
+
+Arrays are numpy: bf16 tensors travel as uint16 bit patterns, fp32 as
+float32.  Plane shapes follow the library convention:
+    codes   [rows_pad, cols_pad // 2]  (row plane, low nibble = even column)
+    codes_t [cols_pad, rows_pad // 2]  (transposed plane)
+    scales  [rows_pad // 32, cols_pad // 32]  E8M0 bytes
+with rows_pad / cols_pad rounded up to multiples of 32.
+"""
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from . import build as _build
+
+DT_BF16, DT_F32 = 1, 2
+ROUND_SR, ROUND_RNE = 0, 1
+OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
+OPS = {"fwd": OP_FWD, "dgrad": OP_DGRAD, "wgrad": OP_WGRAD}
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def lib():
+    """Load the oracle library, building it first if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        L.orc_e2m1_value.restype = ctypes.c_double
+        L.orc_e2m1_value.argtypes = [ctypes.c_int]
+        L.orc_e4m3_value.restype = ctypes.c_double
+        L.orc_e4m3_value.argtypes = [ctypes.c_int]
+        L.orc_e8m0_value.restype = ctypes.c_double
+        L.orc_e8m0_value.argtypes = [ctypes.c_int]
+        L.orc_truncfree_exponent.restype = ctypes.c_int
+        L.orc_truncfree_exponent.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.orc_e2m1_round.restype = ctypes.c_int
+        L.orc_e2m1_round.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_uint32]
+        L.orc_e4m3_round.restype = ctypes.c_int
+        L.orc_e4m3_round.argtypes = [ctypes.c_double]
+        L.orc_philox4x32_10.restype = None
+        L.orc_philox4x32_10.argtypes = [_P, _P, _P]
+        L.orc_sr_counter.restype = None
+        L.orc_sr_counter.argtypes = [_I64, _I64, ctypes.c_uint32, _P, _P]
+        L.orc_sr_bits.restype = ctypes.c_uint32
+        L.orc_sr_bits.argtypes = [ctypes.c_uint64, ctypes.c_uint32, _I64, _I64]
+        L.orc_quant2d.restype = ctypes.c_int
+        L.orc_quant2d.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, ctypes.c_int, ctypes.c_uint64,
+                                  ctypes.c_uint32, _P, _I64, _P, _I64, _P, _I64, _I64, _I64]
+        L.orc_quant1x32_fp4.restype = ctypes.c_int
+        L.orc_quant1x32_fp4.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, ctypes.c_int,
+                                        ctypes.c_uint64, ctypes.c_uint32, _P, _I64, _P, _I64]
+        L.orc_quant1d_mxfp8.restype = ctypes.c_int
+        L.orc_quant1d_mxfp8.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64]
+        L.orc_dequant_fp4.restype = ctypes.c_int
+        L.orc_dequant_fp4.argtypes = [_P, _I64, _P, _I64, ctypes.c_int, _I64, _I64, _P]
+        L.orc_dequant_mxfp8.restype = ctypes.c_int
+        L.orc_dequant_mxfp8.argtypes = [_P, _I64, _P, _I64, _I64, _I64, _P]
+        L.orc_gemm.restype = ctypes.c_int
+        L.orc_gemm.argtypes = [ctypes.c_int, _P, _I64, _I64, _P, _I64, _I64, _P, _P]
+        L.orc_gemm_sampled.restype = ctypes.c_int
+        L.orc_gemm_sampled.argtypes = [ctypes.c_int, _P, _I64, _I64, _P, _I64, _I64, _I64, _P, _P,
+                                       _P, _P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def pad32(n):
+    return (n + 31) // 32 * 32
+
+
+def _dtype_of(x):
+    if x.dtype == np.uint16:
+        return DT_BF16
+    if x.dtype == np.float32:
+        return DT_F32
+    raise TypeError("oracle inputs are uint16 (bf16 bits) or float32, got %s" % x.dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("oracle %s failed with code %d" % (what, rc))
+
+
+# -- element-level entry points -------------------------------------------------
+
+def e2m1_value(nibble):
+    return lib().orc_e2m1_value(int(nibble))
+
+
+def e4m3_value(byte):
+    return lib().orc_e4m3_value(int(byte))
+
+
+def e8m0_value(byte):
+    return lib().orc_e8m0_value(int(byte))
+
+
+def truncfree_exponent(M, qmax=6.0):
+    return lib().orc_truncfree_exponent(float(M), float(qmax))
+
+
+def e2m1_round(v, mode=ROUND_SR, r16=0):
+    return lib().orc_e2m1_round(float(v), int(mode), int(r16))
+
+
+def e4m3_round(v):
+    return lib().orc_e4m3_round(float(v))
+
+
+def philox4x32_10(ctr, key):
+    c = np.asarray(ctr, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_counter(r, c, stream):
+    ctr = np.zeros(4, dtype=np.uint32)
+    lane = ctypes.c_int(0)
+    lib().orc_sr_counter(int(r), int(c), int(stream), _ptr(ctr), ctypes.byref(lane))
+    return ctr, lane.value
+
+
+def sr_bits(seed, stream, r, c):
+    return lib().orc_sr_bits(int(seed), int(stream), int(r), int(c))
+
+
+# -- quantizers ------------------------------------------------------------------
+
+def quant2d(x, round_mode=ROUND_SR, seed=0, stream=0, threads=None):
+    """2D 32x32-block FP4 quantization; returns (codes, codes_t, scales)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    rp, cp = pad32(rows), pad32(cols)
+    codes = np.zeros((rp, cp // 2), dtype=np.uint8)
+    codes_t = np.zeros((cp, rp // 2), dtype=np.uint8)
+    scales = np.zeros((rp // 32, cp // 32), dtype=np.uint8)
+    dt = _dtype_of(x)
+    ntr = rp // 32
+    nthreads = threads or min(8, os.cpu_count() or 1)
+    nthreads = max(1, min(nthreads, ntr))
+
+    def run(lo, hi):
+        return lib().orc_quant2d(_ptr(x), dt, rows, cols, cols, int(round_mode), int(seed),
+                                 int(stream), _ptr(codes), cp // 2, _ptr(codes_t), rp // 2,
+                                 _ptr(scales), cp // 32, lo, hi)
+
+    if nthreads == 1:
+        _check(run(0, ntr), "quant2d")
+    else:
+        bounds = [(ntr * i // nthreads, ntr * (i + 1) // nthreads) for i in range(nthreads)]
+        with ThreadPoolExecutor(nthreads) as ex:
+            for rc in ex.map(lambda b: run(*b), bounds):
+                _check(rc, "quant2d")
+    return codes, codes_t, scales
+
+
+def quant1x32_fp4(x, round_mode=ROUND_SR, seed=0, stream=0):
+    """Conventional 1x32 FP4 quantization along rows; returns (codes, scales)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    cp = pad32(cols)
+    codes = np.zeros((rows, cp // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cp // 32), dtype=np.uint8)
+    _check(lib().orc_quant1x32_fp4(_ptr(x), _dtype_of(x), rows, cols, cols, int(round_mode),
+                                   int(seed), int(stream), _ptr(codes), cp // 2, _ptr(scales),
+                                   cp // 32), "quant1x32_fp4")
+    return codes, scales
+
+
+def quant1d_mxfp8(x):
+    """MXFP8 E4M3 with 1x32 blocks along rows; returns (codes, scales)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    cp = pad32(cols)
+    codes = np.zeros((rows, cp), dtype=np.uint8)
+    scales = np.zeros((rows, cp // 32), dtype=np.uint8)
+    _check(lib().orc_quant1d_mxfp8(_ptr(x), _dtype_of(x), rows, cols, cols, _ptr(codes), cp,
+                                   _ptr(scales), cp // 32), "quant1d_mxfp8")
+    return codes, scales
+
+
+def dequant_fp4(codes, scales, rows, cols, block_rows=32):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty((rows, cols), dtype=np.float64)
+    _check(lib().orc_dequant_fp4(_ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1],
+                                 int(block_rows), rows, cols, _ptr(out)), "dequant_fp4")
+    return out
+
+
+def dequant_mxfp8(codes, scales, rows, cols):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty((rows, cols), dtype=np.float64)
+    _check(lib().orc_dequant_mxfp8(_ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1],
+                                   rows, cols, _ptr(out)), "dequant_mxfp8")
+    return out
+
+
+# -- GEMMs -----------------------------------------------------------------------
+
+def _out_shape(op, A, B):
+    if op == OP_FWD:
+        return A.shape[0], B.shape[0]
+    if op == OP_DGRAD:
+        return A.shape[0], B.shape[1]
+    return A.shape[1], B.shape[1]
+
+
+def gemm(op, A, B):
+    """fp64 GEMM of a linear layer on dequantized operands; returns (C, bound)."""
+    op = OPS.get(op, op)
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    B = np.ascontiguousarray(B, dtype=np.float64)
+    m, n = _out_shape(op, A, B)
+    C = np.empty((m, n), dtype=np.float64)
+    bound = np.empty((m, n), dtype=np.float64)
+    _check(lib().orc_gemm(op, _ptr(A), A.shape[0], A.shape[1], _ptr(B), B.shape[0], B.shape[1],
+                          _ptr(C), _ptr(bound)), "gemm")
+    return C, bound
+
+
+def gemm_sampled(op, A, B, ci, cj):
+    """The same products at sampled coordinates; returns (C[s], bound[s])."""
+    op = OPS.get(op, op)
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    B = np.ascontiguousarray(B, dtype=np.float64)
+    ci = np.ascontiguousarray(ci, dtype=np.int64)
+    cj = np.ascontiguousarray(cj, dtype=np.int64)
+    C = np.empty(len(ci), dtype=np.float64)
+    bound = np.empty(len(ci), dtype=np.float64)
+    _check(lib().orc_gemm_sampled(op, _ptr(A), A.shape[0], A.shape[1], _ptr(B), B.shape[0],
+                                  B.shape[1], len(ci), _ptr(ci), _ptr(cj), _ptr(C), _ptr(bound)),
+           "gemm_sampled")
+    return C, bound

@@ -1,0 +1,121 @@
+/*
+ * fp4q_oracle.h -- CPU oracle for the transposition-invariant 2D-block FP4
+ * quantizer, the MXFP8 1x32 quantizer and the fp64 GEMMs of a linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no source
+ * with the GPU library (fp4_microscaling_quantization_quant2d_amd/csrc) and
+ * includes none of its headers.
+ *
+ * Primary source: "Stable FP4 Training via Transposition-Invariant Block
+ * Quantization" (Rahimifar et al., arXiv 2607.24953):
+ *   - Sec. 2.1 eq. (MXFP4): P_i = round_FP4(X_i / S), X_i ~ P_i * S
+ *   - Sec. 3 "Transposition invariance": S(B_ij) = S(B_ij^T), square b x b blocks
+ *   - Sec. 3 "Application to linear layers": Y = X W^T, dX = dY W, dW = dY^T X
+ *   - Sec. 3.1 eq.: S = 2^ceil(log2(2M / (Qp - Qn)))  (truncation-free scale)
+ *   - Sec. 3.2: MXFP8 for the query and key projections
+ *   - Appendix "Boundary blocks": the scale uses valid entries only
+ *
+ * Parity unpinned (the pages fix none of these; they are this library's own
+ * specification and are pinned only by oracle <-> GPU agreement):
+ *   - the Philox4x32-10 stream and its element -> counter mapping,
+ *   - the stochastic-rounding bit rule (16 random bits, carry rule),
+ *   - the nibble order inside a byte (low nibble = even index).
+ * Every other function is pinned by the CPU test suite against closed forms,
+ * library casts, brute force, invariants or hand-worked examples.
+ *
+ * All pointers are host pointers.  All functions return 0 on success and a
+ * negative value on invalid arguments or non-finite input.
+ */
+#ifndef FP4Q_ORACLE_H
+#define FP4Q_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_DT_BF16 = 1, ORC_DT_F32 = 2 };
+enum { ORC_ROUND_SR = 0, ORC_ROUND_RNE = 1 };
+enum { ORC_OP_FWD = 0, ORC_OP_DGRAD = 1, ORC_OP_WGRAD = 2 };
+
+/* --- element formats ---------------------------------------------------- */
+/* Value of a 4-bit E2M1 nibble (bit 3 = sign). */
+double orc_e2m1_value(int nibble);
+/* Value of an E4M3FN byte; NaN for 0x7F / 0xFF. */
+double orc_e4m3_value(int byte);
+/* 2^(byte-127); NaN for 255. */
+double orc_e8m0_value(int byte);
+
+/* Smallest integer k with qmax * 2^k >= M, clamped to [-127, 127]; M == 0
+ * gives -127.  qmax = 6 for E2M1, 448 for E4M3. */
+int orc_truncfree_exponent(double M, double qmax);
+
+/* Round v (0 <= v <= 6) to an E2M1 magnitude code 0..7.
+ * mode ORC_ROUND_SR uses the 16-bit random field r16; ORC_ROUND_RNE ignores it.
+ * Returns -1 if v is outside [0, 6]. */
+int orc_e2m1_round(double v, int mode, uint32_t r16);
+/* Round v (0 <= v <= 448) to the nearest E4M3FN magnitude code (ties to even). */
+int orc_e4m3_round(double v);
+
+/* --- random stream ------------------------------------------------------ */
+/* Philox4x32-10 (Salmon et al., SC'11) of one counter block under one key. */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+/* Counter block and 16-bit lane used for element (r, c).  The mapping depends
+ * only on the unordered pair {r, c}. */
+void orc_sr_counter(int64_t r, int64_t c, uint32_t stream, uint32_t ctr[4], int* lane);
+/* The 16-bit random field used to round element (r, c). */
+uint32_t orc_sr_bits(uint64_t seed, uint32_t stream, int64_t r, int64_t c);
+
+/* --- quantizers --------------------------------------------------------- */
+/* 2D 32x32-block FP4 quantization of x [rows x cols] (leading dim ldx elements).
+ * Outputs: codes   [rows_pad x ld]   row plane, nibble (r, c) at byte r*ld + c/2
+ *          codes_t [cols_pad x ld_t] transposed plane, nibble (r, c) at c*ld_t + r/2
+ *          scales  [rows_pad/32 x ld_s] E8M0 bytes
+ * (low nibble = even index; padding nibbles are 0).  Only tile rows
+ * [tile_row_begin, tile_row_end) are produced (-1, -1 = all). */
+int orc_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                int round_mode, uint64_t seed, uint32_t stream,
+                uint8_t* codes, int64_t ld, uint8_t* codes_t, int64_t ld_t,
+                uint8_t* scales, int64_t ld_s,
+                int64_t tile_row_begin, int64_t tile_row_end);
+
+/* Conventional 1x32 FP4 quantization along rows (the non-invariant layout the
+ * pages compare against).  codes [rows x ld], scales [rows x ld_s]. */
+int orc_quant1x32_fp4(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                      int round_mode, uint64_t seed, uint32_t stream,
+                      uint8_t* codes, int64_t ld, uint8_t* scales, int64_t ld_s);
+
+/* MXFP8 (E4M3FN, 1x32 blocks along rows, truncation-free scale, RNE).
+ * codes [rows x ld] bytes (padding bytes 0), scales [rows x ld_s]. */
+int orc_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                      uint8_t* codes, int64_t ld, uint8_t* scales, int64_t ld_s);
+
+/* --- dequantization ----------------------------------------------------- */
+/* FP4 plane -> fp64 [rows x cols] (dense, leading dim cols).  The scale of
+ * element (r, c) is scales[(r / block_rows) * ld_s + c / 32]; block_rows is
+ * 32 for the 2D layout and 1 for the 1x32 layout. */
+int orc_dequant_fp4(const uint8_t* codes, int64_t ld, const uint8_t* scales, int64_t ld_s,
+                    int block_rows, int64_t rows, int64_t cols, double* out);
+int orc_dequant_mxfp8(const uint8_t* codes, int64_t ld, const uint8_t* scales, int64_t ld_s,
+                      int64_t rows, int64_t cols, double* out);
+
+/* --- GEMMs of a linear layer (fp64, increasing contraction index) -------- */
+/* op FWD:   A = X  [T x K], B = W [N x K], C = A B^T  [T x N]
+ * op DGRAD: A = dY [T x N], B = W [N x K], C = A B    [T x K]
+ * op WGRAD: A = dY [T x N], B = X [T x K], C = A^T B  [N x K]
+ * bound (may be NULL) receives sum_k |a||b| per output element. */
+int orc_gemm(int op, const double* A, int64_t a_rows, int64_t a_cols,
+             const double* B, int64_t b_rows, int64_t b_cols,
+             double* C, double* bound);
+/* The same products at n sampled output coordinates (ci[s], cj[s]). */
+int orc_gemm_sampled(int op, const double* A, int64_t a_rows, int64_t a_cols,
+                     const double* B, int64_t b_rows, int64_t b_cols,
+                     int64_t n, const int64_t* ci, const int64_t* cj,
+                     double* C, double* bound);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

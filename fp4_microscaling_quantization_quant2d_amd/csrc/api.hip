@@ -1,0 +1,383 @@
+// C ABI of libfp4q: host-side validation and dispatch to the gfx950 kernels.
+// Every argument is checked before anything is enqueued; nothing here
+// allocates device memory or synchronizes.
+#include "fp4q.h"
+#include "fp4q_launch.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return FP4Q_OK;
+}
+
+int hip_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess)
+        return fail(FP4Q_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+    return ok();
+}
+
+inline int64_t pad32(int64_t n) { return (n + 31) / 32 * 32; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+int check_fp4_tensor(const fp4q_qtensor* t, const char* name, bool need_t)
+{
+    if (!t)
+        return fail(FP4Q_EINVAL, "%s: null descriptor", name);
+    if (t->fmt != FP4Q_FMT_FP4_2D32)
+        return fail(FP4Q_EINVAL, "%s: fmt %d is not FP4Q_FMT_FP4_2D32", name, t->fmt);
+    if (t->rows <= 0 || t->cols <= 0 || t->rows > kMaxDim || t->cols > kMaxDim)
+        return fail(FP4Q_EINVAL, "%s: bad shape %lld x %lld", name, (long long)t->rows, (long long)t->cols);
+    const int64_t R = pad32(t->rows), C = pad32(t->cols);
+    if (!t->codes || !t->scales)
+        return fail(FP4Q_EINVAL, "%s: null codes or scales", name);
+    if (t->ld < C / 2 || t->ld % 16 || !aligned16(t->codes))
+        return fail(FP4Q_EINVAL, "%s: row plane needs ld >= %lld, ld %% 16 == 0 and 16-byte alignment", name,
+                    (long long)(C / 2));
+    if (t->ld_s < C / 32)
+        return fail(FP4Q_EINVAL, "%s: ld_s %lld < %lld", name, (long long)t->ld_s, (long long)(C / 32));
+    if (need_t) {
+        if (!t->codes_t)
+            return fail(FP4Q_EINVAL, "%s: the transposed plane is required", name);
+        if (t->ld_t < R / 2 || t->ld_t % 16 || !aligned16(t->codes_t))
+            return fail(FP4Q_EINVAL, "%s: transposed plane needs ld_t >= %lld, ld_t %% 16 == 0, 16-byte alignment",
+                        name, (long long)(R / 2));
+    }
+    if (t->batch < 1)
+        return fail(FP4Q_EINVAL, "%s: batch must be >= 1", name);
+    return FP4Q_OK;
+}
+
+int check_fp8_tensor(const fp4q_qtensor* t, const char* name)
+{
+    if (!t)
+        return fail(FP4Q_EINVAL, "%s: null descriptor", name);
+    if (t->fmt != FP4Q_FMT_MXFP8_1D32)
+        return fail(FP4Q_EINVAL, "%s: fmt %d is not FP4Q_FMT_MXFP8_1D32", name, t->fmt);
+    if (t->rows <= 0 || t->cols <= 0 || t->rows > ((int64_t)1 << 40) || t->cols > kMaxDim)
+        return fail(FP4Q_EINVAL, "%s: bad shape", name);
+    const int64_t C = pad32(t->cols);
+    if (!t->codes || !t->scales)
+        return fail(FP4Q_EINVAL, "%s: null codes or scales", name);
+    if (t->ld < C || t->ld % 16 || !aligned16(t->codes))
+        return fail(FP4Q_EINVAL, "%s: codes need ld >= %lld, ld %% 16 == 0 and 16-byte alignment", name, (long long)C);
+    if (t->ld_s < C / 32)
+        return fail(FP4Q_EINVAL, "%s: ld_s too small", name);
+    if (t->batch < 1)
+        return fail(FP4Q_EINVAL, "%s: batch must be >= 1", name);
+    return FP4Q_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int fp4q_version(void) { return FP4Q_ABI_VERSION; }
+
+const char* fp4q_last_error(void) { return g_err.c_str(); }
+
+int fp4q_quant2d_sizes(int64_t rows, int64_t cols, int64_t* codes_bytes, int64_t* codes_t_bytes,
+                       int64_t* scales_bytes)
+{
+    if (rows <= 0 || cols <= 0 || rows > kMaxDim || cols > kMaxDim)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d_sizes: bad shape %lld x %lld", (long long)rows, (long long)cols);
+    const int64_t R = pad32(rows), C = pad32(cols);
+    if (codes_bytes)
+        *codes_bytes = R * C / 2;
+    if (codes_t_bytes)
+        *codes_t_bytes = C * R / 2;
+    if (scales_bytes)
+        *scales_bytes = (R / 32) * (C / 32);
+    return ok();
+}
+
+int fp4q_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int round_mode,
+                 uint64_t seed, uint32_t stream_id, const fp4q_qtensor* out, void* hip_stream)
+{
+    if (!x)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d: x is null");
+    if (dtype != FP4Q_DT_BF16 && dtype != FP4Q_DT_F32)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d: dtype %d", dtype);
+    if (round_mode != FP4Q_ROUND_SR && round_mode != FP4Q_ROUND_RNE)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d: round_mode %d", round_mode);
+    if (rows <= 0 || cols <= 0 || rows > kMaxDim || cols > kMaxDim || ldx < cols)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d: bad shape %lld x %lld (ldx %lld)", (long long)rows,
+                    (long long)cols, (long long)ldx);
+    int rc = check_fp4_tensor(out, "fp4q_quant2d out", false);
+    if (rc)
+        return rc;
+    if (out->rows != rows || out->cols != cols)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d: out shape %lld x %lld != input", (long long)out->rows,
+                    (long long)out->cols);
+    if (out->batch != 1)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d: out batch must be 1");
+    const int64_t R = pad32(rows), C = pad32(cols);
+    if (out->codes_t && (out->ld_t < R / 2 || out->ld_t % 16 || !aligned16(out->codes_t)))
+        return fail(FP4Q_EINVAL, "fp4q_quant2d: transposed plane needs ld_t >= %lld, multiple of 16, aligned",
+                    (long long)(R / 2));
+    const int esz = dtype == FP4Q_DT_F32 ? 4 : 2;
+    fp4q::Quant2dArgs p;
+    p.x = x;
+    p.ldx = ldx;
+    p.rows = (int)rows;
+    p.cols = (int)cols;
+    p.rows_pad = (int)R;
+    p.cols_pad = (int)C;
+    p.codes = out->codes;
+    p.ld = out->ld;
+    p.codes_t = out->codes_t;
+    p.ld_t = out->ld_t;
+    p.scales = out->scales;
+    p.ld_s = out->ld_s;
+    p.key0 = (uint32_t)seed;
+    p.key1 = (uint32_t)(seed >> 32);
+    p.stream = stream_id;
+    const bool aligned = aligned16(x) && ((ldx * esz) % 16 == 0);
+    return hip_status(fp4q::launch_quant2d(p, dtype == FP4Q_DT_F32, round_mode == FP4Q_ROUND_RNE, aligned,
+                                           static_cast<hipStream_t>(hip_stream)),
+                      "fp4q_quant2d");
+}
+
+int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                       const fp4q_qtensor* out, void* hip_stream)
+{
+    if (!x)
+        return fail(FP4Q_EINVAL, "fp4q_quant1d_mxfp8: x is null");
+    if (dtype != FP4Q_DT_BF16 && dtype != FP4Q_DT_F32)
+        return fail(FP4Q_EINVAL, "fp4q_quant1d_mxfp8: dtype %d", dtype);
+    if (rows <= 0 || cols <= 0 || cols > kMaxDim || ldx < cols || rows > ((int64_t)1 << 40))
+        return fail(FP4Q_EINVAL, "fp4q_quant1d_mxfp8: bad shape");
+    int rc = check_fp8_tensor(out, "fp4q_quant1d_mxfp8 out");
+    if (rc)
+        return rc;
+    if (out->rows != rows || out->cols != cols || out->batch != 1)
+        return fail(FP4Q_EINVAL, "fp4q_quant1d_mxfp8: out shape/batch mismatch");
+    const int esz = dtype == FP4Q_DT_F32 ? 4 : 2;
+    if (rows * (pad32(cols) / 32) >= (int64_t)UINT_MAX * 256)
+        return fail(FP4Q_EINVAL, "fp4q_quant1d_mxfp8: too many groups for one launch");
+    fp4q::Mxfp8Args p;
+    p.x = x;
+    p.ldx = ldx;
+    p.rows = rows;
+    p.cols = (int)cols;
+    p.cols_pad = (int)pad32(cols);
+    p.codes = out->codes;
+    p.ld = out->ld;
+    p.scales = out->scales;
+    p.ld_s = out->ld_s;
+    const bool aligned = aligned16(x) && ((ldx * esz) % 16 == 0);
+    return hip_status(fp4q::launch_quant1d_mxfp8(p, dtype == FP4Q_DT_F32, aligned,
+                                                 static_cast<hipStream_t>(hip_stream)),
+                      "fp4q_quant1d_mxfp8");
+}
+
+int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, int64_t ldc, int64_t c_bstride,
+              const fp4q_groups* groups, void* hip_stream)
+{
+    if (op != FP4Q_OP_FWD && op != FP4Q_OP_DGRAD && op != FP4Q_OP_WGRAD)
+        return fail(FP4Q_EINVAL, "fp4q_gemm: op %d", op);
+    if (!a || !b || !c)
+        return fail(FP4Q_EINVAL, "fp4q_gemm: null a, b or c");
+    if (a->fmt != b->fmt)
+        return fail(FP4Q_EINVAL, "fp4q_gemm: operand formats differ (%d, %d)", a->fmt, b->fmt);
+    const bool fp8 = a->fmt == FP4Q_FMT_MXFP8_1D32;
+    int rc;
+    if (fp8) {
+        if (op != FP4Q_OP_FWD)
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: MXFP8 operands support FWD only");
+        if ((rc = check_fp8_tensor(a, "fp4q_gemm a")) || (rc = check_fp8_tensor(b, "fp4q_gemm b")))
+            return rc;
+    } else {
+        const bool at = op == FP4Q_OP_WGRAD, bt = op != FP4Q_OP_FWD;
+        if ((rc = check_fp4_tensor(a, "fp4q_gemm a", at)) || (rc = check_fp4_tensor(b, "fp4q_gemm b", bt)))
+            return rc;
+    }
+    if (a->batch != b->batch)
+        return fail(FP4Q_EINVAL, "fp4q_gemm: batch mismatch %lld vs %lld", (long long)a->batch,
+                    (long long)b->batch);
+    if (a->batch > 65535)
+        return fail(FP4Q_EINVAL, "fp4q_gemm: batch above 65535");
+    if (groups && (fp8 || a->batch != 1))
+        return fail(FP4Q_EINVAL, "fp4q_gemm: grouped products take FP4 operands with batch 1");
+
+    fp4q::GemmArgs g = {};
+    int64_t M, N, K;
+    bool a_st = false, b_st = false;
+    switch (op) {
+    case FP4Q_OP_FWD:  // X [T x K], W [N x K]
+        if (a->cols != b->cols)
+            return fail(FP4Q_EINVAL, "fp4q_gemm FWD: K mismatch (%lld vs %lld)", (long long)a->cols,
+                        (long long)b->cols);
+        M = a->rows; N = b->rows; K = pad32(a->cols);
+        g.a = a->codes; g.lda = a->ld; g.sa = a->scales; g.lds_a = a->ld_s;
+        g.b = b->codes; g.ldb = b->ld; g.sb = b->scales; g.lds_b = b->ld_s;
+        g.a_rows = (int)(fp8 ? a->rows : pad32(a->rows));
+        g.b_rows = (int)(fp8 ? b->rows : pad32(b->rows));
+        g.bs_a = a->bstride; g.bs_b = b->bstride;
+        break;
+    case FP4Q_OP_DGRAD:  // dY [T x N], W [N x K] -> [T x K]
+        if (a->cols != b->rows && !groups)
+            return fail(FP4Q_EINVAL, "fp4q_gemm DGRAD: dY cols %lld != W rows %lld", (long long)a->cols,
+                        (long long)b->rows);
+        M = a->rows; N = b->cols; K = pad32(a->cols);
+        g.a = a->codes; g.lda = a->ld; g.sa = a->scales; g.lds_a = a->ld_s;
+        g.b = b->codes_t; g.ldb = b->ld_t; g.sb = b->scales; g.lds_b = b->ld_s;
+        b_st = true;
+        g.a_rows = (int)pad32(a->rows);
+        g.b_rows = (int)pad32(b->cols);
+        g.bs_a = a->bstride; g.bs_b = b->bstride_t;
+        break;
+    default:  // WGRAD: dY [T x N], X [T x K] -> [N x K]
+        if (a->rows != b->rows)
+            return fail(FP4Q_EINVAL, "fp4q_gemm WGRAD: dY rows %lld != X rows %lld", (long long)a->rows,
+                        (long long)b->rows);
+        M = a->cols; N = b->cols; K = pad32(a->rows);
+        g.a = a->codes_t; g.lda = a->ld_t; g.sa = a->scales; g.lds_a = a->ld_s;
+        g.b = b->codes_t; g.ldb = b->ld_t; g.sb = b->scales; g.lds_b = b->ld_s;
+        a_st = b_st = true;
+        g.a_rows = (int)pad32(a->cols);
+        g.b_rows = (int)pad32(b->cols);
+        g.bs_a = a->bstride_t; g.bs_b = b->bstride_t;
+        break;
+    }
+    g.bs_sa = a->bstride_s;
+    g.bs_sb = b->bstride_s;
+    g.c = c;
+    g.ldc = ldc;
+    g.bs_c = c_bstride;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    if (fp8 && (a->cols % 32))
+        return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: MXFP8 K must be a multiple of 32");
+
+    int grouped_op = -1;
+    if (!groups) {
+        if (ldc < N)
+            return fail(FP4Q_EINVAL, "fp4q_gemm: ldc %lld < N %lld", (long long)ldc, (long long)N);
+        if (a->batch > 1 && c_bstride < M * ldc)
+            return fail(FP4Q_EINVAL, "fp4q_gemm: c_bstride %lld < M*ldc", (long long)c_bstride);
+    } else {
+        const int n = groups->n;
+        if (n < 1 || n > FP4Q_MAX_GROUPS || !groups->row_off)
+            return fail(FP4Q_EINVAL, "fp4q_gemm: groups->n %d out of [1, %d] or null row_off", n, FP4Q_MAX_GROUPS);
+        const int64_t* off = groups->row_off;
+        const int64_t tok = pad32(op == FP4Q_OP_WGRAD ? a->rows : a->rows);
+        if (off[0] != 0)
+            return fail(FP4Q_EINVAL, "fp4q_gemm: row_off[0] must be 0");
+        for (int i = 0; i < n; ++i)
+            if (off[i + 1] < off[i] || off[i + 1] % 32)
+                return fail(FP4Q_EINVAL, "fp4q_gemm: row_off must be non-decreasing multiples of 32");
+        if (off[n] > tok)
+            return fail(FP4Q_EINVAL, "fp4q_gemm: row_off[n] %lld beyond %lld token rows", (long long)off[n],
+                        (long long)tok);
+        int64_t gn;
+        if (op == FP4Q_OP_FWD) {
+            if (b->rows % n || (b->rows / n) % 32)
+                return fail(FP4Q_EINVAL, "fp4q_gemm grouped FWD: W rows %lld not n x (multiple of 32)",
+                            (long long)b->rows);
+            gn = b->rows / n;
+        } else {
+            gn = a->cols;
+            if (gn % 32)
+                return fail(FP4Q_EINVAL, "fp4q_gemm grouped: per-expert width %lld not a multiple of 32",
+                            (long long)gn);
+            if (op == FP4Q_OP_DGRAD && b->rows != gn * n)
+                return fail(FP4Q_EINVAL, "fp4q_gemm grouped DGRAD: W rows %lld != n x %lld", (long long)b->rows,
+                            (long long)gn);
+        }
+        const int64_t nout = op == FP4Q_OP_FWD ? gn : N;
+        if (ldc < nout)
+            return fail(FP4Q_EINVAL, "fp4q_gemm grouped: ldc %lld < %lld", (long long)ldc, (long long)nout);
+        g.n_groups = n;
+        g.group_n = (int)gn;
+        int64_t tiles = 0;
+        const int tm = fp4q::gemm_tile_m(), tn = fp4q::gemm_tile_n();
+        for (int i = 0; i <= n; ++i) {
+            g.row_off[i] = (int)off[i];
+            g.tile_start[i] = (int)tiles;
+            if (i == n)
+                break;
+            const int64_t mg = op == FP4Q_OP_WGRAD ? gn : off[i + 1] - off[i];
+            const int64_t ng = nout;
+            tiles += ((mg + tm - 1) / tm) * ((ng + tn - 1) / tn);
+        }
+        if (tiles > INT_MAX)
+            return fail(FP4Q_EINVAL, "fp4q_gemm grouped: too many tiles");
+        grouped_op = op;
+    }
+    return hip_status(fp4q::launch_gemm(g, fp8 ? 2 : 1, a_st, b_st, grouped_op, (int)a->batch,
+                                        static_cast<hipStream_t>(hip_stream)),
+                      "fp4q_gemm");
+}
+
+int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, int64_t ldy, void* hip_stream)
+{
+    if (!q || !y)
+        return fail(FP4Q_EINVAL, "fp4q_dequant: null q or y");
+    if (out_dtype != FP4Q_DT_F32 && out_dtype != FP4Q_DT_BF16)
+        return fail(FP4Q_EINVAL, "fp4q_dequant: out_dtype %d", out_dtype);
+    int rc;
+    fp4q::DequantArgs p;
+    int fmt;
+    if (q->fmt == FP4Q_FMT_FP4_2D32) {
+        if ((rc = check_fp4_tensor(q, "fp4q_dequant q", transposed != 0)))
+            return rc;
+        fmt = 1;
+        p.codes = transposed ? q->codes_t : q->codes;
+        p.ld = transposed ? q->ld_t : q->ld;
+        p.scale_transposed = transposed ? 1 : 0;
+        p.rows = (int)(transposed ? q->cols : q->rows);
+        p.cols = (int)(transposed ? q->rows : q->cols);
+    } else if (q->fmt == FP4Q_FMT_MXFP8_1D32) {
+        if ((rc = check_fp8_tensor(q, "fp4q_dequant q")))
+            return rc;
+        if (transposed)
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_dequant: MXFP8 has no transposed plane");
+        if (q->rows > INT_MAX)
+            return fail(FP4Q_EINVAL, "fp4q_dequant: too many rows");
+        fmt = 2;
+        p.codes = q->codes;
+        p.ld = q->ld;
+        p.scale_transposed = 0;
+        p.rows = (int)q->rows;
+        p.cols = (int)q->cols;
+    } else {
+        return fail(FP4Q_EINVAL, "fp4q_dequant: fmt %d", q->fmt);
+    }
+    if (q->batch != 1)
+        return fail(FP4Q_EINVAL, "fp4q_dequant: batch must be 1");
+    if (ldy < p.cols)
+        return fail(FP4Q_EINVAL, "fp4q_dequant: ldy %lld < %d", (long long)ldy, p.cols);
+    p.scales = q->scales;
+    p.ld_s = q->ld_s;
+    p.y = y;
+    p.ldy = ldy;
+    return hip_status(fp4q::launch_dequant(p, fmt, out_dtype == FP4Q_DT_BF16, static_cast<hipStream_t>(hip_stream)),
+                      "fp4q_dequant");
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal launch interface between the C ABI layer (api.hip) and the kernel
+// translation units.  Host code validates every argument before filling
+// these structs; the kernels trust them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+struct Quant2dArgs {
+    const void* x;
+    int64_t ldx;       // elements
+    int rows, cols;    // logical shape
+    int rows_pad, cols_pad;
+    uint8_t* codes;    // [rows_pad x ld]
+    int64_t ld;
+    uint8_t* codes_t;  // [cols_pad x ld_t] or null
+    int64_t ld_t;
+    uint8_t* scales;   // [rows_pad/32 x ld_s]
+    int64_t ld_s;
+    uint32_t key0, key1, stream;
+};
+
+hipError_t launch_quant2d(const Quant2dArgs& p, bool f32, bool rne, bool aligned, hipStream_t s);
+
+struct Mxfp8Args {
+    const void* x;
+    int64_t ldx;
+    int64_t rows;
+    int cols, cols_pad;
+    uint8_t* codes;    // [rows x ld]
+    int64_t ld;
+    uint8_t* scales;   // [rows x ld_s]
+    int64_t ld_s;
+};
+
+hipError_t launch_quant1d_mxfp8(const Mxfp8Args& p, bool f32, bool aligned, hipStream_t s);
+
+struct DequantArgs {
+    const uint8_t* codes;
+    int64_t ld;
+    const uint8_t* scales;
+    int64_t ld_s;
+    int scale_transposed;  // FP4: scale of (r, c) at (c/32)*ld_s + r/32
+    int rows, cols;        // output shape
+    void* y;
+    int64_t ldy;
+};
+
+hipError_t launch_dequant(const DequantArgs& p, int fmt, bool out_bf16, hipStream_t s);
+
+// Block-scaled GEMM C[M x N] = A[M x K] . B[N x K]^T with both operands
+// contraction-contiguous (one row of A or B is K codes).  Scale of A row m,
+// K-block kb:  FP4 2D grid   sa[(m/32)*lds_a + kb]   (a_st = 0)
+//                            sa[kb*lds_a + m/32]     (a_st = 1, transposed grid)
+//              MXFP8 1D grid sa[m*lds_a + kb]
+constexpr int kMaxGroups = 256;
+
+struct GemmArgs {
+    const uint8_t* a;
+    const uint8_t* b;
+    const uint8_t* sa;
+    const uint8_t* sb;
+    float* c;
+    int64_t lda, ldb;      // bytes per operand row
+    int64_t lds_a, lds_b;  // bytes per scale-grid row
+    int64_t ldc;           // floats
+    int M, N, K;           // K in elements, multiple of 32
+    int a_rows, b_rows;    // rows allocated in the operand planes (load bound)
+    // batch (blockIdx.y): per-item strides
+    int64_t bs_a, bs_b, bs_sa, bs_sb, bs_c;
+    // grouped mode: number of groups and row offsets (multiples of 32)
+    int n_groups;
+    int group_n;           // rows of B per group (FWD/DGRAD) or C rows per group (WGRAD)
+    int tile_start[kMaxGroups + 1];
+    int row_off[kMaxGroups + 1];
+};
+
+enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };
+
+// fmt: 1 FP4, 2 FP8.  a_st / b_st: transposed scale grids (FP4 only).
+// grouped_op: -1 dense/batched, else the op whose grouped wiring applies.
+hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int grouped_op, int batch,
+                       hipStream_t s);
+
+// Output tile of the GEMM kernel (grouped launches size their grids with it).
+int gemm_tile_m();
+int gemm_tile_n();
+
+} // namespace fp4q

@@ -114,11 +114,21 @@ LAYERS_7B = [("qkv", 4096, 12288), ("o", 4096, 4096), ("up", 4096, 11008),
 
 
 def config_1b(T=4096) -> List[Linear]:
-    return [linear_layer("1b:" + nm, T, K, N, i) for i, (nm, K, N) in enumerate(LAYERS_1B)]
+    return [layer_1b(i, T) for i in range(len(LAYERS_1B))]
 
 
 def config_7b(T=8192) -> List[Linear]:
-    return [linear_layer("7b:" + nm, T, K, N, i) for i, (nm, K, N) in enumerate(LAYERS_7B)]
+    return [layer_7b(i, T) for i in range(len(LAYERS_7B))]
+
+
+def layer_7b(i, T=8192) -> Linear:
+    nm, K, N = LAYERS_7B[i]
+    return linear_layer("7b:" + nm, T, K, N, i)
+
+
+def layer_1b(i, T=4096) -> Linear:
+    nm, K, N = LAYERS_1B[i]
+    return linear_layer("1b:" + nm, T, K, N, i)
 
 
 @dataclass

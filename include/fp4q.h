@@ -1,0 +1,188 @@
+/*
+ * fp4q.h -- C ABI of the MI355X (gfx950) library for transposition-invariant
+ * 2D-block FP4 quantization and the block-scaled MXFP4 / MXFP8 GEMMs of a
+ * linear layer.
+ *
+ * Method: "Stable FP4 Training via Transposition-Invariant Block
+ * Quantization" (Rahimifar et al., arXiv 2607.24953).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named x, y, c and every pointer inside fp4q_qtensor are DEVICE
+ *    pointers owned by the caller; fp4q_groups.row_off is a HOST array.
+ *    The library never allocates, frees or synchronizes; work is enqueued on
+ *    the caller's stream (a hipStream_t passed as void*, NULL = default
+ *    stream) and descriptors are read only during the call.
+ *  - Return value: FP4Q_OK (0) or a negative fp4q_status.  Argument errors are
+ *    detected on the host before anything is enqueued (outputs untouched);
+ *    fp4q_last_error() then returns a message (thread-local).  Faults inside a
+ *    kernel surface at the caller's next synchronization.
+ *  - Matrices are row-major.  Leading dimensions count elements for x/y/c and
+ *    bytes for code planes and scale grids.
+ *  - Inputs must be finite (no NaN/Inf); this is a documented precondition,
+ *    not checked on the device.
+ *
+ * Formats
+ *  - E2M1 nibble: bit 3 sign, bits 2..0 code of the magnitudes
+ *    {0, 0.5, 1, 1.5, 2, 3, 4, 6}; two nibbles per byte, the LOW nibble holds
+ *    the element with the EVEN column index.
+ *  - E8M0 scale byte b: scale 2^(b - 127), b in [0, 254].
+ *  - E4M3FN byte: sign, 4 exponent bits (bias 7), 3 mantissa bits; max 448.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4Q_ABI_VERSION 1
+
+typedef enum {
+    FP4Q_OK = 0,
+    FP4Q_EINVAL = -1,       /* bad argument: null pointer, shape, alignment, leading dim */
+    FP4Q_EUNSUPPORTED = -2, /* valid request this build does not implement */
+    FP4Q_EHIP = -3          /* the HIP runtime rejected a launch */
+} fp4q_status;
+
+typedef enum { FP4Q_DT_BF16 = 1, FP4Q_DT_F32 = 2 } fp4q_dtype;
+typedef enum { FP4Q_ROUND_SR = 0, FP4Q_ROUND_RNE = 1 } fp4q_round;
+typedef enum { FP4Q_OP_FWD = 0, FP4Q_OP_DGRAD = 1, FP4Q_OP_WGRAD = 2 } fp4q_op;
+typedef enum {
+    FP4Q_FMT_FP4_2D32 = 1,  /* E2M1 codes, one E8M0 scale per 32x32 tile */
+    FP4Q_FMT_MXFP8_1D32 = 2 /* E4M3FN bytes, one E8M0 scale per 1x32 row group */
+} fp4q_fmt;
+
+/*
+ * A quantized matrix of logical shape rows x cols (caller-owned host struct
+ * holding device pointers).
+ *
+ * FP4_2D32 (written by fp4q_quant2d), with R = rows and C = cols rounded up
+ * to multiples of 32:
+ *   codes   [R x ld]    row plane: nibble (r, c) in byte r*ld + c/2
+ *   codes_t [C x ld_t]  transposed plane: nibble (r, c) in byte c*ld_t + r/2
+ *   scales  [R/32 x ld_s] E8M0 byte of tile (r/32, c/32) at (r/32)*ld_s + c/32
+ *   Requires ld >= C/2, ld_t >= R/2, ld_s >= C/32; ld and ld_t multiples of 16
+ *   and the planes 16-byte aligned.  Padding nibbles (r >= rows or c >= cols)
+ *   are written as 0.
+ * MXFP8_1D32 (written by fp4q_quant1d_mxfp8), with C = cols rounded up to 32:
+ *   codes   [rows x ld]   one E4M3FN byte per element (padding bytes 0)
+ *   scales  [rows x ld_s] E8M0 byte of group (r, c/32)
+ *   codes_t unused.  Requires ld >= C (multiple of 16), ld_s >= C/32.
+ * batch >= 1 stacks matrices of the same shape; item i starts at
+ * codes + i*bstride, codes_t + i*bstride_t, scales + i*bstride_s (bytes).
+ */
+typedef struct fp4q_qtensor {
+    int32_t fmt;
+    int32_t reserved;
+    int64_t rows, cols;
+    uint8_t* codes;
+    int64_t ld;
+    uint8_t* codes_t;
+    int64_t ld_t;
+    uint8_t* scales;
+    int64_t ld_s;
+    int64_t batch;
+    int64_t bstride, bstride_t, bstride_s;
+} fp4q_qtensor;
+
+/*
+ * Token groups of a grouped (mixture-of-experts) GEMM.  row_off is a HOST
+ * array of n+1 non-decreasing offsets, each a multiple of 32, with
+ * row_off[0] = 0: group g owns token rows [row_off[g], row_off[g+1]).
+ * 1 <= n <= FP4Q_MAX_GROUPS.
+ */
+#define FP4Q_MAX_GROUPS 256
+typedef struct fp4q_groups {
+    int32_t n;
+    int32_t reserved;
+    const int64_t* row_off;
+} fp4q_groups;
+
+/* ABI version of the loaded library (FP4Q_ABI_VERSION). */
+int fp4q_version(void);
+
+/* Message describing the last non-zero return on this thread ("" if none). */
+const char* fp4q_last_error(void);
+
+/*
+ * Bytes needed by fp4q_quant2d's outputs for a rows x cols matrix with the
+ * tightest leading dimensions (ld = C/2, ld_t = R/2, ld_s = C/32 with R, C
+ * rounded up to 32).  Any out-pointer may be NULL.
+ * Following the size accounting of the pages' Table 1, each code plane is a
+ * quarter of the bf16 bytes; scales add one byte per 32x32 tile.
+ */
+int fp4q_quant2d_sizes(int64_t rows, int64_t cols, int64_t* codes_bytes,
+                       int64_t* codes_t_bytes, int64_t* scales_bytes);
+
+/*
+ * 2D-block FP4 quantization ("Stable FP4 Training via Transposition-Invariant
+ * Block Quantization": Sec. 3 square blocks with S(B) = S(B^T); Sec. 3.1
+ * truncation-free scale S = 2^ceil(log2(2M/(Qp-Qn))) with Qp = 6, Qn = -6
+ * and stochastic rounding; Sec. 2.1 P = round_FP4(X/S); appendix "Boundary
+ * blocks": the amax M covers valid entries only).
+ *
+ *   x        device, rows x cols, leading dim ldx elements, dtype bf16 or f32;
+ *            16-byte aligned rows (ldx*elemsize % 16 == 0) take the fast path.
+ *   round_mode FP4Q_ROUND_SR (stochastic) or FP4Q_ROUND_RNE (nearest-even).
+ *   seed, stream_id  key and fourth counter word of the Philox4x32-10 stream.
+ *            Element (r, c) draws 16 bits from the counter
+ *            ((a%32)*4 + (b%32)/8, a/32, b/32, stream_id), a = min(r,c),
+ *            b = max(r,c), taking half (b%8) of the 128-bit output; rounding
+ *            goes up iff floor(frac * 2^16) + draw >= 2^16.  Hence
+ *            quant(x^T) equals quant(x)^T bit for bit.
+ *   out      fmt = FP4Q_FMT_FP4_2D32, rows/cols equal to the arguments,
+ *            codes, codes_t (may be NULL to skip the transposed plane) and
+ *            scales set; batch must be 1.
+ * One read of x writes the row plane, the transposed plane and the scales.
+ */
+int fp4q_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                 int round_mode, uint64_t seed, uint32_t stream_id,
+                 const fp4q_qtensor* out, void* hip_stream);
+
+/*
+ * MXFP8 quantization of the query/key projections (Sec. 3.2 of the same
+ * page): E4M3FN elements, one E8M0 scale per 1x32 group along each row,
+ * truncation-free (the Sec. 3.1 rule with Qp = 448), round-to-nearest-even.
+ *   x    device, rows x cols, leading dim ldx elements (bf16 or f32).
+ *   out  fmt = FP4Q_FMT_MXFP8_1D32, codes and scales set, batch 1.
+ */
+int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                       const fp4q_qtensor* out, void* hip_stream);
+
+/*
+ * GEMMs of a linear layer on quantized operands (Sec. 3 "Application to
+ * linear layers": Y = X W^T, dX = dY W, dW = dY^T X), fp32 accumulation and
+ * fp32 output C (row-major, leading dim ldc floats).
+ *   op FWD:   a = X  [T x K], b = W [N x K]  ->  C = X W^T   [T x N]
+ *   op DGRAD: a = dY [T x N], b = W [N x K]  ->  C = dY W    [T x K]
+ *   op WGRAD: a = dY [T x N], b = X [T x K]  ->  C = dY^T X  [N x K]
+ * FP4 operands must carry both planes; DGRAD reads W's transposed plane and
+ * WGRAD reads the transposed planes of dY and X, so each tensor is quantized
+ * once.  MXFP8 operands support FWD only (S = Q K^T).
+ *   batch  a->batch == b->batch = B runs B independent products; product i
+ *          writes C + i*c_bstride (floats).
+ *   groups NULL for a dense product; else a grouped (expert) product with
+ *          batch 1: FWD  b = stacked W [n*N x K], C [T x N], group g maps
+ *          rows row_off[g].. of X to expert g's rows of W; DGRAD likewise
+ *          with C [T x K]; WGRAD C = stacked dW [n*N x K], each expert
+ *          contracting over its own token rows.
+ */
+int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, int64_t ldc,
+              int64_t c_bstride, const fp4q_groups* groups, void* hip_stream);
+
+/*
+ * Dequantization X ~ P * S (Sec. 2.1 of the same page) to fp32 or bf16.
+ *   transposed  0: the row plane, y is rows x cols; 1 (FP4 only): the
+ *               transposed plane, y is cols x rows.
+ *   out_dtype   FP4Q_DT_F32 or FP4Q_DT_BF16; ldy in elements.
+ */
+int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, int64_t ldy,
+                 void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4Q_H */

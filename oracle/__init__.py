@@ -142,8 +142,12 @@ def sr_bits(seed, stream, r, c):
 
 # -- quantizers ------------------------------------------------------------------
 
-def quant2d(x, round_mode=ROUND_SR, seed=0, stream=0, threads=None):
-    """2D 32x32-block FP4 quantization; returns (codes, codes_t, scales)."""
+def quant2d(x, round_mode=ROUND_SR, seed=0, stream=0, threads=None, tile_rows=None):
+    """2D 32x32-block FP4 quantization; returns (codes, codes_t, scales).
+
+    tile_rows=(lo, hi) restricts the work to tile rows [lo, hi) (rows
+    32*lo .. 32*hi-1 of the row plane, bytes 16*lo .. 16*hi-1 of every
+    transposed-plane row); the rest of the outputs stays zero."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
     rp, cp = pad32(rows), pad32(cols)
@@ -151,8 +155,9 @@ def quant2d(x, round_mode=ROUND_SR, seed=0, stream=0, threads=None):
     codes_t = np.zeros((cp, rp // 2), dtype=np.uint8)
     scales = np.zeros((rp // 32, cp // 32), dtype=np.uint8)
     dt = _dtype_of(x)
-    ntr = rp // 32
-    nthreads = threads or min(8, os.cpu_count() or 1)
+    t0, t1 = (0, rp // 32) if tile_rows is None else tile_rows
+    ntr = t1 - t0
+    nthreads = threads or min(16, os.cpu_count() or 1)
     nthreads = max(1, min(nthreads, ntr))
 
     def run(lo, hi):
@@ -161,9 +166,10 @@ def quant2d(x, round_mode=ROUND_SR, seed=0, stream=0, threads=None):
                                  _ptr(scales), cp // 32, lo, hi)
 
     if nthreads == 1:
-        _check(run(0, ntr), "quant2d")
+        _check(run(t0, t1), "quant2d")
     else:
-        bounds = [(ntr * i // nthreads, ntr * (i + 1) // nthreads) for i in range(nthreads)]
+        bounds = [(t0 + ntr * i // nthreads, t0 + ntr * (i + 1) // nthreads)
+                  for i in range(nthreads)]
         with ThreadPoolExecutor(nthreads) as ex:
             for rc in ex.map(lambda b: run(*b), bounds):
                 _check(rc, "quant2d")

@@ -1,0 +1,133 @@
+"""The C ABI library loads, exports every entry point declared in
+include/fp4q.h, and rejects bad arguments on the host before any launch
+(no GPU needed: validation runs before the first HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4q.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4q_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def fp4q():
+    import fp4_microscaling_quantization_quant2d_amd as m
+    if not os.path.exists(m.library_path()):
+        from fp4_microscaling_quantization_quant2d_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for fn in ("fp4q_quant2d", "fp4q_quant1d_mxfp8", "fp4q_gemm", "fp4q_dequant",
+               "fp4q_quant2d_sizes", "fp4q_last_error", "fp4q_version"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(fp4q):
+    L = fp4q.lib()
+    for fn in _declared():
+        assert hasattr(L, fn), fn
+    out = os.popen("nm -D --defined-only %s" % fp4q.library_path()).read()
+    for fn in _declared():
+        assert re.search(r"\bT %s\b" % fn, out), fn
+
+
+def test_version_and_sizes(fp4q):
+    assert fp4q.lib().fp4q_version() == 1
+    # Table 1 accounting: codes are a quarter of the bf16 bytes, plus 1 byte per tile
+    assert fp4q.fp4q_quant2d_sizes(4096, 2048) == (4096 * 1024, 2048 * 2048, 128 * 64)
+    assert fp4q.fp4q_quant2d_sizes(33, 65) == (64 * 48, 96 * 32, 2 * 3)
+    with pytest.raises(fp4q.Fp4qError):
+        fp4q.fp4q_quant2d_sizes(0, 5)
+
+
+def _desc(fp4q, fmt=1, rows=64, cols=64, ld=32, ld_t=32, ld_s=2, codes=0x1000, codes_t=0x2000,
+          scales=0x3000, batch=1):
+    d = fp4q._QDesc()
+    d.fmt, d.rows, d.cols, d.ld, d.ld_t, d.ld_s, d.batch = fmt, rows, cols, ld, ld_t, ld_s, batch
+    d.codes, d.codes_t, d.scales = codes, codes_t, scales
+    return d
+
+
+def _err(fp4q):
+    return fp4q.lib().fp4q_last_error().decode()
+
+
+def test_quant2d_rejects_bad_arguments(fp4q):
+    L = fp4q.lib()
+    P = ctypes.c_void_p
+    x = P(0x10000)
+    good = _desc(fp4q)
+    cases = [
+        (P(0), 1, 64, 64, 64, 0, good),          # null x
+        (x, 3, 64, 64, 64, 0, good),             # dtype
+        (x, 1, 0, 64, 64, 0, good),              # rows
+        (x, 1, 64, 64, 32, 0, good),             # ldx < cols
+        (x, 1, 64, 64, 64, 7, good),             # round mode
+        (x, 1, 64, 64, 64, 0, _desc(fp4q, ld=16)),       # ld too small
+        (x, 1, 64, 64, 64, 0, _desc(fp4q, ld=40)),       # ld not multiple of 16
+        (x, 1, 64, 64, 64, 0, _desc(fp4q, codes=0x1008)),  # misaligned plane
+        (x, 1, 64, 64, 64, 0, _desc(fp4q, ld_s=1)),      # scale grid too narrow
+        (x, 1, 64, 64, 64, 0, _desc(fp4q, rows=32)),     # shape mismatch
+        (x, 1, 64, 64, 64, 0, _desc(fp4q, fmt=2)),       # wrong format
+        (x, 1, 64, 64, 64, 0, _desc(fp4q, ld_t=16)),     # transposed plane too small
+    ]
+    for xp, dt, r, c, ldx, rm, d in cases:
+        rc = L.fp4q_quant2d(xp, dt, r, c, ldx, rm, 0, 0, ctypes.byref(d), None)
+        assert rc == -1, (dt, r, c, ldx, rm)
+        assert _err(fp4q)
+
+
+def test_gemm_rejects_bad_arguments(fp4q):
+    L = fp4q.lib()
+    c = ctypes.c_void_p(0x50000)
+    a = _desc(fp4q, rows=64, cols=64)
+    b = _desc(fp4q, rows=96, cols=32, ld=16, ld_t=48, ld_s=1)
+    assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(b), c, 96, 0, None, None) == -1  # K mismatch
+    assert "K mismatch" in _err(fp4q)
+    assert L.fp4q_gemm(5, ctypes.byref(a), ctypes.byref(a), c, 64, 0, None, None) == -1   # op
+    assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(a), c, 32, 0, None, None) == -1   # ldc
+    nt = _desc(fp4q, codes_t=0)
+    assert L.fp4q_gemm(1, ctypes.byref(a), ctypes.byref(nt), c, 64, 0, None, None) == -1  # needs W^T
+    assert L.fp4q_gemm(2, ctypes.byref(nt), ctypes.byref(a), c, 64, 0, None, None) == -1  # needs dY^T
+    f8 = _desc(fp4q, fmt=2, ld=64)
+    assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(f8), c, 64, 0, None, None) == -1  # mixed fmt
+    assert L.fp4q_gemm(1, ctypes.byref(f8), ctypes.byref(f8), c, 64, 0, None, None) == -2  # fp8 dgrad
+    # grouped: offsets must start at 0 and be multiples of 32
+    for offs in ([0, 16, 64], [32, 64], [0, 64, 32], [0, 32, 96]):
+        arr = (ctypes.c_int64 * len(offs))(*offs)
+        g = fp4q._Groups(len(offs) - 1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+        w = _desc(fp4q, rows=64 * (len(offs) - 1), cols=64, ld_t=64 * (len(offs) - 1) // 2)
+        assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(w), c, 64, 0, ctypes.byref(g), None) == -1
+
+
+def test_dequant_and_mxfp8_reject_bad_arguments(fp4q):
+    L = fp4q.lib()
+    y = ctypes.c_void_p(0x70000)
+    q = _desc(fp4q)
+    assert L.fp4q_dequant(ctypes.byref(q), 0, 9, y, 64, None) == -1
+    assert L.fp4q_dequant(ctypes.byref(q), 0, 2, y, 10, None) == -1
+    f8 = _desc(fp4q, fmt=2, ld=64)
+    assert L.fp4q_dequant(ctypes.byref(f8), 1, 2, y, 64, None) == -2
+    assert L.fp4q_quant1d_mxfp8(ctypes.c_void_p(0x10000), 1, 64, 64, 64, ctypes.byref(q), None) == -1
+    bad = _desc(fp4q, fmt=2, ld=48)
+    assert L.fp4q_quant1d_mxfp8(ctypes.c_void_p(0x10000), 1, 64, 64, 64, ctypes.byref(bad), None) == -1
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import fp4_microscaling_quantization_quant2d_amd as m
+    monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(m, "_lib", None)
+    with pytest.raises(m.Fp4qError):
+        m.lib()

@@ -1,0 +1,124 @@
+"""GPU parity of fp4q_gemm (MXFP4, fwd / dgrad / wgrad) with the oracle's
+fp64 GEMM on the oracle's own dequantized operands, to the tolerance
+|err| <= 1e-5 * sum_k |a||b| per element."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import fp4_microscaling_quantization_quant2d_amd as fq
+from fp4_microscaling_quantization_quant2d_amd import workloads as wl
+from gpu_util import assert_planes_equal, check_gemm_tol, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+STREAMS = {"X": 1, "W": 2, "dY": 3}
+
+
+def _quant_all(X, W, dY, seed=0):
+    """GPU and oracle quantization of one layer's tensors."""
+    g, o = {}, {}
+    for nm, t in (("X", X), ("W", W), ("dY", dY)):
+        g[nm] = fq.fp4q_quant2d(to_dev(t), seed=seed, stream_id=STREAMS[nm])
+        o[nm] = orc.quant2d(t, orc.ROUND_SR, seed=seed, stream=STREAMS[nm])
+    return g, o
+
+
+def _deq(o, nm, shape):
+    c, _, s = o[nm]
+    return orc.dequant_fp4(c, s, shape[0], shape[1])
+
+
+def _layer_full_check(X, W, dY, what):
+    g, o = _quant_all(X, W, dY)
+    for nm, t in (("X", X), ("W", W), ("dY", dY)):
+        assert_planes_equal(g[nm], o[nm], "%s %s" % (what, nm))
+    Xd, Wd, dYd = _deq(o, "X", X.shape), _deq(o, "W", W.shape), _deq(o, "dY", dY.shape)
+    worst = 0.0
+    for op, a, b, ra, rb in (("fwd", "X", "W", Xd, Wd), ("dgrad", "dY", "W", dYd, Wd),
+                             ("wgrad", "dY", "X", dYd, Xd)):
+        note("gemm %s %s" % (what, op))
+        C = fq.fp4q_gemm(op, g[a], g[b])
+        torch.cuda.synchronize()
+        ref, bound = orc.gemm(op, ra, rb)
+        worst = max(worst, check_gemm_tol(C.cpu().numpy(), ref, bound, "%s %s" % (what, op)))
+    return worst
+
+
+def test_tiny_all_ops():
+    t = wl.tiny()
+    _layer_full_check(t["A"], t["W"], t["dY"], "tiny")
+
+
+@pytest.mark.parametrize("T,K,N", [(100, 200, 72), (32, 32, 32), (33, 65, 97), (512, 640, 384),
+                                   (260, 300, 520), (64, 1056, 96)])
+def test_ragged_and_multi_tile(T, K, N):
+    L = wl.linear_layer("tiny:ragged", T, K, N, T * 7 + K)
+    _layer_full_check(L.X, L.W, L.dY, "%dx%dx%d" % (T, K, N))
+
+
+def test_exact_on_grid_values():
+    """Operands on the E2M1 grid with unit scales: every product and partial
+    sum is exact in fp32, so the GPU must match the fp64 result exactly."""
+    rng = np.random.default_rng(4)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)
+    X = (grid[rng.integers(0, 8, (64, 128))] * rng.choice([-1, 1], (64, 128))).astype(np.float32)
+    W = (grid[rng.integers(0, 8, (96, 128))] * rng.choice([-1, 1], (96, 128))).astype(np.float32)
+    X[:, 0] = 6.0
+    W[:, 0] = 6.0
+    X[0, :] = 6.0
+    W[0, :] = 6.0
+    note("gemm exact grid")
+    gx = fq.fp4q_quant2d(to_dev(X), round_mode="rne")
+    gw = fq.fp4q_quant2d(to_dev(W), round_mode="rne")
+    C = fq.fp4q_gemm("fwd", gx, gw).cpu().numpy()
+    assert np.array_equal(C.astype(np.float64), X.astype(np.float64) @ W.astype(np.float64).T)
+
+
+def _sampled_layer_check(L, what, n_samples=3000):
+    """Full-size layer: every GPU plane vs the oracle, GEMMs at sampled outputs."""
+    rng = np.random.default_rng(99)
+    g, o = _quant_all(L.X, L.W, L.dY)
+    for nm in ("X", "W", "dY"):
+        assert_planes_equal(g[nm], o[nm], "%s %s" % (what, nm))
+    Xd = _deq(o, "X", L.X.shape)
+    Wd = _deq(o, "W", L.W.shape)
+    dYd = _deq(o, "dY", L.dY.shape)
+    T, K, N = L.T, L.K, L.N
+    for op, a, b, ra, rb, (m, n) in (("fwd", "X", "W", Xd, Wd, (T, N)),
+                                     ("dgrad", "dY", "W", dYd, Wd, (T, K)),
+                                     ("wgrad", "dY", "X", dYd, Xd, (N, K))):
+        note("gemm %s %s (%d x %d)" % (what, op, m, n))
+        C = fq.fp4q_gemm(op, g[a], g[b])
+        ci = np.concatenate([rng.integers(0, m, n_samples), [0, m - 1, m - 1, 0]])
+        cj = np.concatenate([rng.integers(0, n, n_samples), [0, n - 1, 0, n - 1]])
+        got = C[torch.from_numpy(ci).cuda(), torch.from_numpy(cj).cuda()].cpu().numpy()
+        del C
+        ref, bound = orc.gemm_sampled(op, ra, rb, ci, cj)
+        check_gemm_tol(got, ref, bound, "%s %s" % (what, op))
+
+
+@pytest.mark.parametrize("i", [0, 1])
+def test_1b_layers_sampled(i):
+    _sampled_layer_check(wl.layer_1b(i), "1B layer %d" % i)
+
+
+def test_7b_qkv_sampled():
+    _sampled_layer_check(wl.layer_7b(0), "7B qkv")
+
+
+def test_7b_down_sampled():
+    _sampled_layer_check(wl.layer_7b(3), "7B down")
+
+
+def test_gemm_into_strided_output():
+    """C with a leading dimension larger than N; the gap stays untouched."""
+    L = wl.linear_layer("tiny:ldc", 96, 128, 64, 1)
+    g, o = _quant_all(L.X, L.W, L.dY)
+    C = torch.full((96, 80), 7.0, device="cuda")
+    note("gemm strided C")
+    fq.fp4q_gemm("fwd", g["X"], g["W"], c=C[:, :64])
+    ref, bound = orc.gemm("fwd", _deq(o, "X", L.X.shape), _deq(o, "W", L.W.shape))
+    Ch = C.cpu().numpy()
+    check_gemm_tol(Ch[:, :64], ref, bound, "strided")
+    assert np.all(Ch[:, 64:] == 7.0)

@@ -1,0 +1,154 @@
+"""GPU parity of fp4q_quant2d with the oracle: bit-exact codes (row and
+transposed planes) and scale bytes, for SR and RNE, fp32 and bf16, ragged
+and padded shapes, special values, and the BASELINE workload tensors."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import fp4_microscaling_quantization_quant2d_amd as fq
+from fp4_microscaling_quantization_quant2d_amd import workloads as wl
+from gpu_util import assert_planes_equal, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x_np, mode="sr", seed=0, stream=0, ld_pad=0):
+    x = to_dev(x_np)
+    if ld_pad:
+        big = torch.zeros((x.shape[0], x.shape[1] + ld_pad), dtype=x.dtype, device=x.device)
+        big[:, : x.shape[1]] = x
+        x = big[:, : x_np.shape[1]]
+    return fq.fp4q_quant2d(x, round_mode=mode, seed=seed, stream_id=stream)
+
+
+@pytest.mark.parametrize("name", ["A", "W", "dY"])
+@pytest.mark.parametrize("mode", ["sr", "rne"])
+def test_tiny_fp32_bit_exact(name, mode):
+    x = wl.tiny()[name]
+    note("quant2d tiny %s %s" % (name, mode))
+    q = _run(x, mode, seed=0, stream=1)
+    ref = orc.quant2d(x, orc.ROUND_SR if mode == "sr" else orc.ROUND_RNE, seed=0, stream=1)
+    assert_planes_equal(q, ref, "tiny %s" % name)
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (7, 45), (33, 65), (77, 45), (100, 300), (300, 100),
+                                   (31, 200), (129, 257), (256, 256), (64, 64), (192, 320)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_shapes(shape, dtype):
+    rng = np.random.default_rng(hash(shape) % 1000)
+    x = (rng.standard_normal(shape) * np.exp(rng.standard_normal((shape[0], 1)))).astype(np.float32)
+    if dtype == "bf16":
+        x = wl.f32_to_bf16_bits(x)
+    for seed, stream, ldp in ((0, 0, 0), (12345678901, 7, 3)):
+        note("quant2d ragged %s %s seed %d ld_pad %d" % (shape, dtype, seed, ldp))
+        q = _run(x, "sr", seed, stream, ld_pad=ldp)
+        assert_planes_equal(q, orc.quant2d(x, orc.ROUND_SR, seed=seed, stream=stream), str(shape))
+    q = _run(x, "rne")
+    assert_planes_equal(q, orc.quant2d(x, orc.ROUND_RNE), "rne %s" % (shape,))
+
+
+def test_special_values():
+    """Zeros, negative zeros, subnormals, blocks whose scale clamps at 2^-127,
+    tiny blocks (k < -109), huge values and exact grid points."""
+    rng = np.random.default_rng(3)
+    x = np.zeros((256, 256), dtype=np.float32)
+    x[:32, :32] = -0.0
+    sub = rng.integers(1, 1 << 23, size=(32, 32)).astype(np.uint32).view(np.float32)
+    x[:32, 32:64] = sub * np.where(rng.random((32, 32)) < 0.5, -1, 1)            # subnormal block
+    x[:32, 64:96] = rng.standard_normal((32, 32)).astype(np.float32) * 1e-33   # k < -109
+    x[32:64, :32] = rng.standard_normal((32, 32)).astype(np.float32) * 3e37    # huge
+    x[32:64, 32:64] = np.float32(6.0) * rng.integers(-1, 2, (32, 32))           # grid
+    x[64:96, 64:96] = np.float32(7.0)
+    x[96:128, 96:128] = rng.standard_normal((32, 32)).astype(np.float32) * 1e-36
+    x[96:128, 96:100] = sub[:, :4]
+    x[128:, :] = rng.standard_normal((128, 256)).astype(np.float32) * np.exp(
+        rng.uniform(-60, 60, (128, 1))).astype(np.float32)
+    x = x.astype(np.float32)
+    for mode, om in (("sr", orc.ROUND_SR), ("rne", orc.ROUND_RNE)):
+        note("quant2d special values fp32 %s" % mode)
+        assert_planes_equal(_run(x, mode, seed=5), orc.quant2d(x, om, seed=5), "special f32 " + mode)
+        xb = wl.f32_to_bf16_bits(x)
+        note("quant2d special values bf16 %s" % mode)
+        assert_planes_equal(_run(xb, mode, seed=5), orc.quant2d(xb, om, seed=5), "special bf16 " + mode)
+
+
+def test_all_bf16_patterns():
+    """Every finite bf16 pattern appears in a tile with a given amax, over a
+    spread of block exponents (each tile's (0,0) entry pins its amax)."""
+    rng = np.random.default_rng(9)
+    pats = np.arange(0x10000, dtype=np.uint32)
+    pats = pats[((pats >> 7) & 0xFF) != 0xFF].astype(np.uint16)    # finite only
+    R, C = 2048, 1024
+    x = np.zeros((R, C), dtype=np.uint16)
+    for tr in range(R // 32):
+        for tc in range(C // 32):
+            e_max = int(rng.integers(1, 255))
+            m = int(rng.integers(0, 128))
+            amax = (e_max << 7) | m
+            blk = rng.choice(pats, size=(32, 32))
+            mag = blk & 0x7FFF
+            blk = np.where(mag > amax, (blk & 0x8000) | (mag % (amax + 1)), blk).astype(np.uint16)
+            blk[0, 0] = amax | (0x8000 if rng.random() < 0.5 else 0)
+            x[32 * tr:32 * tr + 32, 32 * tc:32 * tc + 32] = blk
+    for mode, om in (("sr", orc.ROUND_SR), ("rne", orc.ROUND_RNE)):
+        note("quant2d all-bf16-patterns %s" % mode)
+        assert_planes_equal(_run(x, mode, seed=77, stream=3), orc.quant2d(x, om, seed=77, stream=3),
+                            "patterns " + mode)
+
+
+def test_transposition_invariance_on_gpu():
+    """quant(x^T) computed on the GPU equals the GPU's quant(x) transposed."""
+    L = wl.linear_layer("1b:up", 512, 384, 256, 0)
+    for t in (L.X, L.W, L.dY):
+        note("quant2d invariance %s" % (t.shape,))
+        a = _run(t, "sr", seed=1, stream=2)
+        b = _run(np.ascontiguousarray(t.T), "sr", seed=1, stream=2)
+        torch.cuda.synchronize()
+        assert torch.equal(a.codes, b.codes_t) and torch.equal(a.codes_t, b.codes)
+        assert torch.equal(a.scales, b.scales.T.contiguous())
+
+
+@pytest.mark.parametrize("which", ["X", "W", "dY"])
+def test_1b_full_size(which):
+    """Full 1B up-projection tensors, every element, against the oracle."""
+    L = wl.config_1b()[0]
+    x = getattr(L, which)
+    stream = {"X": 1, "W": 2, "dY": 3}[which]
+    note("quant2d 1B %s %s" % (which, x.shape))
+    q = _run(x, "sr", seed=0, stream=stream)
+    assert_planes_equal(q, orc.quant2d(x, orc.ROUND_SR, seed=0, stream=stream), "1B " + which)
+
+
+def test_7b_sampled_tile_rows():
+    """7B shapes (QKV weight, down-projection input, QKV output gradient):
+    the GPU's full planes against the oracle on sampled bands of tile rows."""
+    rng = np.random.default_rng(21)
+    qkv, down = wl.layer_7b(0), wl.layer_7b(3)
+    for x, stream in ((qkv.W, 2), (down.X, 1), (qkv.dY, 3)):
+        note("quant2d 7B sampled %s" % (x.shape,))
+        q = _run(x, "sr", seed=0, stream=stream)
+        torch.cuda.synchronize()
+        c, ct, s = q.codes.cpu().numpy(), q.codes_t.cpu().numpy(), q.scales.cpu().numpy()
+        ntr = (x.shape[0] + 31) // 32
+        for lo in sorted(set(rng.integers(0, ntr - 1, 6).tolist()) | {0, ntr - 2}):
+            rc, rct, rs = orc.quant2d(x, orc.ROUND_SR, seed=0, stream=stream, tile_rows=(lo, lo + 2))
+            assert np.array_equal(s[lo:lo + 2], rs[lo:lo + 2])
+            assert np.array_equal(c[32 * lo:32 * lo + 64], rc[32 * lo:32 * lo + 64])
+            assert np.array_equal(ct[:, 16 * lo:16 * lo + 32], rct[:, 16 * lo:16 * lo + 32])
+
+
+def test_rows_only_plane_and_dequant():
+    """codes_t may be omitted; dequant of both planes matches the oracle's."""
+    x = wl.tiny()["W"][:96, :160].copy()
+    note("quant2d rows-only + dequant")
+    q1 = fq.fp4q_quant2d(to_dev(x), seed=3, stream_id=4, transposed=False)
+    q2 = fq.fp4q_quant2d(to_dev(x), seed=3, stream_id=4)
+    torch.cuda.synchronize()
+    assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
+    rc, rct, rs = orc.quant2d(x, seed=3, stream=4)
+    ref = orc.dequant_fp4(rc, rs, 96, 160)
+    for dt in (torch.float32, torch.bfloat16):
+        y = fq.fp4q_dequant(q2, out_dtype=dt).float().cpu().numpy()
+        yt = fq.fp4q_dequant(q2, transposed=True, out_dtype=dt).float().cpu().numpy()
+        assert np.array_equal(y, ref) and np.array_equal(yt, ref.T)

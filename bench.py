@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the 2D-block FP4 linear-layer hot path on one MI355X.
+
+A step is one pass of the whole path over the 7B-class layer set
+(T = 8192 tokens, hidden 4096; QKV 4096->12288, O 4096->4096,
+up 4096->11008, down 11008->4096, bf16 inputs):
+  forward : quant2d(X), quant2d(W), Y = X W^T           per layer
+  backward: quant2d(dY), dX = dY W, dW = dY^T X         per layer (reverse order)
+i.e. 12 quantizer launches and 12 MXFP4 GEMMs, each tensor quantized once and
+its transposed plane reused.  Inputs are resident in HBM before timing.
+
+Prints one JSON line: value = GEMM TFLOP/s of the whole step (all GEMM flops
+/ wall time of the step, quantizer time included), with the quantizer's GB/s
+and the GEMMs' own TFLOP/s beside it, the dominant kernel's roofline and the
+CPU oracle timed on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0       # MI355X dense MXFP4 MFMA
+QUANT_BYTES_PER_ELT_BF16 = 2.0 + 0.5 + 0.5   # read bf16, write two nibble planes
+METRIC = "2D-FP4 quant GB/s + fwd/dgrad/wgrad MXFP4 GEMM TFLOP/s, 7B shapes, 1 GPU"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=20.0,
+                   help="approximate CPU seconds for the oracle sample")
+    return p.parse_args()
+
+
+def quant_bytes(rows, cols):
+    """Algorithmic HBM bytes of one quant2d call on a bf16 rows x cols matrix."""
+    R, C = (rows + 31) // 32 * 32, (cols + 31) // 32 * 32
+    return rows * cols * 2 + R * C // 2 * 2 + (R // 32) * (C // 32)
+
+
+class Step:
+    """Device buffers and the launch sequence of one step."""
+
+    def __init__(self, layers, torch, fq):
+        self.torch, self.fq = torch, fq
+        self.layers = []
+        for L in layers:
+            d = {}
+            for nm in ("X", "W", "dY"):
+                a = getattr(L, nm)
+                d[nm] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+                d["q" + nm] = fq.alloc_fp4(a.shape[0], a.shape[1])
+            T, K, N = L.T, L.K, L.N
+            d["Y"] = torch.empty((T, N), dtype=torch.float32, device="cuda")
+            d["dX"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
+            d["dW"] = torch.empty((N, K), dtype=torch.float32, device="cuda")
+            d["shape"] = (T, K, N)
+            d["name"] = L.name
+            self.layers.append(d)
+        self.launches = []   # (kind, name, work) in launch order
+        for i, d in enumerate(self.layers):
+            T, K, N = d["shape"]
+            self.launches += [("quant", d["name"] + ":X", quant_bytes(T, K)),
+                              ("quant", d["name"] + ":W", quant_bytes(N, K)),
+                              ("gemm", d["name"] + ":fwd", 2.0 * T * N * K)]
+        for i, d in reversed(list(enumerate(self.layers))):
+            T, K, N = d["shape"]
+            self.launches += [("quant", d["name"] + ":dY", quant_bytes(T, N)),
+                              ("gemm", d["name"] + ":dgrad", 2.0 * T * N * K),
+                              ("gemm", d["name"] + ":wgrad", 2.0 * T * N * K)]
+
+    def run(self, seed, events=None):
+        """Enqueue one step; with events, record one (start, end) pair per launch."""
+        fq = self.fq
+        ev = iter(events) if events is not None else None
+
+        def timed(fn):
+            if ev is not None:
+                s, e = next(ev)
+                s.record()
+                fn()
+                e.record()
+            else:
+                fn()
+
+        for i, d in enumerate(self.layers):
+            timed(lambda: fq.fp4q_quant2d(d["X"], d["qX"], seed=seed, stream_id=16 * i + 1))
+            timed(lambda: fq.fp4q_quant2d(d["W"], d["qW"], seed=seed, stream_id=16 * i + 2))
+            timed(lambda: fq.fp4q_gemm("fwd", d["qX"], d["qW"], d["Y"]))
+        for i, d in reversed(list(enumerate(self.layers))):
+            timed(lambda: fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3))
+            timed(lambda: fq.fp4q_gemm("dgrad", d["qdY"], d["qW"], d["dX"]))
+            timed(lambda: fq.fp4q_gemm("wgrad", d["qdY"], d["qX"], d["dW"]))
+
+
+def cpu_baseline(layers, budget_s):
+    """The CPU oracle, single-threaded, on a bounded sample of the same step:
+    quant2d of one 32-row band of every quantized tensor, and for every GEMM a
+    32 x 32 block of outputs computed in fp64 over the full contraction from
+    the oracle's own quantization of the bands it needs.  The step time is
+    extrapolated from the measured rates."""
+    import oracle as orc
+    rng = np.random.default_rng(0)
+    tq = eq = 0.0
+    tg = fg = 0.0
+    total_elts = sum(L.X.size + L.W.size + L.dY.size for L in layers)
+    total_flops = sum(3 * 2.0 * L.T * L.N * L.K for L in layers)
+
+    def band(a, r0):
+        t0 = time.perf_counter()
+        c, _, s = orc.quant2d(np.ascontiguousarray(a[r0:r0 + 32]), seed=0, stream=1, threads=1)
+        d = orc.dequant_fp4(c, s, 32, a.shape[1])
+        return d, time.perf_counter() - t0
+
+    deadline = time.perf_counter() + budget_s
+    rounds = 0
+    while rounds == 0 or time.perf_counter() < deadline:
+        for L in layers:
+            T, K, N = L.T, L.K, L.N
+            rt, rn, rk = (int(rng.integers(0, v // 32)) * 32 for v in (T, N, K))
+            x_b, t1 = band(L.X, rt)                 # X rows  [32 x K]
+            w_b, t2 = band(L.W, rn)                 # W rows  [32 x K]
+            dy_b, t3 = band(L.dY, rt)               # dY rows [32 x N]
+            wt_b, t4 = band(np.ascontiguousarray(L.W.T), rk)     # W^T rows = W cols [32 x N]
+            dyt_b, t5 = band(np.ascontiguousarray(L.dY.T), rn)   # dY^T rows [32 x T]
+            xt_b, t6 = band(np.ascontiguousarray(L.X.T), rk)     # X^T rows [32 x T]
+            tq += t1 + t2 + t3 + t4 + t5 + t6
+            eq += 32 * (2 * K + N + N + T + T)
+            for op, a, b in (("fwd", x_b, w_b), ("dgrad", dy_b, np.ascontiguousarray(wt_b.T)),
+                             ("wgrad", np.ascontiguousarray(dyt_b.T), np.ascontiguousarray(xt_b.T))):
+                t0 = time.perf_counter()
+                orc.gemm(op, a, b)
+                tg += time.perf_counter() - t0
+                kk = a.shape[0] if op == "wgrad" else a.shape[1]
+                fg += 2.0 * 32 * 32 * kk
+        rounds += 1
+    t_step = tq * total_elts / eq + tg * total_flops / fg
+    return {
+        "value": total_flops / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": ("%d rounds over the 4 layers: quant2d of 32-row bands (%.1f M elements, %.2f s) "
+                   "and 32x32 fp64 GEMM output blocks over the full K (%.2f GFLOP, %.2f s); "
+                   "step time extrapolated to %.0f s (quant %.2f M elt/s, GEMM %.3f GFLOP/s)"
+                   % (rounds, eq / 1e6, tq, fg / 1e9, tg, t_step, eq / tq / 1e6, fg / tg / 1e9)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp4_microscaling_quantization_quant2d_amd as fq
+    from fp4_microscaling_quantization_quant2d_amd import workloads as wl
+
+    fq.lib()
+    print("[bench] generating 7B layer inputs", file=sys.stderr, flush=True)
+    layers = wl.config_7b()
+    step = Step(layers, torch, fq)
+    torch.cuda.synchronize()
+    print("[bench] warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
+    for w in range(args.warmup):
+        step.run(seed=w)
+    torch.cuda.synchronize()
+
+    n = len(step.launches)
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(args.steps):
+        step.run(seed=1000 + s, events=events[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+
+    per = np.array([[s.elapsed_time(e) for (s, e) in events[k]] for k in range(args.steps)])  # ms
+    kinds = [k for k, _, _ in step.launches]
+    work = np.array([w for _, _, w in step.launches])
+    qmask = np.array([k == "quant" for k in kinds])
+    gmask = ~qmask
+    q_ms = per[:, qmask].sum(axis=1).mean()
+    g_ms = per[:, gmask].sum(axis=1).mean()
+    q_bytes = work[qmask].sum()
+    g_flops = work[gmask].sum()
+    quant_gbps = q_bytes / (q_ms / 1e3) / 1e9
+    gemm_tflops = g_flops / (g_ms / 1e3) / 1e12
+    value = g_flops / (ms_step / 1e3) / 1e12
+    detail = {}
+    for j, (k, nm, w) in enumerate(step.launches):
+        ms = float(np.median(per[:, j]))
+        detail[nm] = {"ms": round(ms, 4),
+                      ("GB/s" if k == "quant" else "TFLOP/s"):
+                          round(w / (ms / 1e3) / (1e9 if k == "quant" else 1e12), 1)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic (seeded numpy PCG64: X~N(0,1) with 0.1% channels x50, W~N(0,0.02), "
+                "dY~N(0,1e-3), bf16)",
+        "config": {"workload": "7b-linear-layer-step",
+                   "tokens": 8192, "hidden": 4096,
+                   "layers": {nm: [K, N] for nm, K, N in wl.LAYERS_7B},
+                   "per_step": "12 quant2d (SR, 32x32 E8M0 tiles, both planes) + 12 MXFP4 GEMMs "
+                               "(fwd/dgrad/wgrad x 4 layers), fp32 outputs",
+                   "wall_s_timed_region": round(wall, 3)},
+        "quant_GBps": round(quant_gbps, 1),
+        "gemm_TFLOPs": round(gemm_tflops, 1),
+        "quant_ms_per_step": round(q_ms, 4),
+        "gemm_ms_per_step": round(g_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "gemm (MXFP4, 12 launches per step)",
+                     "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4), "traffic": None},
+        "roofline_quant": {"bound": "hbm", "kernel": "quant2d (bf16, 12 launches per step)",
+                           "achieved": round(quant_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": round(quant_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "per_launch_median": detail,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -87,5 +87,7 @@ hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int gro
 // Output tile of the GEMM kernel (grouped launches size their grids with it).
 int gemm_tile_m();
 int gemm_tile_n();
+// Dynamic LDS bytes one GEMM workgroup needs for contraction length K.
+size_t gemm_lds_bytes(int fmt, int K);
 
 } // namespace fp4q

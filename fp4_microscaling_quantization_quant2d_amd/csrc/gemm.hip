@@ -16,8 +16,11 @@
 // tile; each wave owns 128x128 = 4x4 tiles of v_mfma_scale_f32_32x32x64_f8f6f4
 // (256 fp32 accumulators per lane).  Each pipeline stage moves 64 bytes of K
 // per row (128 FP4 or 64 FP8 values) for 256 A rows and 256 B rows from HBM
-// into one of two LDS buffers (XOR-swizzled 16-byte chunks, 64 KB total);
-// global loads for stage s+1 are in flight while stage s is multiplied.
+// straight into a 4-slot LDS ring (buffer->LDS loads, XOR-swizzled 16-byte
+// chunks, 128 KB): three stages are in flight while one is multiplied.  The
+// raw buffer range check zero-fills rows and K chunks beyond the operand, so
+// the loop has no branches; the tile's scale bytes for its whole K range sit
+// in LDS and are read as one dword per 32-row slab per stage.
 // Tiles are ordered so each XCD walks a contiguous, M-grouped range of the
 // tile grid, keeping A/B panels resident in that XCD's L2.
 #include "fp4q_launch.hpp"
@@ -30,16 +33,29 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kThreads = 256;
 constexpr int kRowBytes = 64;                       // K bytes per row per stage
 constexpr int kTileBytes = kBM * kRowBytes;         // 16 KB per operand per stage
-constexpr int kLdsBytes = 2 * 2 * kTileBytes;       // 2 operands x 2 buffers
+constexpr int kStages = 4;                          // LDS ring depth
+constexpr int kStageBytes = 2 * kTileBytes;         // A then B
+constexpr int kTileLds = kStages * kStageBytes;     // 128 KB
+constexpr uint32_t kOob = 0x80000000u;              // buffer offset that reads as zero
+constexpr int kDmaPerStage = 8;                     // buffer->LDS loads per wave per stage
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Byte offset of 16-byte chunk c of row r inside a stage tile.  The xor
 // spreads the 32 rows read by one MFMA operand fetch over all LDS banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ ((r >> 1) & 3)) << 4); }
+__device__ __forceinline__ int swz_x(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ swz_x(r)) << 4); }
+
+// Scale bytes kept in LDS for the whole K range of a tile: FP4 stores one
+// byte per (32-row slab, K-block), MXFP8 one per (row, K-block).
+__host__ __device__ __forceinline__ int scale_kb_pad(int kblocks) { return (kblocks + 7) & ~3; }
+__host__ __device__ __forceinline__ int scale_rows(int fmt) { return fmt == 1 ? kBM / 32 : kBM; }
 
 struct Problem {
     const uint8_t* a;
@@ -63,6 +79,32 @@ __device__ __forceinline__ uint32_t scale_at(const uint8_t* s, int64_t lds, int 
     return s[(int64_t)(row >> 5) * lds + kb];
 }
 
+template <int FMT, bool ST>
+__device__ __forceinline__ void preload_scales(uint8_t* dst, const uint8_t* s, int64_t lds, int row0, int rows_ok,
+                                               int kblocks, int kbpad)
+{
+    const int n = scale_rows(FMT) * kbpad;
+    for (int idx = threadIdx.x; idx < n; idx += kThreads) {
+        const int r = idx / kbpad, kb = idx - r * kbpad;
+        const int row = row0 + (FMT == 1 ? 32 * r : r);
+        uint32_t v = 0;
+        if (row < rows_ok && kb < kblocks)
+            v = scale_at<FMT, ST>(s, lds, row, kb);
+        dst[idx] = (uint8_t)v;
+    }
+}
+
+// Wait until at most N buffer->LDS loads of this wave are outstanding, then
+// meet the other waves.  The empty asm statements keep the compiler from
+// moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_and_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    asm volatile("s_barrier" ::: "memory");
+}
+
 template <int FMT, bool A_ST, bool B_ST>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
 {
@@ -73,64 +115,47 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = P.tm * kBM, n0 = P.tn * kBN;
     const int kbytes = FMT == 1 ? P.K / 2 : P.K;    // K bytes per row
-    const int nstages = (kbytes + kRowBytes - 1) / kRowBytes;
+    const int nst = (kbytes + kRowBytes - 1) / kRowBytes;
     const int kblocks = P.K / 32;
+    const int kbpad = scale_kb_pad(kblocks);
+    uint8_t* sla = lds + kTileLds;
+    uint8_t* slb = sla + scale_rows(FMT) * kbpad;
 
-    // global -> register loader: thread owns rows (tid>>2) + 64p, chunk tid&3
-    const int lrow = tid >> 2, lchk = tid & 3;
-    uint4 ra[4], rb[4];
-    auto gload = [&](int s) {
-        const int kb0 = s * kRowBytes + lchk * 16;
+    // Buffer->LDS loads.  One instruction of a wave fills 1 KB of LDS, lane l
+    // at byte 16*l; wave w issues instructions 4w..4w+3 of each operand tile,
+    // so lane l of instruction i lands on tile row r = 16i + l/4, LDS chunk
+    // l%4.  To realize the swizzle the lane fetches global chunk
+    // (l%4) ^ swz_x(r) of that row.  Rows past the operand and chunks past K
+    // read as zero (raw buffer range check), so every stage issues exactly
+    // kDmaPerStage loads per wave and vmcnt counts stay uniform.
+    const __amdgpu_buffer_rsrc_t rA =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P.a, (short)0, (int)((int64_t)P.a_rows * g.lda), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P.b, (short)0, (int)((int64_t)P.b_rows * g.ldb), 0x00020000);
+    uint32_t offA[4], offB[4];
+    int lchunk[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int r = lrow + 64 * p;
-            const int ar = m0 + r, brr = n0 + r;
-            uint4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-            if (ar < P.a_rows && kb0 < kbytes)
-                va = *reinterpret_cast<const uint4*>(P.a + (int64_t)ar * g.lda + kb0);
-            if (brr < P.b_rows && kb0 < kbytes)
-                vb = *reinterpret_cast<const uint4*>(P.b + (int64_t)brr * g.ldb + kb0);
-            ra[p] = va;
-            rb[p] = vb;
+    for (int q = 0; q < 4; ++q) {
+        const int r = 16 * (4 * wave + q) + (lane >> 2);
+        const int c = (lane & 3) ^ swz_x(r);
+        lchunk[q] = c;
+        const int ar = m0 + r, br = n0 + r;
+        offA[q] = ar < P.a_rows ? (uint32_t)(ar * g.lda + c * 16) : kOob;
+        offB[q] = br < P.b_rows ? (uint32_t)(br * g.ldb + c * 16) : kOob;
+    }
+    auto issue = [&](int s) {
+        uint8_t* base = lds + (s % kStages) * kStageBytes + (4 * wave) * 1024;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t kfar = (uint32_t)(s * kRowBytes + lchunk[q] * 16 - kbytes) >> 31 ? 0u : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(base + q * 1024), 16,
+                                                     (int)((offA[q] + s * kRowBytes) | kfar), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(base + kTileBytes + q * 1024), 16,
+                                                     (int)((offB[q] + s * kRowBytes) | kfar), 0, 0, 0);
         }
     };
-    auto sstore = [&](int buf) {
-        uint8_t* la = lds + buf * 2 * kTileBytes;
-        uint8_t* lb = la + kTileBytes;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int r = lrow + 64 * p;
-            *reinterpret_cast<uint4*>(la + swz(r, lchk)) = ra[p];
-            *reinterpret_cast<uint4*>(lb + swz(r, lchk)) = rb[p];
-        }
-    };
 
-    // per-lane scale operands: byte j = scale of this lane's row for the
-    // K-block used by MFMA step j of the stage
     const int lrow32 = lane & 31, khalf = lane >> 5;
-    uint32_t sA[4], sB[4], sAn[4], sBn[4];
-    auto sload = [&](int s, uint32_t* oa, uint32_t* ob) {
-        const int steps = FMT == 1 ? 2 : 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ar = m0 + wm * 128 + i * 32 + lrow32;
-            const int br_ = n0 + wn * 128 + i * 32 + lrow32;
-            uint32_t va = 0, vb = 0;
-#pragma unroll
-            for (int j = 0; j < steps; ++j) {
-                const int kb = s * (2 * steps) + 2 * j + khalf;
-                if (kb < kblocks) {
-                    if (ar < P.a_rows)
-                        va |= scale_at<FMT, A_ST>(P.sa, g.lds_a, ar, kb) << (8 * j);
-                    if (br_ < P.b_rows)
-                        vb |= scale_at<FMT, B_ST>(P.sb, g.lds_b, br_, kb) << (8 * j);
-                }
-            }
-            oa[i] = va;
-            ob[i] = vb;
-        }
-    };
-
     v16f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -140,30 +165,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
 
-    gload(0);
-    sload(0, sA, sB);
-    sstore(0);
-    __syncthreads();
-
-    for (int s = 0; s < nstages; ++s) {
-        const bool more = s + 1 < nstages;
-        if (more) {
-            gload(s + 1);
-            sload(s + 1, sAn, sBn);
-        }
-        const uint8_t* la = lds + (s & 1) * 2 * kTileBytes;
+    // One K stage out of its LDS ring slot.  Scale operands: for FP4 lane
+    // half h uses K-blocks 4s+h (byte 0, MFMA step 0) and 4s+2+h (byte 2,
+    // step 1); for MXFP8 the row's K-block 2s+h.
+    auto compute = [&](int s) {
+        const uint8_t* la = lds + (s % kStages) * kStageBytes;
         const uint8_t* lb = la + kTileBytes;
+        uint32_t sA[4], sB[4];
         if (FMT == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sA[i] = *reinterpret_cast<const uint32_t*>(sla + (wm * 4 + i) * kbpad + 4 * s) >> (8 * khalf);
+                sB[i] = *reinterpret_cast<const uint32_t*>(slb + (wn * 4 + i) * kbpad + 4 * s) >> (8 * khalf);
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 v8i fa[4], fb[4];
                 const int chk = 2 * j + khalf;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int ar = wm * 128 + i * 32 + lrow32;
-                    const int br_ = wn * 128 + i * 32 + lrow32;
-                    const uint4 xa = *reinterpret_cast<const uint4*>(la + swz(ar, chk));
-                    const uint4 xb = *reinterpret_cast<const uint4*>(lb + swz(br_, chk));
+                    const v4u xa = *reinterpret_cast<const v4u*>(la + swz(wm * 128 + i * 32 + lrow32, chk));
+                    const v4u xb = *reinterpret_cast<const v4u*>(lb + swz(wn * 128 + i * 32 + lrow32, chk));
                     fa[i] = v8i{(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
                     fb[i] = v8i{(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
                 }
@@ -176,19 +198,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
                                 fa[mi], fb[ni], acc[mi][ni], 4, 4, 0, (int)sA[mi], 0, (int)sB[ni]);
                         else
                             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fa[mi], fb[ni], acc[mi][ni], 4, 4, 1, (int)sA[mi], 1, (int)sB[ni]);
+                                fa[mi], fb[ni], acc[mi][ni], 4, 4, 2, (int)sA[mi], 2, (int)sB[ni]);
                     }
             }
         } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sA[i] = sla[(wm * 128 + i * 32 + lrow32) * kbpad + 2 * s + khalf];
+                sB[i] = slb[(wn * 128 + i * 32 + lrow32) * kbpad + 2 * s + khalf];
+            }
             v8i fa[4], fb[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ar = wm * 128 + i * 32 + lrow32;
-                const int br_ = wn * 128 + i * 32 + lrow32;
-                const uint4 xa0 = *reinterpret_cast<const uint4*>(la + swz(ar, 2 * khalf));
-                const uint4 xa1 = *reinterpret_cast<const uint4*>(la + swz(ar, 2 * khalf + 1));
-                const uint4 xb0 = *reinterpret_cast<const uint4*>(lb + swz(br_, 2 * khalf));
-                const uint4 xb1 = *reinterpret_cast<const uint4*>(lb + swz(br_, 2 * khalf + 1));
+                const int br = wn * 128 + i * 32 + lrow32;
+                const v4u xa0 = *reinterpret_cast<const v4u*>(la + swz(ar, 2 * khalf));
+                const v4u xa1 = *reinterpret_cast<const v4u*>(la + swz(ar, 2 * khalf + 1));
+                const v4u xb0 = *reinterpret_cast<const v4u*>(lb + swz(br, 2 * khalf));
+                const v4u xb1 = *reinterpret_cast<const v4u*>(lb + swz(br, 2 * khalf + 1));
                 fa[i] = v8i{(int)xa0.x, (int)xa0.y, (int)xa0.z, (int)xa0.w,
                             (int)xa1.x, (int)xa1.y, (int)xa1.z, (int)xa1.w};
                 fb[i] = v8i{(int)xb0.x, (int)xb0.y, (int)xb0.z, (int)xb0.w,
@@ -201,17 +228,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
                     acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         fa[mi], fb[ni], acc[mi][ni], 0, 0, 0, (int)sA[mi], 0, (int)sB[ni]);
         }
-        if (more)
-            sstore((s + 1) & 1);
-        __syncthreads();
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sA[i] = sAn[i];
-                sB[i] = sBn[i];
-            }
-        }
+    };
+
+    // Ring pipeline: stages s+1 .. s+3 are in flight while stage s is
+    // multiplied.  At the top of iteration s each wave waits for its own loads
+    // of stage s (2 later stages = 16 loads may stay outstanding), the barrier
+    // publishes stage s and retires stage s-1, whose slot is then refilled
+    // with stage s+3.
+    preload_scales<FMT, A_ST>(sla, P.sa, g.lds_a, m0, P.a_rows, kblocks, kbpad);
+    preload_scales<FMT, B_ST>(slb, P.sb, g.lds_b, n0, P.b_rows, kblocks, kbpad);
+    issue(0);
+    issue(1);
+    issue(2);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        wait_vm_and_barrier<(kStages - 2) * kDmaPerStage>();
+        issue(s + kStages - 1);
+        compute(s);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each 32x32 tile
 #pragma unroll
@@ -324,12 +359,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
     gemm_tile<1, A_ST, B_ST>(g, P);
 }
 
+// Dynamic LDS: two stage buffers plus the tile's scale bytes for its K range.
+size_t lds_bytes(int fmt, int K) { return kTileLds + 2 * (size_t)scale_rows(fmt) * scale_kb_pad(K / 32); }
+
+template <typename F>
+hipError_t allow_lds(F* fn, size_t bytes)
+{
+    if (bytes <= 65536)
+        return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+}
+
 template <int FMT, bool A_ST, bool B_ST>
 hipError_t launch_dense(const GemmArgs& g, int batch, hipStream_t s)
 {
     const int ntm = (g.M + kBM - 1) / kBM, ntn = (g.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST>), dim3(ntm * ntn, batch), dim3(kThreads),
-                       kLdsBytes, s, g);
+    const size_t lb = lds_bytes(FMT, g.K);
+    hipError_t e = allow_lds(gemm_dense_kernel<FMT, A_ST, B_ST>, lb);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST>), dim3(ntm * ntn, batch), dim3(kThreads), lb, s, g);
     return hipGetLastError();
 }
 
@@ -339,8 +389,20 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t s)
     const int ntiles = g.tile_start[g.n_groups];
     if (ntiles == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((gemm_grouped_kernel<OP, A_ST, B_ST>), dim3(ntiles), dim3(kThreads), kLdsBytes,
-                       s, g);
+    // K of a group: FWD the full K, DGRAD the expert width, WGRAD the largest token segment
+    int kmax = g.K;
+    if (OP == kGemmDgrad)
+        kmax = g.group_n;
+    if (OP == kGemmWgrad) {
+        kmax = 32;
+        for (int i = 0; i < g.n_groups; ++i)
+            kmax = max(kmax, g.row_off[i + 1] - g.row_off[i]);
+    }
+    const size_t lb = lds_bytes(1, kmax);
+    hipError_t e = allow_lds(gemm_grouped_kernel<OP, A_ST, B_ST>, lb);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((gemm_grouped_kernel<OP, A_ST, B_ST>), dim3(ntiles), dim3(kThreads), lb, s, g);
     return hipGetLastError();
 }
 
@@ -368,5 +430,6 @@ hipError_t launch_gemm(const GemmArgs& g, int fmt, bool a_st, bool b_st, int gro
 
 int gemm_tile_m() { return kBM; }
 int gemm_tile_n() { return kBN; }
+size_t gemm_lds_bytes(int fmt, int K) { return lds_bytes(fmt, K); }
 
 } // namespace fp4q

@@ -47,14 +47,19 @@ constexpr int kDmaPerStage = 8;                     // buffer->LDS loads per wav
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// Byte offset of 16-byte chunk c of row r inside a stage tile.  The xor
-// spreads the 32 rows read by one MFMA operand fetch over all LDS banks.
-__device__ __forceinline__ int swz_x(int r) { return (r >> 1) & 3; }
+// Byte offset of 16-byte chunk c of row r inside a stage tile (64-byte
+// rows).  The xor key makes any 8 consecutive rows hit 8 distinct 16-byte
+// bank groups of a 128-byte window and any 16 consecutive rows 16 distinct
+// groups of a 256-byte window, so an MFMA operand fetch (one chunk of 32
+// consecutive rows) is conflict-free with 32 or 64 LDS banks.
+__device__ __forceinline__ int swz_x(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ swz_x(r)) << 4); }
 
 // Scale bytes kept in LDS for the whole K range of a tile: FP4 stores one
-// byte per (32-row slab, K-block), MXFP8 one per (row, K-block).
-__host__ __device__ __forceinline__ int scale_kb_pad(int kblocks) { return (kblocks + 7) & ~3; }
+// byte per (32-row slab, K-block), MXFP8 one per (row, K-block).  Rows are
+// padded so the reads for the two stages prefetched past the end of K stay
+// inside the row.
+__host__ __device__ __forceinline__ int scale_kb_pad(int kblocks) { return ((kblocks + 3) & ~3) + 12; }
 __host__ __device__ __forceinline__ int scale_rows(int fmt) { return fmt == 1 ? kBM / 32 : kBM; }
 
 struct Problem {
@@ -79,18 +84,49 @@ __device__ __forceinline__ uint32_t scale_at(const uint8_t* s, int64_t lds, int 
     return s[(int64_t)(row >> 5) * lds + kb];
 }
 
+// Copy the tile's scale bytes for its whole K range into LDS, [slab or
+// row][K-block].  Each thread issues 16 independent byte loads per operand
+// before it stores any; the first pass (4 KB per operand, enough for K up to
+// 16K with FP4) sits outside any loop so its loads overlap the tile loads
+// already in flight.
 template <int FMT, bool ST>
-__device__ __forceinline__ void preload_scales(uint8_t* dst, const uint8_t* s, int64_t lds, int row0, int rows_ok,
-                                               int kblocks, int kbpad)
+__device__ __forceinline__ void scale_pass_load(uint32_t (&v)[16], const uint8_t* s, int64_t lds, int row0,
+                                                int rows_ok, int kblocks, int kbpad, int n, int base)
 {
-    const int n = scale_rows(FMT) * kbpad;
-    for (int idx = threadIdx.x; idx < n; idx += kThreads) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int idx = base + u * kThreads + (int)threadIdx.x;
         const int r = idx / kbpad, kb = idx - r * kbpad;
         const int row = row0 + (FMT == 1 ? 32 * r : r);
-        uint32_t v = 0;
-        if (row < rows_ok && kb < kblocks)
-            v = scale_at<FMT, ST>(s, lds, row, kb);
-        dst[idx] = (uint8_t)v;
+        v[u] = (idx < n && row < rows_ok && kb < kblocks) ? scale_at<FMT, ST>(s, lds, row, kb) : 0u;
+    }
+}
+
+__device__ __forceinline__ void scale_pass_store(const uint32_t (&v)[16], uint8_t* dst, int n, int base)
+{
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int idx = base + u * kThreads + (int)threadIdx.x;
+        if (idx < n)
+            dst[idx] = (uint8_t)v[u];
+    }
+}
+
+template <int FMT, bool A_ST, bool B_ST>
+__device__ __forceinline__ void preload_scales(const GemmArgs& g, const Problem& P, uint8_t* sla, uint8_t* slb,
+                                               int m0, int n0, int kblocks, int kbpad)
+{
+    const int n = scale_rows(FMT) * kbpad;
+    uint32_t va[16], vb[16];
+    scale_pass_load<FMT, A_ST>(va, P.sa, g.lds_a, m0, P.a_rows, kblocks, kbpad, n, 0);
+    scale_pass_load<FMT, B_ST>(vb, P.sb, g.lds_b, n0, P.b_rows, kblocks, kbpad, n, 0);
+    scale_pass_store(va, sla, n, 0);
+    scale_pass_store(vb, slb, n, 0);
+    for (int base = 16 * kThreads; base < n; base += 16 * kThreads) {
+        scale_pass_load<FMT, A_ST>(va, P.sa, g.lds_a, m0, P.a_rows, kblocks, kbpad, n, base);
+        scale_pass_load<FMT, B_ST>(vb, P.sb, g.lds_b, n0, P.b_rows, kblocks, kbpad, n, base);
+        scale_pass_store(va, sla, n, base);
+        scale_pass_store(vb, slb, n, base);
     }
 }
 
@@ -165,87 +201,105 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
 
-    // One K stage out of its LDS ring slot.  Scale operands: for FP4 lane
-    // half h uses K-blocks 4s+h (byte 0, MFMA step 0) and 4s+2+h (byte 2,
-    // step 1); for MXFP8 the row's K-block 2s+h.
-    auto compute = [&](int s) {
+    // Operands of one K stage in registers.  FP4: A/B fragments of both
+    // MFMA steps (16 x 16 bytes) and per-slab scale dwords; for lane half h
+    // byte 0 holds K-block 4s+h (step 0) and byte 2 K-block 4s+2+h (step 1).
+    // MXFP8: one MFMA step of 32-byte fragments and the row's K-block 2s+h.
+    struct Frag {
+        v4u a[2][4], b[2][4];
+        uint32_t sa[4], sb[4];
+    };
+    auto load_frags = [&](int s, Frag& F) {
         const uint8_t* la = lds + (s % kStages) * kStageBytes;
         const uint8_t* lb = la + kTileBytes;
-        uint32_t sA[4], sB[4];
         if (FMT == 1) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sA[i] = *reinterpret_cast<const uint32_t*>(sla + (wm * 4 + i) * kbpad + 4 * s) >> (8 * khalf);
-                sB[i] = *reinterpret_cast<const uint32_t*>(slb + (wn * 4 + i) * kbpad + 4 * s) >> (8 * khalf);
+                F.sa[i] = *reinterpret_cast<const uint32_t*>(sla + (wm * 4 + i) * kbpad + 4 * s) >> (8 * khalf);
+                F.sb[i] = *reinterpret_cast<const uint32_t*>(slb + (wn * 4 + i) * kbpad + 4 * s) >> (8 * khalf);
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                v8i fa[4], fb[4];
-                const int chk = 2 * j + khalf;
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const v4u xa = *reinterpret_cast<const v4u*>(la + swz(wm * 128 + i * 32 + lrow32, chk));
-                    const v4u xb = *reinterpret_cast<const v4u*>(lb + swz(wn * 128 + i * 32 + lrow32, chk));
-                    fa[i] = v8i{(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
-                    fb[i] = v8i{(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
+                    F.a[j][i] = *reinterpret_cast<const v4u*>(la + swz(wm * 128 + i * 32 + lrow32, 2 * j + khalf));
+                    F.b[j][i] = *reinterpret_cast<const v4u*>(lb + swz(wn * 128 + i * 32 + lrow32, 2 * j + khalf));
                 }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                F.sa[i] = sla[(wm * 128 + i * 32 + lrow32) * kbpad + 2 * s + khalf];
+                F.sb[i] = slb[(wn * 128 + i * 32 + lrow32) * kbpad + 2 * s + khalf];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    F.a[j][i] = *reinterpret_cast<const v4u*>(la + swz(wm * 128 + i * 32 + lrow32, 2 * khalf + j));
+                    F.b[j][i] = *reinterpret_cast<const v4u*>(lb + swz(wn * 128 + i * 32 + lrow32, 2 * khalf + j));
+                }
+        }
+    };
+    auto mma = [&](const Frag& F) {
+        if (FMT == 1) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni) {
+                        const v4u xa = F.a[j][mi], xb = F.b[j][ni];
+                        const v8i fa = v8i{(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
+                        const v8i fb = v8i{(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
                         if (j == 0)
                             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fa[mi], fb[ni], acc[mi][ni], 4, 4, 0, (int)sA[mi], 0, (int)sB[ni]);
+                                fa, fb, acc[mi][ni], 4, 4, 0, (int)F.sa[mi], 0, (int)F.sb[ni]);
                         else
                             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fa[mi], fb[ni], acc[mi][ni], 4, 4, 2, (int)sA[mi], 2, (int)sB[ni]);
+                                fa, fb, acc[mi][ni], 4, 4, 2, (int)F.sa[mi], 2, (int)F.sb[ni]);
                     }
-            }
         } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sA[i] = sla[(wm * 128 + i * 32 + lrow32) * kbpad + 2 * s + khalf];
-                sB[i] = slb[(wn * 128 + i * 32 + lrow32) * kbpad + 2 * s + khalf];
-            }
-            v8i fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ar = wm * 128 + i * 32 + lrow32;
-                const int br = wn * 128 + i * 32 + lrow32;
-                const v4u xa0 = *reinterpret_cast<const v4u*>(la + swz(ar, 2 * khalf));
-                const v4u xa1 = *reinterpret_cast<const v4u*>(la + swz(ar, 2 * khalf + 1));
-                const v4u xb0 = *reinterpret_cast<const v4u*>(lb + swz(br, 2 * khalf));
-                const v4u xb1 = *reinterpret_cast<const v4u*>(lb + swz(br, 2 * khalf + 1));
-                fa[i] = v8i{(int)xa0.x, (int)xa0.y, (int)xa0.z, (int)xa0.w,
-                            (int)xa1.x, (int)xa1.y, (int)xa1.z, (int)xa1.w};
-                fb[i] = v8i{(int)xb0.x, (int)xb0.y, (int)xb0.z, (int)xb0.w,
-                            (int)xb1.x, (int)xb1.y, (int)xb1.z, (int)xb1.w};
-            }
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
+                for (int ni = 0; ni < 4; ++ni) {
+                    const v4u a0 = F.a[0][mi], a1 = F.a[1][mi], b0 = F.b[0][ni], b1 = F.b[1][ni];
+                    const v8i fa = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                       (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    const v8i fb = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                                       (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
                     acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fa[mi], fb[ni], acc[mi][ni], 0, 0, 0, (int)sA[mi], 0, (int)sB[ni]);
+                        fa, fb, acc[mi][ni], 0, 0, 0, (int)F.sa[mi], 0, (int)F.sb[ni]);
+                }
         }
     };
 
-    // Ring pipeline: stages s+1 .. s+3 are in flight while stage s is
-    // multiplied.  At the top of iteration s each wave waits for its own loads
-    // of stage s (2 later stages = 16 loads may stay outstanding), the barrier
-    // publishes stage s and retires stage s-1, whose slot is then refilled
-    // with stage s+3.
-    preload_scales<FMT, A_ST>(sla, P.sa, g.lds_a, m0, P.a_rows, kblocks, kbpad);
-    preload_scales<FMT, B_ST>(slb, P.sb, g.lds_b, n0, P.b_rows, kblocks, kbpad);
+    // Ring pipeline.  While stage s is multiplied from registers, stage s+1
+    // is read out of LDS into the other register set and stages s+2, s+3 are
+    // in flight from memory.  At the top of each iteration a wave waits for
+    // its own loads of stage s+1 (the 8 loads of stage s+2 may stay
+    // outstanding); the barrier then publishes stage s+1 and guarantees that
+    // every wave has finished reading the slot that stage s+3 refills.
     issue(0);
     issue(1);
     issue(2);
+    preload_scales<FMT, A_ST, B_ST>(g, P, sla, slb, m0, n0, kblocks, kbpad);
     __syncthreads();
-    for (int s = 0; s < nst; ++s) {
-        wait_vm_and_barrier<(kStages - 2) * kDmaPerStage>();
-        issue(s + kStages - 1);
-        compute(s);
+    Frag F0, F1;
+    load_frags(0, F0);
+    int s = 0;
+    for (; s + 1 < nst; s += 2) {
+        wait_vm_and_barrier<kDmaPerStage>();
+        issue(s + 3);
+        load_frags(s + 1, F1);
+        mma(F0);
+        wait_vm_and_barrier<kDmaPerStage>();
+        issue(s + 4);
+        load_frags(s + 2, F0);
+        mma(F1);
     }
+    if (s < nst)
+        mma(F0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each 32x32 tile

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
@@ -41,6 +42,18 @@ int hip_status(hipError_t e, const char* what)
 
 inline int64_t pad32(int64_t n) { return (n + 31) / 32 * 32; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// LDS of one compute unit on gfx950.
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+
+// Largest K (a multiple of 32) whose tile fits in LDS.
+int max_k(int fmt)
+{
+    int k = 32;
+    while (fp4q::gemm_lds_bytes(fmt, k + 32) <= kMaxLdsBytes)
+        k += 32;
+    return k;
+}
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
 int check_fp4_tensor(const fp4q_qtensor* t, const char* name, bool need_t)
@@ -329,6 +342,19 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
             return fail(FP4Q_EINVAL, "fp4q_gemm grouped: too many tiles");
         grouped_op = op;
     }
+    // The tile keeps the scale bytes of its whole K range in LDS.  K of a
+    // group: FWD the full K, DGRAD the expert width, WGRAD its token count.
+    int64_t kmax = K;
+    if (grouped_op == FP4Q_OP_DGRAD)
+        kmax = g.group_n;
+    if (grouped_op == FP4Q_OP_WGRAD) {
+        kmax = 32;
+        for (int i = 0; i < g.n_groups; ++i)
+            kmax = std::max<int64_t>(kmax, g.row_off[i + 1] - g.row_off[i]);
+    }
+    if (fp4q::gemm_lds_bytes(fp8 ? 2 : 1, (int)kmax) > kMaxLdsBytes)
+        return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: K %lld too large for the %s tile (max %d)", (long long)kmax,
+                    fp8 ? "MXFP8" : "FP4", fp8 ? max_k(2) : max_k(1));
     return hip_status(fp4q::launch_gemm(g, fp8 ? 2 : 1, a_st, b_st, grouped_op, (int)a->batch,
                                         static_cast<hipStream_t>(hip_stream)),
                       "fp4q_gemm");

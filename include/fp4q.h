@@ -161,7 +161,12 @@ int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
  *   op WGRAD: a = dY [T x N], b = X [T x K]  ->  C = dY^T X  [N x K]
  * FP4 operands must carry both planes; DGRAD reads W's transposed plane and
  * WGRAD reads the transposed planes of dY and X, so each tensor is quantized
- * once.  MXFP8 operands support FWD only (S = Q K^T).
+ * once.  MXFP8 operands support FWD only (S = Q K^T); every product
+ * a_i*b_j*scale_a*scale_b is formed exactly, so C differs from the exact
+ * sum only by fp32 accumulation rounding, as for FP4.
+ *   K      the tile keeps the scale bytes of its whole K range on chip:
+ *          K (per group for grouped DGRAD / WGRAD) is at most 65152 for
+ *          FP4 and 1664 for MXFP8, else FP4Q_EUNSUPPORTED.
  *   batch  a->batch == b->batch = B runs B independent products; product i
  *          writes C + i*c_bstride (floats).
  *   groups NULL for a dense product; else a grouped (expert) product with

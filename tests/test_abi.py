@@ -104,6 +104,10 @@ def test_gemm_rejects_bad_arguments(fp4q):
     f8 = _desc(fp4q, fmt=2, ld=64)
     assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(f8), c, 64, 0, None, None) == -1  # mixed fmt
     assert L.fp4q_gemm(1, ctypes.byref(f8), ctypes.byref(f8), c, 64, 0, None, None) == -2  # fp8 dgrad
+    # the tile holds the scale bytes of its whole K range in LDS: MXFP8 K is bounded
+    big = _desc(fp4q, fmt=2, cols=4096, ld=4096, ld_s=128)
+    assert L.fp4q_gemm(0, ctypes.byref(big), ctypes.byref(big), c, 64, 0, None, None) == -2
+    assert "too large" in _err(fp4q)
     # grouped: offsets must start at 0 and be multiples of 32
     for offs in ([0, 16, 64], [32, 64], [0, 64, 32], [0, 32, 96]):
         arr = (ctypes.c_int64 * len(offs))(*offs)

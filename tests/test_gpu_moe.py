@@ -1,0 +1,111 @@
+"""GPU parity of the grouped (expert) MXFP4 GEMMs with the oracle: per-expert
+2D quantization of the gathered token buffer (one quant2d call, 32-aligned
+expert segments) and grouped fwd / dgrad / wgrad."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import fp4_microscaling_quantization_quant2d_amd as fq
+from fp4_microscaling_quantization_quant2d_amd import workloads as wl
+from gpu_util import assert_planes_equal, check_gemm_tol, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _band(x, r0, r1, stream):
+    """Oracle dequantization of rows [r0, r1) (32-aligned) of x's 2D quantization."""
+    if r1 <= r0:
+        return np.zeros((0, x.shape[1]))
+    c, _, s = orc.quant2d(x, orc.ROUND_SR, seed=0, stream=stream, tile_rows=(r0 // 32, (r1 + 31) // 32))
+    return orc.dequant_fp4(np.ascontiguousarray(c[r0:r1]), np.ascontiguousarray(s[r0 // 32:(r1 + 31) // 32]),
+                           r1 - r0, x.shape[1])
+
+
+def _small_moe():
+    rng = np.random.default_rng(12)
+    counts = [40, 0, 96, 7, 64, 33]          # an empty expert and ragged ones
+    E, H, F = len(counts), 96, 64
+    padded = [(c + 31) // 32 * 32 for c in counts]
+    off = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+    rows = int(off[-1])
+    X = np.zeros((rows, H), np.float32)
+    dY = np.zeros((rows, F), np.float32)
+    for e, c in enumerate(counts):
+        X[off[e]:off[e] + c] = rng.standard_normal((c, H))
+        dY[off[e]:off[e] + c] = rng.standard_normal((c, F)) * 1e-3
+    W = (rng.standard_normal((E * F, H)) * 0.02).astype(np.float32)
+    bf = wl.f32_to_bf16_bits
+    return E, H, F, off, bf(X), bf(W), bf(dY)
+
+
+def test_grouped_small_all_ops():
+    E, H, F, off, X, W, dY = _small_moe()
+    g = {nm: fq.fp4q_quant2d(to_dev(t), seed=0, stream_id=i + 1) for i, (nm, t) in
+         enumerate((("X", X), ("W", W), ("dY", dY)))}
+    o = {nm: orc.quant2d(t, orc.ROUND_SR, seed=0, stream=i + 1) for i, (nm, t) in
+         enumerate((("X", X), ("W", W), ("dY", dY)))}
+    for nm in g:
+        assert_planes_equal(g[nm], o[nm], "moe-small " + nm)
+    Xd = orc.dequant_fp4(o["X"][0], o["X"][2], *X.shape)
+    Wd = orc.dequant_fp4(o["W"][0], o["W"][2], *W.shape)
+    dYd = orc.dequant_fp4(o["dY"][0], o["dY"][2], *dY.shape)
+    offs = off.tolist()
+    note("moe small grouped fwd/dgrad/wgrad")
+    Y = fq.fp4q_gemm("fwd", g["X"], g["W"], groups=offs).cpu().numpy()
+    dX = fq.fp4q_gemm("dgrad", g["dY"], g["W"], groups=offs).cpu().numpy()
+    dW = fq.fp4q_gemm("wgrad", g["dY"], g["X"], groups=offs).cpu().numpy()
+    assert Y.shape == (off[-1], F) and dX.shape == (off[-1], H) and dW.shape == (E * F, H)
+    for e in range(E):
+        r0, r1 = offs[e], offs[e + 1]
+        We = Wd[e * F:(e + 1) * F]
+        if r1 > r0:
+            ref, b = orc.gemm("fwd", Xd[r0:r1], We)
+            check_gemm_tol(Y[r0:r1], ref, b, "fwd expert %d" % e)
+            ref, b = orc.gemm("dgrad", dYd[r0:r1], We)
+            check_gemm_tol(dX[r0:r1], ref, b, "dgrad expert %d" % e)
+            ref, b = orc.gemm("wgrad", dYd[r0:r1], Xd[r0:r1])
+            check_gemm_tol(dW[e * F:(e + 1) * F], ref, b, "wgrad expert %d" % e)
+        else:
+            assert np.all(dW[e * F:(e + 1) * F] == 0)
+
+
+def test_moe_config_sampled_experts():
+    """30B-class MoE layer (8192 tokens, hidden 2048, 128 experts of 768,
+    top-8): up and down projections, grouped fwd/dgrad/wgrad, checked on a
+    sample of experts (first, last, largest, smallest, random)."""
+    m = wl.config_moe()
+    offs = m.row_off.tolist()
+    E, H, F = m.E, m.H, m.F
+    rng = np.random.default_rng(5)
+    sizes = np.diff(m.row_off)
+    experts = sorted({0, E - 1, int(np.argmax(sizes)), int(np.argmin(sizes))} |
+                     set(rng.integers(0, E, 3).tolist()))
+    for name, X, W, dY, n_out, n_in in (("up", m.X, m.W_up, m.dY, F, H),
+                                        ("down", m.A, m.W_down, m.dY_down, H, F)):
+        note("moe %s quant" % name)
+        g = {"X": fq.fp4q_quant2d(to_dev(X), seed=0, stream_id=1),
+             "W": fq.fp4q_quant2d(to_dev(W), seed=0, stream_id=2),
+             "dY": fq.fp4q_quant2d(to_dev(dY), seed=0, stream_id=3)}
+        note("moe %s grouped gemms" % name)
+        Y = fq.fp4q_gemm("fwd", g["X"], g["W"], groups=offs)
+        dX = fq.fp4q_gemm("dgrad", g["dY"], g["W"], groups=offs)
+        dW = fq.fp4q_gemm("wgrad", g["dY"], g["X"], groups=offs)
+        torch.cuda.synchronize()
+        for e in experts:
+            r0, r1 = offs[e], offs[e + 1]
+            Xe = _band(X, r0, r1, 1)
+            dYe = _band(dY, r0, r1, 3)
+            We = _band(W, e * n_out, (e + 1) * n_out, 2)
+            ci = rng.integers(0, max(1, r1 - r0), 300)
+            for op, got, a, b, (mm, nn), base in (
+                    ("fwd", Y, Xe, We, (r1 - r0, n_out), r0),
+                    ("dgrad", dX, dYe, We, (r1 - r0, n_in), r0),
+                    ("wgrad", dW, dYe, Xe, (n_out, n_in), e * n_out)):
+                if mm == 0:
+                    continue
+                i = rng.integers(0, mm, 400)
+                j = rng.integers(0, nn, 400)
+                ref, bd = orc.gemm_sampled(op, a, b, i, j)
+                gv = got[torch.from_numpy(i + base).cuda(), torch.from_numpy(j).cuda()].cpu().numpy()
+                check_gemm_tol(gv, ref, bd, "moe %s %s expert %d" % (name, op, e))

@@ -1,0 +1,139 @@
+"""GPU parity of the MXFP8 side path (Q/K projections): the 1x32 E4M3
+quantizer bit-exact against the oracle, and the batched block-scaled FP8
+GEMM S = Q K^T within 1e-5 * sum|a||b|; plus the 2D-FP4 O-projection of the
+mixed-precision attention workload."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import fp4_microscaling_quantization_quant2d_amd as fq
+from fp4_microscaling_quantization_quant2d_amd import workloads as wl
+from gpu_util import check_gemm_tol, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_fp8(q, ref, rows):
+    c, s = q.codes.cpu().numpy(), q.scales.cpu().numpy()
+    rc, rs = ref
+    assert np.array_equal(s[:rows], rs), "scales differ at %s" % np.argwhere(s[:rows] != rs)[:5]
+    bad = np.argwhere(c[:rows] != rc)
+    assert bad.size == 0, "codes differ at %s (gpu %s oracle %s)" % (bad[:5].tolist(), c[tuple(bad[0])],
+                                                                      rc[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (5, 70), (33, 100), (64, 128), (7, 32), (300, 257)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mxfp8_quant_bit_exact(shape, dtype):
+    rng = np.random.default_rng(shape[0] * 1000 + shape[1])
+    x = (rng.standard_normal(shape) * np.exp(rng.uniform(-20, 20, (shape[0], 1)))).astype(np.float32)
+    x[0, 0] = 0.0
+    if dtype == "bf16":
+        x = wl.f32_to_bf16_bits(x)
+    note("mxfp8 quant %s %s" % (shape, dtype))
+    q = fq.fp4q_quant1d_mxfp8(to_dev(x))
+    _check_fp8(q, orc.quant1d_mxfp8(x), shape[0])
+
+
+def test_mxfp8_special_values():
+    rng = np.random.default_rng(1)
+    x = np.zeros((8, 128), np.float32)
+    x[0, :32] = 448.0
+    x[0, 32:64] = -448.0 * rng.random(32)
+    x[1, :32] = rng.integers(1, 1 << 23, 32).astype(np.uint32).view(np.float32)     # subnormals
+    x[2, :] = 3e38 * rng.uniform(-1, 1, 128)
+    x[3, :] = 1e-40
+    x[4, :] = -0.0
+    x[5, :] = np.float32(2.0) ** rng.integers(-140, 120, 128)
+    x[6, :] = rng.standard_normal(128) * 1e-30
+    x[7, :] = [(-1) ** i * (i + 0.5) for i in range(128)]
+    for xx in (x, wl.f32_to_bf16_bits(x)):
+        note("mxfp8 special %s" % xx.dtype)
+        _check_fp8(fq.fp4q_quant1d_mxfp8(to_dev(xx)), orc.quant1d_mxfp8(xx), 8)
+
+
+def _batched_fp8(q, B, L, D):
+    """View a [B*L x D] MXFP8 quantization as a batch of B [L x D] matrices."""
+    ld, lds = q.codes.shape[1], q.scales.shape[1]
+    return fq.QTensor(fq.FMT_MXFP8_1D32, L, D, q.codes.view(B, L, ld), q.scales.view(B, L, lds),
+                      batch=B, bstride=L * ld, bstride_s=L * lds)
+
+
+def test_fp8_batched_gemm_small():
+    rng = np.random.default_rng(3)
+    B, L, D = 3, 200, 128
+    Q = wl.f32_to_bf16_bits(rng.standard_normal((B * L, D)).astype(np.float32))
+    K = wl.f32_to_bf16_bits((rng.standard_normal((B * L, D)) * 3).astype(np.float32))
+    note("fp8 batched small")
+    qq = _batched_fp8(fq.fp4q_quant1d_mxfp8(to_dev(Q)), B, L, D)
+    qk = _batched_fp8(fq.fp4q_quant1d_mxfp8(to_dev(K)), B, L, D)
+    S = fq.fp4q_gemm("fwd", qq, qk).cpu().numpy()
+    assert S.shape == (B, L, L)
+    rq, rk = orc.quant1d_mxfp8(Q), orc.quant1d_mxfp8(K)
+    Qd = orc.dequant_mxfp8(rq[0], rq[1], B * L, D)
+    Kd = orc.dequant_mxfp8(rk[0], rk[1], B * L, D)
+    for b in range(B):
+        ref, bd = orc.gemm("fwd", Qd[b * L:(b + 1) * L], Kd[b * L:(b + 1) * L])
+        check_gemm_tol(S[b], ref, bd, "S batch %d" % b)
+
+
+def test_attention_config_sampled():
+    """Q, K [4, 32, 4096, 128] -> MXFP8 -> S = Q K^T for all 128 heads
+    (checked on sampled rows of the quantization and sampled S entries), and
+    the 4096x4096 O-projection at 16384 tokens in 2D FP4."""
+    a = wl.config_attn()
+    B, Hh, L, D = a.Q.shape
+    Qf = a.Q.reshape(B * Hh * L, D)
+    Kf = a.K.reshape(B * Hh * L, D)
+    note("attn mxfp8 quant")
+    qq = fq.fp4q_quant1d_mxfp8(to_dev(Qf))
+    qk = fq.fp4q_quant1d_mxfp8(to_dev(Kf))
+    rng = np.random.default_rng(7)
+    for q, x in ((qq, Qf), (qk, Kf)):
+        r0 = int(rng.integers(0, x.shape[0] - 512))
+        ref = orc.quant1d_mxfp8(np.ascontiguousarray(x[r0:r0 + 512]))
+        c = q.codes[r0:r0 + 512].cpu().numpy()
+        s = q.scales[r0:r0 + 512].cpu().numpy()
+        assert np.array_equal(c, ref[0]) and np.array_equal(s, ref[1])
+    note("attn S = QK^T batched (%d heads)" % (B * Hh))
+    S = fq.fp4q_gemm("fwd", _batched_fp8(qq, B * Hh, L, D), _batched_fp8(qk, B * Hh, L, D))
+    torch.cuda.synchronize()
+    bi = rng.integers(0, B * Hh, 1500)
+    ii = rng.integers(0, L, 1500)
+    jj = rng.integers(0, L, 1500)
+    got = S[torch.from_numpy(bi).cuda(), torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()].cpu().numpy()
+    del S
+    ref = np.empty(len(bi))
+    bnd = np.empty(len(bi))
+    for t, (b, i, j) in enumerate(zip(bi, ii, jj)):
+        qrow = Qf[b * L + i:b * L + i + 1]
+        krow = Kf[b * L + j:b * L + j + 1]
+        rq, rk = orc.quant1d_mxfp8(qrow), orc.quant1d_mxfp8(krow)
+        qd = orc.dequant_mxfp8(rq[0], rq[1], 1, D)
+        kd = orc.dequant_mxfp8(rk[0], rk[1], 1, D)
+        c, bb = orc.gemm("fwd", qd, kd)
+        ref[t], bnd[t] = c[0, 0], bb[0, 0]
+    check_gemm_tol(got, ref, bnd, "attn S")
+
+    L_o = a.o_proj
+    note("attn O-projection quant + gemms")
+    g = {nm: fq.fp4q_quant2d(to_dev(getattr(L_o, nm)), seed=0, stream_id=i + 1)
+         for i, nm in enumerate(("X", "W", "dY"))}
+    o = {nm: orc.quant2d(getattr(L_o, nm), orc.ROUND_SR, seed=0, stream=i + 1)
+         for i, nm in enumerate(("X", "W", "dY"))}
+    for nm in g:
+        torch.cuda.synchronize()
+        assert np.array_equal(g[nm].codes.cpu().numpy(), o[nm][0])
+        assert np.array_equal(g[nm].scales.cpu().numpy(), o[nm][2])
+    deq = {nm: orc.dequant_fp4(o[nm][0], o[nm][2], *getattr(L_o, nm).shape) for nm in g}
+    T, K, N = L_o.T, L_o.K, L_o.N
+    for op, an, bn, (m, n) in (("fwd", "X", "W", (T, N)), ("dgrad", "dY", "W", (T, K)),
+                               ("wgrad", "dY", "X", (N, K))):
+        C = fq.fp4q_gemm(op, g[an], g[bn])
+        i = rng.integers(0, m, 1500)
+        j = rng.integers(0, n, 1500)
+        gv = C[torch.from_numpy(i).cuda(), torch.from_numpy(j).cuda()].cpu().numpy()
+        del C
+        ref, bd = orc.gemm_sampled(op, deq[an], deq[bn], i, j)
+        check_gemm_tol(gv, ref, bd, "O-proj " + op)

@@ -38,7 +38,39 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0,
                    help="approximate CPU seconds for the oracle sample")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="before warmup, run 3 plain device copies of this many MB (untimed); "
+                        "their counter readings calibrate FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_7b_step_pmc.md")
+
+
+def source_sha256(name):
+    import hashlib
+    path = os.path.join(ROOT, "fp4_microscaling_quantization_quant2d_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel_source):
+    """HBM bytes per launch of the kernel built from kernel_source, from the
+    committed counter summary, or None when there is none or the kernel's
+    source has changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    sha, val = None, None
+    for line in open(TRAFFIC_SUMMARY):
+        f = line.split()
+        if len(f) == 3 and f[0] == "source-sha256" and f[1] == kernel_source:
+            sha = f[2]
+        if len(f) == 3 and f[0] == "traffic-bytes-per-launch" and f[1] == kernel_source:
+            val = float(f[2])
+    if sha is None or val is None or sha != source_sha256(kernel_source):
+        return None
+    return val
 
 
 def quant_bytes(rows, cols):
@@ -67,6 +99,11 @@ class Step:
             d["name"] = L.name
             self.layers.append(d)
         self.launches = []   # (kind, name, work) in launch order
+        self.gemm_bytes = 0  # algorithmic HBM bytes of the step's GEMMs: FP4 operands, scales, fp32 C
+        for d in self.layers:
+            T, K, N = d["shape"]
+            for m, n, k in ((T, N, K), (T, K, N), (N, K, T)):
+                self.gemm_bytes += (m * k + n * k) // 2 + (m * k + n * k) // 1024 + 4 * m * n
         for i, d in enumerate(self.layers):
             T, K, N = d["shape"]
             self.launches += [("quant", d["name"] + ":X", quant_bytes(T, K)),
@@ -116,8 +153,9 @@ def cpu_baseline(layers, budget_s):
     total_flops = sum(3 * 2.0 * L.T * L.N * L.K for L in layers)
 
     def band(a, r0):
+        a = np.ascontiguousarray(a[r0:r0 + 32])
         t0 = time.perf_counter()
-        c, _, s = orc.quant2d(np.ascontiguousarray(a[r0:r0 + 32]), seed=0, stream=1, threads=1)
+        c, _, s = orc.quant2d(a, seed=0, stream=1, threads=1)
         d = orc.dequant_fp4(c, s, 32, a.shape[1])
         return d, time.perf_counter() - t0
 
@@ -130,9 +168,9 @@ def cpu_baseline(layers, budget_s):
             x_b, t1 = band(L.X, rt)                 # X rows  [32 x K]
             w_b, t2 = band(L.W, rn)                 # W rows  [32 x K]
             dy_b, t3 = band(L.dY, rt)               # dY rows [32 x N]
-            wt_b, t4 = band(np.ascontiguousarray(L.W.T), rk)     # W^T rows = W cols [32 x N]
-            dyt_b, t5 = band(np.ascontiguousarray(L.dY.T), rn)   # dY^T rows [32 x T]
-            xt_b, t6 = band(np.ascontiguousarray(L.X.T), rk)     # X^T rows [32 x T]
+            wt_b, t4 = band(L.W[:, rk:rk + 32].T, 0)     # W^T rows = W cols [32 x N]
+            dyt_b, t5 = band(L.dY[:, rn:rn + 32].T, 0)   # dY^T rows [32 x T]
+            xt_b, t6 = band(L.X[:, rk:rk + 32].T, 0)     # X^T rows [32 x T]
             tq += t1 + t2 + t3 + t4 + t5 + t6
             eq += 32 * (2 * K + N + N + T + T)
             for op, a, b in (("fwd", x_b, w_b), ("dgrad", dy_b, np.ascontiguousarray(wt_b.T)),
@@ -159,8 +197,8 @@ def cpu_baseline(layers, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import fp4_microscaling_quantization_quant2d_amd as fq
@@ -171,6 +209,13 @@ def main():
     layers = wl.config_7b()
     step = Step(layers, torch, fq)
     torch.cuda.synchronize()
+    if args.copy_calibration_mb > 0:
+        src = torch.ones(args.copy_calibration_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print("[bench] warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
     for w in range(args.warmup):
         step.run(seed=w)
@@ -204,6 +249,16 @@ def main():
     quant_gbps = q_bytes / (q_ms / 1e3) / 1e9
     gemm_tflops = g_flops / (g_ms / 1e3) / 1e12
     value = g_flops / (ms_step / 1e3) / 1e12
+    # per GEMM kernel instantiation (fwd, dgrad, wgrad read different planes)
+    by_op = {}
+    for j, (k, nm, w) in enumerate(step.launches):
+        if k == "gemm":
+            op = nm.split(":")[-1]
+            f, t, c = by_op.get(op, (0.0, 0.0, 0))
+            by_op[op] = (f + w, t + per[:, j].mean(), c + 1)
+    gemm_ops = {op: {"launches_per_step": c, "avg_launch_us": round(t / c * 1e3, 2),
+                     "TFLOP/s": round(f / (t / 1e3) / 1e12, 1)} for op, (f, t, c) in by_op.items()}
+    n_g, n_q = int(gmask.sum()), int(qmask.sum())
     detail = {}
     for j, (k, nm, w) in enumerate(step.launches):
         ms = float(np.median(per[:, j]))
@@ -235,12 +290,20 @@ def main():
         "gemm_TFLOPs": round(gemm_tflops, 1),
         "quant_ms_per_step": round(q_ms, 4),
         "gemm_ms_per_step": round(g_ms, 4),
-        "roofline": {"bound": "mfma", "kernel": "gemm (MXFP4, 12 launches per step)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_dense_kernel (MXFP4; fwd, dgrad, wgrad)",
                      "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4), "traffic": None},
-        "roofline_quant": {"bound": "hbm", "kernel": "quant2d (bf16, 12 launches per step)",
+                     "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("gemm.hip"),
+                     "algorithmic_flops_per_launch": g_flops / n_g,
+                     "avg_launch_us": round(g_ms / n_g * 1e3, 2),
+                     "algorithmic_bytes_per_launch": step.gemm_bytes / n_g},
+        "roofline_quant": {"bound": "hbm", "kernel": "quant2d_kernel (bf16 in, SR)",
                            "achieved": round(quant_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": round(quant_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                           "frac": round(quant_gbps / HBM_PEAK_GBPS, 4),
+                           "traffic": measured_traffic("quant2d.hip"),
+                           "algorithmic_bytes_per_launch": q_bytes / n_q,
+                           "avg_launch_us": round(q_ms / n_q * 1e3, 2)},
+        "gemm_by_op": gemm_ops,
         "per_launch_median": detail,
     }
     if not args.no_cpu_baseline:

@@ -4,7 +4,8 @@
 // Quantization", Sec. 2 / 2.1): E2M1 elements (magnitudes 0, .5, 1, 1.5, 2,
 // 3, 4, 6), E8M0 power-of-two scales, and for the query/key path of Sec. 3.2
 // E4M3FN elements.  These helpers are written for the CDNA4 execution model:
-// 64-wide waves, integer-only scale selection and bit-level element rounding.
+// 64-wide waves, integer-only scale selection, register-level transposes.
+// Element rounding to E2M1 is done by the hardware converters (fp4q_cvt.hpp).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,6 +31,19 @@ struct U4 {
     uint32_t x, y, z, w;
 };
 
+// a ^ b ^ k with k wave-uniform: one gfx950 three-input bit operation
+// (truth table 0x96 = xor of all three) with a scalar operand.
+FP4Q_HD uint32_t xor3_uniform(uint32_t a, uint32_t b, uint32_t k)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+    return r;
+#else
+    return a ^ b ^ k;
+#endif
+}
+
 FP4Q_HD U4 philox10(U4 c, uint32_t k0, uint32_t k1)
 {
 #pragma unroll
@@ -37,9 +51,9 @@ FP4Q_HD U4 philox10(U4 c, uint32_t k0, uint32_t k1)
         const uint64_t p0 = (uint64_t)kPhiloxM0 * c.x;
         const uint64_t p1 = (uint64_t)kPhiloxM1 * c.z;
         U4 n;
-        n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+        n.x = xor3_uniform((uint32_t)(p1 >> 32), c.y, k0);
         n.y = (uint32_t)p1;
-        n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+        n.z = xor3_uniform((uint32_t)(p0 >> 32), c.w, k1);
         n.w = (uint32_t)p0;
         c = n;
         k0 += kPhiloxW0;
@@ -66,6 +80,9 @@ FP4Q_HD int truncfree_exp_e2m1(uint32_t amax_bits)
     return k < -127 ? -127 : k;
 }
 
+FP4Q_HD int imin(int a, int b) { return a < b ? a : b; }
+FP4Q_HD int imax(int a, int b) { return a > b ? a : b; }
+
 FP4Q_HD int truncfree_exp_e4m3(uint32_t amax_bits)
 {
     const int E = (int)(amax_bits >> 23);
@@ -73,61 +90,6 @@ FP4Q_HD int truncfree_exp_e4m3(uint32_t amax_bits)
         return -127;
     const int k = E - 135 + ((amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
     return k < -127 ? -127 : k;
-}
-
-FP4Q_HD int imin(int a, int b) { return a < b ? a : b; }
-FP4Q_HD int imax(int a, int b) { return a > b ? a : b; }
-
-// ---------------------------------------------------------------------------
-// One element -> E2M1 nibble.
-//
-// x32 is the element's fp32 bit pattern (bf16 inputs are shifted up 16 bits,
-// exactly), k the block exponent.  With v = |x| * 2^-k (v <= 6), the rounding
-// step of the grid at v is d = 1/2 below 2, 1 in [2, 4), 2 in [4, 6]; the
-// code of the grid point below v is 2*max(e, 0) + floor(v/d) with
-// e = floor(log2 v).  All of it comes from one fixed-point value
-//     T = floor(v/d * 2^16) = m24 >> s,   s = clamp(6 - e, 6, 31),
-// (m24 = 24-bit significand): T >> 16 is floor(v/d) and the low 16 bits are
-// F = floor(frac * 2^16).  Stochastic rounding goes up iff F + r16 >= 2^16,
-// i.e. the carry of T + r16 into bit 16; round-to-nearest-even looks at F,
-// the bits shifted out, and the parity of the lower code.
-//
-// EXACT_SUB normalizes zero/subnormal x32 (needed when k < -109); for k >= -109 any
-// E == 0 element has s >= 24 and the implicit-bit significand shifts out to
-// 0, which is its exact result.
-// ---------------------------------------------------------------------------
-template <int RNE, bool EXACT_SUB>
-FP4Q_HD uint32_t e2m1_nibble(uint32_t x32, uint32_t r16, int c133k, int c127k)
-{
-    const uint32_t a = x32 & 0x7FFFFFFFu;
-    int E = (int)(a >> 23);
-    uint32_t m24 = (a & 0x7FFFFFu) | 0x800000u;
-    if (EXACT_SUB) {
-        if (E == 0) {  // normalize a zero/subnormal input: E may go below 1
-            if (a == 0) {  // T = 0 and no exponent term: code 0
-                m24 = 0;
-                E = 0;
-            } else {
-                const int lz = __builtin_clz(a) - 8;
-                m24 = a << lz;
-                E = 1 - lz;
-            }
-        }
-    }
-    const int s = imin(imax(c133k - E, 6), 31);
-    const uint32_t T = m24 >> s;
-    uint32_t q;
-    if (RNE) {
-        const uint32_t F = T & 0xFFFFu;
-        const uint32_t q0 = T >> 16;
-        const bool rest = (m24 & ((1u << s) - 1u)) != 0u;
-        const bool up = F > 0x8000u || (F == 0x8000u && (rest || (q0 & 1u)));
-        q = q0 + (up ? 1u : 0u);
-    } else {
-        q = (T + r16) >> 16;
-    }
-    const uint32_t code = q + 2u * (uint32_t)imax(E - c127k, 0);
-    return code | ((x32 >> 28) & 8u);
 }
 
 // ---------------------------------------------------------------------------
@@ -175,20 +137,6 @@ FP4Q_HD void nibble_transpose8(uint32_t w[8])
         const uint32_t a = w[i], b = w[i + 1];
         w[i] = bfi_b32(0x0F0F0F0Fu, a, b << 4);
         w[i + 1] = bfi_b32(0x0F0F0F0Fu, a >> 4, b);
-    }
-}
-
-// 8x8 transpose of 16-bit values held as 8 rows x 4 dwords (value j of row i
-// in half j&1 of dword j>>1).
-FP4Q_HD void half_transpose8(const uint32_t w[8][4], uint32_t t[8][4])
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t lo = w[2 * d][i >> 1], hi = w[2 * d + 1][i >> 1];
-            t[i][d] = perm_b32(hi, lo, (i & 1) ? 0x07060302u : 0x05040100u);
-        }
     }
 }
 

@@ -402,7 +402,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each 32x32 tile
+    // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each 32x32 tile.
+    // C is written non-temporally: the fp32 output streams to memory while
+    // the kernel runs instead of staying dirty in the caches for the next
+    // kernel to write back.
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -414,7 +417,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
                 if (row < P.M)
-                    P.c[(int64_t)row * g.ldc + col] = acc[mi][ni][r];
+                    __builtin_nontemporal_store(acc[mi][ni][r], &P.c[(int64_t)row * g.ldc + col]);
             }
         }
     }

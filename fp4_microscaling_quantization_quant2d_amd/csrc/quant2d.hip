@@ -13,17 +13,20 @@
 // A lane loads its block with 16-byte loads (a wave's load instruction reads
 // 8 rows x 128 contiguous bytes), reduces |x| to a tile amax over the 16
 // lanes of its tile with cross-lane xor shuffles, derives the E8M0 byte,
-// draws 8 Philox blocks, rounds its 64 elements and packs them into 8 row
-// words; an in-register nibble transpose gives the 8 column words of the
-// transposed plane, so both planes and the scale grid come from one read.
+// draws 8 Philox blocks and rounds its 64 elements with the hardware FP4
+// converters (scale folded in; one per element for stochastic rounding, one
+// per pair for round-to-nearest-even), which write the nibbles straight into
+// 8 row words; an in-register nibble transpose gives the 8 column words of
+// the transposed plane, so both planes and the scale grid come from one read.
 //
 // Random bits: element (r, c) uses the Philox block keyed by the unordered
 // pair (a, b) = (min, max) and its 16-bit half b%8.  For a block strictly
 // above the diagonal (block row < block col) the 8 elements of one row share
 // a Philox block; below the diagonal the 8 elements of one column do; on a
 // diagonal block element (i, j) uses block min(i, j), half max(i, j).  Waves
-// entirely above or below the diagonal take a uniform branch; only waves on
-// the diagonal select per lane.
+// entirely above or below the diagonal take a uniform branch and index the
+// words directly; only waves on the diagonal rearrange them per lane.
+#include "fp4q_cvt.hpp"
 #include "fp4q_device.hpp"
 #include "fp4q_launch.hpp"
 
@@ -55,110 +58,194 @@ struct Block8x8<true> {
     __device__ __forceinline__ uint32_t x32(int i, int j) const { return v[i][j]; }
 };
 
+// Loads the lane's 8x8 block at (R0, C0).  A block fully inside an aligned
+// input takes 8 (bf16) or 16 (fp32) 16-byte loads off one base pointer; an
+// edge block loads element by element and zero-fills the padding.
 template <bool F32, bool ALIGNED>
 __device__ __forceinline__ void load_block(Block8x8<F32>& blk, const Quant2dArgs& p, int R0, int C0)
 {
-    const int esz = F32 ? 4 : 2;
-    const char* base = static_cast<const char*>(p.x);
+    constexpr int esz = F32 ? 4 : 2;
+    const int64_t stride = p.ldx * esz;
+    const char* row = static_cast<const char*>(p.x) + ((int64_t)R0 * p.ldx + C0) * esz;
+    if (ALIGNED && R0 + 8 <= p.rows && C0 + 8 <= p.cols) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = R0 + i;
-        const char* row = base + ((int64_t)r * p.ldx) * esz;
-        if (r < p.rows && ALIGNED && C0 + 8 <= p.cols) {
-            if (F32) {
-                const uint4 a = *reinterpret_cast<const uint4*>(row + (int64_t)C0 * 4);
-                const uint4 b = *reinterpret_cast<const uint4*>(row + (int64_t)C0 * 4 + 16);
-                uint32_t* dst = &blk.v[i][0];
-                dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
-                dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
-            } else {
-                const uint4 a = *reinterpret_cast<const uint4*>(row + (int64_t)C0 * 2);
-                uint32_t* dst = &blk.v[i][0];
-                dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = C0 + j;
-                uint32_t val = 0;
-                if (r < p.rows && c < p.cols) {
-                    if (F32)
-                        val = reinterpret_cast<const uint32_t*>(row)[c];
-                    else
-                        val = reinterpret_cast<const uint16_t*>(row)[c];
-                }
-                if (F32) {
-                    blk.v[i][j] = val;
-                } else {
-                    uint32_t* dst = &blk.v[i][0];
-                    if (j & 1)
-                        dst[j >> 1] |= val << 16;
-                    else
-                        dst[j >> 1] = val;
-                }
+        for (int i = 0; i < 8; ++i, row += stride) {
+            const uint4 a = *reinterpret_cast<const uint4*>(row);
+            blk.v[i][0] = a.x; blk.v[i][1] = a.y; blk.v[i][2] = a.z; blk.v[i][3] = a.w;
+            if constexpr (F32) {
+                const uint4 b = *reinterpret_cast<const uint4*>(row + 16);
+                blk.v[i][4] = b.x; blk.v[i][5] = b.y; blk.v[i][6] = b.z; blk.v[i][7] = b.w;
             }
         }
+        return;
     }
-}
-
-template <bool F32, int RNE, bool EXACT_SUB>
-__device__ __forceinline__ void round_block(const Block8x8<F32>& blk, const uint32_t rnd[8][4],
-                                            int c133k, int c127k, uint32_t rw[8])
-{
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t w = 0;
+    for (int i = 0; i < 8; ++i, row += stride) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t rd = rnd[i][j >> 1];
-            const uint32_t r16 = (j & 1) ? (rd >> 16) : (rd & 0xFFFFu);
-            w |= e2m1_nibble<RNE, EXACT_SUB>(blk.x32(i, j), r16, c133k, c127k) << (4 * j);
+            const bool in = R0 + i < p.rows && C0 + j < p.cols;
+            if constexpr (F32) {
+                blk.v[i][j] = in ? reinterpret_cast<const uint32_t*>(row)[j] : 0u;
+            } else {
+                const uint32_t val = in ? reinterpret_cast<const uint16_t*>(row)[j] : 0u;
+                if (j & 1)
+                    blk.v[i][j >> 1] |= val << 16;
+                else
+                    blk.v[i][j >> 1] = val;
+            }
         }
-        rw[i] = w;
     }
 }
 
-template <bool F32, int RNE, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dArgs p)
-{
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int nbx = (p.cols_pad + kRegion - 1) / kRegion;
-    const int by = blockIdx.x / nbx;
-    const int bx = blockIdx.x - by * nbx;
-    const int r0w = by * kRegion + (wave >> 1) * 64;
-    const int c0w = bx * kRegion + (wave & 1) * 64;
-    const int br = lane >> 3, bc = lane & 7;
-    const int R0 = r0w + 8 * br;
-    const int C0 = c0w + 8 * bc;
-    const bool active = R0 < p.rows_pad && C0 < p.cols_pad;
+// Stochastic rounding of the lane's 8x8 block to nibbles, one converter per
+// element (seed = its 16 random bits << 16).  The random bits of element
+// (i, j) are half h of word w[a][b] of the lane's 8 Philox blocks:
+//   ROWS   (block above the diagonal):  (a, b, h) = (i, j/2, j%2)
+//   COLS   (block below the diagonal):  (a, b, h) = (j, i/2, i%2)
+//   on the diagonal block:              a = min(i, j), half max(i, j)
+// MIXED waves (those crossing the diagonal) pick among the three per lane.
+// Even columns fill the bytes of a, odd columns those of b, so row word i is
+// a | b << 4.
+enum { kRows = 0, kCols = 1, kMixed = 2 };
 
-    Block8x8<F32> blk;
-    uint32_t mx = 0;
-    if (active) {
-        load_block<F32, ALIGNED>(blk, p, R0, C0);
+__device__ __forceinline__ uint32_t half_seed(uint32_t rd, int h) { return h ? (rd & 0xFFFF0000u) : (rd << 16); }
+
+template <int MODE>
+__device__ __forceinline__ uint32_t seed_of(const uint32_t w[8][4], int i, int j, bool lower, bool diag)
+{
+    const uint32_t up = half_seed(w[i][j >> 1], j & 1);
+    const uint32_t lo = half_seed(w[j][i >> 1], i & 1);
+    if (MODE == kRows)
+        return up;
+    if (MODE == kCols)
+        return lo;
+    const int a = i < j ? i : j, m = i < j ? j : i;
+    const uint32_t dg = half_seed(w[a][m >> 1], m & 1);
+    return diag ? dg : (lower ? lo : up);
+}
+
+template <int SEL, bool F32>
+__device__ __forceinline__ void sr_pair(uint32_t& a, uint32_t& b, const Block8x8<F32>& blk, int i,
+                                        uint32_t seed_even, uint32_t seed_odd, float scale)
+{
+    cvt_sr_byte<SEL>(a, __uint_as_float(blk.x32(i, 2 * SEL)), seed_even, scale);
+    cvt_sr_byte<SEL>(b, __uint_as_float(blk.x32(i, 2 * SEL + 1)), seed_odd, scale);
+}
+
+template <bool F32, int MODE>
+__device__ __forceinline__ void round_sr(const Block8x8<F32>& blk, const uint32_t w[8][4], float scale,
+                                         bool lower, bool diag, uint32_t rw[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t a = 0, b = 0;
+        sr_pair<0>(a, b, blk, i, seed_of<MODE>(w, i, 0, lower, diag), seed_of<MODE>(w, i, 1, lower, diag), scale);
+        sr_pair<1>(a, b, blk, i, seed_of<MODE>(w, i, 2, lower, diag), seed_of<MODE>(w, i, 3, lower, diag), scale);
+        sr_pair<2>(a, b, blk, i, seed_of<MODE>(w, i, 4, lower, diag), seed_of<MODE>(w, i, 5, lower, diag), scale);
+        sr_pair<3>(a, b, blk, i, seed_of<MODE>(w, i, 6, lower, diag), seed_of<MODE>(w, i, 7, lower, diag), scale);
+        rw[i] = a | (b << 4);
+    }
+}
+
+// Round-to-nearest-even: one converter per pair of elements.
+template <bool F32>
+__device__ __forceinline__ void round_rne(const Block8x8<F32>& blk, float scale, uint32_t rw[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t a = 0;
+        if (F32) {
+            cvt_rne_f32_byte<0>(a, __uint_as_float(blk.x32(i, 0)), __uint_as_float(blk.x32(i, 1)), scale);
+            cvt_rne_f32_byte<1>(a, __uint_as_float(blk.x32(i, 2)), __uint_as_float(blk.x32(i, 3)), scale);
+            cvt_rne_f32_byte<2>(a, __uint_as_float(blk.x32(i, 4)), __uint_as_float(blk.x32(i, 5)), scale);
+            cvt_rne_f32_byte<3>(a, __uint_as_float(blk.x32(i, 6)), __uint_as_float(blk.x32(i, 7)), scale);
+        } else {
+            cvt_rne_bf16_byte<0>(a, blk.v[i][0], scale);
+            cvt_rne_bf16_byte<1>(a, blk.v[i][1], scale);
+            cvt_rne_bf16_byte<2>(a, blk.v[i][2], scale);
+            cvt_rne_bf16_byte<3>(a, blk.v[i][3], scale);
+        }
+        rw[i] = a;
+    }
+}
+
+// Largest |x| bit pattern of the lane's block (fp32 bits).
+template <bool F32>
+__device__ __forceinline__ uint32_t block_amax(const Block8x8<F32>& blk)
+{
+    if (F32) {
+        uint32_t mx = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 mx = max(mx, blk.x32(i, j) & 0x7FFFFFFFu);
+        return mx;
     }
+    // bf16: both halves at once with packed 16-bit max over the magnitudes
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, blk.v[i][d] & 0x7FFF7FFFu));
+    return (uint32_t)max(m.x, m.y) << 16;
+}
+
+// Position of a lane's 8x8 block inside region `region` (128x128 per
+// workgroup, 64x64 per wave).
+struct LanePos {
+    int r0w, c0w;   // wave origin
+    int R0, C0;     // block origin
+    bool active;
+};
+
+__device__ __forceinline__ LanePos lane_pos(const Quant2dArgs& p, int region, int nbx)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int by = region / nbx, bx = region - by * nbx;
+    LanePos q;
+    q.r0w = by * kRegion + (wave >> 1) * 64;
+    q.c0w = bx * kRegion + (wave & 1) * 64;
+    q.R0 = q.r0w + 8 * (lane >> 3);
+    q.C0 = q.c0w + 8 * (lane & 7);
+    q.active = q.R0 < p.rows_pad && q.C0 < p.cols_pad;
+    return q;
+}
+
+template <bool F32, bool ALIGNED>
+__device__ __forceinline__ void fetch(Block8x8<F32>& blk, const Quant2dArgs& p, const LanePos& q)
+{
+    if (q.active)
+        load_block<F32, ALIGNED>(blk, p, q.R0, q.C0);
+}
+
+// Scale, random bits, rounding and stores of one lane block whose data is in blk.
+template <bool F32, int RNE>
+__device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dArgs& p, const LanePos& q)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t mx = q.active ? block_amax<F32>(blk) : 0u;
     // Tile amax: the 16 lanes of a 32x32 tile differ in lane bits 0,1,3,4.
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 8));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
-    if (!active)
+    if (!q.active)
         return;
-
     const int k = truncfree_exp_e2m1(mx);
-
-    // Philox blocks: canonical orientation (P0, Q0) with P0 <= Q0 in block units.
-    const int BR = R0 >> 3, BC = C0 >> 3;
-    const int P0 = BR <= BC ? R0 : C0;
-    const int Q0 = BR <= BC ? C0 : R0;
-    uint32_t w[8][4];
-    if (RNE == 0) {
+    const float scale = e8m0_scale(k);
+    const int R0 = q.R0, C0 = q.C0;
+    uint32_t rw[8];
+    if (RNE) {
+        round_rne<F32>(blk, scale, rw);
+    } else {
+        // Philox blocks: canonical orientation (P0, Q0) with P0 <= Q0 in block units.
+        const int BR = R0 >> 3, BC = C0 >> 3;
+        const int P0 = BR <= BC ? R0 : C0;
+        const int Q0 = BR <= BC ? C0 : R0;
+        uint32_t w[8][4];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             U4 c;
@@ -169,61 +256,78 @@ __global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dArgs p)
             const U4 o = philox10(c, p.key0, p.key1);
             w[t][0] = o.x; w[t][1] = o.y; w[t][2] = o.z; w[t][3] = o.w;
         }
-        const int WR = r0w >> 6, WC = c0w >> 6;
-        if (WR > WC) {
-            uint32_t t2[8][4];
-            half_transpose8(w, t2);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int d = 0; d < 4; ++d)
-                    w[i][d] = t2[i][d];
-        } else if (WR == WC) {
-            uint32_t t2[8][4];
-            half_transpose8(w, t2);
-            const bool lower = BR > BC, diag = BR == BC;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    // diagonal block: (i, j) takes row-block min(i,j), half max(i,j)
-                    uint32_t dv;
-                    if (i <= 2 * d)
-                        dv = w[i][d];
-                    else if (i >= 2 * d + 2)
-                        dv = t2[i][d];
-                    else // i == 2d+1: j = 2d from the transpose, j = 2d+1 = i from w
-                        dv = perm_b32(w[i][d], t2[i][d], 0x07060100u);
-                    w[i][d] = lower ? t2[i][d] : (diag ? dv : w[i][d]);
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-                w[t][d] = 0;
+        // Waves strictly above the diagonal draw along rows, strictly below
+        // along columns; a wave crossing the diagonal selects per lane.
+        const int WR = q.r0w >> 6, WC = q.c0w >> 6;
+        if (WR < WC)
+            round_sr<F32, kRows>(blk, w, scale, false, false, rw);
+        else if (WR > WC)
+            round_sr<F32, kCols>(blk, w, scale, true, false, rw);
+        else
+            round_sr<F32, kMixed>(blk, w, scale, BR > BC, BR == BC, rw);
     }
 
-    uint32_t rw[8];
-    const int c133k = 133 + k, c127k = 127 + k;
-    if (k >= -109)
-        round_block<F32, RNE, false>(blk, w, c133k, c127k, rw);
-    else
-        round_block<F32, RNE, true>(blk, w, c133k, c127k, rw);
-
+    uint8_t* dst = p.codes + (int64_t)R0 * p.ld + (C0 >> 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<uint32_t*>(p.codes + (int64_t)(R0 + i) * p.ld + (C0 >> 1)) = rw[i];
+    for (int i = 0; i < 8; ++i, dst += p.ld)
+        *reinterpret_cast<uint32_t*>(dst) = rw[i];
     if (p.codes_t) {
         nibble_transpose8(rw);
+        uint8_t* dt = p.codes_t + (int64_t)C0 * p.ld_t + (R0 >> 1);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<uint32_t*>(p.codes_t + (int64_t)(C0 + j) * p.ld_t + (R0 >> 1)) = rw[j];
+        for (int j = 0; j < 8; ++j, dt += p.ld_t)
+            *reinterpret_cast<uint32_t*>(dt) = rw[j];
     }
-    if (((br | bc) & 3) == 0)
+    if ((lane & 0x1B) == 0)   // block row and column multiples of 4: the tile's first lane
         p.scales[(int64_t)(R0 >> 5) * p.ld_s + (C0 >> 5)] = (uint8_t)(k + 127);
+}
+
+// Persistent workgroups walk the 128x128 regions with a stride of the grid
+// size; the loads of the next region are issued before the current one is
+// processed, so memory latency overlaps the rounding work.
+template <bool F32, int RNE, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dArgs p, int nregions)
+{
+    const int nbx = (p.cols_pad + kRegion - 1) / kRegion;
+    int ra = blockIdx.x;
+    Block8x8<F32> A, B;
+    LanePos qa = lane_pos(p, ra, nbx);
+    fetch<F32, ALIGNED>(A, p, qa);
+    for (;;) {
+        const int rb = ra + gridDim.x;
+        const LanePos qb = lane_pos(p, rb, nbx);
+        if (rb < nregions)
+            fetch<F32, ALIGNED>(B, p, qb);
+        process<F32, RNE>(A, p, qa);
+        if (rb >= nregions)
+            break;
+        ra = rb + gridDim.x;
+        qa = lane_pos(p, ra, nbx);
+        if (ra < nregions)
+            fetch<F32, ALIGNED>(A, p, qa);
+        process<F32, RNE>(B, p, qb);
+        if (ra >= nregions)
+            break;
+    }
+}
+
+// Resident workgroups of one kernel across the device, cached per device.
+template <typename K>
+int resident_groups(K kernel)
+{
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    if (cached[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), kThreads,
+                                                         0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached[dev] = per_cu * cus;
+    }
+    return cached[dev];
 }
 
 template <bool F32, int RNE, bool ALIGNED>
@@ -231,7 +335,12 @@ hipError_t launch_t(const Quant2dArgs& p, hipStream_t s)
 {
     const int nbx = (p.cols_pad + kRegion - 1) / kRegion;
     const int nby = (p.rows_pad + kRegion - 1) / kRegion;
-    hipLaunchKernelGGL((quant2d_kernel<F32, RNE, ALIGNED>), dim3(nbx * nby), dim3(kThreads), 0, s, p);
+    const int nregions = nbx * nby;
+    int grid = resident_groups(quant2d_kernel<F32, RNE, ALIGNED>);
+    if (grid <= 0)
+        return hipErrorInvalidDeviceFunction;
+    grid = grid < nregions ? grid : nregions;
+    hipLaunchKernelGGL((quant2d_kernel<F32, RNE, ALIGNED>), dim3(grid), dim3(kThreads), 0, s, p, nregions);
     return hipGetLastError();
 }
 

@@ -1,13 +1,11 @@
-// Host build of the kernels' per-element and per-lane building blocks
+// Host build of the kernels' per-lane building blocks
 // (fp4q_device.hpp compiles for the host as well), driven by
 // tests/test_device_logic_cpu.py, which checks its output against the
 // oracle.  Reads commands on stdin, one per line:
-//   nib  <x32 hex> <k> <r16> <rne>   -> nibble
 //   exp2 <amax bits hex>             -> E2M1 block exponent
 //   exp8 <amax bits hex>             -> E4M3 block exponent
 //   phx  c0 c1 c2 c3 k0 k1 (hex)     -> Philox4x32-10 output words
 //   ntr  w0..w7 (hex)                -> nibble_transpose8
-//   htr  32 dwords (hex)             -> half_transpose8
 #include "fp4q_device.hpp"
 
 #include <cstdio>
@@ -17,20 +15,7 @@ int main()
 {
     char cmd[16];
     while (std::scanf("%15s", cmd) == 1) {
-        if (!std::strcmp(cmd, "nib")) {
-            unsigned x, r;
-            int k, rne;
-            std::scanf("%x %d %u %d", &x, &k, &r, &rne);
-            unsigned n;
-            const bool exact = k < -109;
-            if (rne)
-                n = exact ? fp4q::e2m1_nibble<1, true>(x, r, 133 + k, 127 + k)
-                          : fp4q::e2m1_nibble<1, false>(x, r, 133 + k, 127 + k);
-            else
-                n = exact ? fp4q::e2m1_nibble<0, true>(x, r, 133 + k, 127 + k)
-                          : fp4q::e2m1_nibble<0, false>(x, r, 133 + k, 127 + k);
-            std::printf("%u\n", n);
-        } else if (!std::strcmp(cmd, "exp2")) {
+        if (!std::strcmp(cmd, "exp2")) {
             unsigned m;
             std::scanf("%x", &m);
             std::printf("%d\n", fp4q::truncfree_exp_e2m1(m));
@@ -52,15 +37,6 @@ int main()
             fp4q::nibble_transpose8(w);
             for (int i = 0; i < 8; ++i)
                 std::printf("%08x%c", w[i], i == 7 ? '\n' : ' ');
-        } else if (!std::strcmp(cmd, "htr")) {
-            uint32_t w[8][4], t[8][4];
-            for (int i = 0; i < 8; ++i)
-                for (int d = 0; d < 4; ++d)
-                    std::scanf("%x", &w[i][d]);
-            fp4q::half_transpose8(w, t);
-            for (int i = 0; i < 8; ++i)
-                for (int d = 0; d < 4; ++d)
-                    std::printf("%08x%c", t[i][d], (i == 7 && d == 3) ? '\n' : ' ');
         }
     }
     return 0;

@@ -1,7 +1,8 @@
 """CPU check of the kernels' building blocks (fp4q_device.hpp built for the
-host): the element rounding, the block exponents, Philox and the in-register
-transposes agree with the oracle and with numpy, exhaustively over bf16
-patterns.  No GPU needed."""
+host): the block exponents, Philox and the in-register transposes agree with
+the oracle and with numpy.  No GPU needed.  (Element rounding runs on the
+hardware converters; the GPU tests pin it against the oracle over every bf16
+pattern and every block exponent.)"""
 import os
 import shutil
 import subprocess
@@ -29,50 +30,6 @@ def harness(tmp_path_factory):
                              check=True).stdout
         return out.strip().splitlines()
     return run
-
-
-def _bf16_patterns():
-    p = np.arange(0x10000, dtype=np.uint32)
-    return p[((p >> 7) & 0xFF) != 0xFF]
-
-
-@pytest.mark.parametrize("rne", [0, 1])
-def test_element_rounding_exhaustive_bf16(orc, harness, rne):
-    rng = np.random.default_rng(1 + rne)
-    pats = _bf16_patterns()
-    x32 = (pats << 16).astype(np.uint32)
-    xf = x32.view(np.float32).astype(np.float64)
-    lines, expect = [], []
-    for k in (-127, -126, -120, -110, -109, -108, -100, -30, -3, 0, 1, 7, 126):
-        ok = np.abs(xf) * 2.0 ** -k <= 6.0
-        for xb, v in zip(x32[ok].tolist(), xf[ok].tolist()):
-            r = int(rng.integers(0, 65536)) if not rne else 0
-            lines.append("nib %x %d %d %d" % (xb, k, r, rne))
-            code = orc.e2m1_round(abs(v) * 2.0 ** -k, orc.ROUND_RNE if rne else orc.ROUND_SR, r)
-            expect.append(code | (8 if xb >> 31 else 0))
-    got = [int(t) for t in harness(lines)]
-    bad = [i for i, (g, e) in enumerate(zip(got, expect)) if g != e]
-    assert not bad, [lines[i] for i in bad[:5]]
-
-
-def test_element_rounding_fp32_and_boundaries(orc, harness):
-    rng = np.random.default_rng(7)
-    lines, expect = [], []
-    for k in (-127, -115, -109, -60, 0, 3, 100):
-        lim = 6.0 * 2.0 ** k
-        xs = np.concatenate([rng.uniform(-1, 1, 3000) * lim,
-                             rng.uniform(-1, 1, 500) * lim * 2.0 ** -rng.integers(1, 40, 500),
-                             rng.integers(1, 1 << 23, 300).astype(np.uint32).view(np.float32)]
-                            ).astype(np.float32)
-        xs = xs[np.abs(xs.astype(np.float64)) * 2.0 ** -k <= 6.0]
-        for x in xs.tolist():
-            xb = int(np.array([x], dtype=np.float32).view(np.uint32)[0])
-            for r in (0, 65535, int(rng.integers(0, 65536))):
-                lines.append("nib %x %d %d 0" % (xb, k, r))
-                expect.append(orc.e2m1_round(abs(x) * 2.0 ** -k, orc.ROUND_SR, r) | (8 if xb >> 31 else 0))
-    got = [int(t) for t in harness(lines)]
-    bad = [i for i, (g, e) in enumerate(zip(got, expect)) if g != e]
-    assert not bad, [lines[i] for i in bad[:5]]
 
 
 def test_block_exponents(orc, harness):
@@ -106,9 +63,3 @@ def test_register_transposes(harness):
         out = [int(t, 16) for t in harness(["ntr " + " ".join("%x" % w for w in words)])[0].split()]
         assert np.array_equal(np.array([[(out[j] >> (4 * i)) & 15 for i in range(8)]
                                         for j in range(8)]), nib.T)
-        h = rng.integers(0, 1 << 16, size=(8, 8), dtype=np.uint32)
-        dw = [(int(h[i, 2 * d]) | (int(h[i, 2 * d + 1]) << 16)) for i in range(8) for d in range(4)]
-        out = [int(t, 16) for t in harness(["htr " + " ".join("%x" % w for w in dw)])[0].split()]
-        ht = np.array([[(out[i * 4 + (j >> 1)] >> (16 * (j & 1))) & 0xFFFF for j in range(8)]
-                       for i in range(8)])
-        assert np.array_equal(ht, h.T)

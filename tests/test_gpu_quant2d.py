@@ -97,6 +97,44 @@ def test_all_bf16_patterns():
                             "patterns " + mode)
 
 
+def _exponent_sweep(dtype):
+    """A 512 x 512 matrix whose 256 tiles pin the block exponents -127..126
+    (each tile's largest magnitude sets its scale) plus one all-zero tile;
+    the other entries mix uniform values, magnitudes spread over 40 binades
+    below the amax, exact E2M1 grid points and midpoints between them."""
+    rng = np.random.default_rng(21)
+    x = np.zeros((512, 512), dtype=np.float64)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for t in range(256):
+        tr, tc = divmod(t, 16)
+        if t == 255:
+            continue                                   # all-zero tile
+        k = t - 127
+        amax = 6.0 * 2.0 ** k if k <= 125 else 2.0 ** 127 * (2 - 2.0 ** -7)   # largest finite bf16
+        n = 1024
+        u = rng.uniform(-1, 1, n)
+        u[:300] = np.sign(u[:300]) * 2.0 ** -rng.uniform(0, 40, 300)
+        v = u * amax
+        pts = np.concatenate([grid, (grid[1:] + grid[:-1]) / 2]) * 2.0 ** k
+        v[300:330] = rng.choice(pts, 30) * rng.choice([-1, 1], 30)
+        v = np.clip(v, -amax, amax)
+        v[0] = amax * (1 if t % 2 else -1)
+        x[32 * tr:32 * tr + 32, 32 * tc:32 * tc + 32] = v.reshape(32, 32)
+    x32 = x.astype(np.float32)
+    return x32 if dtype == "f32" else wl.f32_to_bf16_bits(x32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["sr", "rne"])
+def test_every_block_exponent(dtype, mode):
+    x = _exponent_sweep(dtype)
+    om = orc.ROUND_SR if mode == "sr" else orc.ROUND_RNE
+    note("quant2d block-exponent sweep %s %s" % (dtype, mode))
+    ref = orc.quant2d(x, om, seed=123, stream=9)
+    assert sorted(set(ref[2].reshape(-1).tolist())) == list(range(0, 254)), "sweep must cover every scale byte"
+    assert_planes_equal(_run(x, mode, seed=123, stream=9), ref, "exponent sweep %s %s" % (dtype, mode))
+
+
 def test_transposition_invariance_on_gpu():
     """quant(x^T) computed on the GPU equals the GPU's quant(x) transposed."""
     L = wl.linear_layer("1b:up", 512, 384, 256, 0)

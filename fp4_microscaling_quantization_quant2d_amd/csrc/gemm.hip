@@ -27,6 +27,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 namespace fp4q {
 
 namespace {
@@ -88,48 +92,48 @@ __device__ __forceinline__ uint32_t scale_at(const uint8_t* s, int64_t lds, int 
 }
 
 // Copy the tile's scale bytes for its whole K range into LDS, [slab or
-// row][K-block].  Each thread issues 16 independent byte loads per operand
-// before it stores any; the first pass (4 KB per operand, enough for K up to
-// 16K with FP4) sits outside any loop so its loads overlap the tile loads
-// already in flight.
+// row][K-block], K-blocks kblocks..kbpad-1 zero.  FP4: thread t covers slab
+// t/32 and K-blocks t%32 + 32u; MXFP8: thread t covers row t.  Each thread
+// issues its loads for both operands in batches of 8 before storing any, so
+// they overlap each other and the tile loads already in flight.
 template <int FMT, bool ST>
-__device__ __forceinline__ void scale_pass_load(uint32_t (&v)[16], const uint8_t* s, int64_t lds, int row0,
-                                                int rows_ok, int kblocks, int kbpad, int n, int base)
+__device__ __forceinline__ void scale_batch_load(uint32_t (&v)[8], const uint8_t* s, int64_t lds, int row,
+                                                 bool row_ok, int kb0, int kstep, int kblocks)
 {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int idx = base + u * kThreads + (int)threadIdx.x;
-        const int r = idx / kbpad, kb = idx - r * kbpad;
-        const int row = row0 + (FMT == 1 ? 32 * r : r);
-        v[u] = (idx < n && row < rows_ok && kb < kblocks) ? scale_at<FMT, ST>(s, lds, row, kb) : 0u;
+    for (int u = 0; u < 8; ++u) {
+        const int kb = kb0 + u * kstep;
+        v[u] = (row_ok && kb < kblocks) ? scale_at<FMT, ST>(s, lds, row, kb) : 0u;
     }
 }
 
-__device__ __forceinline__ void scale_pass_store(const uint32_t (&v)[16], uint8_t* dst, int n, int base)
+__device__ __forceinline__ void scale_batch_store(const uint32_t (&v)[8], uint8_t* dst, int kb0, int kstep,
+                                                  int kbpad)
 {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int idx = base + u * kThreads + (int)threadIdx.x;
-        if (idx < n)
-            dst[idx] = (uint8_t)v[u];
-    }
+    for (int u = 0; u < 8; ++u)
+        if (kb0 + u * kstep < kbpad)
+            dst[kb0 + u * kstep] = (uint8_t)v[u];
 }
 
 template <int FMT, bool A_ST, bool B_ST>
 __device__ __forceinline__ void preload_scales(const GemmArgs& g, const Problem& P, uint8_t* sla, uint8_t* slb,
                                                int m0, int n0, int kblocks, int kbpad)
 {
-    const int n = scale_rows(FMT) * kbpad;
-    uint32_t va[16], vb[16];
-    scale_pass_load<FMT, A_ST>(va, P.sa, g.lds_a, m0, P.a_rows, kblocks, kbpad, n, 0);
-    scale_pass_load<FMT, B_ST>(vb, P.sb, g.lds_b, n0, P.b_rows, kblocks, kbpad, n, 0);
-    scale_pass_store(va, sla, n, 0);
-    scale_pass_store(vb, slb, n, 0);
-    for (int base = 16 * kThreads; base < n; base += 16 * kThreads) {
-        scale_pass_load<FMT, A_ST>(va, P.sa, g.lds_a, m0, P.a_rows, kblocks, kbpad, n, base);
-        scale_pass_load<FMT, B_ST>(vb, P.sb, g.lds_b, n0, P.b_rows, kblocks, kbpad, n, base);
-        scale_pass_store(va, sla, n, base);
-        scale_pass_store(vb, slb, n, base);
+    const int t = threadIdx.x;
+    const int r = FMT == 1 ? t >> 5 : t;                  // slab or row of the tile
+    const int kb0 = FMT == 1 ? t & 31 : 0;
+    const int kstep = FMT == 1 ? 32 : 1;
+    const int ra = m0 + (FMT == 1 ? 32 * r : r), rb = n0 + (FMT == 1 ? 32 * r : r);
+    const bool oka = ra < P.a_rows, okb = rb < P.b_rows;
+    uint8_t* da = sla + r * kbpad;
+    uint8_t* db = slb + r * kbpad;
+    for (int k = kb0; k < kbpad; k += 8 * kstep) {
+        uint32_t va[8], vb[8];
+        scale_batch_load<FMT, A_ST>(va, P.sa, g.lds_a, ra, oka, k, kstep, kblocks);
+        scale_batch_load<FMT, B_ST>(vb, P.sb, g.lds_b, rb, okb, k, kstep, kblocks);
+        scale_batch_store(va, da, k, kstep, kbpad);
+        scale_batch_store(vb, db, k, kstep, kbpad);
     }
 }
 
@@ -405,7 +409,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each 32x32 tile.
     // C is written non-temporally: the fp32 output streams to memory while
     // the kernel runs instead of staying dirty in the caches for the next
-    // kernel to write back.
+    // kernel to write back.  Every store instruction covers two full 128-byte
+    // row segments.  Interior tiles address each store as one per-lane base
+    // plus a wave-uniform row offset and a constant column offset.
+    if (m0 + kBM <= P.M && n0 + kBN <= P.N) {
+        float* cb = P.c + (int64_t)(m0 + wm * 128 + 4 * khalf) * g.ldc + (n0 + wn * 128 + lrow32);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float* rp = cb + (int64_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc;
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    __builtin_nontemporal_store(acc[mi][ni][r], rp + ni * 32);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -519,13 +539,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
 // Dynamic LDS: two stage buffers plus the tile's scale bytes for its K range.
 size_t lds_bytes(int fmt, int K) { return kTileLds + 2 * (size_t)scale_rows(fmt) * scale_kb_pad(K / 32); }
 
+// Raises a kernel's dynamic LDS limit to the whole 160 KB of a CU, once per
+// (kernel, device).
+hipError_t allow_lds_raw(const void* fn, size_t bytes)
+{
+    constexpr int kLdsMax = 160 * 1024;
+    if (bytes <= 65536)
+        return hipSuccess;
+    if (bytes > (size_t)kLdsMax)
+        return hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    static std::mutex mu;
+    static std::vector<std::pair<const void*, int>> done;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& d : done)
+        if (d.first == fn && d.second == dev)
+            return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    if (e == hipSuccess)
+        done.emplace_back(fn, dev);
+    return e;
+}
+
 template <typename F>
 hipError_t allow_lds(F* fn, size_t bytes)
 {
-    if (bytes <= 65536)
-        return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)bytes);
+    return allow_lds_raw(reinterpret_cast<const void*>(fn), bytes);
 }
 
 template <int FMT, bool A_ST, bool B_ST>

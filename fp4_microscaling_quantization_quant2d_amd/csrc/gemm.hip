@@ -366,27 +366,33 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
         }
     };
 
-    // Ring pipeline.  Stages 0..2 and the scale bytes are loaded up front.
-    // FP4: while stage s is multiplied from registers, stage s+1 is read out
-    // of LDS into the other register set and stages s+2, s+3 are in flight.
-    // Before each stage a wave waits for its own loads of the stage it is
-    // about to read (the 8 loads of the newest stage may stay outstanding);
-    // the barrier then publishes that stage and guarantees that every wave
-    // has finished reading the slot the next issue refills.
+    // Ring pipeline.  The first stages and the scale bytes are loaded up
+    // front.  FP4: while stage s is multiplied from registers, stage s+1 is
+    // read out of LDS into the other register set and stages s+2..s+4 are in
+    // flight.  Before each stage a wave waits for its own loads of the stage
+    // it is about to read (the loads of the two newest stages may stay
+    // outstanding); the barrier then publishes that stage and guarantees
+    // that every wave has finished reading the slot the next issue refills.
     issue(0);
     issue(1);
     issue(2);
+    if (FMT == 1)
+        issue(3);
     preload_scales<FMT, A_ST, B_ST>(g, P, sla, slb, m0, n0, kblocks, kbpad);
     __syncthreads();
     Frag F0, F1;
     int s = 0;
     if (FMT == 1) {
+        // While stage s is multiplied from registers its own slot is free
+        // (its fragments were read during stage s-1, and every wave has
+        // passed the barrier since), so stage s+4 is loaded into it: three
+        // stages are in flight and stage s+1's loads have two stages to land.
         load_frags(0, F0);
         for (; s + 1 < nst; s += 2) {
-            wait_vm_and_barrier<kDmaPerStage>();
-            stage_fp4(s + 1, s + 3, F0, F1);
-            wait_vm_and_barrier<kDmaPerStage>();
-            stage_fp4(s + 2, s + 4, F1, F0);
+            wait_vm_and_barrier<2 * kDmaPerStage>();
+            stage_fp4(s + 1, s + 4, F0, F1);
+            wait_vm_and_barrier<2 * kDmaPerStage>();
+            stage_fp4(s + 2, s + 5, F1, F0);
         }
         if (s < nst)
             mma(F0);

@@ -116,22 +116,58 @@ __device__ __forceinline__ void scale_batch_store(const uint32_t (&v)[8], uint8_
             dst[kb0 + u * kstep] = (uint8_t)v[u];
 }
 
-template <int FMT, bool A_ST, bool B_ST>
-__device__ __forceinline__ void preload_scales(const GemmArgs& g, const Problem& P, uint8_t* sla, uint8_t* slb,
-                                               int m0, int n0, int kblocks, int kbpad)
+// The tile's scale bytes in registers: thread t covers (FP4) slab t/32 and
+// K-blocks t%32 + 32u, or (MXFP8) row t, for both operands, in up to two
+// batches of 8 loads per operand.  Loading them before the first tile loads
+// are issued lets the LDS stores wait for these loads alone.
+struct ScaleStage {
+    uint32_t va[2][8], vb[2][8];
+};
+
+template <int FMT>
+__device__ __forceinline__ void scale_geometry(int& r, int& kb0, int& kstep)
 {
     const int t = threadIdx.x;
-    const int r = FMT == 1 ? t >> 5 : t;                  // slab or row of the tile
-    const int kb0 = FMT == 1 ? t & 31 : 0;
-    const int kstep = FMT == 1 ? 32 : 1;
+    r = FMT == 1 ? t >> 5 : t;
+    kb0 = FMT == 1 ? t & 31 : 0;
+    kstep = FMT == 1 ? 32 : 1;
+}
+
+template <int FMT, bool A_ST, bool B_ST>
+__device__ __forceinline__ void scales_load(ScaleStage& st, const GemmArgs& g, const Problem& P, int m0, int n0,
+                                            int kblocks, int kbpad)
+{
+    int r, kb0, kstep;
+    scale_geometry<FMT>(r, kb0, kstep);
     const int ra = m0 + (FMT == 1 ? 32 * r : r), rb = n0 + (FMT == 1 ? 32 * r : r);
-    const bool oka = ra < P.a_rows, okb = rb < P.b_rows;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int k = kb0 + b * 8 * kstep;
+        scale_batch_load<FMT, A_ST>(st.va[b], P.sa, g.lds_a, ra, ra < P.a_rows && k < kbpad, k, kstep, kblocks);
+        scale_batch_load<FMT, B_ST>(st.vb[b], P.sb, g.lds_b, rb, rb < P.b_rows && k < kbpad, k, kstep, kblocks);
+    }
+}
+
+// Stores the batches loaded by scales_load, then loads and stores any
+// K-blocks beyond them.
+template <int FMT, bool A_ST, bool B_ST>
+__device__ __forceinline__ void scales_store(const ScaleStage& st, const GemmArgs& g, const Problem& P,
+                                             uint8_t* sla, uint8_t* slb, int m0, int n0, int kblocks, int kbpad)
+{
+    int r, kb0, kstep;
+    scale_geometry<FMT>(r, kb0, kstep);
     uint8_t* da = sla + r * kbpad;
     uint8_t* db = slb + r * kbpad;
-    for (int k = kb0; k < kbpad; k += 8 * kstep) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        scale_batch_store(st.va[b], da, kb0 + b * 8 * kstep, kstep, kbpad);
+        scale_batch_store(st.vb[b], db, kb0 + b * 8 * kstep, kstep, kbpad);
+    }
+    const int ra = m0 + (FMT == 1 ? 32 * r : r), rb = n0 + (FMT == 1 ? 32 * r : r);
+    for (int k = kb0 + 16 * kstep; k < kbpad; k += 8 * kstep) {
         uint32_t va[8], vb[8];
-        scale_batch_load<FMT, A_ST>(va, P.sa, g.lds_a, ra, oka, k, kstep, kblocks);
-        scale_batch_load<FMT, B_ST>(vb, P.sb, g.lds_b, rb, okb, k, kstep, kblocks);
+        scale_batch_load<FMT, A_ST>(va, P.sa, g.lds_a, ra, ra < P.a_rows, k, kstep, kblocks);
+        scale_batch_load<FMT, B_ST>(vb, P.sb, g.lds_b, rb, rb < P.b_rows, k, kstep, kblocks);
         scale_batch_store(va, da, k, kstep, kbpad);
         scale_batch_store(vb, db, k, kstep, kbpad);
     }
@@ -373,13 +409,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // it is about to read (the loads of the two newest stages may stay
     // outstanding); the barrier then publishes that stage and guarantees
     // that every wave has finished reading the slot the next issue refills.
-    issue(0);
-    issue(1);
-    issue(2);
+    {
+        ScaleStage st;
+        scales_load<FMT, A_ST, B_ST>(st, g, P, m0, n0, kblocks, kbpad);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(0);
+        issue(1);
+        issue(2);
+        if (FMT == 1)
+            issue(3);
+        __builtin_amdgcn_sched_barrier(0);
+        scales_store<FMT, A_ST, B_ST>(st, g, P, sla, slb, m0, n0, kblocks, kbpad);
+    }
+    // Stage 0 and the scale bytes must be in LDS; the later stages may still
+    // be in flight.
     if (FMT == 1)
-        issue(3);
-    preload_scales<FMT, A_ST, B_ST>(g, P, sla, slb, m0, n0, kblocks, kbpad);
-    __syncthreads();
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * kDmaPerStage) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kDmaPerStage) : "memory");
     Frag F0, F1;
     int s = 0;
     if (FMT == 1) {

@@ -196,6 +196,7 @@ __device__ __forceinline__ uint32_t block_amax(const Block8x8<F32>& blk)
 // Position of a lane's 8x8 block inside region `region` (128x128 per
 // workgroup, 64x64 per wave).
 struct LanePos {
+    int rr0, cc0;   // region origin
     int r0w, c0w;   // wave origin
     int R0, C0;     // block origin
     bool active;
@@ -206,6 +207,8 @@ __device__ __forceinline__ LanePos lane_pos(const Quant2dArgs& p, int region, in
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int by = region / nbx, bx = region - by * nbx;
     LanePos q;
+    q.rr0 = by * kRegion;
+    q.cc0 = bx * kRegion;
     q.r0w = by * kRegion + (wave >> 1) * 64;
     q.c0w = bx * kRegion + (wave & 1) * 64;
     q.R0 = q.r0w + 8 * (lane >> 3);
@@ -221,73 +224,116 @@ __device__ __forceinline__ void fetch(Block8x8<F32>& blk, const Quant2dArgs& p, 
         load_block<F32, ALIGNED>(blk, p, q.R0, q.C0);
 }
 
-// Scale, random bits, rounding and stores of one lane block whose data is in blk.
+// Output staging in LDS: both planes of a region, 128 rows of 64 bytes each,
+// rows padded to 68 bytes so that the lanes' dword writes hit 64 distinct
+// banks.  Two buffers alternate between consecutive regions.
+constexpr int kStageRow = 68;
+constexpr int kStagePlane = kRegion * kStageRow;
+constexpr int kStageBuf = 2 * kStagePlane;
+
+// Scale, random bits and rounding of one lane block whose data is in blk,
+// then the stores of the workgroup's region.  Every lane reaches the
+// barrier; lanes outside the padded matrix compute nothing and their
+// staging entries are never stored.
 template <bool F32, int RNE>
-__device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dArgs& p, const LanePos& q)
+__device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dArgs& p, const LanePos& q,
+                                        uint8_t* stage)
 {
-    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     uint32_t mx = q.active ? block_amax<F32>(blk) : 0u;
     // Tile amax: the 16 lanes of a 32x32 tile differ in lane bits 0,1,3,4.
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 8));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
-    if (!q.active)
-        return;
-    const int k = truncfree_exp_e2m1(mx);
-    const float scale = e8m0_scale(k);
     const int R0 = q.R0, C0 = q.C0;
-    uint32_t rw[8];
-    if (RNE) {
-        round_rne<F32>(blk, scale, rw);
-    } else {
-        // Philox blocks: canonical orientation (P0, Q0) with P0 <= Q0 in block units.
-        const int BR = R0 >> 3, BC = C0 >> 3;
-        const int P0 = BR <= BC ? R0 : C0;
-        const int Q0 = BR <= BC ? C0 : R0;
-        uint32_t w[8][4];
+    uint32_t rw[8] = {};
+    if (q.active) {
+        const int k = truncfree_exp_e2m1(mx);
+        const float scale = e8m0_scale(k);
+        if (RNE) {
+            round_rne<F32>(blk, scale, rw);
+        } else {
+            // Philox blocks: canonical orientation (P0, Q0) with P0 <= Q0 in block units.
+            const int BR = R0 >> 3, BC = C0 >> 3;
+            const int P0 = BR <= BC ? R0 : C0;
+            const int Q0 = BR <= BC ? C0 : R0;
+            uint32_t w[8][4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            U4 c;
-            c.x = (uint32_t)(((P0 & 31) + t) * 4 + ((Q0 & 31) >> 3));
-            c.y = (uint32_t)(P0 >> 5);
-            c.z = (uint32_t)(Q0 >> 5);
-            c.w = p.stream;
-            const U4 o = philox10(c, p.key0, p.key1);
-            w[t][0] = o.x; w[t][1] = o.y; w[t][2] = o.z; w[t][3] = o.w;
+            for (int t = 0; t < 8; ++t) {
+                U4 c;
+                c.x = (uint32_t)(((P0 & 31) + t) * 4 + ((Q0 & 31) >> 3));
+                c.y = (uint32_t)(P0 >> 5);
+                c.z = (uint32_t)(Q0 >> 5);
+                c.w = p.stream;
+                const U4 o = philox10(c, p.key0, p.key1);
+                w[t][0] = o.x; w[t][1] = o.y; w[t][2] = o.z; w[t][3] = o.w;
+            }
+            // Waves strictly above the diagonal draw along rows, strictly below
+            // along columns; a wave crossing the diagonal selects per lane.
+            const int WR = q.r0w >> 6, WC = q.c0w >> 6;
+            if (WR < WC)
+                round_sr<F32, kRows>(blk, w, scale, false, false, rw);
+            else if (WR > WC)
+                round_sr<F32, kCols>(blk, w, scale, true, false, rw);
+            else
+                round_sr<F32, kMixed>(blk, w, scale, BR > BC, BR == BC, rw);
         }
-        // Waves strictly above the diagonal draw along rows, strictly below
-        // along columns; a wave crossing the diagonal selects per lane.
-        const int WR = q.r0w >> 6, WC = q.c0w >> 6;
-        if (WR < WC)
-            round_sr<F32, kRows>(blk, w, scale, false, false, rw);
-        else if (WR > WC)
-            round_sr<F32, kCols>(blk, w, scale, true, false, rw);
-        else
-            round_sr<F32, kMixed>(blk, w, scale, BR > BC, BR == BC, rw);
+        if ((lane & 0x1B) == 0)   // block row and column multiples of 4: the tile's first lane
+            p.scales[(int64_t)(R0 >> 5) * p.ld_s + (C0 >> 5)] = (uint8_t)(k + 127);
     }
 
-    uint8_t* dst = p.codes + (int64_t)R0 * p.ld + (C0 >> 1);
+    // Stage the row words and (after an in-register nibble transpose) the
+    // column words of the lane's block.
+    const int br = lane >> 3, bc = lane & 7;
+    uint8_t* srow = stage + ((wave >> 1) * 64 + 8 * br) * kStageRow + (wave & 1) * 32 + 4 * bc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i, dst += p.ld)
-        *reinterpret_cast<uint32_t*>(dst) = rw[i];
-    if (p.codes_t) {
+    for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint32_t*>(srow + i * kStageRow) = rw[i];
+    const bool both = p.codes_t != nullptr;
+    if (both) {
         nibble_transpose8(rw);
-        uint8_t* dt = p.codes_t + (int64_t)C0 * p.ld_t + (R0 >> 1);
+        uint8_t* scol = stage + kStagePlane + ((wave & 1) * 64 + 8 * bc) * kStageRow + (wave >> 1) * 32 + 4 * br;
 #pragma unroll
-        for (int j = 0; j < 8; ++j, dt += p.ld_t)
-            *reinterpret_cast<uint32_t*>(dt) = rw[j];
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<uint32_t*>(scol + j * kStageRow) = rw[j];
     }
-    if ((lane & 0x1B) == 0)   // block row and column multiples of 4: the tile's first lane
-        p.scales[(int64_t)(R0 >> 5) * p.ld_s + (C0 >> 5)] = (uint8_t)(k + 127);
+    // LDS writes visible to the workgroup; the prefetch loads in flight are
+    // not waited for.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // Each plane of the region as 512 16-byte pieces: four consecutive
+    // threads write one 64-byte row segment.  A piece spans 32 columns
+    // (row plane) or 32 rows (transposed plane), so it lies wholly inside or
+    // wholly outside the padded matrix.
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int piece = t + kThreads * m;
+        const int row = piece >> 2, seg = piece & 3;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(stage + row * kStageRow + seg * 16);
+        const uint4 v = {src[0], src[1], src[2], src[3]};
+        if (q.rr0 + row < p.rows_pad && q.cc0 + 32 * seg < p.cols_pad)
+            *reinterpret_cast<uint4*>(p.codes + (int64_t)(q.rr0 + row) * p.ld + (q.cc0 >> 1) + 16 * seg) = v;
+        if (both) {
+            const uint32_t* tsrc = reinterpret_cast<const uint32_t*>(stage + kStagePlane + row * kStageRow + seg * 16);
+            const uint4 u = {tsrc[0], tsrc[1], tsrc[2], tsrc[3]};
+            if (q.cc0 + row < p.cols_pad && q.rr0 + 32 * seg < p.rows_pad)
+                *reinterpret_cast<uint4*>(p.codes_t + (int64_t)(q.cc0 + row) * p.ld_t + (q.rr0 >> 1) + 16 * seg) = u;
+        }
+    }
 }
 
 // Persistent workgroups walk the 128x128 regions with a stride of the grid
 // size; the loads of the next region are issued before the current one is
-// processed, so memory latency overlaps the rounding work.
+// processed, so memory latency overlaps the rounding work.  Consecutive
+// regions use the two staging buffers alternately: a buffer is rewritten
+// only after the barrier of the region in between, which every wave reaches
+// after its stores from that buffer.
 template <bool F32, int RNE, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dArgs p, int nregions)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kStageBuf];
     const int nbx = (p.cols_pad + kRegion - 1) / kRegion;
     int ra = blockIdx.x;
     Block8x8<F32> A, B;
@@ -298,14 +344,14 @@ __global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dArgs p, int nr
         const LanePos qb = lane_pos(p, rb, nbx);
         if (rb < nregions)
             fetch<F32, ALIGNED>(B, p, qb);
-        process<F32, RNE>(A, p, qa);
+        process<F32, RNE>(A, p, qa, stage);
         if (rb >= nregions)
             break;
         ra = rb + gridDim.x;
         qa = lane_pos(p, ra, nbx);
         if (ra < nregions)
             fetch<F32, ALIGNED>(A, p, qa);
-        process<F32, RNE>(B, p, qb);
+        process<F32, RNE>(B, p, qb, stage + kStageBuf);
         if (ra >= nregions)
             break;
     }

@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-side-paths", action="store_true",
+                   help="skip the 1B, MoE and attention measurements reported beside the 7B step")
     p.add_argument("--cpu-budget-s", type=float, default=20.0,
                    help="approximate CPU seconds for the oracle sample")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -137,6 +139,151 @@ class Step:
             timed(lambda: fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3))
             timed(lambda: fq.fp4q_gemm("dgrad", d["qdY"], d["qW"], d["dX"]))
             timed(lambda: fq.fp4q_gemm("wgrad", d["qdY"], d["qX"], d["dW"]))
+
+
+def _timed_launches(torch, launches, iters, warmup):
+    """Median ms per launch of a list of (name, fn) run in order; inputs are
+    resident, each launch bracketed by events on the current stream."""
+    for _ in range(warmup):
+        for _, fn in launches:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
+          for _ in range(iters)]
+    for it in range(iters):
+        for (s, e), (_, fn) in zip(ev[it], launches):
+            s.record()
+            fn()
+            e.record()
+    torch.cuda.synchronize()
+    per = np.array([[s.elapsed_time(e) for (s, e) in ev[it]] for it in range(iters)])
+    return {nm: float(np.median(per[:, j])) for j, (nm, _) in enumerate(launches)}
+
+
+def _summary(ms, work, kinds):
+    """Totals over launches of one kind: ms and rate (GB/s for quantizers, TFLOP/s for GEMMs)."""
+    out = {"ms_per_step": round(sum(ms.values()), 4)}
+    for kind, unit, scale in (("quant", "GB/s", 1e9), ("gemm", "TFLOP/s", 1e12)):
+        names = [n for n in ms if kinds[n] == kind]
+        if names:
+            t = sum(ms[n] for n in names)
+            out[kind + "_ms"] = round(t, 4)
+            out[kind + "_" + unit] = round(sum(work[n] for n in names) / (t / 1e3) / scale, 1)
+    return out
+
+
+def side_1b(torch, fq, wl, iters, warmup):
+    """The 1B-class layer step (up 2048->8192 and down 8192->2048 at 4096 tokens)."""
+    step = Step(wl.config_1b(), torch, fq)
+    work = {nm: w for _, nm, w in step.launches}
+    kinds = {nm: kind for kind, nm, _ in step.launches}
+    for it in range(warmup):
+        step.run(seed=it)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in step.launches] for _ in range(iters)]
+    for it in range(iters):
+        step.run(seed=100 + it, events=ev[it])
+    torch.cuda.synchronize()
+    per = np.array([[s.elapsed_time(e) for (s, e) in ev[it]] for it in range(iters)])
+    ms = {nm: float(np.median(per[:, j])) for j, (_, nm, _) in enumerate(step.launches)}
+    out = {"workload": "1b-linear-layer-step: tokens 4096, hidden 2048, FFN 8192 (up, down)"}
+    out.update(_summary(ms, work, kinds))
+    return out
+
+
+def side_moe(torch, fq, wl, iters, warmup):
+    """One step of the 30B-class MoE expert layer: per-expert 2D quantization
+    (one call over the gathered, 32-aligned expert segments) and grouped
+    fwd / dgrad / wgrad for the up and down projections."""
+    m = wl.config_moe()
+    offs = m.row_off.tolist()
+    rows = int(m.row_off[-1])
+    dev = {}
+    for nm in ("X", "W_up", "dY", "A", "W_down", "dY_down"):
+        a = getattr(m, nm)
+        dev[nm] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        dev["q" + nm] = fq.alloc_fp4(a.shape[0], a.shape[1])
+    E, H, F = m.E, m.H, m.F
+    out_t = {"Y_up": torch.empty((rows, F), device="cuda"), "dX_up": torch.empty((rows, H), device="cuda"),
+             "dW_up": torch.empty((E * F, H), device="cuda"), "Y_dn": torch.empty((rows, H), device="cuda"),
+             "dX_dn": torch.empty((rows, F), device="cuda"), "dW_dn": torch.empty((E * H, F), device="cuda")}
+    launches, work, kinds = [], {}, {}
+
+    def q(nm, sid):
+        launches.append(("quant:" + nm, lambda: fq.fp4q_quant2d(dev[nm], dev["q" + nm], seed=0, stream_id=sid)))
+        r, c = dev[nm].shape
+        work["quant:" + nm], kinds["quant:" + nm] = quant_bytes(r, c), "quant"
+
+    def g(op, a, b, c, nm, n_out, k_in):
+        launches.append((nm, lambda: fq.fp4q_gemm(op, dev[a], dev[b], out_t[c], groups=offs)))
+        work[nm], kinds[nm] = 2.0 * rows * n_out * k_in, "gemm"
+
+    q("X", 1); q("W_up", 2); q("dY", 3)
+    g("fwd", "qX", "qW_up", "Y_up", "up:fwd", F, H)
+    g("dgrad", "qdY", "qW_up", "dX_up", "up:dgrad", F, H)
+    g("wgrad", "qdY", "qX", "dW_up", "up:wgrad", F, H)
+    q("A", 4); q("W_down", 5); q("dY_down", 6)
+    g("fwd", "qA", "qW_down", "Y_dn", "down:fwd", H, F)
+    g("dgrad", "qdY_down", "qW_down", "dX_dn", "down:dgrad", H, F)
+    g("wgrad", "qdY_down", "qA", "dW_dn", "down:wgrad", H, F)
+    ms = _timed_launches(torch, launches, iters, warmup)
+    out = {"workload": "30b-moe-expert-layer-step: 8192 tokens, top-8 of 128 experts, hidden 2048, FFN 768; "
+                       "%d gathered rows (32-aligned segments); flops counted on the gathered rows" % rows}
+    out.update(_summary(ms, work, kinds))
+    return out
+
+
+def side_attn(torch, fq, wl, iters, warmup):
+    """MXFP8 attention side path: Q, K [4, 32, 4096, 128] -> 1x32 E4M3, the
+    batched S = Q K^T over the 128 heads (fp32 S, 8.6 GB), and the 2D-FP4
+    O-projection (4096 x 4096 at 16384 tokens, fwd/dgrad/wgrad)."""
+    a = wl.config_attn()
+    B, Hh, L, D = a.Q.shape
+    n = B * Hh * L
+    dev = {nm: torch.from_numpy(getattr(a, nm).reshape(n, D).view(np.int16)).view(torch.bfloat16).cuda()
+           for nm in ("Q", "K")}
+    qq, qk = fq.alloc_mxfp8(n, D), fq.alloc_mxfp8(n, D)
+
+    def batched(qt):
+        ld, lds = qt.codes.shape[1], qt.scales.shape[1]
+        return fq.QTensor(fq.FMT_MXFP8_1D32, L, D, qt.codes.view(B * Hh, L, ld), qt.scales.view(B * Hh, L, lds),
+                          batch=B * Hh, bstride=L * ld, bstride_s=L * lds)
+    bq, bk = batched(qq), batched(qk)
+    S = torch.empty((B * Hh, L, L), device="cuda")
+    o = a.o_proj
+    od = {}
+    for nm in ("X", "W", "dY"):
+        t = getattr(o, nm)
+        od[nm] = torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).cuda()
+        od["q" + nm] = fq.alloc_fp4(t.shape[0], t.shape[1])
+    T, K, N = o.T, o.K, o.N
+    C = {"fwd": torch.empty((T, N), device="cuda"), "dgrad": torch.empty((T, K), device="cuda"),
+         "wgrad": torch.empty((N, K), device="cuda")}
+    launches = [("quant8:Q", lambda: fq.fp4q_quant1d_mxfp8(dev["Q"], qq)),
+                ("quant8:K", lambda: fq.fp4q_quant1d_mxfp8(dev["K"], qk)),
+                ("S=QK^T", lambda: fq.fp4q_gemm("fwd", bq, bk, S)),
+                ("o:quant:X", lambda: fq.fp4q_quant2d(od["X"], od["qX"], seed=0, stream_id=1)),
+                ("o:quant:W", lambda: fq.fp4q_quant2d(od["W"], od["qW"], seed=0, stream_id=2)),
+                ("o:quant:dY", lambda: fq.fp4q_quant2d(od["dY"], od["qdY"], seed=0, stream_id=3)),
+                ("o:fwd", lambda: fq.fp4q_gemm("fwd", od["qX"], od["qW"], C["fwd"])),
+                ("o:dgrad", lambda: fq.fp4q_gemm("dgrad", od["qdY"], od["qW"], C["dgrad"])),
+                ("o:wgrad", lambda: fq.fp4q_gemm("wgrad", od["qdY"], od["qX"], C["wgrad"]))]
+    ms = _timed_launches(torch, launches, iters, warmup)
+    q8 = 2.0 * (n * D * 2 + n * D + n * D // 32) / 1e9
+    s_ms = ms["S=QK^T"]
+    out = {"workload": "attention-mxfp8: Q,K [4,32,4096,128] bf16; S fp32 for 128 heads; "
+                       "O-projection 4096x4096 at 16384 tokens (2D FP4)",
+           "ms_per_step": round(sum(ms.values()), 4),
+           "mxfp8_quant_GB/s": round(q8 / ((ms["quant8:Q"] + ms["quant8:K"]) / 1e3), 1),
+           "S_ms": round(s_ms, 4),
+           "S_TFLOP/s": round(2.0 * B * Hh * L * L * D / (s_ms / 1e3) / 1e12, 1),
+           "S_write_GB/s": round(4.0 * B * Hh * L * L / (s_ms / 1e3) / 1e9, 1),
+           "oproj_gemm_TFLOP/s": round(3 * 2.0 * T * N * K / ((ms["o:fwd"] + ms["o:dgrad"] + ms["o:wgrad"]) / 1e3)
+                                       / 1e12, 1),
+           "oproj_quant_GB/s": round((quant_bytes(T, K) + quant_bytes(N, K) + quant_bytes(T, N))
+                                     / ((ms["o:quant:X"] + ms["o:quant:W"] + ms["o:quant:dY"]) / 1e3) / 1e9, 1)}
+    return out
 
 
 def cpu_baseline(layers, budget_s):
@@ -306,6 +453,13 @@ def main():
         "gemm_by_op": gemm_ops,
         "per_launch_median": detail,
     }
+    if not args.no_side_paths:
+        side = {}
+        for name, fn in (("1b", side_1b), ("moe", side_moe), ("attn", side_attn)):
+            print("[bench] side path %s" % name, file=sys.stderr, flush=True)
+            side[name] = fn(torch, fq, wl, iters=5, warmup=2)
+            torch.cuda.empty_cache()
+        out["side_paths"] = side
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget_s)

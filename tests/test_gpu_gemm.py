@@ -122,3 +122,41 @@ def test_gemm_into_strided_output():
     Ch = C.cpu().numpy()
     check_gemm_tol(Ch[:, :64], ref, bound, "strided")
     assert np.all(Ch[:, 64:] == 7.0)
+
+
+@pytest.mark.parametrize("T,K,N", [(64, 20480, 96), (20480, 64, 96)])
+def test_long_contraction(T, K, N):
+    """Contractions of 20480: fwd over K (first shape) and wgrad over the
+    tokens (second shape) run past the first two batches of preloaded scale
+    bytes."""
+    L = wl.linear_layer("tiny:longk", T, K, N, T + K)
+    _layer_full_check(L.X, L.W, L.dY, "long %dx%dx%d" % (T, K, N))
+
+
+def _batched(q, n_items, rows, rows_t):
+    """View a stacked 2D-FP4 quantization as n_items independent matrices of
+    `rows` rows each; the transposed plane advances rows/2 bytes per item."""
+    ld, lds = q.codes.shape[1], q.scales.shape[1]
+    return fq.QTensor(fq.FMT_FP4_2D32, rows, q.cols, q.codes.view(n_items, rows, ld),
+                      q.scales.view(n_items, rows // 32, lds), q.codes_t, batch=n_items,
+                      bstride=rows * ld, bstride_t=rows // 2, bstride_s=(rows // 32) * lds)
+
+
+def test_batched_fp4_all_ops():
+    """Three independent layers stacked along the token (X, dY) and output
+    (W) dimensions, multiplied as one batched call per op."""
+    B, T, K, N = 3, 96, 160, 64
+    L = wl.linear_layer("tiny:batch", B * T, K, B * N, 5)
+    X, W = L.X, L.W
+    dY = wl.f32_to_bf16_bits(np.random.default_rng(6).standard_normal((B * T, N)).astype(np.float32) * 1e-3)
+    g, o = _quant_all(X, W, dY)
+    Xd, Wd, dYd = _deq(o, "X", X.shape), _deq(o, "W", W.shape), _deq(o, "dY", dY.shape)
+    bx, bw, bdy = _batched(g["X"], B, T, T), _batched(g["W"], B, N, N), _batched(g["dY"], B, T, T)
+    for op, a, b, ra, rb, ma, mb in (("fwd", bx, bw, Xd, Wd, T, N), ("dgrad", bdy, bw, dYd, Wd, T, N),
+                                     ("wgrad", bdy, bx, dYd, Xd, T, T)):
+        note("gemm batched fp4 %s" % op)
+        C = fq.fp4q_gemm(op, a, b).cpu().numpy()
+        assert C.shape[0] == B
+        for i in range(B):
+            ref, bound = orc.gemm(op, ra[i * ma:(i + 1) * ma], rb[i * mb:(i + 1) * mb])
+            check_gemm_tol(C[i], ref, bound, "batched %s item %d" % (op, i))

@@ -78,6 +78,25 @@ def test_fp8_batched_gemm_small():
         check_gemm_tol(S[b], ref, bd, "S batch %d" % b)
 
 
+@pytest.mark.parametrize("D", [32, 96, 256, 512])
+def test_fp8_head_sizes(D):
+    """Contractions of one to sixteen K-blocks, including a partial last
+    stage (96) and several stages (256, 512)."""
+    rng = np.random.default_rng(D)
+    B, L = 2, 72
+    Q = wl.f32_to_bf16_bits((rng.standard_normal((B * L, D)) * 2).astype(np.float32))
+    K = wl.f32_to_bf16_bits(rng.standard_normal((B * L, D)).astype(np.float32))
+    note("fp8 head size %d" % D)
+    S = fq.fp4q_gemm("fwd", _batched_fp8(fq.fp4q_quant1d_mxfp8(to_dev(Q)), B, L, D),
+                     _batched_fp8(fq.fp4q_quant1d_mxfp8(to_dev(K)), B, L, D)).cpu().numpy()
+    rq, rk = orc.quant1d_mxfp8(Q), orc.quant1d_mxfp8(K)
+    Qd = orc.dequant_mxfp8(rq[0], rq[1], B * L, D)
+    Kd = orc.dequant_mxfp8(rk[0], rk[1], B * L, D)
+    for b in range(B):
+        ref, bd = orc.gemm("fwd", Qd[b * L:(b + 1) * L], Kd[b * L:(b + 1) * L])
+        check_gemm_tol(S[b], ref, bd, "D=%d batch %d" % (D, b))
+
+
 def test_attention_config_sampled():
     """Q, K [4, 32, 4096, 128] -> MXFP8 -> S = Q K^T for all 128 heads
     (checked on sampled rows of the quantization and sampled S entries), and

@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time the step as eager launches instead of replays of a captured HIP graph")
     p.add_argument("--no-side-paths", action="store_true",
                    help="skip the 1B, MoE and attention measurements reported beside the 7B step")
     p.add_argument("--cpu-budget-s", type=float, default=20.0,
@@ -385,6 +387,36 @@ def main():
     ms_step = ms_total / args.steps
 
     per = np.array([[s.elapsed_time(e) for (s, e) in events[k]] for k in range(args.steps)])  # ms
+    ms_step_eager = ms_step
+
+    # Whole-step time: the step's launches captured once in a HIP graph (one
+    # fixed seed) and replayed K times between two events, so launch gaps and
+    # the per-launch events above do not count.  Per-kernel rates come from
+    # the eager pass.
+    graph = None
+    if not args.no_graph:
+        print("[bench] capturing the step in a HIP graph", file=sys.stderr, flush=True)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step.run(seed=7)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step.run(seed=7)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_step = g0.elapsed_time(g1) / args.steps
     kinds = [k for k, _, _ in step.launches]
     work = np.array([w for _, _, w in step.launches])
     qmask = np.array([k == "quant" for k in kinds])
@@ -421,6 +453,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager": round(ms_step_eager, 4),
+        "step_timing": "hip-graph replay" if graph is not None else "eager launches",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -278,6 +278,13 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
     }
     g.bs_sa = a->bstride_s;
     g.bs_sb = b->bstride_s;
+    // The kernels address each operand plane through a buffer descriptor with
+    // a 32-bit byte range; a tile may reach one tile height past the last row.
+    {
+        const int64_t reach = fp4q::gemm_tile_m();
+        if ((g.a_rows + reach) * g.lda > INT_MAX || (g.b_rows + reach) * g.ldb > INT_MAX)
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: an operand plane exceeds 2 GiB");
+    }
     g.c = c;
     g.ldc = ldc;
     g.bs_c = c_bstride;

@@ -14,13 +14,15 @@
 //
 // Tiling (CDNA4): a 256-thread workgroup (4 waves, 2x2) computes a 256x256
 // tile; each wave owns 128x128 = 4x4 tiles of v_mfma_scale_f32_32x32x64_f8f6f4
-// (256 fp32 accumulators per lane).  Each pipeline stage moves 64 bytes of K
-// per row (128 FP4 or 64 FP8 values) for 256 A rows and 256 B rows from HBM
-// straight into a 4-slot LDS ring (buffer->LDS loads, XOR-swizzled 16-byte
-// chunks, 128 KB): three stages are in flight while one is multiplied.  The
-// raw buffer range check zero-fills rows and K chunks beyond the operand, so
-// the loop has no branches; the tile's scale bytes for its whole K range sit
-// in LDS and are read as one dword per 32-row slab per stage.
+// (256 fp32 accumulators per lane).  Operands go from HBM straight into LDS
+// with buffer->LDS loads (XOR-swizzled 16-byte chunks, 128 KB of ring):
+//   FP4: two slots of 128 K-bytes per row (256 FP4 values) for 256 A rows and
+//   256 B rows, so every load instruction fills whole cache lines; each slot
+//   is multiplied as two 64-byte half stages while the other slot fills.
+//   MXFP8: four slots of 64 K-bytes per row, three in flight.
+// The raw buffer range check zero-fills rows and K chunks beyond the
+// operand, so the loop has no branches; the tile's scale bytes for its whole
+// K range sit in LDS.
 // Tiles are ordered so each XCD walks a contiguous, M-grouped range of the
 // tile grid, keeping A/B panels resident in that XCD's L2.
 #include "fp4q_launch.hpp"
@@ -28,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -61,6 +64,21 @@ constexpr int kTileCpol = 16;                       // sc1 on the streamed tile 
 // consecutive rows) is conflict-free with 32 or 64 LDS banks.
 __device__ __forceinline__ int swz_x(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ swz_x(r)) << 4); }
+
+// FP4 ring: two slots of 128 K-bytes per row (two 64-byte half stages), so
+// that one buffer->LDS instruction fills 8 rows x 128 bytes, i.e. 8 whole
+// cache lines.  On MI355X such an instruction streams at twice the rate of
+// one covering 16 half lines (16 rows x 64 bytes), measured with every CU
+// refilling.  Chunk c of row r sits at 16-byte position c ^ swz2_x(r): any 8
+// aligned consecutive rows use 8 distinct positions, and any 16 aligned
+// consecutive rows 16 distinct 16-byte groups of a 256-byte window, so the
+// MFMA operand fetch (one chunk of 32 consecutive rows) is conflict-free.
+constexpr int kPairRowBytes = 2 * kRowBytes;
+constexpr int kPairTileBytes = kBM * kPairRowBytes;  // 32 KB per operand
+constexpr int kPairBytes = 2 * kPairTileBytes;       // A then B
+static_assert(2 * kPairBytes == kTileLds, "two pair slots fill the tile ring");
+__device__ __forceinline__ int swz2_x(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz2(int r, int c) { return r * kPairRowBytes + ((c ^ swz2_x(r)) << 4); }
 
 // Scale bytes kept in LDS for the whole K range of a tile: FP4 stores one
 // byte per (32-row slab, K-block), MXFP8 one per (row, K-block).  Rows are
@@ -107,13 +125,20 @@ __device__ __forceinline__ void scale_batch_load(uint32_t (&v)[8], const uint8_t
     }
 }
 
+// LDS byte of K-block kb in an operand's scale area.  FP4 (8 slabs):
+// [kb/4][slab][kb%4], so the four slabs a wave multiplies have their bytes
+// for K-blocks 4h..4h+3 in one 16-byte word; MXFP8: [row][kb].
+template <int FMT>
+__device__ __forceinline__ int scale_lds_index(int kb) { return FMT == 1 ? (kb >> 2) * 32 + (kb & 3) : kb; }
+
+template <int FMT>
 __device__ __forceinline__ void scale_batch_store(const uint32_t (&v)[8], uint8_t* dst, int kb0, int kstep,
                                                   int kbpad)
 {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
         if (kb0 + u * kstep < kbpad)
-            dst[kb0 + u * kstep] = (uint8_t)v[u];
+            dst[scale_lds_index<FMT>(kb0 + u * kstep)] = (uint8_t)v[u];
 }
 
 // The tile's scale bytes in registers: thread t covers (FP4) slab t/32 and
@@ -156,20 +181,20 @@ __device__ __forceinline__ void scales_store(const ScaleStage& st, const GemmArg
 {
     int r, kb0, kstep;
     scale_geometry<FMT>(r, kb0, kstep);
-    uint8_t* da = sla + r * kbpad;
-    uint8_t* db = slb + r * kbpad;
+    uint8_t* da = FMT == 1 ? sla + 4 * r : sla + r * kbpad;
+    uint8_t* db = FMT == 1 ? slb + 4 * r : slb + r * kbpad;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-        scale_batch_store(st.va[b], da, kb0 + b * 8 * kstep, kstep, kbpad);
-        scale_batch_store(st.vb[b], db, kb0 + b * 8 * kstep, kstep, kbpad);
+        scale_batch_store<FMT>(st.va[b], da, kb0 + b * 8 * kstep, kstep, kbpad);
+        scale_batch_store<FMT>(st.vb[b], db, kb0 + b * 8 * kstep, kstep, kbpad);
     }
     const int ra = m0 + (FMT == 1 ? 32 * r : r), rb = n0 + (FMT == 1 ? 32 * r : r);
     for (int k = kb0 + 16 * kstep; k < kbpad; k += 8 * kstep) {
         uint32_t va[8], vb[8];
         scale_batch_load<FMT, A_ST>(va, P.sa, g.lds_a, ra, ra < P.a_rows, k, kstep, kblocks);
         scale_batch_load<FMT, B_ST>(vb, P.sb, g.lds_b, rb, rb < P.b_rows, k, kstep, kblocks);
-        scale_batch_store(va, da, k, kstep, kbpad);
-        scale_batch_store(vb, db, k, kstep, kbpad);
+        scale_batch_store<FMT>(va, da, k, kstep, kbpad);
+        scale_batch_store<FMT>(vb, db, k, kstep, kbpad);
     }
 }
 
@@ -213,27 +238,49 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
         __builtin_amdgcn_make_buffer_rsrc((void*)P.b, (short)0, (int)((int64_t)P.b_rows * g.ldb), 0x00020000);
     uint32_t offA[4], offB[4];
     int lchunk[4];
+    if (FMT == 2) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = 16 * (4 * wave + q) + (lane >> 2);
-        const int c = (lane & 3) ^ swz_x(r);
-        lchunk[q] = c;
-        const int ar = m0 + r, br = n0 + r;
-        offA[q] = ar < P.a_rows ? (uint32_t)(ar * g.lda + c * 16) : kOob;
-        offB[q] = br < P.b_rows ? (uint32_t)(br * g.ldb + c * 16) : kOob;
+        for (int q = 0; q < 4; ++q) {
+            const int r = 16 * (4 * wave + q) + (lane >> 2);
+            const int c = (lane & 3) ^ swz_x(r);
+            lchunk[q] = c;
+            const int ar = m0 + r, br = n0 + r;
+            offA[q] = ar < P.a_rows ? (uint32_t)(ar * g.lda + c * 16) : kOob;
+            offB[q] = br < P.b_rows ? (uint32_t)(br * g.ldb + c * 16) : kOob;
+        }
     }
-    // Tile load number op (0..7) of stage s: instruction q = op/2 of operand
-    // A (op even) or B (op odd).
-    auto issue_one = [&](int s, int op) {
-        const int q = op >> 1;
-        uint8_t* base = lds + (s % kStages) * kStageBytes + (4 * wave) * 1024 + q * 1024;
-        const uint32_t kfar = (uint32_t)(s * kRowBytes + lchunk[q] * 16 - kbytes) >> 31 ? 0u : kOob;
-        if ((op & 1) == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(base), 16, (int)((offA[q] + s * kRowBytes) | kfar),
-                                                     0, 0, kTileCpol);
+    // FP4 pair loads: wave w fills rows 64w..64w+63 of each operand tile with
+    // 8 instructions; lane l of instruction q lands on row
+    // r = 64w + 8q + l/8, LDS position l%8, and fetches global chunk
+    // (l%8) ^ swz2_x(r) = (l%8) ^ (l/8) ^ (q%2) of the pair.  Rows past the
+    // operand lie past the buffer's end and read as zero.
+    uint32_t pbA[2], pbB[2];
+    int pchunk[2];
+    if (FMT == 1) {
+        pchunk[0] = (lane & 7) ^ (lane >> 3);
+        pchunk[1] = pchunk[0] ^ 1;
+        const int r = 64 * wave + (lane >> 3);
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            pbA[par] = (uint32_t)((m0 + r) * g.lda + pchunk[par] * 16);
+            pbB[par] = (uint32_t)((n0 + r) * g.ldb + pchunk[par] * 16);
+        }
+    }
+    // Loads q of both operands for pair p (128 K-bytes per row) into slot p%2.
+    // Load k (0..15) of pair p into slot p%2: instruction k/2 of operand A
+    // (k even) or B (k odd).
+    auto issue_load = [&](int p, int k) {
+        const int q = k >> 1;
+        uint8_t* base = lds + (p & 1) * kPairBytes + (8 * wave + q) * 1024;
+        const uint32_t kfar = (uint32_t)(p * kPairRowBytes + pchunk[q & 1] * 16 - kbytes) >> 31 ? 0u : kOob;
+        if ((k & 1) == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rA, LDS_PTR(base), 16, (int)((pbA[q & 1] + (uint32_t)(8 * q * g.lda + p * kPairRowBytes)) | kfar),
+                0, 0, kTileCpol);
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(base + kTileBytes), 16,
-                                                     (int)((offB[q] + s * kRowBytes) | kfar), 0, 0, kTileCpol);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rB, LDS_PTR(base + kPairTileBytes), 16,
+                (int)((pbB[q & 1] + (uint32_t)(8 * q * g.ldb + p * kPairRowBytes)) | kfar), 0, 0, kTileCpol);
     };
     auto issue = [&](int s) {
         uint8_t* base = lds + (s % kStages) * kStageBytes + (4 * wave) * 1024;
@@ -265,51 +312,39 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // MXFP8: one MFMA step of 32-byte fragments and the row's K-block 2s+h.
     struct Frag {
         v4u a[2][4], b[2][4];
-        uint32_t sa[4], sb[4];
+        v4u sa, sb;
     };
-    auto load_frags = [&](int s, Frag& F) {
-        const uint8_t* la = lds + (s % kStages) * kStageBytes;
-        const uint8_t* lb = la + kTileBytes;
-        if (FMT == 1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                F.sa[i] = *reinterpret_cast<const uint32_t*>(sla + (wm * 4 + i) * kbpad + 4 * s);
-                F.sb[i] = *reinterpret_cast<const uint32_t*>(slb + (wn * 4 + i) * kbpad + 4 * s);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    F.a[j][i] = *reinterpret_cast<const v4u*>(la + swz(wm * 128 + i * 32 + lrow32, 2 * j + khalf));
-                    F.b[j][i] = *reinterpret_cast<const v4u*>(lb + swz(wn * 128 + i * 32 + lrow32, 2 * j + khalf));
-                }
+    // Half stage h of the FP4 ring: pair h/2 in slot (h/2)%2, chunks 4(h%2)..4(h%2)+3.
+    auto half_a = [&](int h, int i, int j) {
+        return *reinterpret_cast<const v4u*>(lds + ((h >> 1) & 1) * kPairBytes +
+                                             swz2(wm * 128 + i * 32 + lrow32, 4 * (h & 1) + 2 * j + khalf));
+    };
+    auto half_b = [&](int h, int i, int j) {
+        return *reinterpret_cast<const v4u*>(lds + ((h >> 1) & 1) * kPairBytes + kPairTileBytes +
+                                             swz2(wn * 128 + i * 32 + lrow32, 4 * (h & 1) + 2 * j + khalf));
+    };
+    // LDS reads of half h into N, in the order the next half consumes them:
+    // the scale words, then K-step 0's fragments (a0, b0..b3, a1..a3), then
+    // K-step 1's likewise.  Item e of 18.
+    auto read_item = [&](int h, int e, Frag& N) {
+        if (e == 0) {
+            N.sa = *reinterpret_cast<const v4u*>(sla + h * 32 + wm * 16);
+        } else if (e == 1) {
+            N.sb = *reinterpret_cast<const v4u*>(slb + h * 32 + wn * 16);
+        } else {
+            const int j = (e - 2) >> 3, k = (e - 2) & 7;
+            if (k == 0)
+                N.a[j][0] = half_a(h, 0, j);
+            else if (k <= 4)
+                N.b[j][k - 1] = half_b(h, k - 1, j);
+            else
+                N.a[j][k - 4] = half_a(h, k - 4, j);
         }
     };
-    auto mma = [&](const Frag& F) {
-        if (FMT == 1) {
-            uint32_t ssa[4], ssb[4];
+    auto load_frags = [&](int h, Frag& F) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ssa[i] = F.sa[i] >> (8 * khalf);
-                ssb[i] = F.sb[i] >> (8 * khalf);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const v4u xa = F.a[j][mi], xb = F.b[j][ni];
-                        const v8i fa = v8i{(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
-                        const v8i fb = v8i{(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
-                        if (j == 0)
-                            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fa, fb, acc[mi][ni], 4, 4, 0, (int)ssa[mi], 0, (int)ssb[ni]);
-                        else
-                            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fa, fb, acc[mi][ni], 4, 4, 2, (int)ssa[mi], 2, (int)ssb[ni]);
-                    }
-        }
+        for (int e = 0; e < 18; ++e)
+            read_item(h, e, F);
     };
 
     auto scale_f32 = [](uint32_t b) {
@@ -355,94 +390,136 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
         }
     };
 
-    // FP4 stage body: the 32 MFMAs of the stage held in C run as 8 groups of
-    // 4 (K-step j, A fragment mi, all four B fragments); after each group the
-    // wave issues one tile load of stage s_issue and a quarter of the LDS
-    // reads of stage s_next into N.  The scheduling barriers keep this mix so
-    // the matrix unit never waits behind a burst of memory instructions.
-    auto stage_fp4 = [&](int s_next, int s_issue, const Frag& C, Frag& N) {
-        const uint8_t* la = lds + (s_next % kStages) * kStageBytes;
-        const uint8_t* lb = la + kTileBytes;
-        uint32_t ssa[4], ssb[4];
+    // FP4 half-stage bodies.  The 32 MFMAs held in C run as 8 groups of 4
+    // (K-step j, A fragment mi, all four B fragments); the memory work of the
+    // half is placed between the groups, and the scheduling barriers keep
+    // that mix so the matrix unit never waits behind a burst of memory
+    // instructions.
+    auto mfma_group = [&](const Frag& C, int g8) {
+        const int j = g8 >> 2, mi = g8 & 3;
+        // lane half h multiplies K-block 4s+2j+h: byte 2j+h of the slab's word
+        const int ssa = (int)(C.sa[mi] >> (8 * khalf));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ssa[i] = C.sa[i] >> (8 * khalf);
-            ssb[i] = C.sb[i] >> (8 * khalf);
+        for (int ni = 0; ni < 4; ++ni) {
+            const int ssb = (int)(C.sb[ni] >> (8 * khalf));
+            const v4u xa = C.a[j][mi], xb = C.b[j][ni];
+            const v8i fa = v8i{(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
+            const v8i fb = v8i{(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
+            if (j == 0)
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[mi][ni], 4, 4, 0, ssa, 0,
+                                                                             ssb);
+            else
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[mi][ni], 4, 4, 2, ssa, 2,
+                                                                             ssb);
         }
+    };
+    // Quarter u (0..3) of the reads of half h: items [kq[u], kq[u+1]).
+    auto read_quarter = [&](int h, int u, Frag& N) {
+        constexpr int kq[5] = {0, 5, 9, 14, 18};
+#pragma unroll
+        for (int e = kq[u]; e < kq[u + 1]; ++e)
+            read_item(h, e, N);
+    };
+    // The two halves of pair P.  Every group issues one 1 KB load, so each
+    // pair streams in over 16 groups: pair P+1's loads 12..15 in the even
+    // half's first four groups, pair P+2's loads 0..3 in its last four (slot
+    // P%2 is free from the even half's barrier on) and 4..11 in the odd half.
+    // LOADS: 2 with both pairs, 1 with pair P+1 only (P+2 is past K), 0 none.
+    //   Even half 2P (C): the first four groups read half 2P+1 (the rest of
+    //   pair P) into N; then every wave is done with slot P%2.
+    //   Odd half 2P+1 (C): after four groups each wave waits for its loads of
+    //   pair P+1 (pair P+2's eight may stay outstanding), the barrier
+    //   publishes pair P+1, and the last four groups read its first half
+    //   into N.
+    auto half_even = [&](auto loads, int h_next, int p, const Frag& C, Frag& N) {
+        constexpr int L = decltype(loads)::value;
 #pragma unroll
         for (int g8 = 0; g8 < 8; ++g8) {
-            const int j = g8 >> 2, mi = g8 & 3;
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const v4u xa = C.a[j][mi], xb = C.b[j][ni];
-                const v8i fa = v8i{(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
-                const v8i fb = v8i{(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
-                if (j == 0)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[mi][ni], 4, 4, 0,
-                                                                                 (int)ssa[mi], 0, (int)ssb[ni]);
-                else
-                    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[mi][ni], 4, 4, 2,
-                                                                                 (int)ssa[mi], 2, (int)ssb[ni]);
+            mfma_group(C, g8);
+            if (g8 < 4) {
+                read_quarter(h_next, g8, N);
+                if constexpr (L >= 1)
+                    issue_load(p + 1, 12 + g8);
             }
-            issue_one(s_issue, g8);
-            // reads 2*g8, 2*g8+1 of the list a[0][0], b[0][0], a[0][1], ..., b[1][3]
+            if (g8 == 3)
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if constexpr (L == 2)
+                if (g8 >= 4)
+                    issue_load(p + 2, g8 - 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto half_odd = [&](auto loads, int h_next, int p, const Frag& C, Frag& N) {
+        constexpr int L = decltype(loads)::value;
 #pragma unroll
-            for (int e = 2 * g8; e < 2 * g8 + 2; ++e) {
-                const int jj = e >> 3, ii = (e >> 1) & 3;
-                if ((e & 1) == 0)
-                    N.a[jj][ii] = *reinterpret_cast<const v4u*>(la + swz(wm * 128 + ii * 32 + lrow32, 2 * jj + khalf));
+        for (int g8 = 0; g8 < 8; ++g8) {
+            mfma_group(C, g8);
+            if constexpr (L == 2)
+                issue_load(p + 2, 4 + g8);
+            if (g8 == 3) {
+                if constexpr (L == 2)
+                    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
                 else
-                    N.b[jj][ii] = *reinterpret_cast<const v4u*>(lb + swz(wn * 128 + ii * 32 + lrow32, 2 * jj + khalf));
+                    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
             }
-            if (g8 < 4)
-                N.sa[g8] = *reinterpret_cast<const uint32_t*>(sla + (wm * 4 + g8) * kbpad + 4 * s_next);
-            else
-                N.sb[g8 - 4] = *reinterpret_cast<const uint32_t*>(slb + (wn * 4 + g8 - 4) * kbpad + 4 * s_next);
+            if (g8 >= 4)
+                read_quarter(h_next, g8 - 4, N);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Ring pipeline.  The first stages and the scale bytes are loaded up
-    // front.  FP4: while stage s is multiplied from registers, stage s+1 is
-    // read out of LDS into the other register set and stages s+2..s+4 are in
-    // flight.  Before each stage a wave waits for its own loads of the stage
-    // it is about to read (the loads of the two newest stages may stay
-    // outstanding); the barrier then publishes that stage and guarantees
-    // that every wave has finished reading the slot the next issue refills.
+    // Pipelines.  The first stages (FP4: pairs 0 and 1) and the scale bytes
+    // are loaded up front.
+    //   FP4: half stages h = 0, 1, ... of 64 K-bytes; pair h/2 lives in slot
+    //   (h/2)%2.  While half h is multiplied from registers, half h+1 is read
+    //   out of LDS into the other register set.  An even half's successor is
+    //   in its own pair, so it runs without waiting.  Before an odd half h+1
+    //   each wave waits for its loads of pair h/2+1 and for its LDS reads; the
+    //   barrier then publishes that pair and guarantees that every wave is
+    //   done with pair h/2, whose slot the odd half refills with pair h/2+2.
+    //   MXFP8: a 4-slot ring of 64-byte stages, three in flight.
+    const int npair = (kbytes + kPairRowBytes - 1) / kPairRowBytes;
     {
         ScaleStage st;
         scales_load<FMT, A_ST, B_ST>(st, g, P, m0, n0, kblocks, kbpad);
         __builtin_amdgcn_sched_barrier(0);
-        issue(0);
-        issue(1);
-        issue(2);
-        if (FMT == 1)
-            issue(3);
+        if (FMT == 1) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                issue_load(0, k);
+#pragma unroll
+            for (int k = 0; k < 12; ++k)
+                issue_load(1, k);
+        } else {
+            issue(0);
+            issue(1);
+            issue(2);
+        }
         __builtin_amdgcn_sched_barrier(0);
         scales_store<FMT, A_ST, B_ST>(st, g, P, sla, slb, m0, n0, kblocks, kbpad);
     }
     // Stage 0 and the scale bytes must be in LDS; the later stages may still
     // be in flight.
     if (FMT == 1)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * kDmaPerStage) : "memory");
+        asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kDmaPerStage) : "memory");
-    Frag F0, F1;
     int s = 0;
     if (FMT == 1) {
-        // While stage s is multiplied from registers its own slot is free
-        // (its fragments were read during stage s-1, and every wave has
-        // passed the barrier since), so stage s+4 is loaded into it: three
-        // stages are in flight and stage s+1's loads have two stages to land.
+        Frag F0, F1;
         load_frags(0, F0);
-        for (; s + 1 < nst; s += 2) {
-            wait_vm_and_barrier<2 * kDmaPerStage>();
-            stage_fp4(s + 1, s + 4, F0, F1);
-            wait_vm_and_barrier<2 * kDmaPerStage>();
-            stage_fp4(s + 2, s + 5, F1, F0);
+        // Every pair issues the loads of the two pairs after it; loads of
+        // pairs past the end of K read as zero (the K range check), so the
+        // body is the same for every pair.
+        const std::integral_constant<int, 2> both;
+        const std::integral_constant<int, 0> none;
+        int p = 0;
+        for (; 2 * p + 1 < nst; ++p) {
+            half_even(both, 2 * p + 1, p, F0, F1);
+            half_odd(both, 2 * p + 2, p, F1, F0);
         }
-        if (s < nst)
-            mma(F0);
+        if (2 * p < nst)  // odd count: the last half (its successor reads are unused)
+            half_even(none, 2 * p + 1, p, F0, F1);
     } else {
         // MXFP8: products are formed exactly.  Each 16-wide K step, a lane
         // converts its 8 E4M3 bytes (row lane%32, K bytes [16t + 8h, +8)) to

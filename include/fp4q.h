@@ -167,6 +167,9 @@ int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
  *   K      the tile keeps the scale bytes of its whole K range on chip:
  *          K (per group for grouped DGRAD / WGRAD) is at most 65152 for
  *          FP4 and 1664 for MXFP8, else FP4Q_EUNSUPPORTED.
+ *   size   each operand plane read (rows padded to 32, plus 256 rows of
+ *          reach) times its leading dimension must stay below 2 GiB, else
+ *          FP4Q_EUNSUPPORTED.
  *   batch  a->batch == b->batch = B runs B independent products; product i
  *          writes C + i*c_bstride (floats).
  *   groups NULL for a dense product; else a grouped (expert) product with

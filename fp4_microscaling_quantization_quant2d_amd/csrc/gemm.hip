@@ -209,7 +209,10 @@ __device__ __forceinline__ void wait_vm_and_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <int FMT, bool A_ST, bool B_ST>
+// KT: K may end inside an FP4 pair (K % 256 != 0), so loads check the K
+// range; without it only pairs past the end of K (loaded but never
+// multiplied) may read past a row's K bytes.
+template <int FMT, bool A_ST, bool B_ST, bool KT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -269,10 +272,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // Loads q of both operands for pair p (128 K-bytes per row) into slot p%2.
     // Load k (0..15) of pair p into slot p%2: instruction k/2 of operand A
     // (k even) or B (k odd).
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // LDS addresses in scalar registers
     auto issue_load = [&](int p, int k) {
         const int q = k >> 1;
-        uint8_t* base = lds + (p & 1) * kPairBytes + (8 * wave + q) * 1024;
-        const uint32_t kfar = (uint32_t)(p * kPairRowBytes + pchunk[q & 1] * 16 - kbytes) >> 31 ? 0u : kOob;
+        uint8_t* base = lds + (p & 1) * kPairBytes + (8 * wave_s + q) * 1024;
+        const uint32_t kfar =
+            KT && ((uint32_t)(p * kPairRowBytes + pchunk[q & 1] * 16 - kbytes) >> 31) == 0 ? kOob : 0u;
         if ((k & 1) == 0)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rA, LDS_PTR(base), 16, (int)((pbA[q & 1] + (uint32_t)(8 * q * g.lda + p * kPairRowBytes)) | kfar),
@@ -588,7 +593,7 @@ __device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int&
     tn = in / rows;
 }
 
-template <int FMT, bool A_ST, bool B_ST>
+template <int FMT, bool A_ST, bool B_ST, bool KT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
 {
     const int bz = blockIdx.y;
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
     P.b_rows = g.b_rows;
     const int ntm = (g.M + kBM - 1) / kBM, ntn = (g.N + kBN - 1) / kBN;
     tile_of(blockIdx.x, ntm, ntn, P.tm, P.tn);
-    gemm_tile<FMT, A_ST, B_ST>(g, P);
+    gemm_tile<FMT, A_ST, B_ST, KT>(g, P);
 }
 
 // Grouped (expert) products.  Group g owns token rows [row_off[g], row_off[g+1]).
@@ -663,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
     const int local = pid - g.tile_start[grp];
     P.tm = local / ntn;
     P.tn = local - P.tm * ntn;
-    gemm_tile<1, A_ST, B_ST>(g, P);
+    gemm_tile<1, A_ST, B_ST, true>(g, P);
 }
 
 // Dynamic LDS: two stage buffers plus the tile's scale bytes for its K range.
@@ -700,16 +705,24 @@ hipError_t allow_lds(F* fn, size_t bytes)
     return allow_lds_raw(reinterpret_cast<const void*>(fn), bytes);
 }
 
-template <int FMT, bool A_ST, bool B_ST>
-hipError_t launch_dense(const GemmArgs& g, int batch, hipStream_t s)
+template <int FMT, bool A_ST, bool B_ST, bool KT>
+hipError_t launch_dense_k(const GemmArgs& g, int batch, hipStream_t s)
 {
     const int ntm = (g.M + kBM - 1) / kBM, ntn = (g.N + kBN - 1) / kBN;
     const size_t lb = lds_bytes(FMT, g.K);
-    hipError_t e = allow_lds(gemm_dense_kernel<FMT, A_ST, B_ST>, lb);
+    hipError_t e = allow_lds(gemm_dense_kernel<FMT, A_ST, B_ST, KT>, lb);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST>), dim3(ntm * ntn, batch), dim3(kThreads), lb, s, g);
+    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST, KT>), dim3(ntm * ntn, batch), dim3(kThreads), lb, s, g);
     return hipGetLastError();
+}
+
+template <int FMT, bool A_ST, bool B_ST>
+hipError_t launch_dense(const GemmArgs& g, int batch, hipStream_t s)
+{
+    if (FMT == 1 && g.K % 256 == 0)
+        return launch_dense_k<FMT, A_ST, B_ST, false>(g, batch, s);
+    return launch_dense_k<FMT, A_ST, B_ST, true>(g, batch, s);
 }
 
 template <int OP, bool A_ST, bool B_ST>

@@ -41,6 +41,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -56,6 +57,19 @@ constexpr int kDmaPerStage = 8;                     // buffer->LDS loads per wav
 constexpr int kTileCpol = 16;                       // sc1 on the streamed tile loads (measured ~3% faster)
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// f(std::integral_constant<int, i>) for i = 0..N-1, unrolled, so i can feed
+// instruction immediates.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>());
+}
 
 // Byte offset of 16-byte chunk c of row r inside a stage tile (64-byte
 // rows).  The xor key makes any 8 consecutive rows hit 8 distinct 16-byte
@@ -125,11 +139,16 @@ __device__ __forceinline__ void scale_batch_load(uint32_t (&v)[8], const uint8_t
     }
 }
 
-// LDS byte of K-block kb in an operand's scale area.  FP4 (8 slabs):
-// [kb/4][slab][kb%4], so the four slabs a wave multiplies have their bytes
-// for K-blocks 4h..4h+3 in one 16-byte word; MXFP8: [row][kb].
+// LDS byte of K-block kb in an operand's scale area.  FP4 (8 slabs): K-block
+// kb = 4q + 2j + h sits at [q][h][slab][j], so for half stage q a lane of MFMA
+// lane half h finds the bytes of the wave's four slabs in one 8-byte word,
+// slab i's K-step-j byte at byte 2(i%2) + j of dword i/2 -- directly the
+// MFMA's scale byte select.  MXFP8: [row][kb].
 template <int FMT>
-__device__ __forceinline__ int scale_lds_index(int kb) { return FMT == 1 ? (kb >> 2) * 32 + (kb & 3) : kb; }
+__device__ __forceinline__ int scale_lds_index(int kb)
+{
+    return FMT == 1 ? (kb >> 2) * 32 + (kb & 1) * 16 + ((kb >> 1) & 1) : kb;
+}
 
 template <int FMT>
 __device__ __forceinline__ void scale_batch_store(const uint32_t (&v)[8], uint8_t* dst, int kb0, int kstep,
@@ -181,8 +200,8 @@ __device__ __forceinline__ void scales_store(const ScaleStage& st, const GemmArg
 {
     int r, kb0, kstep;
     scale_geometry<FMT>(r, kb0, kstep);
-    uint8_t* da = FMT == 1 ? sla + 4 * r : sla + r * kbpad;
-    uint8_t* db = FMT == 1 ? slb + 4 * r : slb + r * kbpad;
+    uint8_t* da = FMT == 1 ? sla + 2 * r : sla + r * kbpad;
+    uint8_t* db = FMT == 1 ? slb + 2 * r : slb + r * kbpad;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         scale_batch_store<FMT>(st.va[b], da, kb0 + b * 8 * kstep, kstep, kbpad);
@@ -309,15 +328,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
 
-    // Operands of one K stage in registers.  FP4: A/B fragments of both
-    // MFMA steps (16 x 16 bytes; lane half h holds the 32 codes of K-block h
-    // of the step) and the per-slab scale dwords (K-blocks 4s..4s+3);
-    // shifted right by 8h for lane half h, byte 0 holds K-block 4s+h (step 0)
-    // and byte 2 K-block 4s+2+h (step 1).
-    // MXFP8: one MFMA step of 32-byte fragments and the row's K-block 2s+h.
+    // FP4 operands of one half stage s in registers: A/B fragments of both
+    // MFMA K-steps (16 x 16 bytes; lane half h holds the 32 codes of K-block
+    // h of the step) and the scale bytes of the wave's four slabs of A and of
+    // B for the lane's K-blocks 4s + 2j + h (layout at scale_lds_index).  The
+    // vector types keep the compiler's view of these LDS reads precise, so it
+    // adds no waits for the buffer->LDS loads in flight.
     struct Frag {
         v4u a[2][4], b[2][4];
-        v4u sa, sb;
+        v2u sa, sb;
     };
     // Half stage h of the FP4 ring: pair h/2 in slot (h/2)%2, chunks 4(h%2)..4(h%2)+3.
     auto half_a = [&](int h, int i, int j) {
@@ -333,9 +352,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // K-step 1's likewise.  Item e of 18.
     auto read_item = [&](int h, int e, Frag& N) {
         if (e == 0) {
-            N.sa = *reinterpret_cast<const v4u*>(sla + h * 32 + wm * 16);
+            N.sa = *reinterpret_cast<const v2u*>(sla + h * 32 + khalf * 16 + wm * 8);
         } else if (e == 1) {
-            N.sb = *reinterpret_cast<const v4u*>(slb + h * 32 + wn * 16);
+            N.sb = *reinterpret_cast<const v2u*>(slb + h * 32 + khalf * 16 + wn * 8);
         } else {
             const int j = (e - 2) >> 3, k = (e - 2) & 7;
             if (k == 0)
@@ -400,23 +419,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // half is placed between the groups, and the scheduling barriers keep
     // that mix so the matrix unit never waits behind a burst of memory
     // instructions.
-    auto mfma_group = [&](const Frag& C, int g8) {
-        const int j = g8 >> 2, mi = g8 & 3;
-        // lane half h multiplies K-block 4s+2j+h: byte 2j+h of the slab's word
-        const int ssa = (int)(C.sa[mi] >> (8 * khalf));
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int ssb = (int)(C.sb[ni] >> (8 * khalf));
+    auto mfma_group = [&](const Frag& C, auto G) {
+        constexpr int j = decltype(G)::value >> 2, mi = decltype(G)::value & 3;
+        const int ssa = (int)(mi >> 1 ? C.sa.y : C.sa.x);
+        static_for<4>([&](auto NI) {
+            constexpr int ni = decltype(NI)::value;
+            const int ssb = (int)(ni >> 1 ? C.sb.y : C.sb.x);
             const v4u xa = C.a[j][mi], xb = C.b[j][ni];
             const v8i fa = v8i{(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
             const v8i fb = v8i{(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
-            if (j == 0)
-                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[mi][ni], 4, 4, 0, ssa, 0,
-                                                                             ssb);
-            else
-                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[mi][ni], 4, 4, 2, ssa, 2,
-                                                                             ssb);
-        }
+            // slab i's K-step-j scale: byte 2(i%2) + j of dword i/2
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fa, fb, acc[mi][ni], 4, 4, 2 * (mi & 1) + j, ssa, 2 * (ni & 1) + j, ssb);
+        });
     };
     // Quarter u (0..3) of the reads of half h: items [kq[u], kq[u+1]).
     auto read_quarter = [&](int h, int u, Frag& N) {
@@ -438,9 +453,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     //   into N.
     auto half_even = [&](auto loads, int h_next, int p, const Frag& C, Frag& N) {
         constexpr int L = decltype(loads)::value;
-#pragma unroll
-        for (int g8 = 0; g8 < 8; ++g8) {
-            mfma_group(C, g8);
+        static_for<8>([&](auto G) {
+            constexpr int g8 = decltype(G)::value;
+            mfma_group(C, G);
             if (g8 < 4) {
                 read_quarter(h_next, g8, N);
                 if constexpr (L >= 1)
@@ -452,13 +467,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
                 if (g8 >= 4)
                     issue_load(p + 2, g8 - 4);
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
     auto half_odd = [&](auto loads, int h_next, int p, const Frag& C, Frag& N) {
         constexpr int L = decltype(loads)::value;
-#pragma unroll
-        for (int g8 = 0; g8 < 8; ++g8) {
-            mfma_group(C, g8);
+        static_for<8>([&](auto G) {
+            constexpr int g8 = decltype(G)::value;
+            mfma_group(C, G);
             if constexpr (L == 2)
                 issue_load(p + 2, 4 + g8);
             if (g8 == 3) {
@@ -470,7 +485,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             if (g8 >= 4)
                 read_quarter(h_next, g8 - 4, N);
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
 
     // Pipelines.  The first stages (FP4: pairs 0 and 1) and the scale bytes

@@ -58,6 +58,14 @@ constexpr int kTileCpol = 16;                       // sc1 on the streamed tile 
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// The other ring slot, at compile time when the slot is known there.
+template <int V>
+__device__ __forceinline__ std::integral_constant<int, 1 - V> other_slot(std::integral_constant<int, V>)
+{
+    return {};
+}
+__device__ __forceinline__ int other_slot(int slot) { return 1 - slot; }
+
 // f(std::integral_constant<int, i>) for i = 0..N-1, unrolled, so i can feed
 // instruction immediates.
 template <typename F, int... I>
@@ -88,9 +96,9 @@ __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ 
 // consecutive rows 16 distinct 16-byte groups of a 256-byte window, so the
 // MFMA operand fetch (one chunk of 32 consecutive rows) is conflict-free.
 constexpr int kPairRowBytes = 2 * kRowBytes;
-constexpr int kPairTileBytes = kBM * kPairRowBytes;  // 32 KB per operand
-constexpr int kPairBytes = 2 * kPairTileBytes;       // A then B
-static_assert(2 * kPairBytes == kTileLds, "two pair slots fill the tile ring");
+constexpr int kPairTileBytes = kBM * kPairRowBytes;  // 32 KB per operand and slot
+constexpr int kPairB = 2 * kPairTileBytes;           // A slots 0, 1, then B slots 0, 1
+static_assert(4 * kPairTileBytes == kTileLds, "two pair slots fill the tile ring");
 __device__ __forceinline__ int swz2_x(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz2(int r, int c) { return r * kPairRowBytes + ((c ^ swz2_x(r)) << 4); }
 
@@ -294,7 +302,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // LDS addresses in scalar registers
     auto issue_load = [&](int p, int k) {
         const int q = k >> 1;
-        uint8_t* base = lds + (p & 1) * kPairBytes + (8 * wave_s + q) * 1024;
+        uint8_t* base = lds + (p & 1) * kPairTileBytes + (8 * wave_s + q) * 1024;
         const uint32_t kfar =
             KT && ((uint32_t)(p * kPairRowBytes + pchunk[q & 1] * 16 - kbytes) >> 31) == 0 ? kOob : 0u;
         if ((k & 1) == 0)
@@ -303,7 +311,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
                 0, 0, kTileCpol);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rB, LDS_PTR(base + kPairTileBytes), 16,
+                rB, LDS_PTR(base + kPairB), 16,
                 (int)((pbB[q & 1] + (uint32_t)(8 * q * g.ldb + p * kPairRowBytes)) | kfar), 0, 0, kTileCpol);
     };
     auto issue = [&](int s) {
@@ -339,18 +347,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
         v2u sa, sb;
     };
     // Half stage h of the FP4 ring: pair h/2 in slot (h/2)%2, chunks 4(h%2)..4(h%2)+3.
-    auto half_a = [&](int h, int i, int j) {
-        return *reinterpret_cast<const v4u*>(lds + ((h >> 1) & 1) * kPairBytes +
-                                             swz2(wm * 128 + i * 32 + lrow32, 4 * (h & 1) + 2 * j + khalf));
+    // Fragment (i, j) of a half stage held in slot SLOT, half PAR of its pair
+    // (chunks 4 PAR .. 4 PAR + 3).  With SLOT and PAR fixed at compile time the
+    // address is a per-lane offset plus an instruction immediate.
+    auto half_a = [&](int slot, int par, int i, int j) {
+        return *reinterpret_cast<const v4u*>(lds + slot * kPairTileBytes +
+                                             swz2(wm * 128 + i * 32 + lrow32, 4 * par + 2 * j + khalf));
     };
-    auto half_b = [&](int h, int i, int j) {
-        return *reinterpret_cast<const v4u*>(lds + ((h >> 1) & 1) * kPairBytes + kPairTileBytes +
-                                             swz2(wn * 128 + i * 32 + lrow32, 4 * (h & 1) + 2 * j + khalf));
+    auto half_b = [&](int slot, int par, int i, int j) {
+        return *reinterpret_cast<const v4u*>(lds + kPairB + slot * kPairTileBytes +
+                                             swz2(wn * 128 + i * 32 + lrow32, 4 * par + 2 * j + khalf));
     };
-    // LDS reads of half h into N, in the order the next half consumes them:
-    // the scale words, then K-step 0's fragments (a0, b0..b3, a1..a3), then
-    // K-step 1's likewise.  Item e of 18.
-    auto read_item = [&](int h, int e, Frag& N) {
+    // LDS reads of half h (in slot SLOT, half PAR of its pair) into N, in the
+    // order the next half consumes them: the scale words, then K-step 0's
+    // fragments (a0, b0..b3, a1..a3), then K-step 1's likewise.  Item e of 18.
+    auto read_item = [&](int h, auto SLOT, auto PAR, int e, Frag& N) {
+        const int slot = SLOT, par = PAR;  // compile-time constants or (the slot) a uniform value
         if (e == 0) {
             N.sa = *reinterpret_cast<const v2u*>(sla + h * 32 + khalf * 16 + wm * 8);
         } else if (e == 1) {
@@ -358,17 +370,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
         } else {
             const int j = (e - 2) >> 3, k = (e - 2) & 7;
             if (k == 0)
-                N.a[j][0] = half_a(h, 0, j);
+                N.a[j][0] = half_a(slot, par, 0, j);
             else if (k <= 4)
-                N.b[j][k - 1] = half_b(h, k - 1, j);
+                N.b[j][k - 1] = half_b(slot, par, k - 1, j);
             else
-                N.a[j][k - 4] = half_a(h, k - 4, j);
+                N.a[j][k - 4] = half_a(slot, par, k - 4, j);
         }
     };
-    auto load_frags = [&](int h, Frag& F) {
+    auto load_frags0 = [&](Frag& F) {
 #pragma unroll
         for (int e = 0; e < 18; ++e)
-            read_item(h, e, F);
+            read_item(0, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), e, F);
     };
 
     auto scale_f32 = [](uint32_t b) {
@@ -434,11 +446,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
         });
     };
     // Quarter u (0..3) of the reads of half h: items [kq[u], kq[u+1]).
-    auto read_quarter = [&](int h, int u, Frag& N) {
+    auto read_quarter = [&](int h, auto SLOT, auto PAR, int u, Frag& N) {
         constexpr int kq[5] = {0, 5, 9, 14, 18};
 #pragma unroll
         for (int e = kq[u]; e < kq[u + 1]; ++e)
-            read_item(h, e, N);
+            read_item(h, SLOT, PAR, e, N);
     };
     // The two halves of pair P.  Every group issues one 1 KB load, so each
     // pair streams in over 16 groups: pair P+1's loads 12..15 in the even
@@ -451,13 +463,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     //   pair P+1 (pair P+2's eight may stay outstanding), the barrier
     //   publishes pair P+1, and the last four groups read its first half
     //   into N.
-    auto half_even = [&](auto loads, int h_next, int p, const Frag& C, Frag& N) {
+    // SLOT: P%2, the slot of pair P, a compile-time constant where the loop
+    // is unrolled over two pairs, else a uniform value.
+    auto half_even = [&](auto loads, auto SLOT, int h_next, int p, const Frag& C, Frag& N) {
         constexpr int L = decltype(loads)::value;
         static_for<8>([&](auto G) {
             constexpr int g8 = decltype(G)::value;
             mfma_group(C, G);
             if (g8 < 4) {
-                read_quarter(h_next, g8, N);
+                read_quarter(h_next, SLOT, std::integral_constant<int, 1>(), g8, N);
                 if constexpr (L >= 1)
                     issue_load(p + 1, 12 + g8);
             }
@@ -469,7 +483,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    auto half_odd = [&](auto loads, int h_next, int p, const Frag& C, Frag& N) {
+    auto half_odd = [&](auto loads, auto SLOT, int h_next, int p, const Frag& C, Frag& N) {
+        const auto next_slot = other_slot(SLOT);
         constexpr int L = decltype(loads)::value;
         static_for<8>([&](auto G) {
             constexpr int g8 = decltype(G)::value;
@@ -483,7 +498,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
                     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
             }
             if (g8 >= 4)
-                read_quarter(h_next, g8 - 4, N);
+                read_quarter(h_next, next_slot, std::integral_constant<int, 0>(), g8 - 4, N);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -527,19 +542,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     int s = 0;
     if (FMT == 1) {
         Frag F0, F1;
-        load_frags(0, F0);
+        load_frags0(F0);
         // Every pair issues the loads of the two pairs after it; loads of
-        // pairs past the end of K read as zero (the K range check), so the
-        // body is the same for every pair.
+        // pairs past the end of K read as zero or are never multiplied, so
+        // the body is the same for every pair.
         const std::integral_constant<int, 2> both;
         const std::integral_constant<int, 0> none;
         int p = 0;
-        for (; 2 * p + 1 < nst; ++p) {
-            half_even(both, 2 * p + 1, p, F0, F1);
-            half_odd(both, 2 * p + 2, p, F1, F0);
+        if constexpr (!KT) {
+            // Whole pairs only: two pairs per iteration fix each half's slot
+            // at compile time, then at most one more pair, in slot 0.
+            const std::integral_constant<int, 0> slot0;
+            const std::integral_constant<int, 1> slot1;
+            for (; 2 * p + 3 < nst; p += 2) {
+                half_even(both, slot0, 2 * p + 1, p, F0, F1);
+                half_odd(both, slot0, 2 * p + 2, p, F1, F0);
+                half_even(both, slot1, 2 * p + 3, p + 1, F0, F1);
+                half_odd(both, slot1, 2 * p + 4, p + 1, F1, F0);
+            }
+            if (2 * p + 1 < nst) {
+                half_even(both, slot0, 2 * p + 1, p, F0, F1);
+                half_odd(both, slot0, 2 * p + 2, p, F1, F0);
+            }
+        } else {
+            for (; 2 * p + 1 < nst; ++p) {
+                half_even(both, p & 1, 2 * p + 1, p, F0, F1);
+                half_odd(both, p & 1, 2 * p + 2, p, F1, F0);
+            }
+            if (2 * p < nst)  // odd count: the last half (its successor reads are unused)
+                half_even(none, p & 1, 2 * p + 1, p, F0, F1);
         }
-        if (2 * p < nst)  // odd count: the last half (its successor reads are unused)
-            half_even(none, 2 * p + 1, p, F0, F1);
     } else {
         // MXFP8: products are formed exactly.  Each 16-wide K step, a lane
         // converts its 8 E4M3 bytes (row lane%32, K bytes [16t + 8h, +8)) to

@@ -1,6 +1,8 @@
 """The hot path captured in a HIP graph: replays, with eager work and
 synchronizations between them, reproduce the eager results bit for bit
-(quantizer planes and GEMM outputs)."""
+(quantizer planes and GEMM outputs), for the launches captured on one stream
+and for the quantizers on a second stream with each GEMM waiting on events
+for the operands it reads."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +14,8 @@ from gpu_util import note, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("streams", [1, 2])
+def test_graph_replays_match_eager(streams):
     L = wl.linear_layer("tiny:graph", 320, 448, 288, 3)
     x, w, dy = to_dev(L.X), to_dev(L.W), to_dev(L.dY)
     q = {nm: fq.alloc_fp4(*t.shape) for nm, t in (("X", x), ("W", w), ("dY", dy))}
@@ -27,6 +30,27 @@ def test_graph_replays_match_eager():
         fq.fp4q_gemm("dgrad", q["dY"], q["W"], C["dgrad"])
         fq.fp4q_gemm("wgrad", q["dY"], q["X"], C["wgrad"])
 
+    side = torch.cuda.Stream()
+
+    def two_streams():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        done = {}
+        with torch.cuda.stream(side):
+            for nm, t, sid in (("X", x, 1), ("W", w, 2), ("dY", dy, 3)):
+                fq.fp4q_quant2d(t, q[nm], seed=11, stream_id=sid)
+                done[nm] = torch.cuda.Event()
+                done[nm].record(side)
+        main.wait_event(done["X"])
+        main.wait_event(done["W"])
+        fq.fp4q_gemm("fwd", q["X"], q["W"], C["fwd"])
+        main.wait_event(done["dY"])
+        fq.fp4q_gemm("dgrad", q["dY"], q["W"], C["dgrad"])
+        fq.fp4q_gemm("wgrad", q["dY"], q["X"], C["wgrad"])
+        main.wait_stream(side)
+
+    captured = seq if streams == 1 else two_streams
+
     def snapshot():
         torch.cuda.synchronize()
         return {**{nm: (t.codes.clone(), t.codes_t.clone(), t.scales.clone()) for nm, t in q.items()},
@@ -38,13 +62,13 @@ def test_graph_replays_match_eager():
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
-        seq()
+        captured()
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    note("graph: capture")
+    note("graph: capture (%d stream%s)" % (streams, "s" if streams > 1 else ""))
     with torch.cuda.graph(g):
-        seq()
+        captured()
     other = to_dev(wl.f32_to_bf16_bits(np.random.default_rng(1).standard_normal((256, 256)).astype(np.float32)))
     for rep in range(4):
         # clobber the outputs eagerly, run unrelated eager work, then replay

@@ -124,6 +124,36 @@ def test_gemm_into_strided_output():
     assert np.all(Ch[:, 64:] == 7.0)
 
 
+def _padded_scales(q, pad_byte):
+    """The same quantized tensor with its scale grid copied into rows padded
+    to a multiple of 8 bytes (plus 8), the padding filled with pad_byte."""
+    R32, C32 = q.scales.shape
+    wide = torch.full((R32, (C32 + 7) // 8 * 8 + 8), pad_byte, dtype=torch.uint8, device="cuda")
+    wide[:, :C32].copy_(q.scales)
+    return fq.QTensor(q.fmt, q.rows, q.cols, q.codes, wide[:, :C32], q.codes_t)
+
+
+@pytest.mark.parametrize("T,K,N", [(300, 1184, 200), (520, 96, 744)])
+def test_padded_scale_grids(T, K, N):
+    """Scale grids with padded rows (ld_s beyond C/32, garbage in the
+    padding) give the same C, bit for bit, as the tight grids, for ragged
+    K-block counts and partial slab tiles in every orientation; both are
+    within the bound of the oracle."""
+    L = wl.linear_layer("tiny:scalepad", T, K, N, T + 3 * K + 5 * N)
+    g, o = _quant_all(L.X, L.W, L.dY)
+    gp = {nm: _padded_scales(q, 0xA7) for nm, q in g.items()}
+    Xd, Wd, dYd = _deq(o, "X", L.X.shape), _deq(o, "W", L.W.shape), _deq(o, "dY", L.dY.shape)
+    for op, a, b, ra, rb in (("fwd", "X", "W", Xd, Wd), ("dgrad", "dY", "W", dYd, Wd),
+                             ("wgrad", "dY", "X", dYd, Xd)):
+        note("gemm padded scale grids %dx%dx%d %s" % (T, K, N, op))
+        tight = fq.fp4q_gemm(op, g[a], g[b])
+        padded = fq.fp4q_gemm(op, gp[a], gp[b])
+        torch.cuda.synchronize()
+        assert torch.equal(tight, padded), "%s: padded scale grids change C" % op
+        ref, bound = orc.gemm(op, ra, rb)
+        check_gemm_tol(padded.cpu().numpy(), ref, bound, "padded %s" % op)
+
+
 @pytest.mark.parametrize("T,K,N", [(64, 20480, 96), (20480, 64, 96)])
 def test_long_contraction(T, K, N):
     """Contractions of 20480: fwd over K (first shape) and wgrad over the

@@ -142,6 +142,27 @@ class Step:
             timed(lambda: fq.fp4q_gemm("dgrad", d["qdY"], d["qW"], d["dX"]))
             timed(lambda: fq.fp4q_gemm("wgrad", d["qdY"], d["qX"], d["dW"]))
 
+    def run_two_streams(self, seed, side):
+        """Enqueue one step with each layer's wgrad on stream `side`, beside
+        the next launches of the current stream (a training step's usual
+        schedule: dgrad feeds the layer below, wgrad only the optimizer).
+        Same launches and results as run(); tiles of the two products mix on
+        the compute units, so their store phases stop coinciding."""
+        torch, fq = self.torch, self.fq
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        for i, d in enumerate(self.layers):
+            fq.fp4q_quant2d(d["X"], d["qX"], seed=seed, stream_id=16 * i + 1)
+            fq.fp4q_quant2d(d["W"], d["qW"], seed=seed, stream_id=16 * i + 2)
+            fq.fp4q_gemm("fwd", d["qX"], d["qW"], d["Y"])
+        for i, d in reversed(list(enumerate(self.layers))):
+            fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3)
+            side.wait_stream(main)
+            fq.fp4q_gemm("dgrad", d["qdY"], d["qW"], d["dX"])
+            with torch.cuda.stream(side):
+                fq.fp4q_gemm("wgrad", d["qdY"], d["qX"], d["dW"])
+        main.wait_stream(side)
+
 
 def _timed_launches(torch, launches, iters, warmup):
     """Median ms per launch of a list of (name, fn) run in order; inputs are
@@ -391,32 +412,40 @@ def main():
 
     # Whole-step time: the step's launches captured once in a HIP graph (one
     # fixed seed) and replayed K times between two events, so launch gaps and
-    # the per-launch events above do not count.  Per-kernel rates come from
-    # the eager pass.
+    # the per-launch events above do not count.  The captured step runs each
+    # layer's wgrad on a second stream (run_two_streams); the same launches
+    # captured on one stream are timed too.  Per-kernel rates come from the
+    # eager pass.
     graph = None
-    if not args.no_graph:
-        print("[bench] capturing the step in a HIP graph", file=sys.stderr, flush=True)
-        graph = torch.cuda.CUDAGraph()
+    ms_step_one_stream = None
+
+    def graph_ms(schedule):
+        g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            step.run(seed=7)
+            schedule()
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        with torch.cuda.graph(graph):
-            step.run(seed=7)
+        with torch.cuda.graph(g):
+            schedule()
         for _ in range(args.warmup):
-            graph.replay()
+            g.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        wall0 = time.perf_counter()
+        w0 = time.perf_counter()
         g0.record()
         for _ in range(args.steps):
-            graph.replay()
+            g.replay()
         g1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        ms_step = g0.elapsed_time(g1) / args.steps
+        return g, g0.elapsed_time(g1) / args.steps, time.perf_counter() - w0
+
+    if not args.no_graph:
+        print("[bench] capturing the step in HIP graphs", file=sys.stderr, flush=True)
+        _, ms_step_one_stream, _ = graph_ms(lambda: step.run(seed=7))
+        side = torch.cuda.Stream()
+        graph, ms_step, wall = graph_ms(lambda: step.run_two_streams(7, side))
     kinds = [k for k, _, _ in step.launches]
     work = np.array([w for _, _, w in step.launches])
     qmask = np.array([k == "quant" for k in kinds])
@@ -454,7 +483,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_eager": round(ms_step_eager, 4),
-        "step_timing": "hip-graph replay" if graph is not None else "eager launches",
+        "ms_per_step_graph_one_stream": None if ms_step_one_stream is None else round(ms_step_one_stream, 4),
+        "step_timing": ("hip-graph replay, wgrad on a second stream" if graph is not None
+                        else "eager launches"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -1,8 +1,8 @@
 """The hot path captured in a HIP graph: replays, with eager work and
 synchronizations between them, reproduce the eager results bit for bit
-(quantizer planes and GEMM outputs), for the launches captured on one stream
-and for the quantizers on a second stream with each GEMM waiting on events
-for the operands it reads."""
+(quantizer planes and GEMM outputs), for the launches captured on one stream,
+for the quantizers on a second stream with each GEMM waiting on events for
+the operands it reads, and for wgrad on a second stream beside dgrad."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +14,7 @@ from gpu_util import note, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("streams", [1, 2])
+@pytest.mark.parametrize("streams", [1, 2, 3])
 def test_graph_replays_match_eager(streams):
     L = wl.linear_layer("tiny:graph", 320, 448, 288, 3)
     x, w, dy = to_dev(L.X), to_dev(L.W), to_dev(L.dY)
@@ -49,7 +49,20 @@ def test_graph_replays_match_eager(streams):
         fq.fp4q_gemm("wgrad", q["dY"], q["X"], C["wgrad"])
         main.wait_stream(side)
 
-    captured = seq if streams == 1 else two_streams
+    def wgrad_beside():
+        # the bench step's schedule: wgrad on a second stream beside dgrad
+        main = torch.cuda.current_stream()
+        fq.fp4q_quant2d(x, q["X"], seed=11, stream_id=1)
+        fq.fp4q_quant2d(w, q["W"], seed=11, stream_id=2)
+        fq.fp4q_gemm("fwd", q["X"], q["W"], C["fwd"])
+        fq.fp4q_quant2d(dy, q["dY"], seed=11, stream_id=3)
+        side.wait_stream(main)
+        fq.fp4q_gemm("dgrad", q["dY"], q["W"], C["dgrad"])
+        with torch.cuda.stream(side):
+            fq.fp4q_gemm("wgrad", q["dY"], q["X"], C["wgrad"])
+        main.wait_stream(side)
+
+    captured = {1: seq, 2: two_streams, 3: wgrad_beside}[streams]
 
     def snapshot():
         torch.cuda.synchronize()
@@ -66,7 +79,7 @@ def test_graph_replays_match_eager(streams):
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    note("graph: capture (%d stream%s)" % (streams, "s" if streams > 1 else ""))
+    note("graph: capture (schedule %d)" % streams)
     with torch.cuda.graph(g):
         captured()
     other = to_dev(wl.f32_to_bf16_bits(np.random.default_rng(1).standard_normal((256, 256)).astype(np.float32)))

@@ -148,6 +148,10 @@ int fp4q_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
     if (out->batch != 1)
         return fail(FP4Q_EINVAL, "fp4q_quant2d: out batch must be 1");
     const int64_t R = pad32(rows), C = pad32(cols);
+    // One 256-thread workgroup per 128x128 region; a launch holds fewer than 2^32 work-items.
+    if (((R + 127) / 128) * ((C + 127) / 128) >= ((int64_t)1 << 24))
+        return fail(FP4Q_EUNSUPPORTED, "fp4q_quant2d: %lld x %lld has 2^24 or more 128x128 regions",
+                    (long long)rows, (long long)cols);
     if (out->codes_t && (out->ld_t < R / 2 || out->ld_t % 16 || !aligned16(out->codes_t)))
         return fail(FP4Q_EINVAL, "fp4q_quant2d: transposed plane needs ld_t >= %lld, multiple of 16, aligned",
                     (long long)(R / 2));

@@ -226,7 +226,7 @@ __device__ __forceinline__ void fetch(Block8x8<F32>& blk, const Quant2dArgs& p, 
 
 // Output staging in LDS: both planes of a region, 128 rows of 64 bytes each,
 // rows padded to 68 bytes so that the lanes' dword writes hit 64 distinct
-// banks.  Two buffers alternate between consecutive regions.
+// banks.
 constexpr int kStageRow = 68;
 constexpr int kStagePlane = kRegion * kStageRow;
 constexpr int kStageBuf = 2 * kStagePlane;
@@ -298,8 +298,7 @@ __device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dA
         for (int j = 0; j < 8; ++j)
             *reinterpret_cast<uint32_t*>(scol + j * kStageRow) = rw[j];
     }
-    // LDS writes visible to the workgroup; the prefetch loads in flight are
-    // not waited for.
+    // LDS writes visible to the workgroup.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // Each plane of the region as 512 16-byte pieces: four consecutive
@@ -324,56 +323,20 @@ __device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dA
     }
 }
 
-// Persistent workgroups walk the 128x128 regions with a stride of the grid
-// size; the loads of the next region are issued before the current one is
-// processed, so memory latency overlaps the rounding work.  Consecutive
-// regions use the two staging buffers alternately: a buffer is rewritten
-// only after the barrier of the region in between, which every wave reaches
-// after its stores from that buffer.
+// One workgroup per 128x128 region.  The hardware dispatcher hands regions
+// to compute units as earlier ones retire, which balances the device better
+// than a persistent grid walking the regions with a fixed stride: there the
+// oldest-first wave priority inside a compute unit lets some workgroups
+// finish well before others.
 template <bool F32, int RNE, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dArgs p, int nregions)
+__global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dArgs p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kStageBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBuf];
     const int nbx = (p.cols_pad + kRegion - 1) / kRegion;
-    int ra = blockIdx.x;
-    Block8x8<F32> A, B;
-    LanePos qa = lane_pos(p, ra, nbx);
-    fetch<F32, ALIGNED>(A, p, qa);
-    for (;;) {
-        const int rb = ra + gridDim.x;
-        const LanePos qb = lane_pos(p, rb, nbx);
-        if (rb < nregions)
-            fetch<F32, ALIGNED>(B, p, qb);
-        process<F32, RNE>(A, p, qa, stage);
-        if (rb >= nregions)
-            break;
-        ra = rb + gridDim.x;
-        qa = lane_pos(p, ra, nbx);
-        if (ra < nregions)
-            fetch<F32, ALIGNED>(A, p, qa);
-        process<F32, RNE>(B, p, qb, stage + kStageBuf);
-        if (ra >= nregions)
-            break;
-    }
-}
-
-// Resident workgroups of one kernel across the device, cached per device.
-template <typename K>
-int resident_groups(K kernel)
-{
-    static int cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 0;
-    if (cached[dev] == 0) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), kThreads,
-                                                         0) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        cached[dev] = per_cu * cus;
-    }
-    return cached[dev];
+    Block8x8<F32> blk;
+    const LanePos q = lane_pos(p, blockIdx.x, nbx);
+    fetch<F32, ALIGNED>(blk, p, q);
+    process<F32, RNE>(blk, p, q, stage);
 }
 
 template <bool F32, int RNE, bool ALIGNED>
@@ -382,11 +345,7 @@ hipError_t launch_t(const Quant2dArgs& p, hipStream_t s)
     const int nbx = (p.cols_pad + kRegion - 1) / kRegion;
     const int nby = (p.rows_pad + kRegion - 1) / kRegion;
     const int nregions = nbx * nby;
-    int grid = resident_groups(quant2d_kernel<F32, RNE, ALIGNED>);
-    if (grid <= 0)
-        return hipErrorInvalidDeviceFunction;
-    grid = grid < nregions ? grid : nregions;
-    hipLaunchKernelGGL((quant2d_kernel<F32, RNE, ALIGNED>), dim3(grid), dim3(kThreads), 0, s, p, nregions);
+    hipLaunchKernelGGL((quant2d_kernel<F32, RNE, ALIGNED>), dim3(nregions), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

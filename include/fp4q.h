@@ -137,6 +137,8 @@ int fp4q_quant2d_sizes(int64_t rows, int64_t cols, int64_t* codes_bytes,
  *            codes, codes_t (may be NULL to skip the transposed plane) and
  *            scales set; batch must be 1.
  * One read of x writes the row plane, the transposed plane and the scales.
+ * A matrix of 2^24 or more 128x128 regions (one workgroup each) returns
+ * FP4Q_EUNSUPPORTED; that is over 2^38 elements, beyond device memory.
  */
 int fp4q_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                  int round_mode, uint64_t seed, uint32_t stream_id,

@@ -87,6 +87,11 @@ def test_quant2d_rejects_bad_arguments(fp4q):
         rc = L.fp4q_quant2d(xp, dt, r, c, ldx, rm, 0, 0, ctypes.byref(d), None)
         assert rc == -1, (dt, r, c, ldx, rm)
         assert _err(fp4q)
+    # one workgroup per 128x128 region: 2^24 regions exceed one launch
+    n = 1 << 19
+    big = _desc(fp4q, rows=n, cols=n, ld=n // 2, ld_t=n // 2, ld_s=n // 32)
+    assert L.fp4q_quant2d(x, 1, n, n, n, 0, 0, 0, ctypes.byref(big), None) == -2
+    assert "regions" in _err(fp4q)
 
 
 def test_gemm_rejects_bad_arguments(fp4q):

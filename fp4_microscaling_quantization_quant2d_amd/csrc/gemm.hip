@@ -606,16 +606,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // row segments.  Interior tiles address each store as one per-lane base
     // plus a wave-uniform row offset and a constant column offset.
     if (m0 + kBM <= P.M && n0 + kBN <= P.N) {
+        // The store phases of all CUs coincide, and tiles otherwise write
+        // the same relative rows at the same moment; for leading dimensions
+        // near powers of two those writes crowd the same memory channels.
+        // Each tile therefore starts at 32-row block (tm + tn) % 4 of its
+        // wave's quarter (measured 7-9% faster for N = 4096 outputs, 3% for
+        // N = 11008, like padding the rows of C).
         float* cb = P.c + (int64_t)(m0 + wm * 128 + 4 * khalf) * g.ldc + (n0 + wn * 128 + lrow32);
+        auto store_from = [&](auto ROT) {
+            static_for<4>([&](auto B) {
+                constexpr int mi = (decltype(B)::value + decltype(ROT)::value) & 3;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
+                for (int r = 0; r < 16; ++r) {
+                    float* rp = cb + (int64_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float* rp = cb + (int64_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc;
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    __builtin_nontemporal_store(acc[mi][ni][r], rp + ni * 32);
-            }
+                    for (int ni = 0; ni < 4; ++ni)
+                        __builtin_nontemporal_store(acc[mi][ni][r], rp + ni * 32);
+                }
+            });
+        };
+        switch ((P.tm + P.tn) & 3) {
+        case 0: store_from(std::integral_constant<int, 0>()); break;
+        case 1: store_from(std::integral_constant<int, 1>()); break;
+        case 2: store_from(std::integral_constant<int, 2>()); break;
+        default: store_from(std::integral_constant<int, 3>()); break;
         }
         return;
     }

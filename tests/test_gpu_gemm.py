@@ -111,6 +111,17 @@ def test_7b_down_sampled():
     _sampled_layer_check(wl.layer_7b(3), "7B down")
 
 
+# Grids of 512 or more 256x256 tiles (two or more per CU), one op per shape
+# with the large grid: fwd, dgrad (transposed B scales), wgrad (both
+# transposed).  K = 1056 ends inside a 256-value pair; the last shape has
+# ragged edges in both output dimensions.
+@pytest.mark.parametrize("T,K,N", [(4096, 1056, 8192), (4096, 8192, 1056), (1056, 4096, 8192),
+                                   (4056, 1056, 8092)])
+def test_large_grids_sampled(T, K, N):
+    L = wl.linear_layer("tiny:grid", T, K, N, T + 3 * K + 7 * N)
+    _sampled_layer_check(L, "grid %dx%dx%d" % (T, K, N), n_samples=20000)
+
+
 def test_gemm_into_strided_output():
     """C with a leading dimension larger than N; the gap stays untouched."""
     L = wl.linear_layer("tiny:ldc", 96, 128, 64, 1)

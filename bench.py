@@ -110,14 +110,18 @@ class Step:
                 self.gemm_bytes += (m * k + n * k) // 2 + (m * k + n * k) // 1024 + 4 * m * n
         for i, d in enumerate(self.layers):
             T, K, N = d["shape"]
-            self.launches += [("quant", d["name"] + ":X", quant_bytes(T, K)),
-                              ("quant", d["name"] + ":W", quant_bytes(N, K)),
+            self.launches += [("quant", d["name"] + ":X+W", quant_bytes(T, K) + quant_bytes(N, K)),
                               ("gemm", d["name"] + ":fwd", 2.0 * T * N * K)]
         for i, d in reversed(list(enumerate(self.layers))):
             T, K, N = d["shape"]
             self.launches += [("quant", d["name"] + ":dY", quant_bytes(T, N)),
                               ("gemm", d["name"] + ":dgrad", 2.0 * T * N * K),
                               ("gemm", d["name"] + ":wgrad", 2.0 * T * N * K)]
+
+    def quant_xw(self, i, d, seed):
+        """The layer's activations and weights, quantized in one batch launch."""
+        self.fq.fp4q_quant2d_batch([(d["X"], d["qX"], 16 * i + 1), (d["W"], d["qW"], 16 * i + 2)],
+                                   seed=seed)
 
     def run(self, seed, events=None):
         """Enqueue one step; with events, record one (start, end) pair per launch."""
@@ -134,8 +138,7 @@ class Step:
                 fn()
 
         for i, d in enumerate(self.layers):
-            timed(lambda: fq.fp4q_quant2d(d["X"], d["qX"], seed=seed, stream_id=16 * i + 1))
-            timed(lambda: fq.fp4q_quant2d(d["W"], d["qW"], seed=seed, stream_id=16 * i + 2))
+            timed(lambda: self.quant_xw(i, d, seed))
             timed(lambda: fq.fp4q_gemm("fwd", d["qX"], d["qW"], d["Y"]))
         for i, d in reversed(list(enumerate(self.layers))):
             timed(lambda: fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3))
@@ -152,8 +155,7 @@ class Step:
         main = torch.cuda.current_stream()
         side.wait_stream(main)
         for i, d in enumerate(self.layers):
-            fq.fp4q_quant2d(d["X"], d["qX"], seed=seed, stream_id=16 * i + 1)
-            fq.fp4q_quant2d(d["W"], d["qW"], seed=seed, stream_id=16 * i + 2)
+            self.quant_xw(i, d, seed)
             fq.fp4q_gemm("fwd", d["qX"], d["qW"], d["Y"])
         for i, d in reversed(list(enumerate(self.layers))):
             fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3)
@@ -495,7 +497,8 @@ def main():
         "config": {"workload": "7b-linear-layer-step",
                    "tokens": 8192, "hidden": 4096,
                    "layers": {nm: [K, N] for nm, K, N in wl.LAYERS_7B},
-                   "per_step": "12 quant2d (SR, 32x32 E8M0 tiles, both planes) + 12 MXFP4 GEMMs "
+                   "per_step": "12 tensors quantized (SR, 32x32 E8M0 tiles, both planes; each "
+                               "layer's X and W in one batch launch) + 12 MXFP4 GEMMs "
                                "(fwd/dgrad/wgrad x 4 layers), fp32 outputs",
                    "wall_s_timed_region": round(wall, 3)},
         "quant_GBps": round(quant_gbps, 1),

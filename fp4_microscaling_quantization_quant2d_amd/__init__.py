@@ -45,6 +45,15 @@ class _QDesc(ctypes.Structure):
                 ("bstride_t", ctypes.c_int64), ("bstride_s", ctypes.c_int64)]
 
 
+class _QItem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ldx", ctypes.c_int64), ("stream_id", ctypes.c_uint32),
+                ("out", ctypes.POINTER(_QDesc))]
+
+
+QUANT2D_BATCH_MAX = 8
+
+
 class _Groups(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("row_off", ctypes.POINTER(ctypes.c_int64))]
@@ -72,12 +81,14 @@ def _load():
                                      ctypes.POINTER(I64)]
     L.fp4q_quant2d.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.c_int, ctypes.c_uint64,
                                ctypes.c_uint32, ctypes.POINTER(_QDesc), P]
+    L.fp4q_quant2d_batch.argtypes = [ctypes.c_int, ctypes.POINTER(_QItem), ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_uint64, P]
     L.fp4q_quant1d_mxfp8.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.POINTER(_QDesc), P]
     L.fp4q_gemm.argtypes = [ctypes.c_int, ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc), P, I64,
                             I64, ctypes.POINTER(_Groups), P]
     L.fp4q_dequant.argtypes = [ctypes.POINTER(_QDesc), ctypes.c_int, ctypes.c_int, P, I64, P]
-    for fn in ("fp4q_quant2d_sizes", "fp4q_quant2d", "fp4q_quant1d_mxfp8", "fp4q_gemm",
-               "fp4q_dequant"):
+    for fn in ("fp4q_quant2d_sizes", "fp4q_quant2d", "fp4q_quant2d_batch", "fp4q_quant1d_mxfp8",
+               "fp4q_gemm", "fp4q_dequant"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -193,6 +204,38 @@ def fp4q_quant2d(x, out: Optional[QTensor] = None, round_mode="sr", seed=0, stre
                                 int(stream_id) & 0xFFFFFFFF, ctypes.byref(d), _stream_ptr(stream)),
            "fp4q_quant2d")
     return out
+
+
+def fp4q_quant2d_batch(items, round_mode="sr", seed=0, stream=None):
+    """Several fp4q_quant2d calls in one launch.  items: (x, out, stream_id)
+    triples (out a QTensor from alloc_fp4, or None to allocate one), all x of
+    one dtype; returns the outputs in order."""
+    items = list(items)
+    if not 1 <= len(items) <= QUANT2D_BATCH_MAX:
+        raise Fp4qError("fp4q_quant2d_batch takes 1..%d items, got %d" % (QUANT2D_BATCH_MAX, len(items)))
+    outs, descs = [], []
+    arr = (_QItem * len(items))()
+    dtype = None
+    for k, (x, out, stream_id) in enumerate(items):
+        _check_matrix(x)
+        dt = _dtype_code(x)
+        if dtype is not None and dt != dtype:
+            raise Fp4qError("fp4q_quant2d_batch: items of one dtype only")
+        dtype = dt
+        rows, cols = x.shape
+        if out is None:
+            out = alloc_fp4(rows, cols, x.device)
+        d = out.desc()
+        descs.append(d)
+        outs.append(out)
+        arr[k].x = _ptr(x)
+        arr[k].rows, arr[k].cols, arr[k].ldx = rows, cols, x.stride(0)
+        arr[k].stream_id = int(stream_id) & 0xFFFFFFFF
+        arr[k].out = ctypes.pointer(d)
+    _check(_load().fp4q_quant2d_batch(len(items), arr, dtype, ROUND[round_mode],
+                                      int(seed) & ((1 << 64) - 1), _stream_ptr(stream)),
+           "fp4q_quant2d_batch")
+    return outs
 
 
 def fp4q_quant1d_mxfp8(x, out: Optional[QTensor] = None, stream=None):

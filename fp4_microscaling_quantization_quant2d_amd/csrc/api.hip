@@ -104,6 +104,69 @@ int check_fp8_tensor(const fp4q_qtensor* t, const char* name)
     return FP4Q_OK;
 }
 
+// Validates every item, then quantizes all of them in one launch.
+int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dtype, int round_mode,
+                   uint64_t seed, void* hip_stream)
+{
+    static_assert(FP4Q_QUANT2D_BATCH_MAX == fp4q::kQuant2dBatchMax, "batch limit");
+    if (dtype != FP4Q_DT_BF16 && dtype != FP4Q_DT_F32)
+        return fail(FP4Q_EINVAL, "%s: dtype %d", fn, dtype);
+    if (round_mode != FP4Q_ROUND_SR && round_mode != FP4Q_ROUND_RNE)
+        return fail(FP4Q_EINVAL, "%s: round_mode %d", fn, round_mode);
+    const int esz = dtype == FP4Q_DT_F32 ? 4 : 2;
+    fp4q::Quant2dBatch b;
+    b.n = n;
+    b.first[0] = 0;
+    bool aligned = true;
+    int64_t regions = 0;
+    for (int i = 0; i < n; ++i) {
+        const fp4q_quant2d_item& it = items[i];
+        if (!it.x)
+            return fail(FP4Q_EINVAL, "%s: item %d: x is null", fn, i);
+        if (it.rows <= 0 || it.cols <= 0 || it.rows > kMaxDim || it.cols > kMaxDim || it.ldx < it.cols)
+            return fail(FP4Q_EINVAL, "%s: item %d: bad shape %lld x %lld (ldx %lld)", fn, i, (long long)it.rows,
+                        (long long)it.cols, (long long)it.ldx);
+        const fp4q_qtensor* out = it.out;
+        int rc = check_fp4_tensor(out, fn, false);
+        if (rc)
+            return rc;
+        if (out->rows != it.rows || out->cols != it.cols)
+            return fail(FP4Q_EINVAL, "%s: item %d: out shape %lld x %lld != input", fn, i, (long long)out->rows,
+                        (long long)out->cols);
+        if (out->batch != 1)
+            return fail(FP4Q_EINVAL, "%s: item %d: out batch must be 1", fn, i);
+        const int64_t R = pad32(it.rows), C = pad32(it.cols);
+        if (out->codes_t && (out->ld_t < R / 2 || out->ld_t % 16 || !aligned16(out->codes_t)))
+            return fail(FP4Q_EINVAL, "%s: item %d: transposed plane needs ld_t >= %lld, multiple of 16, aligned", fn,
+                        i, (long long)(R / 2));
+        // One 256-thread workgroup per 128x128 region; a launch holds fewer than 2^32 work-items.
+        regions += fp4q::quant2d_regions(R, C);
+        if (regions >= ((int64_t)1 << 24))
+            return fail(FP4Q_EUNSUPPORTED, "%s: 2^24 or more 128x128 regions in one launch", fn);
+        fp4q::Quant2dArgs& p = b.item[i];
+        p.x = it.x;
+        p.ldx = it.ldx;
+        p.rows = (int)it.rows;
+        p.cols = (int)it.cols;
+        p.rows_pad = (int)R;
+        p.cols_pad = (int)C;
+        p.codes = out->codes;
+        p.ld = out->ld;
+        p.codes_t = out->codes_t;
+        p.ld_t = out->ld_t;
+        p.scales = out->scales;
+        p.ld_s = out->ld_s;
+        p.key0 = (uint32_t)seed;
+        p.key1 = (uint32_t)(seed >> 32);
+        p.stream = it.stream_id;
+        b.first[i + 1] = (int)regions;
+        aligned = aligned && aligned16(it.x) && (it.ldx * esz) % 16 == 0;
+    }
+    return hip_status(fp4q::launch_quant2d(b, dtype == FP4Q_DT_F32, round_mode == FP4Q_ROUND_RNE, aligned,
+                                           static_cast<hipStream_t>(hip_stream)),
+                      fn);
+}
+
 } // namespace
 
 extern "C" {
@@ -130,52 +193,24 @@ int fp4q_quant2d_sizes(int64_t rows, int64_t cols, int64_t* codes_bytes, int64_t
 int fp4q_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int round_mode,
                  uint64_t seed, uint32_t stream_id, const fp4q_qtensor* out, void* hip_stream)
 {
-    if (!x)
-        return fail(FP4Q_EINVAL, "fp4q_quant2d: x is null");
-    if (dtype != FP4Q_DT_BF16 && dtype != FP4Q_DT_F32)
-        return fail(FP4Q_EINVAL, "fp4q_quant2d: dtype %d", dtype);
-    if (round_mode != FP4Q_ROUND_SR && round_mode != FP4Q_ROUND_RNE)
-        return fail(FP4Q_EINVAL, "fp4q_quant2d: round_mode %d", round_mode);
-    if (rows <= 0 || cols <= 0 || rows > kMaxDim || cols > kMaxDim || ldx < cols)
-        return fail(FP4Q_EINVAL, "fp4q_quant2d: bad shape %lld x %lld (ldx %lld)", (long long)rows,
-                    (long long)cols, (long long)ldx);
-    int rc = check_fp4_tensor(out, "fp4q_quant2d out", false);
-    if (rc)
-        return rc;
-    if (out->rows != rows || out->cols != cols)
-        return fail(FP4Q_EINVAL, "fp4q_quant2d: out shape %lld x %lld != input", (long long)out->rows,
-                    (long long)out->cols);
-    if (out->batch != 1)
-        return fail(FP4Q_EINVAL, "fp4q_quant2d: out batch must be 1");
-    const int64_t R = pad32(rows), C = pad32(cols);
-    // One 256-thread workgroup per 128x128 region; a launch holds fewer than 2^32 work-items.
-    if (((R + 127) / 128) * ((C + 127) / 128) >= ((int64_t)1 << 24))
-        return fail(FP4Q_EUNSUPPORTED, "fp4q_quant2d: %lld x %lld has 2^24 or more 128x128 regions",
-                    (long long)rows, (long long)cols);
-    if (out->codes_t && (out->ld_t < R / 2 || out->ld_t % 16 || !aligned16(out->codes_t)))
-        return fail(FP4Q_EINVAL, "fp4q_quant2d: transposed plane needs ld_t >= %lld, multiple of 16, aligned",
-                    (long long)(R / 2));
-    const int esz = dtype == FP4Q_DT_F32 ? 4 : 2;
-    fp4q::Quant2dArgs p;
-    p.x = x;
-    p.ldx = ldx;
-    p.rows = (int)rows;
-    p.cols = (int)cols;
-    p.rows_pad = (int)R;
-    p.cols_pad = (int)C;
-    p.codes = out->codes;
-    p.ld = out->ld;
-    p.codes_t = out->codes_t;
-    p.ld_t = out->ld_t;
-    p.scales = out->scales;
-    p.ld_s = out->ld_s;
-    p.key0 = (uint32_t)seed;
-    p.key1 = (uint32_t)(seed >> 32);
-    p.stream = stream_id;
-    const bool aligned = aligned16(x) && ((ldx * esz) % 16 == 0);
-    return hip_status(fp4q::launch_quant2d(p, dtype == FP4Q_DT_F32, round_mode == FP4Q_ROUND_RNE, aligned,
-                                           static_cast<hipStream_t>(hip_stream)),
-                      "fp4q_quant2d");
+    fp4q_quant2d_item it;
+    it.x = x;
+    it.rows = rows;
+    it.cols = cols;
+    it.ldx = ldx;
+    it.stream_id = stream_id;
+    it.out = out;
+    return quant2d_launch("fp4q_quant2d", 1, &it, dtype, round_mode, seed, hip_stream);
+}
+
+int fp4q_quant2d_batch(int n, const fp4q_quant2d_item* items, int dtype, int round_mode, uint64_t seed,
+                       void* hip_stream)
+{
+    if (n < 1 || n > FP4Q_QUANT2D_BATCH_MAX)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d_batch: n %d outside 1..%d", n, FP4Q_QUANT2D_BATCH_MAX);
+    if (!items)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d_batch: items is null");
+    return quant2d_launch("fp4q_quant2d_batch", n, items, dtype, round_mode, seed, hip_stream);
 }
 
 int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,

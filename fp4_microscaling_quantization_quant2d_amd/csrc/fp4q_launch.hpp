@@ -22,7 +22,19 @@ struct Quant2dArgs {
     uint32_t key0, key1, stream;
 };
 
-hipError_t launch_quant2d(const Quant2dArgs& p, bool f32, bool rne, bool aligned, hipStream_t s);
+// Up to kQuant2dBatchMax matrices in one launch: item i owns workgroups
+// [first[i], first[i+1]), one per 128x128 region of its padded matrix.
+constexpr int kQuant2dBatchMax = 8;
+struct Quant2dBatch {
+    Quant2dArgs item[kQuant2dBatchMax];
+    int first[kQuant2dBatchMax + 1];
+    int n;
+};
+
+// Regions (workgroups) of one padded matrix.
+int64_t quant2d_regions(int64_t rows_pad, int64_t cols_pad);
+
+hipError_t launch_quant2d(const Quant2dBatch& b, bool f32, bool rne, bool aligned, hipStream_t s);
 
 struct Mxfp8Args {
     const void* x;

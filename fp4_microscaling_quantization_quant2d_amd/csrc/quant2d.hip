@@ -327,41 +327,48 @@ __device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dA
 // to compute units as earlier ones retire, which balances the device better
 // than a persistent grid walking the regions with a fixed stride: there the
 // oldest-first wave priority inside a compute unit lets some workgroups
-// finish well before others.
+// finish well before others.  A batch launch covers the regions of several
+// matrices, so their ramps and tails overlap.
 template <bool F32, int RNE, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dArgs p)
+__global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dBatch b)
 {
     __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBuf];
+    int i = 0;
+    while (i + 1 < b.n && (int)blockIdx.x >= b.first[i + 1])
+        ++i;
+    const Quant2dArgs p = b.item[i];
     const int nbx = (p.cols_pad + kRegion - 1) / kRegion;
     Block8x8<F32> blk;
-    const LanePos q = lane_pos(p, blockIdx.x, nbx);
+    const LanePos q = lane_pos(p, (int)blockIdx.x - b.first[i], nbx);
     fetch<F32, ALIGNED>(blk, p, q);
     process<F32, RNE>(blk, p, q, stage);
 }
 
 template <bool F32, int RNE, bool ALIGNED>
-hipError_t launch_t(const Quant2dArgs& p, hipStream_t s)
+hipError_t launch_t(const Quant2dBatch& b, hipStream_t s)
 {
-    const int nbx = (p.cols_pad + kRegion - 1) / kRegion;
-    const int nby = (p.rows_pad + kRegion - 1) / kRegion;
-    const int nregions = nbx * nby;
-    hipLaunchKernelGGL((quant2d_kernel<F32, RNE, ALIGNED>), dim3(nregions), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((quant2d_kernel<F32, RNE, ALIGNED>), dim3(b.first[b.n]), dim3(kThreads), 0, s, b);
     return hipGetLastError();
 }
 
 template <bool F32, int RNE>
-hipError_t launch_a(const Quant2dArgs& p, bool aligned, hipStream_t s)
+hipError_t launch_a(const Quant2dBatch& b, bool aligned, hipStream_t s)
 {
-    return aligned ? launch_t<F32, RNE, true>(p, s) : launch_t<F32, RNE, false>(p, s);
+    return aligned ? launch_t<F32, RNE, true>(b, s) : launch_t<F32, RNE, false>(b, s);
 }
 
 } // namespace
 
-hipError_t launch_quant2d(const Quant2dArgs& p, bool f32, bool rne, bool aligned, hipStream_t s)
+int64_t quant2d_regions(int64_t rows_pad, int64_t cols_pad)
+{
+    return ((rows_pad + kRegion - 1) / kRegion) * ((cols_pad + kRegion - 1) / kRegion);
+}
+
+hipError_t launch_quant2d(const Quant2dBatch& b, bool f32, bool rne, bool aligned, hipStream_t s)
 {
     if (f32)
-        return rne ? launch_a<true, 1>(p, aligned, s) : launch_a<true, 0>(p, aligned, s);
-    return rne ? launch_a<false, 1>(p, aligned, s) : launch_a<false, 0>(p, aligned, s);
+        return rne ? launch_a<true, 1>(b, aligned, s) : launch_a<true, 0>(b, aligned, s);
+    return rne ? launch_a<false, 1>(b, aligned, s) : launch_a<false, 0>(b, aligned, s);
 }
 
 } // namespace fp4q

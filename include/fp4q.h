@@ -145,6 +145,31 @@ int fp4q_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
                  const fp4q_qtensor* out, void* hip_stream);
 
 /*
+ * Several fp4q_quant2d calls in one launch (same dtype, rounding mode and
+ * seed): the quantization of each item is exactly that of fp4q_quant2d with
+ * the item's arguments, bit for bit, and the launch overlaps the items' ramp
+ * and tail.  For example the activations and the weights of one linear
+ * layer.
+ *   n      1 .. FP4Q_QUANT2D_BATCH_MAX items.
+ *   items  host array of n item descriptors; x and out as for fp4q_quant2d,
+ *          stream_id is the item's fourth Philox counter word.  Items must
+ *          not overlap in memory.
+ * Every item is validated before anything is launched; an error in any of
+ * them launches nothing and returns as fp4q_quant2d would.  2^24 or more
+ * 128x128 regions in total return FP4Q_EUNSUPPORTED.
+ */
+#define FP4Q_QUANT2D_BATCH_MAX 8
+typedef struct fp4q_quant2d_item {
+    const void* x;
+    int64_t rows, cols, ldx;
+    uint32_t stream_id;
+    const fp4q_qtensor* out;
+} fp4q_quant2d_item;
+
+int fp4q_quant2d_batch(int n, const fp4q_quant2d_item* items, int dtype, int round_mode,
+                       uint64_t seed, void* hip_stream);
+
+/*
  * MXFP8 quantization of the query/key projections (Sec. 3.2 of the same
  * page): E4M3FN elements, one E8M0 scale per 1x32 group along each row,
  * truncation-free (the Sec. 3.1 rule with Qp = 448), round-to-nearest-even.

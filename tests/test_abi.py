@@ -94,6 +94,43 @@ def test_quant2d_rejects_bad_arguments(fp4q):
     assert "regions" in _err(fp4q)
 
 
+def test_quant2d_batch_rejects_bad_arguments(fp4q):
+    L = fp4q.lib()
+    P = ctypes.c_void_p
+    good = _desc(fp4q)
+
+    def items(*specs):
+        arr = (fp4q._QItem * max(len(specs), 1))()
+        keep = []
+        for k, (x, r, c, ldx, d) in enumerate(specs):
+            keep.append(d)
+            arr[k].x, arr[k].rows, arr[k].cols, arr[k].ldx = x, r, c, ldx
+            arr[k].stream_id = k
+            arr[k].out = ctypes.pointer(d)
+        return arr, keep
+
+    ok_item = (0x10000, 64, 64, 64, good)
+    arr, keep = items(ok_item, ok_item)
+    assert L.fp4q_quant2d_batch(0, arr, 1, 0, 0, None) == -1                  # n = 0
+    assert L.fp4q_quant2d_batch(fp4q.QUANT2D_BATCH_MAX + 1, arr, 1, 0, 0, None) == -1
+    assert L.fp4q_quant2d_batch(2, None, 1, 0, 0, None) == -1                 # null items
+    assert L.fp4q_quant2d_batch(2, arr, 5, 0, 0, None) == -1                  # dtype
+    assert L.fp4q_quant2d_batch(2, arr, 1, 9, 0, None) == -1                  # round mode
+    for bad in ((0, 64, 64, 64, good),                 # null x in the second item
+                (0x20000, 64, 64, 32, good),           # ldx < cols
+                (0x20000, 64, 64, 64, _desc(fp4q, rows=32)),   # shape mismatch
+                (0x20000, 64, 64, 64, _desc(fp4q, ld_t=16))):  # transposed plane too small
+        arr, keep = items(ok_item, bad)
+        assert L.fp4q_quant2d_batch(2, arr, 1, 0, 0, None) == -1
+        assert _err(fp4q).startswith("fp4q_quant2d_batch")
+    # the region limit counts all items together: two of 2^23 regions each
+    n = 1 << 19
+    half = _desc(fp4q, rows=n // 2, cols=n, ld=n // 2, ld_t=n // 4, ld_s=n // 32)
+    arr, keep = items((0x10000, n // 2, n, n, half), (0x10000, n // 2, n, n, half))
+    assert L.fp4q_quant2d_batch(2, arr, 1, 0, 0, None) == -2
+    assert "regions" in _err(fp4q)
+
+
 def test_gemm_rejects_bad_arguments(fp4q):
     L = fp4q.lib()
     c = ctypes.c_void_p(0x50000)

@@ -2,7 +2,8 @@
 synchronizations between them, reproduce the eager results bit for bit
 (quantizer planes and GEMM outputs), for the launches captured on one stream,
 for the quantizers on a second stream with each GEMM waiting on events for
-the operands it reads, and for wgrad on a second stream beside dgrad."""
+the operands it reads, and for the bench step's schedule (X and W in one
+batch launch, wgrad on a second stream beside dgrad)."""
 import numpy as np
 import pytest
 import torch
@@ -50,10 +51,10 @@ def test_graph_replays_match_eager(streams):
         main.wait_stream(side)
 
     def wgrad_beside():
-        # the bench step's schedule: wgrad on a second stream beside dgrad
+        # the bench step's schedule: X and W in one batch launch, wgrad on a
+        # second stream beside dgrad
         main = torch.cuda.current_stream()
-        fq.fp4q_quant2d(x, q["X"], seed=11, stream_id=1)
-        fq.fp4q_quant2d(w, q["W"], seed=11, stream_id=2)
+        fq.fp4q_quant2d_batch([(x, q["X"], 1), (w, q["W"], 2)], seed=11)
         fq.fp4q_gemm("fwd", q["X"], q["W"], C["fwd"])
         fq.fp4q_quant2d(dy, q["dY"], seed=11, stream_id=3)
         side.wait_stream(main)

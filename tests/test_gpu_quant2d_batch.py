@@ -67,3 +67,26 @@ def test_batch_equals_single_calls():
         for a, b in ((outs[k].codes, single.codes), (outs[k].codes_t, single.codes_t),
                      (outs[k].scales, single.scales)):
             assert torch.equal(a, b), "item %d" % k
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_unaligned_item_runs_the_whole_batch_unaligned(dtype):
+    """One item with a leading dimension that breaks 16-byte rows sends every
+    item of the launch through the element-wise load path; results stay exact."""
+    shapes = [(200, 96), (130, 70), (64, 256)]
+    xs = _inputs(shapes, 19, dtype)
+    devs = []
+    for k, x in enumerate(xs):
+        d = to_dev(x)
+        if k == 1:   # ldx = cols + 1 elements
+            big = torch.zeros((d.shape[0], d.shape[1] + 1), dtype=d.dtype, device=d.device)
+            big[:, : d.shape[1]] = d
+            d = big[:, : d.shape[1]]
+        devs.append(d)
+    assert devs[1].stride(0) == shapes[1][1] + 1
+    note("quant2d_batch unaligned %s" % dtype)
+    outs = fq.fp4q_quant2d_batch([(d, None, 40 + k) for k, d in enumerate(devs)], seed=9)
+    torch.cuda.synchronize()
+    for k, o in enumerate(outs):
+        ref = orc.quant2d(xs[k], orc.ROUND_SR, seed=9, stream=40 + k)
+        assert_planes_equal(o, ref, "unaligned batch item %d" % k)

@@ -54,7 +54,7 @@ constexpr int kStageBytes = 2 * kTileBytes;         // A then B
 constexpr int kTileLds = kStages * kStageBytes;     // 128 KB
 constexpr uint32_t kOob = 0x80000000u;              // buffer offset that reads as zero
 constexpr int kDmaPerStage = 8;                     // buffer->LDS loads per wave per stage
-constexpr int kTileCpol = 16;                       // sc1 on the streamed tile loads (measured ~3% faster)
+constexpr int kTileCpol = 16;                       // sc1 on the streamed tile loads (default: same time; nt: 16% slower)
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 

@@ -56,6 +56,13 @@ def lib():
         L.orc_quant2d.restype = ctypes.c_int
         L.orc_quant2d.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, ctypes.c_int, ctypes.c_uint64,
                                   ctypes.c_uint32, _P, _I64, _P, _I64, _P, _I64, _I64, _I64]
+        L.orc_quant2d_block.restype = ctypes.c_int
+        L.orc_quant2d_block.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, ctypes.c_int,
+                                        ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, _P, _I64, _P,
+                                        _I64, _P, _I64]
+        L.orc_dequant_fp4_blocks.restype = ctypes.c_int
+        L.orc_dequant_fp4_blocks.argtypes = [_P, _I64, _P, _I64, ctypes.c_int, ctypes.c_int, _I64, _I64,
+                                             _P]
         L.orc_quant1x32_fp4.restype = ctypes.c_int
         L.orc_quant1x32_fp4.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, ctypes.c_int,
                                         ctypes.c_uint64, ctypes.c_uint32, _P, _I64, _P, _I64]
@@ -174,6 +181,33 @@ def quant2d(x, round_mode=ROUND_SR, seed=0, stream=0, threads=None, tile_rows=No
             for rc in ex.map(lambda b: run(*b), bounds):
                 _check(rc, "quant2d")
     return codes, codes_t, scales
+
+
+def quant2d_block(x, block, round_mode=ROUND_SR, seed=0, stream=0):
+    """Square block x block FP4 quantization (block 32 or 64); returns
+    (codes, codes_t, scales) with the scale grid [ceil(R/b) x ceil(C/b)]."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    rp, cp = pad32(rows), pad32(cols)
+    nbr, nbc = -(-rows // block), -(-cols // block)
+    codes = np.zeros((rp, cp // 2), dtype=np.uint8)
+    codes_t = np.zeros((cp, rp // 2), dtype=np.uint8)
+    scales = np.zeros((nbr, nbc), dtype=np.uint8)
+    _check(lib().orc_quant2d_block(_ptr(x), _dtype_of(x), rows, cols, cols, int(round_mode), int(seed),
+                                   int(stream), int(block), _ptr(codes), cp // 2, _ptr(codes_t), rp // 2,
+                                   _ptr(scales), nbc), "quant2d_block")
+    return codes, codes_t, scales
+
+
+def dequant_fp4_blocks(codes, scales, rows, cols, block_rows, block_cols):
+    """A code plane times its block_rows x block_cols scale grid, in fp64."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty((rows, cols), dtype=np.float64)
+    _check(lib().orc_dequant_fp4_blocks(_ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1],
+                                        int(block_rows), int(block_cols), rows, cols, _ptr(out)),
+           "dequant_fp4_blocks")
+    return out
 
 
 def quant1x32_fp4(x, round_mode=ROUND_SR, seed=0, stream=0):

@@ -307,6 +307,64 @@ int orc_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
     return 0;
 }
 
+/* Square b x b blocks for b in {32, 64} (Sec. 3 defines the scheme for any
+ * square block; Table 4 compares b = 8, 16, 32, 64).  The same definition as
+ * orc_quant2d with the block side as a parameter: one scale per b x b block
+ * from the amax of its valid entries, every element rounded with its own
+ * random field, so the element-to-random mapping does not depend on b.
+ * Scale grid [ceil(rows/b) x ld_s]; the code planes keep the 32-padded
+ * shapes of orc_quant2d. */
+int orc_quant2d_block(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                      int round_mode, uint64_t seed, uint32_t stream, int block,
+                      uint8_t* codes, int64_t ld, uint8_t* codes_t, int64_t ld_t,
+                      uint8_t* scales, int64_t ld_s)
+{
+    int64_t rows_pad = pad32(rows), cols_pad = pad32(cols);
+    int64_t br, bc, i, j;
+    if (!x || rows <= 0 || cols <= 0 || ldx < cols || (block != 32 && block != 64))
+        return -1;
+    if ((dtype != ORC_DT_BF16 && dtype != ORC_DT_F32) ||
+        (round_mode != ORC_ROUND_SR && round_mode != ORC_ROUND_RNE))
+        return -1;
+    if (ld < cols_pad / 2 || ld_t < rows_pad / 2 || ld_s < (cols + block - 1) / block)
+        return -1;
+    for (br = 0; br * block < rows; br++) {
+        for (bc = 0; bc * block < cols; bc++) {
+            double M = 0.0;
+            int k;
+            for (i = block * br; i < block * br + block && i < rows; i++) {
+                for (j = block * bc; j < block * bc + block && j < cols; j++) {
+                    double a = fabs(load_elem(x, dtype, i, j, ldx));
+                    if (!isfinite(a))
+                        return -2;
+                    if (a > M)
+                        M = a;
+                }
+            }
+            k = orc_truncfree_exponent(M, 6.0);
+            if (scales)
+                scales[br * ld_s + bc] = (uint8_t)(k + 127);
+            for (i = block * br; i < block * br + block && i < rows_pad; i++) {
+                for (j = block * bc; j < block * bc + block && j < cols_pad; j++) {
+                    int nib = 0;
+                    if (i < rows && j < cols) {
+                        uint32_t r16 = round_mode == ORC_ROUND_SR ? orc_sr_bits(seed, stream, i, j) : 0;
+                        nib = quant_elem(load_elem(x, dtype, i, j, ldx),
+                                         elem_sign(x, dtype, i, j, ldx), k, round_mode, r16);
+                        if (nib < 0)
+                            return -3;
+                    }
+                    if (codes)
+                        put_nibble(codes, ld, i, j, nib);
+                    if (codes_t)
+                        put_nibble(codes_t, ld_t, j, i, nib);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 int orc_quant1x32_fp4(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                       int round_mode, uint64_t seed, uint32_t stream,
                       uint8_t* codes, int64_t ld, uint8_t* scales, int64_t ld_s)
@@ -395,6 +453,24 @@ int orc_dequant_fp4(const uint8_t* codes, int64_t ld, const uint8_t* scales, int
         for (c = 0; c < cols; c++) {
             int nib = (codes[r * ld + c / 2] >> ((c % 2) * 4)) & 0xf;
             int sb = scales[(r / block_rows) * ld_s + c / 32];
+            out[r * cols + c] = orc_e2m1_value(nib) * orc_e8m0_value(sb);
+        }
+    }
+    return 0;
+}
+
+/* Dequantization with a block_rows x block_cols scale grid (32 x 32 or
+ * 64 x 64 for the square layouts, 1 x 32 for the row layout). */
+int orc_dequant_fp4_blocks(const uint8_t* codes, int64_t ld, const uint8_t* scales, int64_t ld_s,
+                           int block_rows, int block_cols, int64_t rows, int64_t cols, double* out)
+{
+    int64_t r, c;
+    if (!codes || !scales || !out || rows <= 0 || cols <= 0 || block_rows <= 0 || block_cols <= 0)
+        return -1;
+    for (r = 0; r < rows; r++) {
+        for (c = 0; c < cols; c++) {
+            int nib = (codes[r * ld + c / 2] >> ((c % 2) * 4)) & 0xf;
+            int sb = scales[(r / block_rows) * ld_s + c / block_cols];
             out[r * cols + c] = orc_e2m1_value(nib) * orc_e8m0_value(sb);
         }
     }

@@ -81,6 +81,14 @@ int orc_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
                 uint8_t* scales, int64_t ld_s,
                 int64_t tile_row_begin, int64_t tile_row_end);
 
+/* Square b x b blocks, b in {32, 64}: as orc_quant2d with the block side as a
+ * parameter (same per-element random fields).  scales [ceil(rows/b) x ld_s],
+ * ld_s >= ceil(cols/b); code planes as orc_quant2d. */
+int orc_quant2d_block(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                      int round_mode, uint64_t seed, uint32_t stream, int block,
+                      uint8_t* codes, int64_t ld, uint8_t* codes_t, int64_t ld_t,
+                      uint8_t* scales, int64_t ld_s);
+
 /* Conventional 1x32 FP4 quantization along rows (the non-invariant layout the
  * pages compare against).  codes [rows x ld], scales [rows x ld_s]. */
 int orc_quant1x32_fp4(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
@@ -98,6 +106,9 @@ int orc_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int6
  * 32 for the 2D layout and 1 for the 1x32 layout. */
 int orc_dequant_fp4(const uint8_t* codes, int64_t ld, const uint8_t* scales, int64_t ld_s,
                     int block_rows, int64_t rows, int64_t cols, double* out);
+/* As orc_dequant_fp4 with a block_rows x block_cols scale grid. */
+int orc_dequant_fp4_blocks(const uint8_t* codes, int64_t ld, const uint8_t* scales, int64_t ld_s,
+                           int block_rows, int block_cols, int64_t rows, int64_t cols, double* out);
 int orc_dequant_mxfp8(const uint8_t* codes, int64_t ld, const uint8_t* scales, int64_t ld_s,
                       int64_t rows, int64_t cols, double* out);
 

@@ -25,7 +25,7 @@ __all__ = ["QTensor", "fp4q_quant2d", "fp4q_quant1d_mxfp8", "fp4q_gemm", "fp4q_d
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp4q.so")
 
-FMT_FP4_2D32, FMT_MXFP8_1D32 = 1, 2
+FMT_FP4_2D32, FMT_MXFP8_1D32, FMT_FP4_2D64 = 1, 2, 3
 DT_BF16, DT_F32 = 1, 2
 ROUND = {"sr": 0, "rne": 1}
 OPS = {"fwd": 0, "dgrad": 1, "wgrad": 2}
@@ -125,8 +125,10 @@ class QTensor:
 
     fmt 1 (FP4, 2D 32x32 blocks): codes [R, ld] row plane, codes_t [C, ld_t]
     transposed plane (optional), scales [R/32, ld_s] E8M0 -- R, C = rows, cols
-    rounded up to 32.  fmt 2 (MXFP8, 1x32): codes [rows, ld] E4M3 bytes,
-    scales [rows, ld_s].  batch > 1 stacks items at the given byte strides.
+    rounded up to 32.  fmt 3 (FP4, 2D 64x64 blocks): the same planes with
+    scales [ceil(rows/64), ld_s].  fmt 2 (MXFP8, 1x32): codes [rows, ld] E4M3
+    bytes, scales [rows, ld_s].  batch > 1 stacks items at the given byte
+    strides.
     """
     fmt: int
     rows: int
@@ -162,13 +164,16 @@ def fp4q_quant2d_sizes(rows, cols):
     return a.value, b.value, c.value
 
 
-def alloc_fp4(rows, cols, device="cuda", transposed=True):
-    """Output buffers for fp4q_quant2d with the tightest leading dimensions."""
+def alloc_fp4(rows, cols, device="cuda", transposed=True, block=32):
+    """Output buffers for fp4q_quant2d with the tightest leading dimensions;
+    block 32 or 64 picks the square scale block (FMT_FP4_2D32 / FMT_FP4_2D64)."""
+    if block not in (32, 64):
+        raise Fp4qError("block must be 32 or 64, got %r" % (block,))
     R, C = _pad32(rows), _pad32(cols)
     codes = torch.empty((R, C // 2), dtype=torch.uint8, device=device)
     codes_t = torch.empty((C, R // 2), dtype=torch.uint8, device=device) if transposed else None
-    scales = torch.empty((R // 32, C // 32), dtype=torch.uint8, device=device)
-    return QTensor(FMT_FP4_2D32, rows, cols, codes, scales, codes_t)
+    scales = torch.empty((-(-rows // block), -(-cols // block)), dtype=torch.uint8, device=device)
+    return QTensor(FMT_FP4_2D32 if block == 32 else FMT_FP4_2D64, rows, cols, codes, scales, codes_t)
 
 
 def alloc_mxfp8(rows, cols, device="cuda"):

@@ -60,8 +60,8 @@ int check_fp4_tensor(const fp4q_qtensor* t, const char* name, bool need_t)
 {
     if (!t)
         return fail(FP4Q_EINVAL, "%s: null descriptor", name);
-    if (t->fmt != FP4Q_FMT_FP4_2D32)
-        return fail(FP4Q_EINVAL, "%s: fmt %d is not FP4Q_FMT_FP4_2D32", name, t->fmt);
+    if (t->fmt != FP4Q_FMT_FP4_2D32 && t->fmt != FP4Q_FMT_FP4_2D64)
+        return fail(FP4Q_EINVAL, "%s: fmt %d is not FP4Q_FMT_FP4_2D32 or FP4Q_FMT_FP4_2D64", name, t->fmt);
     if (t->rows <= 0 || t->cols <= 0 || t->rows > kMaxDim || t->cols > kMaxDim)
         return fail(FP4Q_EINVAL, "%s: bad shape %lld x %lld", name, (long long)t->rows, (long long)t->cols);
     const int64_t R = pad32(t->rows), C = pad32(t->cols);
@@ -70,8 +70,10 @@ int check_fp4_tensor(const fp4q_qtensor* t, const char* name, bool need_t)
     if (t->ld < C / 2 || t->ld % 16 || !aligned16(t->codes))
         return fail(FP4Q_EINVAL, "%s: row plane needs ld >= %lld, ld %% 16 == 0 and 16-byte alignment", name,
                     (long long)(C / 2));
-    if (t->ld_s < C / 32)
-        return fail(FP4Q_EINVAL, "%s: ld_s %lld < %lld", name, (long long)t->ld_s, (long long)(C / 32));
+    const int64_t blk = t->fmt == FP4Q_FMT_FP4_2D64 ? 64 : 32;
+    if (t->ld_s < (t->cols + blk - 1) / blk)
+        return fail(FP4Q_EINVAL, "%s: ld_s %lld < %lld", name, (long long)t->ld_s,
+                    (long long)((t->cols + blk - 1) / blk));
     if (need_t) {
         if (!t->codes_t)
             return fail(FP4Q_EINVAL, "%s: the transposed plane is required", name);
@@ -118,6 +120,7 @@ int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dt
     b.n = n;
     b.first[0] = 0;
     bool aligned = true;
+    int fmt = 0;
     int64_t regions = 0;
     for (int i = 0; i < n; ++i) {
         const fp4q_quant2d_item& it = items[i];
@@ -133,6 +136,9 @@ int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dt
         if (out->rows != it.rows || out->cols != it.cols)
             return fail(FP4Q_EINVAL, "%s: item %d: out shape %lld x %lld != input", fn, i, (long long)out->rows,
                         (long long)out->cols);
+        if (i > 0 && out->fmt != fmt)
+            return fail(FP4Q_EINVAL, "%s: item %d: block size differs from item 0", fn, i);
+        fmt = out->fmt;
         if (out->batch != 1)
             return fail(FP4Q_EINVAL, "%s: item %d: out batch must be 1", fn, i);
         const int64_t R = pad32(it.rows), C = pad32(it.cols);
@@ -163,7 +169,7 @@ int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dt
         aligned = aligned && aligned16(it.x) && (it.ldx * esz) % 16 == 0;
     }
     return hip_status(fp4q::launch_quant2d(b, dtype == FP4Q_DT_F32, round_mode == FP4Q_ROUND_RNE, aligned,
-                                           static_cast<hipStream_t>(hip_stream)),
+                                           fmt == FP4Q_FMT_FP4_2D64 ? 64 : 32, static_cast<hipStream_t>(hip_stream)),
                       fn);
 }
 
@@ -253,9 +259,9 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
         return fail(FP4Q_EINVAL, "fp4q_gemm: op %d", op);
     if (!a || !b || !c)
         return fail(FP4Q_EINVAL, "fp4q_gemm: null a, b or c");
-    if (a->fmt != b->fmt)
-        return fail(FP4Q_EINVAL, "fp4q_gemm: operand formats differ (%d, %d)", a->fmt, b->fmt);
     const bool fp8 = a->fmt == FP4Q_FMT_MXFP8_1D32;
+    if (fp8 != (b->fmt == FP4Q_FMT_MXFP8_1D32))
+        return fail(FP4Q_EINVAL, "fp4q_gemm: operand formats differ (%d, %d)", a->fmt, b->fmt);
     int rc;
     if (fp8) {
         if (op != FP4Q_OP_FWD)
@@ -274,6 +280,8 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
         return fail(FP4Q_EINVAL, "fp4q_gemm: batch above 65535");
     if (groups && (fp8 || a->batch != 1))
         return fail(FP4Q_EINVAL, "fp4q_gemm: grouped products take FP4 operands with batch 1");
+    if (groups && (a->fmt != FP4Q_FMT_FP4_2D32 || b->fmt != FP4Q_FMT_FP4_2D32))
+        return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: grouped products take 32x32-block operands");
 
     fp4q::GemmArgs g = {};
     int64_t M, N, K;
@@ -317,6 +325,8 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
     }
     g.bs_sa = a->bstride_s;
     g.bs_sb = b->bstride_s;
+    g.sh_a = a->fmt == FP4Q_FMT_FP4_2D64 ? 6 : 5;
+    g.sh_b = b->fmt == FP4Q_FMT_FP4_2D64 ? 6 : 5;
     // The kernels address each operand plane through a buffer descriptor with
     // a 32-bit byte range; a tile may reach one tile height past the last row.
     {
@@ -415,10 +425,11 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
     int rc;
     fp4q::DequantArgs p;
     int fmt;
-    if (q->fmt == FP4Q_FMT_FP4_2D32) {
+    if (q->fmt == FP4Q_FMT_FP4_2D32 || q->fmt == FP4Q_FMT_FP4_2D64) {
         if ((rc = check_fp4_tensor(q, "fp4q_dequant q", transposed != 0)))
             return rc;
         fmt = 1;
+        p.block_shift = q->fmt == FP4Q_FMT_FP4_2D64 ? 6 : 5;
         p.codes = transposed ? q->codes_t : q->codes;
         p.ld = transposed ? q->ld_t : q->ld;
         p.scale_transposed = transposed ? 1 : 0;
@@ -432,6 +443,7 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
         if (q->rows > INT_MAX)
             return fail(FP4Q_EINVAL, "fp4q_dequant: too many rows");
         fmt = 2;
+        p.block_shift = 5;
         p.codes = q->codes;
         p.ld = q->ld;
         p.scale_transposed = 0;

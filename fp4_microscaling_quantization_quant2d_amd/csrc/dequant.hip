@@ -55,8 +55,9 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs p)
             if (FMT == 1) {
                 const uint32_t byte = p.codes[(int64_t)r * p.ld + (c >> 1)];
                 const uint32_t nib = (byte >> (4 * (c & 1))) & 15u;
-                const uint32_t sb = p.scale_transposed ? p.scales[(int64_t)(c >> 5) * p.ld_s + (r >> 5)]
-                                                       : p.scales[(int64_t)(r >> 5) * p.ld_s + (c >> 5)];
+                const int bs = p.block_shift;
+                const uint32_t sb = p.scale_transposed ? p.scales[(int64_t)(c >> bs) * p.ld_s + (r >> bs)]
+                                                       : p.scales[(int64_t)(r >> bs) * p.ld_s + (c >> bs)];
                 val = e2m1_val(nib) * pow2_e8m0(sb);
             } else {
                 const uint32_t byte = p.codes[(int64_t)r * p.ld + c];

@@ -34,7 +34,8 @@ struct Quant2dBatch {
 // Regions (workgroups) of one padded matrix.
 int64_t quant2d_regions(int64_t rows_pad, int64_t cols_pad);
 
-hipError_t launch_quant2d(const Quant2dBatch& b, bool f32, bool rne, bool aligned, hipStream_t s);
+// block: 32 or 64 (square scale blocks).
+hipError_t launch_quant2d(const Quant2dBatch& b, bool f32, bool rne, bool aligned, int block, hipStream_t s);
 
 struct Mxfp8Args {
     const void* x;
@@ -54,7 +55,8 @@ struct DequantArgs {
     int64_t ld;
     const uint8_t* scales;
     int64_t ld_s;
-    int scale_transposed;  // FP4: scale of (r, c) at (c/32)*ld_s + r/32
+    int scale_transposed;  // FP4: scale of (r, c) at (c/b)*ld_s + r/b
+    int block_shift;       // FP4: log2 of the square block side b (5 or 6)
     int rows, cols;        // output shape
     void* y;
     int64_t ldy;
@@ -77,6 +79,7 @@ struct GemmArgs {
     float* c;
     int64_t lda, ldb;      // bytes per operand row
     int64_t lds_a, lds_b;  // bytes per scale-grid row
+    int sh_a, sh_b;        // FP4: log2 of each operand's square scale block (5: 32x32, 6: 64x64)
     int64_t ldc;           // floats
     int M, N, K;           // K in elements, multiple of 32
     int a_rows, b_rows;    // rows allocated in the operand planes (load bound)

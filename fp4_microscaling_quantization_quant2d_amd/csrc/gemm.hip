@@ -120,15 +120,17 @@ struct Problem {
     int tm, tn;           // tile coordinates
 };
 
-// Scale byte of (row, kb) for one operand.
+// Scale byte of (row, kb) for one operand.  FP4 grids hold one byte per
+// square block of side 2^sh (sh = 5 for 32x32, 6 for 64x64): a 64x64 block's
+// byte serves both of its 32-row slabs and both of its 32-wide K-blocks.
 template <int FMT, bool ST>
-__device__ __forceinline__ uint32_t scale_at(const uint8_t* s, int64_t lds, int row, int kb)
+__device__ __forceinline__ uint32_t scale_at(const uint8_t* s, int64_t lds, int row, int kb, int sh)
 {
     if (FMT == 2)
         return s[(int64_t)row * lds + kb];
     if (ST)
-        return s[(int64_t)kb * lds + (row >> 5)];
-    return s[(int64_t)(row >> 5) * lds + kb];
+        return s[(int64_t)(kb >> (sh - 5)) * lds + (row >> sh)];
+    return s[(int64_t)(row >> sh) * lds + (kb >> (sh - 5))];
 }
 
 // Copy the tile's scale bytes for its whole K range into LDS, [slab or
@@ -138,12 +140,12 @@ __device__ __forceinline__ uint32_t scale_at(const uint8_t* s, int64_t lds, int 
 // they overlap each other and the tile loads already in flight.
 template <int FMT, bool ST>
 __device__ __forceinline__ void scale_batch_load(uint32_t (&v)[8], const uint8_t* s, int64_t lds, int row,
-                                                 bool row_ok, int kb0, int kstep, int kblocks)
+                                                 bool row_ok, int kb0, int kstep, int kblocks, int sh)
 {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int kb = kb0 + u * kstep;
-        v[u] = (row_ok && kb < kblocks) ? scale_at<FMT, ST>(s, lds, row, kb) : 0u;
+        v[u] = (row_ok && kb < kblocks) ? scale_at<FMT, ST>(s, lds, row, kb, sh) : 0u;
     }
 }
 
@@ -195,8 +197,10 @@ __device__ __forceinline__ void scales_load(ScaleStage& st, const GemmArgs& g, c
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int k = kb0 + b * 8 * kstep;
-        scale_batch_load<FMT, A_ST>(st.va[b], P.sa, g.lds_a, ra, ra < P.a_rows && k < kbpad, k, kstep, kblocks);
-        scale_batch_load<FMT, B_ST>(st.vb[b], P.sb, g.lds_b, rb, rb < P.b_rows && k < kbpad, k, kstep, kblocks);
+        scale_batch_load<FMT, A_ST>(st.va[b], P.sa, g.lds_a, ra, ra < P.a_rows && k < kbpad, k, kstep, kblocks,
+                                    g.sh_a);
+        scale_batch_load<FMT, B_ST>(st.vb[b], P.sb, g.lds_b, rb, rb < P.b_rows && k < kbpad, k, kstep, kblocks,
+                                    g.sh_b);
     }
 }
 
@@ -218,8 +222,8 @@ __device__ __forceinline__ void scales_store(const ScaleStage& st, const GemmArg
     const int ra = m0 + (FMT == 1 ? 32 * r : r), rb = n0 + (FMT == 1 ? 32 * r : r);
     for (int k = kb0 + 16 * kstep; k < kbpad; k += 8 * kstep) {
         uint32_t va[8], vb[8];
-        scale_batch_load<FMT, A_ST>(va, P.sa, g.lds_a, ra, ra < P.a_rows, k, kstep, kblocks);
-        scale_batch_load<FMT, B_ST>(vb, P.sb, g.lds_b, rb, rb < P.b_rows, k, kstep, kblocks);
+        scale_batch_load<FMT, A_ST>(va, P.sa, g.lds_a, ra, ra < P.a_rows, k, kstep, kblocks, g.sh_a);
+        scale_batch_load<FMT, B_ST>(vb, P.sb, g.lds_b, rb, rb < P.b_rows, k, kstep, kblocks, g.sh_b);
         scale_batch_store<FMT>(va, da, k, kstep, kbpad);
         scale_batch_store<FMT>(vb, db, k, kstep, kbpad);
     }

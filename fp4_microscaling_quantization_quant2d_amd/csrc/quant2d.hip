@@ -234,18 +234,24 @@ constexpr int kStageBuf = 2 * kStagePlane;
 // Scale, random bits and rounding of one lane block whose data is in blk,
 // then the stores of the workgroup's region.  Every lane reaches the
 // barrier; lanes outside the padded matrix compute nothing and their
-// staging entries are never stored.
-template <bool F32, int RNE>
+// staging entries are never stored.  B64: one scale per 64x64 block, which
+// is exactly one wave's region.
+template <bool F32, int RNE, bool B64>
 __device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dArgs& p, const LanePos& q,
                                         uint8_t* stage)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     uint32_t mx = q.active ? block_amax<F32>(blk) : 0u;
-    // Tile amax: the 16 lanes of a 32x32 tile differ in lane bits 0,1,3,4.
+    // Tile amax: the 16 lanes of a 32x32 tile differ in lane bits 0,1,3,4;
+    // a 64x64 block takes all 64 lanes (bits 2 and 5 as well).
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 8));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+    if (B64) {
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+    }
     const int R0 = q.R0, C0 = q.C0;
     uint32_t rw[8] = {};
     if (q.active) {
@@ -279,8 +285,8 @@ __device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dA
             else
                 round_sr<F32, kMixed>(blk, w, scale, BR > BC, BR == BC, rw);
         }
-        if ((lane & 0x1B) == 0)   // block row and column multiples of 4: the tile's first lane
-            p.scales[(int64_t)(R0 >> 5) * p.ld_s + (C0 >> 5)] = (uint8_t)(k + 127);
+        if (B64 ? lane == 0 : (lane & 0x1B) == 0)   // the block's first lane
+            p.scales[(int64_t)(R0 >> (B64 ? 6 : 5)) * p.ld_s + (C0 >> (B64 ? 6 : 5))] = (uint8_t)(k + 127);
     }
 
     // Stage the row words and (after an in-register nibble transpose) the
@@ -329,7 +335,7 @@ __device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dA
 // oldest-first wave priority inside a compute unit lets some workgroups
 // finish well before others.  A batch launch covers the regions of several
 // matrices, so their ramps and tails overlap.
-template <bool F32, int RNE, bool ALIGNED>
+template <bool F32, int RNE, bool ALIGNED, bool B64>
 __global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dBatch b)
 {
     __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBuf];
@@ -341,20 +347,26 @@ __global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dBatch b)
     Block8x8<F32> blk;
     const LanePos q = lane_pos(p, (int)blockIdx.x - b.first[i], nbx);
     fetch<F32, ALIGNED>(blk, p, q);
-    process<F32, RNE>(blk, p, q, stage);
+    process<F32, RNE, B64>(blk, p, q, stage);
 }
 
-template <bool F32, int RNE, bool ALIGNED>
+template <bool F32, int RNE, bool ALIGNED, bool B64>
 hipError_t launch_t(const Quant2dBatch& b, hipStream_t s)
 {
-    hipLaunchKernelGGL((quant2d_kernel<F32, RNE, ALIGNED>), dim3(b.first[b.n]), dim3(kThreads), 0, s, b);
+    hipLaunchKernelGGL((quant2d_kernel<F32, RNE, ALIGNED, B64>), dim3(b.first[b.n]), dim3(kThreads), 0, s, b);
     return hipGetLastError();
 }
 
-template <bool F32, int RNE>
+template <bool F32, int RNE, bool B64>
 hipError_t launch_a(const Quant2dBatch& b, bool aligned, hipStream_t s)
 {
-    return aligned ? launch_t<F32, RNE, true>(b, s) : launch_t<F32, RNE, false>(b, s);
+    return aligned ? launch_t<F32, RNE, true, B64>(b, s) : launch_t<F32, RNE, false, B64>(b, s);
+}
+
+template <bool F32, int RNE>
+hipError_t launch_b(const Quant2dBatch& b, bool aligned, int block, hipStream_t s)
+{
+    return block == 64 ? launch_a<F32, RNE, true>(b, aligned, s) : launch_a<F32, RNE, false>(b, aligned, s);
 }
 
 } // namespace
@@ -364,11 +376,11 @@ int64_t quant2d_regions(int64_t rows_pad, int64_t cols_pad)
     return ((rows_pad + kRegion - 1) / kRegion) * ((cols_pad + kRegion - 1) / kRegion);
 }
 
-hipError_t launch_quant2d(const Quant2dBatch& b, bool f32, bool rne, bool aligned, hipStream_t s)
+hipError_t launch_quant2d(const Quant2dBatch& b, bool f32, bool rne, bool aligned, int block, hipStream_t s)
 {
     if (f32)
-        return rne ? launch_a<true, 1>(b, aligned, s) : launch_a<true, 0>(b, aligned, s);
-    return rne ? launch_a<false, 1>(b, aligned, s) : launch_a<false, 0>(b, aligned, s);
+        return rne ? launch_b<true, 1>(b, aligned, block, s) : launch_b<true, 0>(b, aligned, block, s);
+    return rne ? launch_b<false, 1>(b, aligned, block, s) : launch_b<false, 0>(b, aligned, block, s);
 }
 
 } // namespace fp4q

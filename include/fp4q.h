@@ -51,8 +51,10 @@ typedef enum { FP4Q_DT_BF16 = 1, FP4Q_DT_F32 = 2 } fp4q_dtype;
 typedef enum { FP4Q_ROUND_SR = 0, FP4Q_ROUND_RNE = 1 } fp4q_round;
 typedef enum { FP4Q_OP_FWD = 0, FP4Q_OP_DGRAD = 1, FP4Q_OP_WGRAD = 2 } fp4q_op;
 typedef enum {
-    FP4Q_FMT_FP4_2D32 = 1,  /* E2M1 codes, one E8M0 scale per 32x32 tile */
-    FP4Q_FMT_MXFP8_1D32 = 2 /* E4M3FN bytes, one E8M0 scale per 1x32 row group */
+    FP4Q_FMT_FP4_2D32 = 1,   /* E2M1 codes, one E8M0 scale per 32x32 tile */
+    FP4Q_FMT_MXFP8_1D32 = 2, /* E4M3FN bytes, one E8M0 scale per 1x32 row group */
+    FP4Q_FMT_FP4_2D64 = 3    /* E2M1 codes, one E8M0 scale per 64x64 tile; code planes as 2D32,
+                                scale grid ceil(rows/64) x ceil(cols/64) (ld_s >= ceil(cols/64)) */
 } fp4q_fmt;
 
 /*
@@ -112,7 +114,9 @@ const char* fp4q_last_error(void);
  * tightest leading dimensions (ld = C/2, ld_t = R/2, ld_s = C/32 with R, C
  * rounded up to 32).  Any out-pointer may be NULL.
  * Following the size accounting of the pages' Table 1, each code plane is a
- * quarter of the bf16 bytes; scales add one byte per 32x32 tile.
+ * quarter of the bf16 bytes; scales add one byte per 32x32 tile.  (With
+ * 64x64 blocks the planes are the same and the grid is
+ * ceil(rows/64) x ceil(cols/64) bytes.)
  */
 int fp4q_quant2d_sizes(int64_t rows, int64_t cols, int64_t* codes_bytes,
                        int64_t* codes_t_bytes, int64_t* scales_bytes);
@@ -133,7 +137,10 @@ int fp4q_quant2d_sizes(int64_t rows, int64_t cols, int64_t* codes_bytes,
  *            b = max(r,c), taking half (b%8) of the 128-bit output; rounding
  *            goes up iff floor(frac * 2^16) + draw >= 2^16.  Hence
  *            quant(x^T) equals quant(x)^T bit for bit.
- *   out      fmt = FP4Q_FMT_FP4_2D32, rows/cols equal to the arguments,
+ *   out      fmt = FP4Q_FMT_FP4_2D32 (32x32 blocks) or FP4Q_FMT_FP4_2D64
+ *            (64x64 blocks, one of the block sides compared in the page's
+ *            Table 4: same rule per block, same per-element random fields),
+ *            rows/cols equal to the arguments,
  *            codes, codes_t (may be NULL to skip the transposed plane) and
  *            scales set; batch must be 1.
  * One read of x writes the row plane, the transposed plane and the scales.
@@ -186,6 +193,9 @@ int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
  *   op FWD:   a = X  [T x K], b = W [N x K]  ->  C = X W^T   [T x N]
  *   op DGRAD: a = dY [T x N], b = W [N x K]  ->  C = dY W    [T x K]
  *   op WGRAD: a = dY [T x N], b = X [T x K]  ->  C = dY^T X  [N x K]
+ * FP4 operands may each have 32x32 or 64x64 scale blocks (a 64x64 block's
+ * byte is used for both of its 32-row slabs and both of its 32-wide K
+ * blocks); grouped products take 32x32 blocks only (FP4Q_EUNSUPPORTED).
  * FP4 operands must carry both planes; DGRAD reads W's transposed plane and
  * WGRAD reads the transposed planes of dY and X, so each tensor is quantized
  * once.  MXFP8 operands support FWD only (S = Q K^T); every product
@@ -209,7 +219,8 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
               int64_t c_bstride, const fp4q_groups* groups, void* hip_stream);
 
 /*
- * Dequantization X ~ P * S (Sec. 2.1 of the same page) to fp32 or bf16.
+ * Dequantization X ~ P * S (Sec. 2.1 of the same page) to fp32 or bf16, for
+ * all three formats.
  *   transposed  0: the row plane, y is rows x cols; 1 (FP4 only): the
  *               transposed plane, y is cols x rows.
  *   out_dtype   FP4Q_DT_F32 or FP4Q_DT_BF16; ldy in elements.

@@ -82,6 +82,7 @@ def test_quant2d_rejects_bad_arguments(fp4q):
         (x, 1, 64, 64, 64, 0, _desc(fp4q, rows=32)),     # shape mismatch
         (x, 1, 64, 64, 64, 0, _desc(fp4q, fmt=2)),       # wrong format
         (x, 1, 64, 64, 64, 0, _desc(fp4q, ld_t=16)),     # transposed plane too small
+        (x, 1, 64, 200, 200, 0, _desc(fp4q, fmt=3, cols=200, ld=112, ld_s=3)),  # 64-block grid too narrow
     ]
     for xp, dt, r, c, ldx, rm, d in cases:
         rc = L.fp4q_quant2d(xp, dt, r, c, ldx, rm, 0, 0, ctypes.byref(d), None)
@@ -156,6 +157,12 @@ def test_gemm_rejects_bad_arguments(fp4q):
         g = fp4q._Groups(len(offs) - 1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
         w = _desc(fp4q, rows=64 * (len(offs) - 1), cols=64, ld_t=64 * (len(offs) - 1) // 2)
         assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(w), c, 64, 0, ctypes.byref(g), None) == -1
+    # grouped products take 32x32 blocks only
+    arr = (ctypes.c_int64 * 2)(0, 64)
+    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+    a64 = _desc(fp4q, fmt=3, rows=64, cols=64)
+    assert L.fp4q_gemm(0, ctypes.byref(a64), ctypes.byref(a), c, 64, 0, ctypes.byref(g), None) == -2
+    assert "32x32" in _err(fp4q)
 
 
 def test_dequant_and_mxfp8_reject_bad_arguments(fp4q):

@@ -86,7 +86,7 @@ def quant_bytes(rows, cols):
 class Step:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, layers, torch, fq):
+    def __init__(self, layers, torch, fq, block=32):
         self.torch, self.fq = torch, fq
         self.layers = []
         for L in layers:
@@ -94,7 +94,7 @@ class Step:
             for nm in ("X", "W", "dY"):
                 a = getattr(L, nm)
                 d[nm] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-                d["q" + nm] = fq.alloc_fp4(a.shape[0], a.shape[1])
+                d["q" + nm] = fq.alloc_fp4(a.shape[0], a.shape[1], block=block)
             T, K, N = L.T, L.K, L.N
             d["Y"] = torch.empty((T, N), dtype=torch.float32, device="cuda")
             d["dX"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
@@ -197,9 +197,8 @@ def _summary(ms, work, kinds):
     return out
 
 
-def side_1b(torch, fq, wl, iters, warmup):
-    """The 1B-class layer step (up 2048->8192 and down 8192->2048 at 4096 tokens)."""
-    step = Step(wl.config_1b(), torch, fq)
+def _eager_step(step, torch, iters, warmup):
+    """Median per-launch times of a Step run eagerly, and their totals by kind."""
     work = {nm: w for _, nm, w in step.launches}
     kinds = {nm: kind for kind, nm, _ in step.launches}
     for it in range(warmup):
@@ -212,8 +211,28 @@ def side_1b(torch, fq, wl, iters, warmup):
     torch.cuda.synchronize()
     per = np.array([[s.elapsed_time(e) for (s, e) in ev[it]] for it in range(iters)])
     ms = {nm: float(np.median(per[:, j])) for j, (_, nm, _) in enumerate(step.launches)}
+    return _summary(ms, work, kinds)
+
+
+def side_1b(torch, fq, wl, iters, warmup):
+    """The 1B-class layer step (up 2048->8192 and down 8192->2048 at 4096 tokens)."""
     out = {"workload": "1b-linear-layer-step: tokens 4096, hidden 2048, FFN 8192 (up, down)"}
-    out.update(_summary(ms, work, kinds))
+    out.update(_eager_step(Step(wl.config_1b(), torch, fq), torch, iters, warmup))
+    return out
+
+
+def side_block64(torch, fq, wl, iters, warmup):
+    """The 7B layer step with 64x64 scale blocks beside the same step with
+    32x32 blocks, both timed eagerly with per-launch events: the block-size
+    throughput comparison of the page's Table 4, measured."""
+    out = {"workload": "7b-linear-layer-step with 64x64 and with 32x32 scale blocks (eager, per-launch events)"}
+    for b in (32, 64):
+        step = Step(wl.config_7b(), torch, fq, block=b)
+        out["b%d" % b] = _eager_step(step, torch, iters, warmup)
+        del step
+        torch.cuda.empty_cache()
+    for key in ("ms_per_step", "quant_ms", "gemm_ms"):
+        out[key + "_b64_over_b32"] = round(out["b64"][key] / out["b32"][key], 4)
     return out
 
 
@@ -523,7 +542,7 @@ def main():
     }
     if not args.no_side_paths:
         side = {}
-        for name, fn in (("1b", side_1b), ("moe", side_moe), ("attn", side_attn)):
+        for name, fn in (("1b", side_1b), ("moe", side_moe), ("attn", side_attn), ("block64", side_block64)):
             print("[bench] side path %s" % name, file=sys.stderr, flush=True)
             side[name] = fn(torch, fq, wl, iters=5, warmup=2)
             torch.cuda.empty_cache()

@@ -223,6 +223,35 @@ def quant1x32_fp4(x, round_mode=ROUND_SR, seed=0, stream=0):
     return codes, scales
 
 
+def quant_act1d(x, round_mode=ROUND_SR, seed=0, stream=0):
+    """1D (1x32) FP4 layout of an activation matrix X [rows x cols] for the
+    three products of a linear layer (appendix "Activations": activations are
+    quantized in 1D blocks along the hidden channels).  The forward product
+    contracts over the channels, so its plane is X quantized in 1x32 blocks
+    along its rows; the weight-gradient product contracts over the tokens, so
+    its plane is X^T quantized in 1x32 blocks along its rows (32 tokens of one
+    channel).  Each element keeps its one random field (the field of the
+    unordered pair (r, c)) in both planes.
+
+    Returns (codes [R x C/2], codes_t [C x R/2], scales [R x C/32],
+    scales_t [C x R/32]) with R, C = rows, cols rounded up to 32; rows and
+    columns in the padding hold code 0 and scale byte 0."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    rp, cp = pad32(rows), pad32(cols)
+    codes = np.zeros((rp, cp // 2), dtype=np.uint8)
+    codes_t = np.zeros((cp, rp // 2), dtype=np.uint8)
+    scales = np.zeros((rp, cp // 32), dtype=np.uint8)
+    scales_t = np.zeros((cp, rp // 32), dtype=np.uint8)
+    c, s = quant1x32_fp4(x, round_mode, seed, stream)
+    ct, st = quant1x32_fp4(np.ascontiguousarray(x.T), round_mode, seed, stream)
+    codes[:rows] = c
+    scales[:rows] = s
+    codes_t[:cols] = ct
+    scales_t[:cols] = st
+    return codes, codes_t, scales, scales_t
+
+
 def quant1d_mxfp8(x):
     """MXFP8 E4M3 with 1x32 blocks along rows; returns (codes, scales)."""
     x = np.ascontiguousarray(x)

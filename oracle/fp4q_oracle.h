@@ -89,8 +89,11 @@ int orc_quant2d_block(const void* x, int dtype, int64_t rows, int64_t cols, int6
                       uint8_t* codes, int64_t ld, uint8_t* codes_t, int64_t ld_t,
                       uint8_t* scales, int64_t ld_s);
 
-/* Conventional 1x32 FP4 quantization along rows (the non-invariant layout the
- * pages compare against).  codes [rows x ld], scales [rows x ld_s]. */
+/* 1x32 FP4 quantization along rows: the conventional layout the pages
+ * compare against, and (appendix "Activations") the activations' layout.
+ * The 1D activation layout is this function applied to X (forward plane)
+ * and to X^T (weight-gradient plane); each element draws the random field
+ * of its unordered pair in both.  codes [rows x ld], scales [rows x ld_s]. */
 int orc_quant1x32_fp4(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                       int round_mode, uint64_t seed, uint32_t stream,
                       uint8_t* codes, int64_t ld, uint8_t* scales, int64_t ld_s);

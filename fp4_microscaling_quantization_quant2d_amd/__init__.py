@@ -25,7 +25,7 @@ __all__ = ["QTensor", "fp4q_quant2d", "fp4q_quant1d_mxfp8", "fp4q_gemm", "fp4q_d
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp4q.so")
 
-FMT_FP4_2D32, FMT_MXFP8_1D32, FMT_FP4_2D64 = 1, 2, 3
+FMT_FP4_2D32, FMT_MXFP8_1D32, FMT_FP4_2D64, FMT_FP4_1D32 = 1, 2, 3, 4
 DT_BF16, DT_F32 = 1, 2
 ROUND = {"sr": 0, "rne": 1}
 OPS = {"fwd": 0, "dgrad": 1, "wgrad": 2}
@@ -42,7 +42,8 @@ class _QDesc(ctypes.Structure):
                 ("codes_t", ctypes.c_void_p), ("ld_t", ctypes.c_int64),
                 ("scales", ctypes.c_void_p), ("ld_s", ctypes.c_int64),
                 ("batch", ctypes.c_int64), ("bstride", ctypes.c_int64),
-                ("bstride_t", ctypes.c_int64), ("bstride_s", ctypes.c_int64)]
+                ("bstride_t", ctypes.c_int64), ("bstride_s", ctypes.c_int64),
+                ("scales_t", ctypes.c_void_p), ("ld_st", ctypes.c_int64)]
 
 
 class _QItem(ctypes.Structure):
@@ -126,7 +127,11 @@ class QTensor:
     fmt 1 (FP4, 2D 32x32 blocks): codes [R, ld] row plane, codes_t [C, ld_t]
     transposed plane (optional), scales [R/32, ld_s] E8M0 -- R, C = rows, cols
     rounded up to 32.  fmt 3 (FP4, 2D 64x64 blocks): the same planes with
-    scales [ceil(rows/64), ld_s].  fmt 2 (MXFP8, 1x32): codes [rows, ld] E4M3
+    scales [ceil(rows/64), ld_s].  fmt 4 (FP4, 1D activation layout): the
+    same planes, with one byte per 1x32 block of each plane row in tiled
+    grids: scales [ceil(R/128), ld_s] for the row plane, scales_t
+    [ceil(C/128), ld_st] for the transposed plane, one 512-byte chunk per
+    128 rows x 128 codes (ld_s, ld_st multiples of 16).  fmt 2 (MXFP8, 1x32): codes [rows, ld] E4M3
     bytes, scales [rows, ld_s].  batch > 1 stacks items at the given byte
     strides.
     """
@@ -140,6 +145,7 @@ class QTensor:
     bstride: int = 0
     bstride_t: int = 0
     bstride_s: int = 0
+    scales_t: Optional[torch.Tensor] = None
 
     def desc(self):
         d = _QDesc()
@@ -151,6 +157,9 @@ class QTensor:
             d.ld_t = self.codes_t.stride(-2)
         d.scales = self.scales.data_ptr()
         d.ld_s = self.scales.stride(-2)
+        if self.scales_t is not None:
+            d.scales_t = self.scales_t.data_ptr()
+            d.ld_st = self.scales_t.stride(-2)
         d.batch, d.bstride, d.bstride_t, d.bstride_s = (self.batch, self.bstride, self.bstride_t,
                                                         self.bstride_s)
         return d
@@ -166,12 +175,19 @@ def fp4q_quant2d_sizes(rows, cols):
 
 def alloc_fp4(rows, cols, device="cuda", transposed=True, block=32):
     """Output buffers for fp4q_quant2d with the tightest leading dimensions;
-    block 32 or 64 picks the square scale block (FMT_FP4_2D32 / FMT_FP4_2D64)."""
-    if block not in (32, 64):
-        raise Fp4qError("block must be 32 or 64, got %r" % (block,))
+    block 32 or 64 picks the square scale block (FMT_FP4_2D32 / FMT_FP4_2D64),
+    block "1d" the activation layout (FMT_FP4_1D32)."""
+    if block not in (32, 64, "1d"):
+        raise Fp4qError("block must be 32, 64 or '1d', got %r" % (block,))
     R, C = _pad32(rows), _pad32(cols)
     codes = torch.empty((R, C // 2), dtype=torch.uint8, device=device)
     codes_t = torch.empty((C, R // 2), dtype=torch.uint8, device=device) if transposed else None
+    if block == "1d":
+        # tiled grids: one 512-byte chunk per 128 rows x 128 codes of a plane
+        g = lambda n: -(-n // 128)
+        scales = torch.empty((g(R), 512 * g(C)), dtype=torch.uint8, device=device)
+        scales_t = torch.empty((g(C), 512 * g(R)), dtype=torch.uint8, device=device) if transposed else None
+        return QTensor(FMT_FP4_1D32, rows, cols, codes, scales, codes_t, scales_t=scales_t)
     scales = torch.empty((-(-rows // block), -(-cols // block)), dtype=torch.uint8, device=device)
     return QTensor(FMT_FP4_2D32 if block == 32 else FMT_FP4_2D64, rows, cols, codes, scales, codes_t)
 

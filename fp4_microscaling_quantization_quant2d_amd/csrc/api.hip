@@ -56,12 +56,26 @@ int max_k(int fmt)
 }
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
+// 1D layout: a plane with `width` codes per row has a tiled scale grid of
+// one 512-byte chunk per 128 rows x 128 codes, ld bytes per 128-row group.
+inline int64_t act1d_grid_ld(int64_t width) { return 512 * ((width + 127) / 128); }
+
+int check_1d_grid(const uint8_t* s, int64_t ld, int64_t width, const char* name, const char* what)
+{
+    if (!s)
+        return fail(FP4Q_EINVAL, "%s: null %s", name, what);
+    if (ld < act1d_grid_ld(width) || ld % 16 || !aligned16(s))
+        return fail(FP4Q_EINVAL, "%s: %s needs a leading dim >= %lld, a multiple of 16, and 16-byte alignment",
+                    name, what, (long long)act1d_grid_ld(width));
+    return FP4Q_OK;
+}
+
 int check_fp4_tensor(const fp4q_qtensor* t, const char* name, bool need_t)
 {
     if (!t)
         return fail(FP4Q_EINVAL, "%s: null descriptor", name);
-    if (t->fmt != FP4Q_FMT_FP4_2D32 && t->fmt != FP4Q_FMT_FP4_2D64)
-        return fail(FP4Q_EINVAL, "%s: fmt %d is not FP4Q_FMT_FP4_2D32 or FP4Q_FMT_FP4_2D64", name, t->fmt);
+    if (t->fmt != FP4Q_FMT_FP4_2D32 && t->fmt != FP4Q_FMT_FP4_2D64 && t->fmt != FP4Q_FMT_FP4_1D32)
+        return fail(FP4Q_EINVAL, "%s: fmt %d is not an FP4 format", name, t->fmt);
     if (t->rows <= 0 || t->cols <= 0 || t->rows > kMaxDim || t->cols > kMaxDim)
         return fail(FP4Q_EINVAL, "%s: bad shape %lld x %lld", name, (long long)t->rows, (long long)t->cols);
     const int64_t R = pad32(t->rows), C = pad32(t->cols);
@@ -70,16 +84,28 @@ int check_fp4_tensor(const fp4q_qtensor* t, const char* name, bool need_t)
     if (t->ld < C / 2 || t->ld % 16 || !aligned16(t->codes))
         return fail(FP4Q_EINVAL, "%s: row plane needs ld >= %lld, ld %% 16 == 0 and 16-byte alignment", name,
                     (long long)(C / 2));
-    const int64_t blk = t->fmt == FP4Q_FMT_FP4_2D64 ? 64 : 32;
-    if (t->ld_s < (t->cols + blk - 1) / blk)
-        return fail(FP4Q_EINVAL, "%s: ld_s %lld < %lld", name, (long long)t->ld_s,
-                    (long long)((t->cols + blk - 1) / blk));
-    if (need_t) {
+    const bool is1d = t->fmt == FP4Q_FMT_FP4_1D32;
+    if (is1d) {
+        int rc = check_1d_grid(t->scales, t->ld_s, C, name, "scales");
+        if (rc)
+            return rc;
+    } else {
+        const int64_t blk = t->fmt == FP4Q_FMT_FP4_2D64 ? 64 : 32;
+        if (t->ld_s < (t->cols + blk - 1) / blk)
+            return fail(FP4Q_EINVAL, "%s: ld_s %lld < %lld", name, (long long)t->ld_s,
+                        (long long)((t->cols + blk - 1) / blk));
+    }
+    if (need_t || (is1d && t->codes_t)) {
         if (!t->codes_t)
             return fail(FP4Q_EINVAL, "%s: the transposed plane is required", name);
         if (t->ld_t < R / 2 || t->ld_t % 16 || !aligned16(t->codes_t))
             return fail(FP4Q_EINVAL, "%s: transposed plane needs ld_t >= %lld, ld_t %% 16 == 0, 16-byte alignment",
                         name, (long long)(R / 2));
+        if (is1d) {
+            int rc = check_1d_grid(t->scales_t, t->ld_st, R, name, "scales_t");
+            if (rc)
+                return rc;
+        }
     }
     if (t->batch < 1)
         return fail(FP4Q_EINVAL, "%s: batch must be >= 1", name);
@@ -137,7 +163,7 @@ int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dt
             return fail(FP4Q_EINVAL, "%s: item %d: out shape %lld x %lld != input", fn, i, (long long)out->rows,
                         (long long)out->cols);
         if (i > 0 && out->fmt != fmt)
-            return fail(FP4Q_EINVAL, "%s: item %d: block size differs from item 0", fn, i);
+            return fail(FP4Q_EINVAL, "%s: item %d: format differs from item 0", fn, i);
         fmt = out->fmt;
         if (out->batch != 1)
             return fail(FP4Q_EINVAL, "%s: item %d: out batch must be 1", fn, i);
@@ -162,6 +188,8 @@ int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dt
         p.ld_t = out->ld_t;
         p.scales = out->scales;
         p.ld_s = out->ld_s;
+        p.scales_t = out->fmt == FP4Q_FMT_FP4_1D32 ? out->scales_t : nullptr;
+        p.ld_st = out->ld_st;
         p.key0 = (uint32_t)seed;
         p.key1 = (uint32_t)(seed >> 32);
         p.stream = it.stream_id;
@@ -169,7 +197,10 @@ int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dt
         aligned = aligned && aligned16(it.x) && (it.ldx * esz) % 16 == 0;
     }
     return hip_status(fp4q::launch_quant2d(b, dtype == FP4Q_DT_F32, round_mode == FP4Q_ROUND_RNE, aligned,
-                                           fmt == FP4Q_FMT_FP4_2D64 ? 64 : 32, static_cast<hipStream_t>(hip_stream)),
+                                           fmt == FP4Q_FMT_FP4_1D32   ? fp4q::kLayout1D
+                                           : fmt == FP4Q_FMT_FP4_2D64 ? fp4q::kLayout2D64
+                                                                      : fp4q::kLayout2D32,
+                                           static_cast<hipStream_t>(hip_stream)),
                       fn);
 }
 
@@ -327,6 +358,33 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
     g.bs_sb = b->bstride_s;
     g.sh_a = a->fmt == FP4Q_FMT_FP4_2D64 ? 6 : 5;
     g.sh_b = b->fmt == FP4Q_FMT_FP4_2D64 ? 6 : 5;
+    // 1D-layout operands: the plane read takes its own tiled grid (scales for
+    // the row plane, scales_t for the transposed plane).
+    int oned = 0;
+    {
+        const bool a1 = a->fmt == FP4Q_FMT_FP4_1D32, b1 = b->fmt == FP4Q_FMT_FP4_1D32;
+        if ((a1 || b1) && a->batch != 1)
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: 1D-layout operands take batch 1");
+        if (a1) {
+            oned |= 1;
+            if (a_st) {
+                g.sa = a->scales_t;
+                g.lds_a = a->ld_st;
+            }
+            a_st = false;
+        }
+        if (b1) {
+            oned |= 2;
+            if (b_st) {
+                g.sb = b->scales_t;
+                g.lds_b = b->ld_st;
+            }
+            b_st = false;
+        }
+        if (((oned & 1) && ((int64_t)g.a_rows + 127) / 128 * g.lds_a > INT_MAX) ||
+            ((oned & 2) && ((int64_t)g.b_rows + 127) / 128 * g.lds_b > INT_MAX))
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: a 1D scale grid exceeds 2 GiB");
+    }
     // The kernels address each operand plane through a buffer descriptor with
     // a 32-bit byte range; a tile may reach one tile height past the last row.
     {
@@ -411,7 +469,7 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
     if (fp4q::gemm_lds_bytes(fp8 ? 2 : 1, (int)kmax) > kMaxLdsBytes)
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: K %lld too large for the %s tile (max %d)", (long long)kmax,
                     fp8 ? "MXFP8" : "FP4", fp8 ? max_k(2) : max_k(1));
-    return hip_status(fp4q::launch_gemm(g, fp8 ? 2 : 1, a_st, b_st, grouped_op, (int)a->batch,
+    return hip_status(fp4q::launch_gemm(g, fp8 ? 2 : 1, a_st, b_st, oned, grouped_op, (int)a->batch,
                                         static_cast<hipStream_t>(hip_stream)),
                       "fp4q_gemm");
 }
@@ -425,7 +483,9 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
     int rc;
     fp4q::DequantArgs p;
     int fmt;
-    if (q->fmt == FP4Q_FMT_FP4_2D32 || q->fmt == FP4Q_FMT_FP4_2D64) {
+    const uint8_t* scales = q->scales;
+    int64_t ld_s = q->ld_s;
+    if (q->fmt == FP4Q_FMT_FP4_2D32 || q->fmt == FP4Q_FMT_FP4_2D64 || q->fmt == FP4Q_FMT_FP4_1D32) {
         if ((rc = check_fp4_tensor(q, "fp4q_dequant q", transposed != 0)))
             return rc;
         fmt = 1;
@@ -433,6 +493,13 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
         p.codes = transposed ? q->codes_t : q->codes;
         p.ld = transposed ? q->ld_t : q->ld;
         p.scale_transposed = transposed ? 1 : 0;
+        if (q->fmt == FP4Q_FMT_FP4_1D32) {
+            p.scale_transposed = 2;
+            if (transposed) {
+                scales = q->scales_t;
+                ld_s = q->ld_st;
+            }
+        }
         p.rows = (int)(transposed ? q->cols : q->rows);
         p.cols = (int)(transposed ? q->rows : q->cols);
     } else if (q->fmt == FP4Q_FMT_MXFP8_1D32) {
@@ -456,8 +523,8 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
         return fail(FP4Q_EINVAL, "fp4q_dequant: batch must be 1");
     if (ldy < p.cols)
         return fail(FP4Q_EINVAL, "fp4q_dequant: ldy %lld < %d", (long long)ldy, p.cols);
-    p.scales = q->scales;
-    p.ld_s = q->ld_s;
+    p.scales = scales;
+    p.ld_s = ld_s;
     p.y = y;
     p.ldy = ldy;
     return hip_status(fp4q::launch_dequant(p, fmt, out_dtype == FP4Q_DT_BF16, static_cast<hipStream_t>(hip_stream)),

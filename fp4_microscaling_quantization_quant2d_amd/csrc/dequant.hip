@@ -1,6 +1,6 @@
 // Dequantization X ~ P * S ("Stable FP4 Training via Transposition-Invariant
-// Block Quantization", Sec. 2.1) of a FP4 2D-block plane (row or transposed)
-// or a MXFP8 1x32 plane, to fp32 or bf16.  One lane per 8 output elements.
+// Block Quantization", Sec. 2.1) of a FP4 2D-block plane (row or transposed),
+// a plane of the 1D activation layout, or a MXFP8 1x32 plane, to fp32 or bf16.  One lane per 8 output elements.
 // Every E2M1 or E4M3 value times a power of two is exact in fp32, and the
 // FP4 products (at most 2 significant bits) are exact in bf16 as well.
 #include "fp4q_device.hpp"
@@ -56,8 +56,13 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs p)
                 const uint32_t byte = p.codes[(int64_t)r * p.ld + (c >> 1)];
                 const uint32_t nib = (byte >> (4 * (c & 1))) & 15u;
                 const int bs = p.block_shift;
-                const uint32_t sb = p.scale_transposed ? p.scales[(int64_t)(c >> bs) * p.ld_s + (r >> bs)]
-                                                       : p.scales[(int64_t)(r >> bs) * p.ld_s + (c >> bs)];
+                uint32_t sb;
+                if (p.scale_transposed == 2)  // 1D layout: tiled grid of this plane
+                    sb = p.scales[(int64_t)(r >> 7) * p.ld_s + (c >> 7) * 512 + ((c >> 5) & 1) * 256 + (r & 31) * 8 +
+                                  ((r >> 5) & 3) * 2 + ((c >> 6) & 1)];
+                else
+                    sb = p.scale_transposed ? p.scales[(int64_t)(c >> bs) * p.ld_s + (r >> bs)]
+                                            : p.scales[(int64_t)(r >> bs) * p.ld_s + (c >> bs)];
                 val = e2m1_val(nib) * pow2_e8m0(sb);
             } else {
                 const uint32_t byte = p.codes[(int64_t)r * p.ld + c];

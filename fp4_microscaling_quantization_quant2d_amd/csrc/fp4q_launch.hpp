@@ -17,8 +17,10 @@ struct Quant2dArgs {
     int64_t ld;
     uint8_t* codes_t;  // [cols_pad x ld_t] or null
     int64_t ld_t;
-    uint8_t* scales;   // [rows_pad/32 x ld_s]
+    uint8_t* scales;   // 2D: [rows_pad/b x ld_s]; 1D: [rows_pad x ld_s], ld_s % 4 == 0
     int64_t ld_s;
+    uint8_t* scales_t; // 1D only: [cols_pad x ld_st] scales of the transposed plane, ld_st % 4 == 0
+    int64_t ld_st;
     uint32_t key0, key1, stream;
 };
 
@@ -34,8 +36,10 @@ struct Quant2dBatch {
 // Regions (workgroups) of one padded matrix.
 int64_t quant2d_regions(int64_t rows_pad, int64_t cols_pad);
 
-// block: 32 or 64 (square scale blocks).
-hipError_t launch_quant2d(const Quant2dBatch& b, bool f32, bool rne, bool aligned, int block, hipStream_t s);
+// Scale layouts: square 32x32 or 64x64 blocks, or the 1D activation layout
+// (1x32 blocks along the rows of each plane).
+enum QuantLayout { kLayout2D32 = 0, kLayout2D64 = 1, kLayout1D = 2 };
+hipError_t launch_quant2d(const Quant2dBatch& b, bool f32, bool rne, bool aligned, int layout, hipStream_t s);
 
 struct Mxfp8Args {
     const void* x;
@@ -55,7 +59,7 @@ struct DequantArgs {
     int64_t ld;
     const uint8_t* scales;
     int64_t ld_s;
-    int scale_transposed;  // FP4: scale of (r, c) at (c/b)*ld_s + r/b
+    int scale_transposed;  // FP4: 1 -- scale of (r, c) at (c/b)*ld_s + r/b; 2 -- the 1D layout's tiled grid
     int block_shift;       // FP4: log2 of the square block side b (5 or 6)
     int rows, cols;        // output shape
     void* y;
@@ -95,8 +99,10 @@ struct GemmArgs {
 enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };
 
 // fmt: 1 FP4, 2 FP8.  a_st / b_st: transposed scale grids (FP4 only).
+// oned: bit 0 / bit 1 -- A / B carry the 1D layout's tiled scale grid
+// (chunk (g, q) of rows 128g.., K-blocks 4q.. at g*lds + q*512; FP4, dense).
 // grouped_op: -1 dense/batched, else the op whose grouped wiring applies.
-hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int grouped_op, int batch,
+hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
                        hipStream_t s);
 
 // Output tile of the GEMM kernel (grouped launches size their grids with it).

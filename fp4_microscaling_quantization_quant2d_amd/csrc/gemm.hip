@@ -22,7 +22,10 @@
 //   MXFP8: four slots of 64 K-bytes per row, three in flight.
 // The raw buffer range check zero-fills rows and K chunks beyond the
 // operand, so the loop has no branches; the tile's scale bytes for its whole
-// K range sit in LDS.
+// K range sit in LDS.  An FP4 operand in the 1D activation layout (one scale
+// per row and K-block) has 256 rows x K/32 bytes per tile, too many to keep;
+// its tiled scale grid streams into a two-slot ring beside the pair ring,
+// 2 KB per pair, already in the byte order of the 2D path's per-stage words.
 // Tiles are ordered so each XCD walks a contiguous, M-grouped range of the
 // tile grid, keeping A/B panels resident in that XCD's L2.
 #include "fp4q_launch.hpp"
@@ -108,6 +111,9 @@ __device__ __forceinline__ int swz2(int r, int c) { return r * kPairRowBytes + (
 // inside the row.
 __host__ __device__ __forceinline__ int scale_kb_pad(int kblocks) { return ((kblocks + 3) & ~3) + 12; }
 __host__ __device__ __forceinline__ int scale_rows(int fmt) { return fmt == 1 ? kBM / 32 : kBM; }
+// LDS ring of a 1D-layout operand's scale chunks: two slots of one pair
+// (256 rows x 8 K-blocks).
+constexpr int kRing1D = 2 * 2048;
 
 struct Problem {
     const uint8_t* a;
@@ -187,7 +193,7 @@ __device__ __forceinline__ void scale_geometry(int& r, int& kb0, int& kstep)
     kstep = FMT == 1 ? 32 : 1;
 }
 
-template <int FMT, bool A_ST, bool B_ST>
+template <int FMT, bool A_ST, bool B_ST, bool A1D, bool B1D>
 __device__ __forceinline__ void scales_load(ScaleStage& st, const GemmArgs& g, const Problem& P, int m0, int n0,
                                             int kblocks, int kbpad)
 {
@@ -197,16 +203,18 @@ __device__ __forceinline__ void scales_load(ScaleStage& st, const GemmArgs& g, c
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int k = kb0 + b * 8 * kstep;
-        scale_batch_load<FMT, A_ST>(st.va[b], P.sa, g.lds_a, ra, ra < P.a_rows && k < kbpad, k, kstep, kblocks,
-                                    g.sh_a);
-        scale_batch_load<FMT, B_ST>(st.vb[b], P.sb, g.lds_b, rb, rb < P.b_rows && k < kbpad, k, kstep, kblocks,
-                                    g.sh_b);
+        if constexpr (!A1D)
+            scale_batch_load<FMT, A_ST>(st.va[b], P.sa, g.lds_a, ra, ra < P.a_rows && k < kbpad, k, kstep, kblocks,
+                                        g.sh_a);
+        if constexpr (!B1D)
+            scale_batch_load<FMT, B_ST>(st.vb[b], P.sb, g.lds_b, rb, rb < P.b_rows && k < kbpad, k, kstep, kblocks,
+                                        g.sh_b);
     }
 }
 
 // Stores the batches loaded by scales_load, then loads and stores any
 // K-blocks beyond them.
-template <int FMT, bool A_ST, bool B_ST>
+template <int FMT, bool A_ST, bool B_ST, bool A1D, bool B1D>
 __device__ __forceinline__ void scales_store(const ScaleStage& st, const GemmArgs& g, const Problem& P,
                                              uint8_t* sla, uint8_t* slb, int m0, int n0, int kblocks, int kbpad)
 {
@@ -216,16 +224,24 @@ __device__ __forceinline__ void scales_store(const ScaleStage& st, const GemmArg
     uint8_t* db = FMT == 1 ? slb + 2 * r : slb + r * kbpad;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-        scale_batch_store<FMT>(st.va[b], da, kb0 + b * 8 * kstep, kstep, kbpad);
-        scale_batch_store<FMT>(st.vb[b], db, kb0 + b * 8 * kstep, kstep, kbpad);
+        if constexpr (!A1D)
+            scale_batch_store<FMT>(st.va[b], da, kb0 + b * 8 * kstep, kstep, kbpad);
+        if constexpr (!B1D)
+            scale_batch_store<FMT>(st.vb[b], db, kb0 + b * 8 * kstep, kstep, kbpad);
     }
+    if constexpr (A1D && B1D)
+        return;
     const int ra = m0 + (FMT == 1 ? 32 * r : r), rb = n0 + (FMT == 1 ? 32 * r : r);
     for (int k = kb0 + 16 * kstep; k < kbpad; k += 8 * kstep) {
         uint32_t va[8], vb[8];
-        scale_batch_load<FMT, A_ST>(va, P.sa, g.lds_a, ra, ra < P.a_rows, k, kstep, kblocks, g.sh_a);
-        scale_batch_load<FMT, B_ST>(vb, P.sb, g.lds_b, rb, rb < P.b_rows, k, kstep, kblocks, g.sh_b);
-        scale_batch_store<FMT>(va, da, k, kstep, kbpad);
-        scale_batch_store<FMT>(vb, db, k, kstep, kbpad);
+        if constexpr (!A1D)
+            scale_batch_load<FMT, A_ST>(va, P.sa, g.lds_a, ra, ra < P.a_rows, k, kstep, kblocks, g.sh_a);
+        if constexpr (!B1D)
+            scale_batch_load<FMT, B_ST>(vb, P.sb, g.lds_b, rb, rb < P.b_rows, k, kstep, kblocks, g.sh_b);
+        if constexpr (!A1D)
+            scale_batch_store<FMT>(va, da, k, kstep, kbpad);
+        if constexpr (!B1D)
+            scale_batch_store<FMT>(vb, db, k, kstep, kbpad);
     }
 }
 
@@ -243,9 +259,12 @@ __device__ __forceinline__ void wait_vm_and_barrier()
 // KT: K may end inside an FP4 pair (K % 256 != 0), so loads check the K
 // range; without it only pairs past the end of K (loaded but never
 // multiplied) may read past a row's K bytes.
-template <int FMT, bool A_ST, bool B_ST, bool KT>
+// ONED: bit 0 -- A is an FP4 operand in the 1D activation layout, bit 1 -- B.
+template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
 {
+    constexpr bool A1D = FMT == 1 && (ONED & 1), B1D = FMT == 1 && (ONED & 2);
+    constexpr int kS1D = 2 * ((int)A1D + (int)B1D);  // 1D scale loads per wave and pair
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -257,7 +276,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     const int kblocks = P.K / 32;
     const int kbpad = scale_kb_pad(kblocks);
     uint8_t* sla = lds + kTileLds;
-    uint8_t* slb = sla + scale_rows(FMT) * kbpad;
+    uint8_t* slb = sla + (A1D ? kRing1D : scale_rows(FMT) * kbpad);
 
     // Buffer->LDS loads.  One instruction of a wave fills 1 KB of LDS, lane l
     // at byte 16*l; wave w issues instructions 4w..4w+3 of each operand tile,
@@ -300,11 +319,47 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             pbB[par] = (uint32_t)((n0 + r) * g.ldb + pchunk[par] * 16);
         }
     }
+    // 1D scale chunks: pair p needs chunks (2tm + gl, 2p + par) of the tiled
+    // grid for gl, par in {0, 1} -- 2 KB, eight 256-byte DMA loads.  Wave w
+    // issues two: chunk-row gl = w/2, half stage par = w%2, quarters v = 0, 1;
+    // in the ring slot they land at gl*1024 + par*512 + v*256.  Chunks past
+    // the K-blocks of the operand, and rows past its groups, read as zero.
+    const int nq = (kblocks + 3) >> 2;
+    uint32_t s1a = 0, s1b = 0;
+    __amdgpu_buffer_rsrc_t rSA = rA, rSB = rB;
+    if constexpr (A1D) {
+        rSA = __builtin_amdgcn_make_buffer_rsrc((void*)P.sa, (short)0,
+                                                (int)((int64_t)((P.a_rows + 127) >> 7) * g.lds_a), 0x00020000);
+        s1a = (uint32_t)((2 * P.tm + (wave >> 1)) * g.lds_a + (wave & 1) * 512 + 4 * lane);
+    }
+    if constexpr (B1D) {
+        rSB = __builtin_amdgcn_make_buffer_rsrc((void*)P.sb, (short)0,
+                                                (int)((int64_t)((P.b_rows + 127) >> 7) * g.lds_b), 0x00020000);
+        s1b = (uint32_t)((2 * P.tn + (wave >> 1)) * g.lds_b + (wave & 1) * 512 + 4 * lane);
+    }
+    auto issue_scales1d = [&](int p, int wv) {
+        const uint32_t far = 2 * p + (wv & 1) >= nq ? kOob : 0u;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int dst = (p & 1) * 2048 + (wv >> 1) * 1024 + (wv & 1) * 512 + v * 256;
+            if constexpr (A1D)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, LDS_PTR(sla + dst), 4,
+                                                         (int)((s1a + (uint32_t)(p * 1024 + v * 256)) | far), 0, 0, 0);
+            if constexpr (B1D)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, LDS_PTR(slb + dst), 4,
+                                                         (int)((s1b + (uint32_t)(p * 1024 + v * 256)) | far), 0, 0, 0);
+        }
+    };
     // Loads q of both operands for pair p (128 K-bytes per row) into slot p%2.
     // Load k (0..15) of pair p into slot p%2: instruction k/2 of operand A
     // (k even) or B (k odd).
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // LDS addresses in scalar registers
     auto issue_load = [&](int p, int k) {
+        // a pair's 1D scale loads go out just before its first data load, so
+        // every wait that covers the pair's data covers them as well
+        if (A1D || B1D)
+            if (k == 0)
+                issue_scales1d(p, wave_s);
         const int q = k >> 1;
         uint8_t* base = lds + (p & 1) * kPairTileBytes + (8 * wave_s + q) * 1024;
         const uint32_t kfar =
@@ -368,9 +423,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     auto read_item = [&](int h, auto SLOT, auto PAR, int e, Frag& N) {
         const int slot = SLOT, par = PAR;  // compile-time constants or (the slot) a uniform value
         if (e == 0) {
-            N.sa = *reinterpret_cast<const v2u*>(sla + h * 32 + khalf * 16 + wm * 8);
+            if constexpr (A1D)
+                N.sa = *reinterpret_cast<const v2u*>(sla + slot * 2048 + wm * 1024 + par * 512 + khalf * 256 +
+                                                     lrow32 * 8);
+            else
+                N.sa = *reinterpret_cast<const v2u*>(sla + h * 32 + khalf * 16 + wm * 8);
         } else if (e == 1) {
-            N.sb = *reinterpret_cast<const v2u*>(slb + h * 32 + khalf * 16 + wn * 8);
+            if constexpr (B1D)
+                N.sb = *reinterpret_cast<const v2u*>(slb + slot * 2048 + wn * 1024 + par * 512 + khalf * 256 +
+                                                     lrow32 * 8);
+            else
+                N.sb = *reinterpret_cast<const v2u*>(slb + h * 32 + khalf * 16 + wn * 8);
         } else {
             const int j = (e - 2) >> 3, k = (e - 2) & 7;
             if (k == 0)
@@ -508,7 +571,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             mfma_group(C, G, 2, 4);
             if (g8 == 3) {
                 if constexpr (L == 2)
-                    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+                    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(8 + kS1D) : "memory");
                 else
                     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
             }
@@ -531,7 +594,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     const int npair = (kbytes + kPairRowBytes - 1) / kPairRowBytes;
     {
         ScaleStage st;
-        scales_load<FMT, A_ST, B_ST>(st, g, P, m0, n0, kblocks, kbpad);
+        scales_load<FMT, A_ST, B_ST, A1D, B1D>(st, g, P, m0, n0, kblocks, kbpad);
         __builtin_amdgcn_sched_barrier(0);
         if (FMT == 1) {
 #pragma unroll
@@ -546,12 +609,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             issue(2);
         }
         __builtin_amdgcn_sched_barrier(0);
-        scales_store<FMT, A_ST, B_ST>(st, g, P, sla, slb, m0, n0, kblocks, kbpad);
+        scales_store<FMT, A_ST, B_ST, A1D, B1D>(st, g, P, sla, slb, m0, n0, kblocks, kbpad);
     }
     // Stage 0 and the scale bytes must be in LDS; the later stages may still
     // be in flight.
     if (FMT == 1)
-        asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(12 + kS1D) : "memory");
     else
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kDmaPerStage) : "memory");
     int s = 0;
@@ -673,7 +736,7 @@ __device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int&
     tn = in / rows;
 }
 
-template <int FMT, bool A_ST, bool B_ST, bool KT>
+template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
 {
     const int bz = blockIdx.y;
@@ -690,7 +753,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
     P.b_rows = g.b_rows;
     const int ntm = (g.M + kBM - 1) / kBM, ntn = (g.N + kBN - 1) / kBN;
     tile_of<FMT == 1 ? 4 : 8>(blockIdx.x, ntm, ntn, P.tm, P.tn);
-    gemm_tile<FMT, A_ST, B_ST, KT>(g, P);
+    gemm_tile<FMT, A_ST, B_ST, KT, ONED>(g, P);
 }
 
 // Grouped (expert) products.  Group g owns token rows [row_off[g], row_off[g+1]).
@@ -748,11 +811,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
     const int local = pid - g.tile_start[grp];
     P.tm = local / ntn;
     P.tn = local - P.tm * ntn;
-    gemm_tile<1, A_ST, B_ST, true>(g, P);
+    gemm_tile<1, A_ST, B_ST, true, 0>(g, P);
 }
 
-// Dynamic LDS: two stage buffers plus the tile's scale bytes for its K range.
-size_t lds_bytes(int fmt, int K) { return kTileLds + 2 * (size_t)scale_rows(fmt) * scale_kb_pad(K / 32); }
+// Dynamic LDS: two stage buffers plus, per operand, the tile's scale bytes
+// for its K range or (1D layout) the scale chunk ring.
+size_t lds_bytes(int fmt, int K, int oned = 0)
+{
+    const size_t full = (size_t)scale_rows(fmt) * scale_kb_pad(K / 32);
+    return kTileLds + ((oned & 1) ? kRing1D : full) + ((oned & 2) ? kRing1D : full);
+}
 
 // Raises a kernel's dynamic LDS limit to the whole 160 KB of a CU, once per
 // (kernel, device).
@@ -785,24 +853,25 @@ hipError_t allow_lds(F* fn, size_t bytes)
     return allow_lds_raw(reinterpret_cast<const void*>(fn), bytes);
 }
 
-template <int FMT, bool A_ST, bool B_ST, bool KT>
+template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED>
 hipError_t launch_dense_k(const GemmArgs& g, int batch, hipStream_t s)
 {
     const int ntm = (g.M + kBM - 1) / kBM, ntn = (g.N + kBN - 1) / kBN;
-    const size_t lb = lds_bytes(FMT, g.K);
-    hipError_t e = allow_lds(gemm_dense_kernel<FMT, A_ST, B_ST, KT>, lb);
+    const size_t lb = lds_bytes(FMT, g.K, ONED);
+    hipError_t e = allow_lds(gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED>, lb);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST, KT>), dim3(ntm * ntn, batch), dim3(kThreads), lb, s, g);
+    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED>), dim3(ntm * ntn, batch), dim3(kThreads), lb, s,
+                       g);
     return hipGetLastError();
 }
 
-template <int FMT, bool A_ST, bool B_ST>
+template <int FMT, bool A_ST, bool B_ST, int ONED = 0>
 hipError_t launch_dense(const GemmArgs& g, int batch, hipStream_t s)
 {
     if (FMT == 1 && g.K % 256 == 0)
-        return launch_dense_k<FMT, A_ST, B_ST, false>(g, batch, s);
-    return launch_dense_k<FMT, A_ST, B_ST, true>(g, batch, s);
+        return launch_dense_k<FMT, A_ST, B_ST, false, ONED>(g, batch, s);
+    return launch_dense_k<FMT, A_ST, B_ST, true, ONED>(g, batch, s);
 }
 
 template <int OP, bool A_ST, bool B_ST>
@@ -830,9 +899,18 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t s)
 
 } // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, int fmt, bool a_st, bool b_st, int grouped_op, int batch,
+hipError_t launch_gemm(const GemmArgs& g, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
                        hipStream_t s)
 {
+    // 1D-layout operands (FP4, dense): the grid orientation of such an
+    // operand does not apply.
+    if (fmt == 1 && grouped_op < 0 && oned != 0) {
+        if (oned == 3)
+            return launch_dense<1, false, false, 3>(g, batch, s);
+        if (oned == 1)
+            return b_st ? launch_dense<1, false, true, 1>(g, batch, s) : launch_dense<1, false, false, 1>(g, batch, s);
+        return a_st ? launch_dense<1, true, false, 2>(g, batch, s) : launch_dense<1, false, false, 2>(g, batch, s);
+    }
     if (grouped_op == kGemmFwd)
         return launch_grouped<kGemmFwd, false, false>(g, s);
     if (grouped_op == kGemmDgrad)
@@ -852,6 +930,6 @@ hipError_t launch_gemm(const GemmArgs& g, int fmt, bool a_st, bool b_st, int gro
 
 int gemm_tile_m() { return kBM; }
 int gemm_tile_n() { return kBN; }
-size_t gemm_lds_bytes(int fmt, int K) { return lds_bytes(fmt, K); }
+size_t gemm_lds_bytes(int fmt, int K) { return lds_bytes(fmt, K, 0); }
 
 } // namespace fp4q

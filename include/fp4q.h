@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 1
+#define FP4Q_ABI_VERSION 2
 
 typedef enum {
     FP4Q_OK = 0,
@@ -53,8 +53,10 @@ typedef enum { FP4Q_OP_FWD = 0, FP4Q_OP_DGRAD = 1, FP4Q_OP_WGRAD = 2 } fp4q_op;
 typedef enum {
     FP4Q_FMT_FP4_2D32 = 1,   /* E2M1 codes, one E8M0 scale per 32x32 tile */
     FP4Q_FMT_MXFP8_1D32 = 2, /* E4M3FN bytes, one E8M0 scale per 1x32 row group */
-    FP4Q_FMT_FP4_2D64 = 3    /* E2M1 codes, one E8M0 scale per 64x64 tile; code planes as 2D32,
+    FP4Q_FMT_FP4_2D64 = 3,   /* E2M1 codes, one E8M0 scale per 64x64 tile; code planes as 2D32,
                                 scale grid ceil(rows/64) x ceil(cols/64) (ld_s >= ceil(cols/64)) */
+    FP4Q_FMT_FP4_1D32 = 4    /* E2M1 codes, activation layout: one E8M0 scale per 1x32 block of
+                                each plane's rows (layout below) */
 } fp4q_fmt;
 
 /*
@@ -69,6 +71,21 @@ typedef enum {
  *   Requires ld >= C/2, ld_t >= R/2, ld_s >= C/32; ld and ld_t multiples of 16
  *   and the planes 16-byte aligned.  Padding nibbles (r >= rows or c >= cols)
  *   are written as 0.
+ * FP4_1D32 (written by fp4q_quant2d; appendix "Activations" of the page
+ * below: activations take 1D blocks along the hidden channels), with R, C
+ * as for FP4_2D32 and R4 = R/32, C4 = C/32 each rounded up to a multiple
+ * of 4:
+ *   codes    [R x ld]     row plane, x in 1x32 blocks along its rows (the
+ *                         forward product contracts over the columns)
+ *   scales   [R x ld_s]   E8M0 byte of block (r, c/32) at r*ld_s + c/32
+ *   codes_t  [C x ld_t]   transposed plane: x^T in 1x32 blocks along its
+ *                         rows, i.e. 32 rows of one column of x (the
+ *                         weight-gradient product contracts over the rows)
+ *   scales_t [C x ld_st]  E8M0 byte of block (c, r/32) at c*ld_st + r/32
+ *   Requires ld_s >= C4 and ld_st >= R4, both multiples of 4, and 4-byte
+ *   aligned grids; bytes past C/32 (R/32) up to C4 (R4) and the rows in the
+ *   padding are written as 0.  Code planes as for FP4_2D32.  codes_t and
+ *   scales_t may both be NULL.  batch must be 1.
  * MXFP8_1D32 (written by fp4q_quant1d_mxfp8), with C = cols rounded up to 32:
  *   codes   [rows x ld]   one E4M3FN byte per element (padding bytes 0)
  *   scales  [rows x ld_s] E8M0 byte of group (r, c/32)
@@ -88,6 +105,8 @@ typedef struct fp4q_qtensor {
     int64_t ld_s;
     int64_t batch;
     int64_t bstride, bstride_t, bstride_s;
+    uint8_t* scales_t;  /* FP4_1D32 only: scale grid of the transposed plane */
+    int64_t ld_st;
 } fp4q_qtensor;
 
 /*
@@ -137,12 +156,16 @@ int fp4q_quant2d_sizes(int64_t rows, int64_t cols, int64_t* codes_bytes,
  *            b = max(r,c), taking half (b%8) of the 128-bit output; rounding
  *            goes up iff floor(frac * 2^16) + draw >= 2^16.  Hence
  *            quant(x^T) equals quant(x)^T bit for bit.
- *   out      fmt = FP4Q_FMT_FP4_2D32 (32x32 blocks) or FP4Q_FMT_FP4_2D64
+ *   out      fmt = FP4Q_FMT_FP4_2D32 (32x32 blocks), FP4Q_FMT_FP4_2D64
  *            (64x64 blocks, one of the block sides compared in the page's
- *            Table 4: same rule per block, same per-element random fields),
+ *            Table 4: same rule per block, same per-element random fields)
+ *            or FP4Q_FMT_FP4_1D32 (the activation layout: each plane in
+ *            1x32 blocks along its rows, each element rounded once per
+ *            plane with its one random field; the pages' appendix
+ *            "Activations"),
  *            rows/cols equal to the arguments,
  *            codes, codes_t (may be NULL to skip the transposed plane) and
- *            scales set; batch must be 1.
+ *            scales set (FP4_1D32: scales_t with codes_t); batch must be 1.
  * One read of x writes the row plane, the transposed plane and the scales.
  * A matrix of 2^24 or more 128x128 regions (one workgroup each) returns
  * FP4Q_EUNSUPPORTED; that is over 2^38 elements, beyond device memory.

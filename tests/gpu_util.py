@@ -46,7 +46,7 @@ def assert_planes_equal(q: fq.QTensor, ref, what=""):
 
 
 def check_gemm_tol(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, what=""):
-    """Tolerance of the benchmark spec: |err| <= 1e-5 * sum_k |a||b| per element."""
+    """The GEMM tolerance: |err| <= 1e-5 * sum_k |a||b| per element."""
     err = np.abs(got.astype(np.float64) - ref)
     tol = 1e-5 * bound
     bad = err > tol

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(fp4q):
 
 
 def test_version_and_sizes(fp4q):
-    assert fp4q.lib().fp4q_version() == 1
+    assert fp4q.lib().fp4q_version() == 2
     # Table 1 accounting: codes are a quarter of the bf16 bytes, plus 1 byte per tile
     assert fp4q.fp4q_quant2d_sizes(4096, 2048) == (4096 * 1024, 2048 * 2048, 128 * 64)
     assert fp4q.fp4q_quant2d_sizes(33, 65) == (64 * 48, 96 * 32, 2 * 3)
@@ -165,6 +165,51 @@ def test_gemm_rejects_bad_arguments(fp4q):
     assert "32x32" in _err(fp4q)
 
 
+def _desc1d(fp4q, rows=64, cols=64, ld_s=512, ld_st=512, scales=0x3000, scales_t=0x4000, **kw):
+    d = _desc(fp4q, fmt=4, rows=rows, cols=cols, ld_s=ld_s, scales=scales, **kw)
+    d.scales_t, d.ld_st = scales_t, ld_st
+    return d
+
+
+def test_act1d_layout_rejects_bad_arguments(fp4q):
+    """The 1D activation layout's tiled scale grids: one 512-byte chunk per
+    128 rows x 128 codes, leading dims multiples of 16, 16-byte aligned; the
+    transposed plane needs its own grid; dense products with batch 1 only."""
+    L = fp4q.lib()
+    x = ctypes.c_void_p(0x10000)
+    good = _desc1d(fp4q, rows=64, cols=300, ld=160, ld_s=1536)
+    assert good.ld_s == 512 * 3
+    for bad in (_desc1d(fp4q, rows=64, cols=300, ld=160, ld_s=1024),            # grid too narrow
+                _desc1d(fp4q, rows=64, cols=300, ld=160, ld_s=1544),            # ld_s % 16
+                _desc1d(fp4q, rows=64, cols=300, ld=160, ld_s=1536, scales=0x3004),  # misaligned
+                _desc1d(fp4q, rows=64, cols=300, ld=160, ld_s=1536, scales_t=0),     # no scales_t
+                _desc1d(fp4q, rows=64, cols=300, ld=160, ld_s=1536, ld_st=256, ld_t=32)):  # scales_t narrow
+        assert L.fp4q_quant2d(x, 1, 64, 300, 300, 0, 0, 0, ctypes.byref(bad), None) == -1
+        assert "scales" in _err(fp4q)
+    # batch items must share the layout
+    arr = (fp4q._QItem * 2)()
+    d2 = _desc(fp4q)
+    for k, d in enumerate((good, d2)):
+        arr[k].x, arr[k].rows, arr[k].cols, arr[k].ldx = 0x10000, d.rows, d.cols, d.cols
+        arr[k].out = ctypes.pointer(d)
+    assert L.fp4q_quant2d_batch(2, arr, 1, 0, 0, None) == -1
+    assert "format differs" in _err(fp4q)
+    c = ctypes.c_void_p(0x50000)
+    a = _desc1d(fp4q)
+    w = _desc(fp4q)
+    ab = _desc1d(fp4q, batch=2)
+    wb = _desc(fp4q, batch=2)
+    assert L.fp4q_gemm(0, ctypes.byref(ab), ctypes.byref(wb), c, 64, 64 * 64, None, None) == -2
+    assert "batch 1" in _err(fp4q)
+    arr = (ctypes.c_int64 * 2)(0, 64)
+    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+    assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(w), c, 64, 0, ctypes.byref(g), None) == -2
+    nt = _desc1d(fp4q, scales_t=0)
+    assert L.fp4q_gemm(2, ctypes.byref(w), ctypes.byref(nt), c, 64, 0, None, None) == -1  # X^T grid
+    y = ctypes.c_void_p(0x70000)
+    assert L.fp4q_dequant(ctypes.byref(nt), 1, 2, y, 64, None) == -1
+
+
 def test_dequant_and_mxfp8_reject_bad_arguments(fp4q):
     L = fp4q.lib()
     y = ctypes.c_void_p(0x70000)
@@ -184,3 +229,16 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(m, "_lib", None)
     with pytest.raises(m.Fp4qError):
         m.lib()
+
+
+def test_alloc_act1d_meets_the_grid_rules(fp4q):
+    """alloc_fp4(block="1d") sizes the tiled grids as the validation requires:
+    ceil(R/128) x 512*ceil(C/128) for the row plane, the transpose for the
+    transposed plane (host tensors: no device needed)."""
+    for rows, cols in ((1, 1), (300, 257), (128, 128), (129, 385)):
+        q = fp4q.alloc_fp4(rows, cols, device="cpu", block="1d")
+        R, C = -(-rows // 32) * 32, -(-cols // 32) * 32
+        d = q.desc()
+        assert d.fmt == 4 and q.scales.shape == (-(-R // 128), 512 * -(-C // 128))
+        assert q.scales_t.shape == (-(-C // 128), 512 * -(-R // 128))
+        assert d.ld_s % 16 == 0 and d.ld_st % 16 == 0 and d.ld_s >= 512 * -(-C // 128)

@@ -83,18 +83,30 @@ def quant_bytes(rows, cols):
     return rows * cols * 2 + R * C // 2 * 2 + (R // 32) * (C // 32)
 
 
+def quant_bytes_1d(rows, cols):
+    """Algorithmic HBM bytes of the 1D activation layout on a bf16 rows x cols
+    matrix: the read, both code planes and one scale byte per 1x32 block of
+    each plane."""
+    R, C = (rows + 31) // 32 * 32, (cols + 31) // 32 * 32
+    return rows * cols * 2 + R * C // 2 * 2 + 2 * (R * C // 32)
+
+
 class Step:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, layers, torch, fq, block=32):
+    def __init__(self, layers, torch, fq, block=32, x_block=None):
         self.torch, self.fq = torch, fq
         self.layers = []
+        # x_block "1d": activations in the 1D layout, quantized in a launch of
+        # their own (a launch takes one layout); W and dY keep `block`.
+        self.x_sep = x_block is not None and x_block != block
         for L in layers:
             d = {}
             for nm in ("X", "W", "dY"):
                 a = getattr(L, nm)
                 d[nm] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-                d["q" + nm] = fq.alloc_fp4(a.shape[0], a.shape[1], block=block)
+                d["q" + nm] = fq.alloc_fp4(a.shape[0], a.shape[1], block=x_block if nm == "X" and self.x_sep
+                                           else block)
             T, K, N = L.T, L.K, L.N
             d["Y"] = torch.empty((T, N), dtype=torch.float32, device="cuda")
             d["dX"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
@@ -110,8 +122,12 @@ class Step:
                 self.gemm_bytes += (m * k + n * k) // 2 + (m * k + n * k) // 1024 + 4 * m * n
         for i, d in enumerate(self.layers):
             T, K, N = d["shape"]
-            self.launches += [("quant", d["name"] + ":X+W", quant_bytes(T, K) + quant_bytes(N, K)),
-                              ("gemm", d["name"] + ":fwd", 2.0 * T * N * K)]
+            if self.x_sep:
+                self.launches += [("quant", d["name"] + ":X", quant_bytes_1d(T, K)),
+                                  ("quant", d["name"] + ":W", quant_bytes(N, K))]
+            else:
+                self.launches += [("quant", d["name"] + ":X+W", quant_bytes(T, K) + quant_bytes(N, K))]
+            self.launches += [("gemm", d["name"] + ":fwd", 2.0 * T * N * K)]
         for i, d in reversed(list(enumerate(self.layers))):
             T, K, N = d["shape"]
             self.launches += [("quant", d["name"] + ":dY", quant_bytes(T, N)),
@@ -138,7 +154,11 @@ class Step:
                 fn()
 
         for i, d in enumerate(self.layers):
-            timed(lambda: self.quant_xw(i, d, seed))
+            if self.x_sep:
+                timed(lambda: fq.fp4q_quant2d(d["X"], d["qX"], seed=seed, stream_id=16 * i + 1))
+                timed(lambda: fq.fp4q_quant2d(d["W"], d["qW"], seed=seed, stream_id=16 * i + 2))
+            else:
+                timed(lambda: self.quant_xw(i, d, seed))
             timed(lambda: fq.fp4q_gemm("fwd", d["qX"], d["qW"], d["Y"]))
         for i, d in reversed(list(enumerate(self.layers))):
             timed(lambda: fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3))
@@ -197,7 +217,7 @@ def _summary(ms, work, kinds):
     return out
 
 
-def _eager_step(step, torch, iters, warmup):
+def _eager_step(step, torch, iters, warmup, keep_launches=False):
     """Median per-launch times of a Step run eagerly, and their totals by kind."""
     work = {nm: w for _, nm, w in step.launches}
     kinds = {nm: kind for kind, nm, _ in step.launches}
@@ -211,7 +231,10 @@ def _eager_step(step, torch, iters, warmup):
     torch.cuda.synchronize()
     per = np.array([[s.elapsed_time(e) for (s, e) in ev[it]] for it in range(iters)])
     ms = {nm: float(np.median(per[:, j])) for j, (_, nm, _) in enumerate(step.launches)}
-    return _summary(ms, work, kinds)
+    out = _summary(ms, work, kinds)
+    if keep_launches:
+        out["_per_launch"] = ms
+    return out
 
 
 def side_1b(torch, fq, wl, iters, warmup):
@@ -233,6 +256,29 @@ def side_block64(torch, fq, wl, iters, warmup):
         torch.cuda.empty_cache()
     for key in ("ms_per_step", "quant_ms", "gemm_ms"):
         out[key + "_b64_over_b32"] = round(out["b64"][key] / out["b32"][key], 4)
+    return out
+
+
+def side_act1d(torch, fq, wl, iters, warmup):
+    """The 7B layer step with the activations in the 1D layout (appendix
+    "Activations": X in 1x32 blocks along the channels for the forward
+    product, along the tokens for the weight gradient; W and dY in 32x32
+    blocks) beside the all-2D step, both eager with per-launch events."""
+    out = {"workload": "7b-linear-layer-step with X in the 1D layout and with X in 32x32 blocks "
+                       "(eager, per-launch events; the 1D step quantizes X and W in separate launches)"}
+    for key, xb in (("x2d", None), ("x1d", "1d")):
+        step = Step(wl.config_7b(), torch, fq, block=32, x_block=xb)
+        r = _eager_step(step, torch, iters, warmup, keep_launches=True)
+        ms = r.pop("_per_launch")
+        for kind in ("fwd", "wgrad"):
+            r[kind + "_ms"] = round(sum(v for n, v in ms.items() if n.endswith(":" + kind)), 4)
+        xw = [n for n in ms if n.endswith(":X") or n.endswith(":W") or n.endswith(":X+W")]
+        r["quant_xw_ms"] = round(sum(ms[n] for n in xw), 4)
+        out[key] = r
+        del step
+        torch.cuda.empty_cache()
+    for key in ("ms_per_step", "quant_ms", "quant_xw_ms", "gemm_ms", "fwd_ms", "wgrad_ms"):
+        out[key + "_x1d_over_x2d"] = round(out["x1d"][key] / out["x2d"][key], 4)
     return out
 
 
@@ -542,7 +588,8 @@ def main():
     }
     if not args.no_side_paths:
         side = {}
-        for name, fn in (("1b", side_1b), ("moe", side_moe), ("attn", side_attn), ("block64", side_block64)):
+        for name, fn in (("1b", side_1b), ("moe", side_moe), ("attn", side_attn), ("block64", side_block64),
+                         ("act1d", side_act1d)):
             print("[bench] side path %s" % name, file=sys.stderr, flush=True)
             side[name] = fn(torch, fq, wl, iters=5, warmup=2)
             torch.cuda.empty_cache()

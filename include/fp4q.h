@@ -73,19 +73,22 @@ typedef enum {
  *   are written as 0.
  * FP4_1D32 (written by fp4q_quant2d; appendix "Activations" of the page
  * below: activations take 1D blocks along the hidden channels), with R, C
- * as for FP4_2D32 and R4 = R/32, C4 = C/32 each rounded up to a multiple
- * of 4:
+ * as for FP4_2D32:
  *   codes    [R x ld]     row plane, x in 1x32 blocks along its rows (the
  *                         forward product contracts over the columns)
- *   scales   [R x ld_s]   E8M0 byte of block (r, c/32) at r*ld_s + c/32
  *   codes_t  [C x ld_t]   transposed plane: x^T in 1x32 blocks along its
  *                         rows, i.e. 32 rows of one column of x (the
  *                         weight-gradient product contracts over the rows)
- *   scales_t [C x ld_st]  E8M0 byte of block (c, r/32) at c*ld_st + r/32
- *   Requires ld_s >= C4 and ld_st >= R4, both multiples of 4, and 4-byte
- *   aligned grids; bytes past C/32 (R/32) up to C4 (R4) and the rows in the
- *   padding are written as 0.  Code planes as for FP4_2D32.  codes_t and
- *   scales_t may both be NULL.  batch must be 1.
+ *   scales   [ceil(R/128) x ld_s]   tiled E8M0 grid of the row plane
+ *   scales_t [ceil(C/128) x ld_st]  tiled E8M0 grid of the transposed plane
+ *   A tiled grid of a plane with n rows of w codes holds one 512-byte chunk
+ *   per 128 rows x 128 codes: the byte of plane row r, 1x32 block kb sits at
+ *     (r/128)*ld + (kb/4)*512 + (kb%2)*256 + (r%32)*8 + ((r/32)%4)*2 + (kb/2)%2
+ *   (the order in which the GEMM's matrix-core lanes consume them).  Requires
+ *   ld_s >= 512*ceil(C/128) and ld_st >= 512*ceil(R/128), multiples of 16,
+ *   and 16-byte aligned grids; every chunk byte past the matrix is written
+ *   as 0.  Code planes as for FP4_2D32.  codes_t and scales_t may both be
+ *   NULL.  batch must be 1.
  * MXFP8_1D32 (written by fp4q_quant1d_mxfp8), with C = cols rounded up to 32:
  *   codes   [rows x ld]   one E4M3FN byte per element (padding bytes 0)
  *   scales  [rows x ld_s] E8M0 byte of group (r, c/32)
@@ -218,7 +221,10 @@ int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
  *   op WGRAD: a = dY [T x N], b = X [T x K]  ->  C = dY^T X  [N x K]
  * FP4 operands may each have 32x32 or 64x64 scale blocks (a 64x64 block's
  * byte is used for both of its 32-row slabs and both of its 32-wide K
- * blocks); grouped products take 32x32 blocks only (FP4Q_EUNSUPPORTED).
+ * blocks) or the 1D activation layout (each plane read with its own tiled
+ * grid: FWD reads X's row plane, WGRAD X's transposed plane; dense products
+ * with batch 1 only, else FP4Q_EUNSUPPORTED); grouped products take 32x32
+ * blocks only (FP4Q_EUNSUPPORTED).
  * FP4 operands must carry both planes; DGRAD reads W's transposed plane and
  * WGRAD reads the transposed planes of dY and X, so each tensor is quantized
  * once.  MXFP8 operands support FWD only (S = Q K^T); every product

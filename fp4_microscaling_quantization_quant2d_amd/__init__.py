@@ -29,6 +29,7 @@ FMT_FP4_2D32, FMT_MXFP8_1D32, FMT_FP4_2D64, FMT_FP4_1D32 = 1, 2, 3, 4
 DT_BF16, DT_F32 = 1, 2
 ROUND = {"sr": 0, "rne": 1}
 OPS = {"fwd": 0, "dgrad": 1, "wgrad": 2}
+GEMM_ACCUMULATE = 1
 
 
 class Fp4qError(RuntimeError):
@@ -85,11 +86,13 @@ def _load():
     L.fp4q_quant2d_batch.argtypes = [ctypes.c_int, ctypes.POINTER(_QItem), ctypes.c_int, ctypes.c_int,
                                      ctypes.c_uint64, P]
     L.fp4q_quant1d_mxfp8.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.POINTER(_QDesc), P]
+    L.fp4q_gemm_ex.argtypes = [ctypes.c_int, ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc), P, I64,
+                               I64, ctypes.POINTER(_Groups), ctypes.c_int, P]
     L.fp4q_gemm.argtypes = [ctypes.c_int, ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc), P, I64,
                             I64, ctypes.POINTER(_Groups), P]
     L.fp4q_dequant.argtypes = [ctypes.POINTER(_QDesc), ctypes.c_int, ctypes.c_int, P, I64, P]
     for fn in ("fp4q_quant2d_sizes", "fp4q_quant2d", "fp4q_quant2d_batch", "fp4q_quant1d_mxfp8",
-               "fp4q_gemm", "fp4q_dequant"):
+               "fp4q_gemm", "fp4q_gemm_ex", "fp4q_dequant"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -288,11 +291,14 @@ def gemm_out_shape(op, a: QTensor, b: QTensor, groups: Optional[Sequence[int]] =
 
 
 def fp4q_gemm(op, a: QTensor, b: QTensor, c: Optional[torch.Tensor] = None,
-              groups: Optional[Sequence[int]] = None, stream=None):
+              groups: Optional[Sequence[int]] = None, stream=None, accumulate=False):
     """C = X W^T (fwd), dY W (dgrad) or dY^T X (wgrad) in fp32; groups = host
-    row offsets (multiples of 32) for a grouped expert product."""
+    row offsets (multiples of 32) for a grouped expert product.  accumulate:
+    C += the product (fp4q_gemm_ex with FP4Q_GEMM_ACCUMULATE; c required)."""
     opc = OPS.get(op, op)
     M, N = gemm_out_shape(opc, a, b, groups)
+    if accumulate and c is None:
+        raise Fp4qError("accumulate needs the C to add to")
     if c is None:
         shape = (a.batch, M, N) if a.batch > 1 else (M, N)
         c = torch.empty(shape, dtype=torch.float32, device=a.codes.device)
@@ -305,6 +311,11 @@ def fp4q_gemm(op, a: QTensor, b: QTensor, c: Optional[torch.Tensor] = None,
         arr = (ctypes.c_int64 * len(groups))(*[int(v) for v in groups])
         g = _Groups(len(groups) - 1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
     da, db = a.desc(), b.desc()
+    if accumulate:
+        _check(_load().fp4q_gemm_ex(opc, ctypes.byref(da), ctypes.byref(db), _ptr(c), ldc, cbs,
+                                    ctypes.byref(g) if g is not None else None, GEMM_ACCUMULATE,
+                                    _stream_ptr(stream)), "fp4q_gemm_ex")
+        return c
     _check(_load().fp4q_gemm(opc, ctypes.byref(da), ctypes.byref(db), _ptr(c), ldc, cbs,
                              ctypes.byref(g) if g is not None else None, _stream_ptr(stream)),
            "fp4q_gemm")

@@ -286,8 +286,17 @@ int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
 int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, int64_t ldc, int64_t c_bstride,
               const fp4q_groups* groups, void* hip_stream)
 {
+    return fp4q_gemm_ex(op, a, b, c, ldc, c_bstride, groups, 0, hip_stream);
+}
+
+int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, int64_t ldc, int64_t c_bstride,
+                 const fp4q_groups* groups, int flags, void* hip_stream)
+{
     if (op != FP4Q_OP_FWD && op != FP4Q_OP_DGRAD && op != FP4Q_OP_WGRAD)
         return fail(FP4Q_EINVAL, "fp4q_gemm: op %d", op);
+    if (flags & ~FP4Q_GEMM_ACCUMULATE)
+        return fail(FP4Q_EINVAL, "fp4q_gemm_ex: unknown flags 0x%x", flags);
+    const bool accumulate = (flags & FP4Q_GEMM_ACCUMULATE) != 0;
     if (!a || !b || !c)
         return fail(FP4Q_EINVAL, "fp4q_gemm: null a, b or c");
     const bool fp8 = a->fmt == FP4Q_FMT_MXFP8_1D32;
@@ -466,10 +475,13 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
         for (int i = 0; i < g.n_groups; ++i)
             kmax = std::max<int64_t>(kmax, g.row_off[i + 1] - g.row_off[i]);
     }
+    if (accumulate && (fp8 || groups || (oned & 1)))
+        return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_ex: accumulation takes dense FP4 products whose A operand "
+                                       "has a square-block grid");
     if (fp4q::gemm_lds_bytes(fp8 ? 2 : 1, (int)kmax) > kMaxLdsBytes)
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: K %lld too large for the %s tile (max %d)", (long long)kmax,
                     fp8 ? "MXFP8" : "FP4", fp8 ? max_k(2) : max_k(1));
-    return hip_status(fp4q::launch_gemm(g, fp8 ? 2 : 1, a_st, b_st, oned, grouped_op, (int)a->batch,
+    return hip_status(fp4q::launch_gemm(g, fp8 ? 2 : 1, a_st, b_st, oned, grouped_op, (int)a->batch, accumulate,
                                         static_cast<hipStream_t>(hip_stream)),
                       "fp4q_gemm");
 }

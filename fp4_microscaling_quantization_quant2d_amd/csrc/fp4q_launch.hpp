@@ -102,8 +102,9 @@ enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };
 // oned: bit 0 / bit 1 -- A / B carry the 1D layout's tiled scale grid
 // (chunk (g, q) of rows 128g.., K-blocks 4q.. at g*lds + q*512; FP4, dense).
 // grouped_op: -1 dense/batched, else the op whose grouped wiring applies.
+// accumulate: C += A B^T (FP4, dense; oned 0 or 2 only).
 hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
-                       hipStream_t s);
+                       bool accumulate, hipStream_t s);
 
 // Output tile of the GEMM kernel (grouped launches size their grids with it).
 int gemm_tile_m();

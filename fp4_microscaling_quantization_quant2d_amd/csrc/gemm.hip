@@ -260,7 +260,8 @@ __device__ __forceinline__ void wait_vm_and_barrier()
 // range; without it only pairs past the end of K (loaded but never
 // multiplied) may read past a row's K bytes.
 // ONED: bit 0 -- A is an FP4 operand in the 1D activation layout, bit 1 -- B.
-template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED>
+// ACC: C += A B^T (C is read in the epilogue) instead of C = A B^T.
+template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
 {
     constexpr bool A1D = FMT == 1 && (ONED & 1), B1D = FMT == 1 && (ONED & 2);
@@ -686,9 +687,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float* rp = cb + (int64_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc;
+                    if constexpr (ACC) {
+                        // read the old values of this store's four columns, then
+                        // store the sums (the compiler runs the loads ahead)
+                        float old[4];
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        __builtin_nontemporal_store(acc[mi][ni][r], rp + ni * 32);
+                        for (int ni = 0; ni < 4; ++ni)
+                            old[ni] = __builtin_nontemporal_load(rp + ni * 32);
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni)
+                            __builtin_nontemporal_store(acc[mi][ni][r] + old[ni], rp + ni * 32);
+                    } else {
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni)
+                            __builtin_nontemporal_store(acc[mi][ni][r], rp + ni * 32);
+                    }
                 }
             });
         };
@@ -710,8 +723,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-                if (row < P.M)
-                    __builtin_nontemporal_store(acc[mi][ni][r], &P.c[(int64_t)row * g.ldc + col]);
+                if (row < P.M) {
+                    float* cp = &P.c[(int64_t)row * g.ldc + col];
+                    if constexpr (ACC)
+                        __builtin_nontemporal_store(acc[mi][ni][r] + __builtin_nontemporal_load(cp), cp);
+                    else
+                        __builtin_nontemporal_store(acc[mi][ni][r], cp);
+                }
             }
         }
     }
@@ -736,7 +754,7 @@ __device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int&
     tn = in / rows;
 }
 
-template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED>
+template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC>
 __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
 {
     const int bz = blockIdx.y;
@@ -753,7 +771,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
     P.b_rows = g.b_rows;
     const int ntm = (g.M + kBM - 1) / kBM, ntn = (g.N + kBN - 1) / kBN;
     tile_of<FMT == 1 ? 4 : 8>(blockIdx.x, ntm, ntn, P.tm, P.tn);
-    gemm_tile<FMT, A_ST, B_ST, KT, ONED>(g, P);
+    gemm_tile<FMT, A_ST, B_ST, KT, ONED, ACC>(g, P);
 }
 
 // Grouped (expert) products.  Group g owns token rows [row_off[g], row_off[g+1]).
@@ -853,25 +871,41 @@ hipError_t allow_lds(F* fn, size_t bytes)
     return allow_lds_raw(reinterpret_cast<const void*>(fn), bytes);
 }
 
-template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED>
+template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC>
 hipError_t launch_dense_k(const GemmArgs& g, int batch, hipStream_t s)
 {
     const int ntm = (g.M + kBM - 1) / kBM, ntn = (g.N + kBN - 1) / kBN;
     const size_t lb = lds_bytes(FMT, g.K, ONED);
-    hipError_t e = allow_lds(gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED>, lb);
+    hipError_t e = allow_lds(gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED, ACC>, lb);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED>), dim3(ntm * ntn, batch), dim3(kThreads), lb, s,
-                       g);
+    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED, ACC>), dim3(ntm * ntn, batch), dim3(kThreads),
+                       lb, s, g);
     return hipGetLastError();
 }
 
-template <int FMT, bool A_ST, bool B_ST, int ONED = 0>
+template <int FMT, bool A_ST, bool B_ST, int ONED = 0, bool ACC = false>
 hipError_t launch_dense(const GemmArgs& g, int batch, hipStream_t s)
 {
     if (FMT == 1 && g.K % 256 == 0)
-        return launch_dense_k<FMT, A_ST, B_ST, false, ONED>(g, batch, s);
-    return launch_dense_k<FMT, A_ST, B_ST, true, ONED>(g, batch, s);
+        return launch_dense_k<FMT, A_ST, B_ST, false, ONED, ACC>(g, batch, s);
+    return launch_dense_k<FMT, A_ST, B_ST, true, ONED, ACC>(g, batch, s);
+}
+
+// C += A B^T for FP4 operands with 32x32 or 64x64 blocks, or a 1D-layout B
+// (the weight gradient of a 1D activation).
+hipError_t launch_dense_acc(const GemmArgs& g, bool a_st, bool b_st, int oned, int batch, hipStream_t s)
+{
+    if (oned == 2)
+        return a_st ? launch_dense<1, true, false, 2, true>(g, batch, s)
+                    : launch_dense<1, false, false, 2, true>(g, batch, s);
+    if (!a_st && !b_st)
+        return launch_dense<1, false, false, 0, true>(g, batch, s);
+    if (!a_st && b_st)
+        return launch_dense<1, false, true, 0, true>(g, batch, s);
+    if (a_st && b_st)
+        return launch_dense<1, true, true, 0, true>(g, batch, s);
+    return launch_dense<1, true, false, 0, true>(g, batch, s);
 }
 
 template <int OP, bool A_ST, bool B_ST>
@@ -900,8 +934,10 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t s)
 } // namespace
 
 hipError_t launch_gemm(const GemmArgs& g, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
-                       hipStream_t s)
+                       bool accumulate, hipStream_t s)
 {
+    if (accumulate)
+        return launch_dense_acc(g, a_st, b_st, oned, batch, s);
     // 1D-layout operands (FP4, dense): the grid orientation of such an
     // operand does not apply.
     if (fmt == 1 && grouped_op < 0 && oned != 0) {

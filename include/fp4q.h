@@ -248,6 +248,21 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
               int64_t c_bstride, const fp4q_groups* groups, void* hip_stream);
 
 /*
+ * fp4q_gemm with flags.  FP4Q_GEMM_ACCUMULATE: C += op(a, b) instead of
+ * C = op(a, b) -- gradient accumulation over micro-batches (the weight
+ * gradient dW = dY^T X of Sec. 3 "Application to linear layers", summed
+ * into a resident fp32 dW).  C must hold the values to add to; each element
+ * is read once and written once, the sum rounded once to fp32.  Dense FP4
+ * products only, and A must have a square-block grid (FWD/DGRAD/WGRAD with
+ * 32x32 or 64x64 blocks, and WGRAD with X in the 1D layout); anything else
+ * returns FP4Q_EUNSUPPORTED.  flags 0 is fp4q_gemm.  Unknown flag bits
+ * return FP4Q_EINVAL.
+ */
+#define FP4Q_GEMM_ACCUMULATE 1
+int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, int64_t ldc,
+                 int64_t c_bstride, const fp4q_groups* groups, int flags, void* hip_stream);
+
+/*
  * Dequantization X ~ P * S (Sec. 2.1 of the same page) to fp32 or bf16, for
  * all three formats.
  *   transposed  0: the row plane, y is rows x cols; 1 (FP4 only): the

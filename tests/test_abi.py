@@ -29,7 +29,7 @@ def fp4q():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for fn in ("fp4q_quant2d", "fp4q_quant1d_mxfp8", "fp4q_gemm", "fp4q_dequant",
+    for fn in ("fp4q_quant2d", "fp4q_quant1d_mxfp8", "fp4q_gemm", "fp4q_gemm_ex", "fp4q_dequant",
                "fp4q_quant2d_sizes", "fp4q_last_error", "fp4q_version"):
         assert fn in names
 
@@ -208,6 +208,27 @@ def test_act1d_layout_rejects_bad_arguments(fp4q):
     assert L.fp4q_gemm(2, ctypes.byref(w), ctypes.byref(nt), c, 64, 0, None, None) == -1  # X^T grid
     y = ctypes.c_void_p(0x70000)
     assert L.fp4q_dequant(ctypes.byref(nt), 1, 2, y, 64, None) == -1
+
+
+def test_gemm_ex_accumulate_rejects_unsupported(fp4q):
+    """fp4q_gemm_ex: unknown flags are invalid; accumulation takes dense FP4
+    products whose A operand has a square-block grid."""
+    L = fp4q.lib()
+    c = ctypes.c_void_p(0x50000)
+    a = _desc(fp4q)
+    assert L.fp4q_gemm_ex(0, ctypes.byref(a), ctypes.byref(a), c, 64, 0, None, 4, None) == -1
+    assert "flags" in _err(fp4q)
+    f8 = _desc(fp4q, fmt=2, ld=64)
+    assert L.fp4q_gemm_ex(0, ctypes.byref(f8), ctypes.byref(f8), c, 64, 0, None, 1, None) == -2
+    arr = (ctypes.c_int64 * 2)(0, 64)
+    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+    assert L.fp4q_gemm_ex(0, ctypes.byref(a), ctypes.byref(a), c, 64, 0, ctypes.byref(g), 1, None) == -2
+    x1 = _desc1d(fp4q)
+    assert L.fp4q_gemm_ex(0, ctypes.byref(x1), ctypes.byref(a), c, 64, 0, None, 1, None) == -2
+    assert "accumulation" in _err(fp4q)
+    with pytest.raises(fp4q.Fp4qError):
+        fp4q.fp4q_gemm("wgrad", fp4q.alloc_fp4(64, 64, device="cpu"), fp4q.alloc_fp4(64, 64, device="cpu"),
+                       accumulate=True)
 
 
 def test_dequant_and_mxfp8_reject_bad_arguments(fp4q):

@@ -94,8 +94,10 @@ def quant_bytes_1d(rows, cols):
 class Step:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, layers, torch, fq, block=32, x_block=None):
+    def __init__(self, layers, torch, fq, block=32, x_block=None, wgrad_accumulate=False):
         self.torch, self.fq = torch, fq
+        # wgrad_accumulate: dW += dY^T X, as in a micro-batch after the first
+        self.wgrad_acc = wgrad_accumulate
         self.layers = []
         # x_block "1d": activations in the 1D layout, quantized in a launch of
         # their own (a launch takes one layout); W and dY keep `block`.
@@ -163,7 +165,7 @@ class Step:
         for i, d in reversed(list(enumerate(self.layers))):
             timed(lambda: fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3))
             timed(lambda: fq.fp4q_gemm("dgrad", d["qdY"], d["qW"], d["dX"]))
-            timed(lambda: fq.fp4q_gemm("wgrad", d["qdY"], d["qX"], d["dW"]))
+            timed(lambda: fq.fp4q_gemm("wgrad", d["qdY"], d["qX"], d["dW"], accumulate=self.wgrad_acc))
 
     def run_two_streams(self, seed, side):
         """Enqueue one step with each layer's wgrad on stream `side`, beside
@@ -279,6 +281,27 @@ def side_act1d(torch, fq, wl, iters, warmup):
         torch.cuda.empty_cache()
     for key in ("ms_per_step", "quant_ms", "quant_xw_ms", "gemm_ms", "fwd_ms", "wgrad_ms"):
         out[key + "_x1d_over_x2d"] = round(out["x1d"][key] / out["x2d"][key], 4)
+    return out
+
+
+def side_wgrad_acc(torch, fq, wl, iters, warmup):
+    """The 7B layer step with every weight gradient accumulated onto its
+    resident fp32 dW (a micro-batch after the first) beside the plain step:
+    the read-modify-write epilogue reads 4 more bytes per dW element."""
+    out = {"workload": "7b-linear-layer-step with wgrad accumulating into dW (C += dY^T X) and plain "
+                       "(eager, per-launch events)"}
+    for key, accf in (("plain", False), ("acc", True)):
+        step = Step(wl.config_7b(), torch, fq, wgrad_accumulate=accf)
+        for d in step.layers:
+            d["dW"].zero_()
+        r = _eager_step(step, torch, iters, warmup, keep_launches=True)
+        ms = r.pop("_per_launch")
+        r["wgrad_ms"] = round(sum(v for n, v in ms.items() if n.endswith(":wgrad")), 4)
+        out[key] = r
+        del step
+        torch.cuda.empty_cache()
+    for key in ("ms_per_step", "gemm_ms", "wgrad_ms"):
+        out[key + "_acc_over_plain"] = round(out["acc"][key] / out["plain"][key], 4)
     return out
 
 
@@ -589,7 +612,7 @@ def main():
     if not args.no_side_paths:
         side = {}
         for name, fn in (("1b", side_1b), ("moe", side_moe), ("attn", side_attn), ("block64", side_block64),
-                         ("act1d", side_act1d)):
+                         ("act1d", side_act1d), ("wgrad_acc", side_wgrad_acc)):
             print("[bench] side path %s" % name, file=sys.stderr, flush=True)
             side[name] = fn(torch, fq, wl, iters=5, warmup=2)
             torch.cuda.empty_cache()

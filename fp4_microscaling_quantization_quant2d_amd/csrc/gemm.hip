@@ -684,20 +684,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
         auto store_from = [&](auto ROT) {
             static_for<4>([&](auto B) {
                 constexpr int mi = (decltype(B)::value + decltype(ROT)::value) & 3;
+                if constexpr (ACC) {
+                    // C += A B^T: all 64 old values of the 32-row block are
+                    // loaded before any sum is stored (the operand registers
+                    // are free by now), so a block costs one memory round
+                    // trip.  Loading the next block's values before these
+                    // stores measured the same: the cost is the extra read.
+                    float old[16][4];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float* rp = cb + (int64_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc;
-                    if constexpr (ACC) {
-                        // read the old values of this store's four columns, then
-                        // store the sums (the compiler runs the loads ahead)
-                        float old[4];
+                    for (int r = 0; r < 16; ++r) {
+                        const float* rp = cb + (int64_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc;
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni)
-                            old[ni] = __builtin_nontemporal_load(rp + ni * 32);
+                            old[r][ni] = __builtin_nontemporal_load(rp + ni * 32);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float* rp = cb + (int64_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc;
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni)
-                            __builtin_nontemporal_store(acc[mi][ni][r] + old[ni], rp + ni * 32);
-                    } else {
+                            __builtin_nontemporal_store(acc[mi][ni][r] + old[r][ni], rp + ni * 32);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float* rp = cb + (int64_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc;
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni)
                             __builtin_nontemporal_store(acc[mi][ni][r], rp + ni * 32);

@@ -57,8 +57,11 @@ QUANT2D_BATCH_MAX = 8
 
 
 class _Groups(ctypes.Structure):
-    _fields_ = [("n", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("row_off", ctypes.POINTER(ctypes.c_int64))]
+    _fields_ = [("n", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("row_off", ctypes.POINTER(ctypes.c_int64)), ("max_rows", ctypes.c_int64)]
+
+
+GROUPS_DEVICE = 1
 
 
 _lib = None
@@ -291,10 +294,12 @@ def gemm_out_shape(op, a: QTensor, b: QTensor, groups: Optional[Sequence[int]] =
 
 
 def fp4q_gemm(op, a: QTensor, b: QTensor, c: Optional[torch.Tensor] = None,
-              groups: Optional[Sequence[int]] = None, stream=None, accumulate=False):
-    """C = X W^T (fwd), dY W (dgrad) or dY^T X (wgrad) in fp32; groups = host
-    row offsets (multiples of 32) for a grouped expert product.  accumulate:
-    C += the product (fp4q_gemm_ex with FP4Q_GEMM_ACCUMULATE; c required)."""
+              groups=None, stream=None, accumulate=False, max_group_rows=None):
+    """C = X W^T (fwd), dY W (dgrad) or dY^T X (wgrad) in fp32.  groups: row
+    offsets (multiples of 32) of a grouped expert product -- a host sequence,
+    or an int64 CUDA tensor read by the kernels (FP4Q_GROUPS_DEVICE; wgrad then
+    needs max_group_rows, a bound on any group's rows).  accumulate: C += the
+    product (fp4q_gemm_ex with FP4Q_GEMM_ACCUMULATE; c required)."""
     opc = OPS.get(op, op)
     M, N = gemm_out_shape(opc, a, b, groups)
     if accumulate and c is None:
@@ -307,9 +312,15 @@ def fp4q_gemm(op, a: QTensor, b: QTensor, c: Optional[torch.Tensor] = None,
     ldc = c.stride(-2)
     cbs = c.stride(0) if c.dim() == 3 else 0
     g = None
-    if groups is not None:
+    if isinstance(groups, torch.Tensor):
+        if not groups.is_cuda or groups.dtype != torch.int64 or groups.dim() != 1 or not groups.is_contiguous():
+            raise Fp4qError("device group offsets must be a contiguous 1-D int64 CUDA tensor")
+        g = _Groups(groups.numel() - 1, GROUPS_DEVICE,
+                    ctypes.cast(ctypes.c_void_p(groups.data_ptr()), ctypes.POINTER(ctypes.c_int64)),
+                    int(max_group_rows or 0))
+    elif groups is not None:
         arr = (ctypes.c_int64 * len(groups))(*[int(v) for v in groups])
-        g = _Groups(len(groups) - 1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+        g = _Groups(len(groups) - 1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), 0)
     da, db = a.desc(), b.desc()
     if accumulate:
         _check(_load().fp4q_gemm_ex(opc, ctypes.byref(da), ctypes.byref(db), _ptr(c), ldc, cbs,

@@ -420,16 +420,27 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c,
         const int n = groups->n;
         if (n < 1 || n > FP4Q_MAX_GROUPS || !groups->row_off)
             return fail(FP4Q_EINVAL, "fp4q_gemm: groups->n %d out of [1, %d] or null row_off", n, FP4Q_MAX_GROUPS);
+        if (groups->flags & ~FP4Q_GROUPS_DEVICE)
+            return fail(FP4Q_EINVAL, "fp4q_gemm: unknown groups->flags 0x%x", groups->flags);
+        const bool dev = (groups->flags & FP4Q_GROUPS_DEVICE) != 0;
         const int64_t* off = groups->row_off;
-        const int64_t tok = pad32(op == FP4Q_OP_WGRAD ? a->rows : a->rows);
-        if (off[0] != 0)
-            return fail(FP4Q_EINVAL, "fp4q_gemm: row_off[0] must be 0");
-        for (int i = 0; i < n; ++i)
-            if (off[i + 1] < off[i] || off[i + 1] % 32)
-                return fail(FP4Q_EINVAL, "fp4q_gemm: row_off must be non-decreasing multiples of 32");
-        if (off[n] > tok)
-            return fail(FP4Q_EINVAL, "fp4q_gemm: row_off[n] %lld beyond %lld token rows", (long long)off[n],
-                        (long long)tok);
+        // Group rows index C's rows (FWD, DGRAD) and the token range of the
+        // planes; they end at or before the last whole 32 rows of a.
+        const int64_t tok = a->rows / 32 * 32;
+        if (dev) {
+            if (op == FP4Q_OP_WGRAD && (groups->max_rows < 32 || groups->max_rows % 32 || groups->max_rows > tok))
+                return fail(FP4Q_EINVAL, "fp4q_gemm: device-offset WGRAD needs max_rows, a multiple of 32 in "
+                                         "[32, %lld]", (long long)tok);
+        } else {
+            if (off[0] != 0)
+                return fail(FP4Q_EINVAL, "fp4q_gemm: row_off[0] must be 0");
+            for (int i = 0; i < n; ++i)
+                if (off[i + 1] < off[i] || off[i + 1] % 32)
+                    return fail(FP4Q_EINVAL, "fp4q_gemm: row_off must be non-decreasing multiples of 32");
+            if (off[n] > tok)
+                return fail(FP4Q_EINVAL, "fp4q_gemm: row_off[n] %lld beyond %lld token rows", (long long)off[n],
+                            (long long)tok);
+        }
         int64_t gn;
         if (op == FP4Q_OP_FWD) {
             if (b->rows % n || (b->rows / n) % 32)
@@ -452,7 +463,19 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c,
         g.group_n = (int)gn;
         int64_t tiles = 0;
         const int tm = fp4q::gemm_tile_m(), tn = fp4q::gemm_tile_n();
-        for (int i = 0; i <= n; ++i) {
+        if (dev) {
+            // the kernel builds the tile table; the grid is an upper bound:
+            // sum_g ceil(rows_g / tm) <= ceil(tok / tm) + n
+            const int64_t ntn = (nout + tn - 1) / tn;
+            tiles = op == FP4Q_OP_WGRAD ? n * ((gn + tm - 1) / tm) * ntn : ((tok + tm - 1) / tm + n) * ntn;
+            if (tiles > INT_MAX)
+                return fail(FP4Q_EINVAL, "fp4q_gemm grouped: too many tiles");
+            g.row_off_dev = off;
+            g.tok_rows = (int)tok;
+            g.max_rows = op == FP4Q_OP_WGRAD ? (int)groups->max_rows : 0;
+            g.tile_bound = (int)tiles;
+        }
+        for (int i = 0; i <= n && !dev; ++i) {
             g.row_off[i] = (int)off[i];
             g.tile_start[i] = (int)tiles;
             if (i == n)
@@ -472,8 +495,11 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c,
         kmax = g.group_n;
     if (grouped_op == FP4Q_OP_WGRAD) {
         kmax = 32;
-        for (int i = 0; i < g.n_groups; ++i)
-            kmax = std::max<int64_t>(kmax, g.row_off[i + 1] - g.row_off[i]);
+        if (g.row_off_dev)
+            kmax = g.max_rows;
+        else
+            for (int i = 0; i < g.n_groups; ++i)
+                kmax = std::max<int64_t>(kmax, g.row_off[i + 1] - g.row_off[i]);
     }
     if (accumulate && (fp8 || groups || (oned & 1)))
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_ex: accumulation takes dense FP4 products whose A operand "

@@ -94,6 +94,12 @@ struct GemmArgs {
     int group_n;           // rows of B per group (FWD/DGRAD) or C rows per group (WGRAD)
     int tile_start[kMaxGroups + 1];
     int row_off[kMaxGroups + 1];
+    // grouped mode with device offsets (row_off_dev non-null): n_groups + 1
+    // int64 offsets in device memory, clamped by the kernel to [0, tok_rows];
+    // WGRAD groups are cut to max_rows rows; the grid has tile_bound
+    // workgroups (an upper bound on the tiles).
+    const int64_t* row_off_dev;
+    int tok_rows, max_rows, tile_bound;
 };
 
 enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };

@@ -789,20 +789,73 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
 //   FWD:   A = X rows of g,  B = W rows [g*gn, (g+1)*gn),       C rows of g
 //   DGRAD: A = dY rows of g, B = W^T plane, K range of expert g, C rows of g
 //   WGRAD: A = dY^T, B = X^T planes over the token range of g,  C rows [g*gn, ..)
-template <int OP, bool A_ST, bool B_ST>
+// DEV: the offsets are in device memory (g.row_off_dev).  Every workgroup
+// then builds the group -> tile table itself in LDS: group t's offsets are
+// clamped into [0, tok_rows], rounded down to multiples of 32 and made
+// non-decreasing pairwise (a WGRAD group also to at most max_rows rows, the
+// K its LDS was sized for), so every access stays inside the operands for
+// any offsets; workgroups past the last tile exit.
+template <int OP, bool A_ST, bool B_ST, bool DEV>
 __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
 {
     const int pid = blockIdx.x;
-    int lo = 0, hi = g.n_groups;  // find grp with tile_start[grp] <= pid < tile_start[grp+1]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (g.tile_start[mid] <= pid)
-            lo = mid;
-        else
-            hi = mid;
+    int grp, r0, r1, local;
+    const int ntn_g = ((OP == kGemmFwd ? g.group_n : g.N) + kBN - 1) / kBN;
+    if constexpr (DEV) {
+        extern __shared__ __attribute__((aligned(16))) uint8_t lds_tab[];
+        int* incl = reinterpret_cast<int*>(lds_tab);  // inclusive tile prefix per group
+        int* lo_s = incl + kThreads;
+        int* hi_s = lo_s + kThreads;
+        const int t = threadIdx.x, n = g.n_groups;
+        int cnt = 0;
+        if (t < n) {
+            const int64_t tok = g.tok_rows;
+            int64_t a = g.row_off_dev[t], b = g.row_off_dev[t + 1];
+            a = (a < 0 ? 0 : (a > tok ? tok : a)) & ~(int64_t)31;
+            b = (b < a ? a : (b > tok ? tok : b)) & ~(int64_t)31;
+            if (OP == kGemmWgrad && b - a > g.max_rows)
+                b = a + g.max_rows;
+            lo_s[t] = (int)a;
+            hi_s[t] = (int)b;
+            cnt = (OP == kGemmWgrad ? (g.group_n + kBM - 1) / kBM : (int)((b - a + kBM - 1) / kBM)) * ntn_g;
+        }
+        incl[t] = cnt;
+        __syncthreads();
+        for (int off = 1; off < kThreads; off <<= 1) {
+            const int v = t >= off ? incl[t - off] : 0;
+            __syncthreads();
+            incl[t] += v;
+            __syncthreads();
+        }
+        if (pid >= incl[n - 1])
+            return;  // uniform over the workgroup
+        int lo = 0, hi = n - 1;  // first group whose inclusive count exceeds pid
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (incl[mid] > pid)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        grp = lo;
+        r0 = lo_s[grp];
+        r1 = hi_s[grp];
+        local = pid - (grp ? incl[grp - 1] : 0);
+        __syncthreads();  // the tile reuses this LDS
+    } else {
+        int lo = 0, hi = g.n_groups;  // find grp with tile_start[grp] <= pid < tile_start[grp+1]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (g.tile_start[mid] <= pid)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        grp = lo;
+        r0 = g.row_off[grp];
+        r1 = g.row_off[grp + 1];
+        local = pid - g.tile_start[grp];
     }
-    const int grp = lo;
-    const int r0 = g.row_off[grp], r1 = g.row_off[grp + 1];
     const int gn = g.group_n;
     Problem P;
     if (OP == kGemmFwd || OP == kGemmDgrad) {
@@ -837,7 +890,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
         P.c = g.c + (int64_t)grp * gn * g.ldc;
     }
     const int ntn = (P.N + kBN - 1) / kBN;
-    const int local = pid - g.tile_start[grp];
     P.tm = local / ntn;
     P.tn = local - P.tm * ntn;
     gemm_tile<1, A_ST, B_ST, true, 0>(g, P);
@@ -919,26 +971,32 @@ hipError_t launch_dense_acc(const GemmArgs& g, bool a_st, bool b_st, int oned, i
     return launch_dense<1, true, false, 0, true>(g, batch, s);
 }
 
-template <int OP, bool A_ST, bool B_ST>
+template <int OP, bool A_ST, bool B_ST, bool DEV>
 hipError_t launch_grouped(const GemmArgs& g, hipStream_t s)
 {
-    const int ntiles = g.tile_start[g.n_groups];
+    // Host offsets: the exact tile count.  Device offsets: the bound the host
+    // computed (g.tile_bound); surplus workgroups exit.
+    const int ntiles = DEV ? g.tile_bound : g.tile_start[g.n_groups];
     if (ntiles == 0)
         return hipSuccess;
-    // K of a group: FWD the full K, DGRAD the expert width, WGRAD the largest token segment
+    // K of a group: FWD the full K, DGRAD the expert width, WGRAD the largest
+    // token segment (device offsets: the caller's bound max_rows)
     int kmax = g.K;
     if (OP == kGemmDgrad)
         kmax = g.group_n;
     if (OP == kGemmWgrad) {
         kmax = 32;
-        for (int i = 0; i < g.n_groups; ++i)
-            kmax = max(kmax, g.row_off[i + 1] - g.row_off[i]);
+        if (DEV)
+            kmax = max(kmax, g.max_rows);
+        else
+            for (int i = 0; i < g.n_groups; ++i)
+                kmax = max(kmax, g.row_off[i + 1] - g.row_off[i]);
     }
     const size_t lb = lds_bytes(1, kmax);
-    hipError_t e = allow_lds(gemm_grouped_kernel<OP, A_ST, B_ST>, lb);
+    hipError_t e = allow_lds(gemm_grouped_kernel<OP, A_ST, B_ST, DEV>, lb);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((gemm_grouped_kernel<OP, A_ST, B_ST>), dim3(ntiles), dim3(kThreads), lb, s, g);
+    hipLaunchKernelGGL((gemm_grouped_kernel<OP, A_ST, B_ST, DEV>), dim3(ntiles), dim3(kThreads), lb, s, g);
     return hipGetLastError();
 }
 
@@ -958,12 +1016,19 @@ hipError_t launch_gemm(const GemmArgs& g, int fmt, bool a_st, bool b_st, int one
             return b_st ? launch_dense<1, false, true, 1>(g, batch, s) : launch_dense<1, false, false, 1>(g, batch, s);
         return a_st ? launch_dense<1, true, false, 2>(g, batch, s) : launch_dense<1, false, false, 2>(g, batch, s);
     }
+    if (grouped_op >= 0 && g.row_off_dev) {
+        if (grouped_op == kGemmFwd)
+            return launch_grouped<kGemmFwd, false, false, true>(g, s);
+        if (grouped_op == kGemmDgrad)
+            return launch_grouped<kGemmDgrad, false, true, true>(g, s);
+        return launch_grouped<kGemmWgrad, true, true, true>(g, s);
+    }
     if (grouped_op == kGemmFwd)
-        return launch_grouped<kGemmFwd, false, false>(g, s);
+        return launch_grouped<kGemmFwd, false, false, false>(g, s);
     if (grouped_op == kGemmDgrad)
-        return launch_grouped<kGemmDgrad, false, true>(g, s);
+        return launch_grouped<kGemmDgrad, false, true, false>(g, s);
     if (grouped_op == kGemmWgrad)
-        return launch_grouped<kGemmWgrad, true, true>(g, s);
+        return launch_grouped<kGemmWgrad, true, true, false>(g, s);
     if (fmt == 2)
         return launch_dense<2, false, false>(g, batch, s);
     if (!a_st && !b_st)

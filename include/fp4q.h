@@ -8,7 +8,8 @@
  *
  * Conventions shared by every entry point
  *  - Pointers named x, y, c and every pointer inside fp4q_qtensor are DEVICE
- *    pointers owned by the caller; fp4q_groups.row_off is a HOST array.
+ *    pointers owned by the caller; fp4q_groups.row_off is a host array
+ *    unless its flags say device.
  *    The library never allocates, frees or synchronizes; work is enqueued on
  *    the caller's stream (a hipStream_t passed as void*, NULL = default
  *    stream) and descriptors are read only during the call.
@@ -38,7 +39,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 2
+#define FP4Q_ABI_VERSION 3
 
 typedef enum {
     FP4Q_OK = 0,
@@ -113,16 +114,28 @@ typedef struct fp4q_qtensor {
 } fp4q_qtensor;
 
 /*
- * Token groups of a grouped (mixture-of-experts) GEMM.  row_off is a HOST
- * array of n+1 non-decreasing offsets, each a multiple of 32, with
- * row_off[0] = 0: group g owns token rows [row_off[g], row_off[g+1]).
- * 1 <= n <= FP4Q_MAX_GROUPS.
+ * Token groups of a grouped (mixture-of-experts) GEMM: group g owns token
+ * rows [row_off[g], row_off[g+1]).  1 <= n <= FP4Q_MAX_GROUPS.
+ *   flags 0: row_off is a HOST array of n+1 non-decreasing offsets, each a
+ *     multiple of 32, row_off[0] = 0 and row_off[n] <= the token rows of a
+ *     (validated; FP4Q_EINVAL otherwise).
+ *   flags FP4Q_GROUPS_DEVICE: row_off is a DEVICE array of n+1 int64
+ *     offsets, read by the kernels when they run (for routing computed on
+ *     the GPU; no host synchronization).  They should satisfy the same
+ *     rules; the kernels make any values memory-safe by clamping each
+ *     offset into [0, T32] (T32 = the token rows of a rounded down to 32),
+ *     rounding it down to a multiple of 32 and treating a decreasing pair as
+ *     an empty group.  WGRAD needs max_rows: a bound, a multiple of 32, on
+ *     any group's rows (its LDS is sized for it); a group's rows past it
+ *     are ignored.  max_rows is unused otherwise.
  */
 #define FP4Q_MAX_GROUPS 256
+#define FP4Q_GROUPS_DEVICE 1
 typedef struct fp4q_groups {
     int32_t n;
-    int32_t reserved;
+    int32_t flags;
     const int64_t* row_off;
+    int64_t max_rows;
 } fp4q_groups;
 
 /* ABI version of the loaded library (FP4Q_ABI_VERSION). */

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(fp4q):
 
 
 def test_version_and_sizes(fp4q):
-    assert fp4q.lib().fp4q_version() == 2
+    assert fp4q.lib().fp4q_version() == 3
     # Table 1 accounting: codes are a quarter of the bf16 bytes, plus 1 byte per tile
     assert fp4q.fp4q_quant2d_sizes(4096, 2048) == (4096 * 1024, 2048 * 2048, 128 * 64)
     assert fp4q.fp4q_quant2d_sizes(33, 65) == (64 * 48, 96 * 32, 2 * 3)
@@ -154,12 +154,12 @@ def test_gemm_rejects_bad_arguments(fp4q):
     # grouped: offsets must start at 0 and be multiples of 32
     for offs in ([0, 16, 64], [32, 64], [0, 64, 32], [0, 32, 96]):
         arr = (ctypes.c_int64 * len(offs))(*offs)
-        g = fp4q._Groups(len(offs) - 1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+        g = fp4q._Groups(len(offs) - 1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), 0)
         w = _desc(fp4q, rows=64 * (len(offs) - 1), cols=64, ld_t=64 * (len(offs) - 1) // 2)
         assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(w), c, 64, 0, ctypes.byref(g), None) == -1
     # grouped products take 32x32 blocks only
     arr = (ctypes.c_int64 * 2)(0, 64)
-    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), 0)
     a64 = _desc(fp4q, fmt=3, rows=64, cols=64)
     assert L.fp4q_gemm(0, ctypes.byref(a64), ctypes.byref(a), c, 64, 0, ctypes.byref(g), None) == -2
     assert "32x32" in _err(fp4q)
@@ -202,7 +202,7 @@ def test_act1d_layout_rejects_bad_arguments(fp4q):
     assert L.fp4q_gemm(0, ctypes.byref(ab), ctypes.byref(wb), c, 64, 64 * 64, None, None) == -2
     assert "batch 1" in _err(fp4q)
     arr = (ctypes.c_int64 * 2)(0, 64)
-    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), 0)
     assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(w), c, 64, 0, ctypes.byref(g), None) == -2
     nt = _desc1d(fp4q, scales_t=0)
     assert L.fp4q_gemm(2, ctypes.byref(w), ctypes.byref(nt), c, 64, 0, None, None) == -1  # X^T grid
@@ -221,7 +221,7 @@ def test_gemm_ex_accumulate_rejects_unsupported(fp4q):
     f8 = _desc(fp4q, fmt=2, ld=64)
     assert L.fp4q_gemm_ex(0, ctypes.byref(f8), ctypes.byref(f8), c, 64, 0, None, 1, None) == -2
     arr = (ctypes.c_int64 * 2)(0, 64)
-    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), 0)
     assert L.fp4q_gemm_ex(0, ctypes.byref(a), ctypes.byref(a), c, 64, 0, ctypes.byref(g), 1, None) == -2
     x1 = _desc1d(fp4q)
     assert L.fp4q_gemm_ex(0, ctypes.byref(x1), ctypes.byref(a), c, 64, 0, None, 1, None) == -2
@@ -229,6 +229,32 @@ def test_gemm_ex_accumulate_rejects_unsupported(fp4q):
     with pytest.raises(fp4q.Fp4qError):
         fp4q.fp4q_gemm("wgrad", fp4q.alloc_fp4(64, 64, device="cpu"), fp4q.alloc_fp4(64, 64, device="cpu"),
                        accumulate=True)
+
+
+def test_device_group_offsets_validation(fp4q):
+    """Device offsets cannot be checked on the host; what can be is: known
+    flags, and for WGRAD a max_rows bound that is a multiple of 32 within the
+    token rows (the kernels clamp the offsets themselves)."""
+    L = fp4q.lib()
+    c = ctypes.c_void_p(0x50000)
+    a = _desc(fp4q, rows=256, cols=64, ld_t=128)
+    w = _desc(fp4q, rows=128, cols=64)
+    dev_off = ctypes.cast(ctypes.c_void_p(0x90000), ctypes.POINTER(ctypes.c_int64))
+    for flags, max_rows in ((2, 64), (3, 64)):
+        g = fp4q._Groups(2, flags, dev_off, max_rows)
+        assert L.fp4q_gemm(0, ctypes.byref(a), ctypes.byref(w), c, 64, 0, ctypes.byref(g), None) == -1
+        assert "flags" in _err(fp4q)
+    dy = _desc(fp4q, rows=256, cols=64, ld_t=128)
+    for max_rows in (0, 48, 512):
+        g = fp4q._Groups(2, 1, dev_off, max_rows)
+        assert L.fp4q_gemm(2, ctypes.byref(dy), ctypes.byref(a), c, 64, 0, ctypes.byref(g), None) == -1
+        assert "max_rows" in _err(fp4q)
+    # host offsets must end within the whole 32-row blocks of a
+    arr = (ctypes.c_int64 * 2)(0, 256)
+    g = fp4q._Groups(1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), 0)
+    a250 = _desc(fp4q, rows=250, cols=64, ld_t=128)
+    assert L.fp4q_gemm(0, ctypes.byref(a250), ctypes.byref(w), c, 64, 0, ctypes.byref(g), None) == -1
+    assert "beyond" in _err(fp4q)
 
 
 def test_dequant_and_mxfp8_reject_bad_arguments(fp4q):

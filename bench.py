@@ -344,6 +344,26 @@ def side_moe(torch, fq, wl, iters, warmup):
     out = {"workload": "30b-moe-expert-layer-step: 8192 tokens, top-8 of 128 experts, hidden 2048, FFN 768; "
                        "%d gathered rows (32-aligned segments); flops counted on the gathered rows" % rows}
     out.update(_summary(ms, work, kinds))
+    # The same grouped GEMMs with the offsets in device memory (routing that
+    # never visits the host): the grid is a bound and every workgroup builds
+    # the tile table itself.
+    dev_off = torch.tensor(offs, dtype=torch.int64, device="cuda")
+    max_rows = int(np.diff(m.row_off).max())
+    dev_launches = []
+    for nm, fn in launches:
+        if nm.startswith("quant:"):
+            continue
+        op = nm.split(":")[1]
+        a, b, c = {"up:fwd": ("qX", "qW_up", "Y_up"), "up:dgrad": ("qdY", "qW_up", "dX_up"),
+                   "up:wgrad": ("qdY", "qX", "dW_up"), "down:fwd": ("qA", "qW_down", "Y_dn"),
+                   "down:dgrad": ("qdY_down", "qW_down", "dX_dn"), "down:wgrad": ("qdY_down", "qA", "dW_dn")}[nm]
+        dev_launches.append((nm, lambda op=op, a=a, b=b, c=c: fq.fp4q_gemm(
+            op, dev[a], dev[b], out_t[c], groups=dev_off, max_group_rows=max_rows)))
+    ms_dev = _timed_launches(torch, dev_launches, iters, warmup)
+    g_host = sum(v for n, v in ms.items() if kinds[n] == "gemm")
+    g_dev = sum(ms_dev.values())
+    out["gemm_ms_device_offsets"] = round(g_dev, 4)
+    out["gemm_device_over_host_offsets"] = round(g_dev / g_host, 4)
     return out
 
 

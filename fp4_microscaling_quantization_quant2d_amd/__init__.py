@@ -29,7 +29,7 @@ FMT_FP4_2D32, FMT_MXFP8_1D32, FMT_FP4_2D64, FMT_FP4_1D32 = 1, 2, 3, 4
 DT_BF16, DT_F32 = 1, 2
 ROUND = {"sr": 0, "rne": 1}
 OPS = {"fwd": 0, "dgrad": 1, "wgrad": 2}
-GEMM_ACCUMULATE = 1
+GEMM_ACCUMULATE, GEMM_OUT_BF16 = 1, 2
 
 
 class Fp4qError(RuntimeError):
@@ -294,21 +294,23 @@ def gemm_out_shape(op, a: QTensor, b: QTensor, groups: Optional[Sequence[int]] =
 
 
 def fp4q_gemm(op, a: QTensor, b: QTensor, c: Optional[torch.Tensor] = None,
-              groups=None, stream=None, accumulate=False, max_group_rows=None):
+              groups=None, stream=None, accumulate=False, max_group_rows=None, out_dtype=torch.float32):
     """C = X W^T (fwd), dY W (dgrad) or dY^T X (wgrad) in fp32.  groups: row
     offsets (multiples of 32) of a grouped expert product -- a host sequence,
     or an int64 CUDA tensor read by the kernels (FP4Q_GROUPS_DEVICE; wgrad then
     needs max_group_rows, a bound on any group's rows).  accumulate: C += the
-    product (fp4q_gemm_ex with FP4Q_GEMM_ACCUMULATE; c required)."""
+    product (fp4q_gemm_ex with FP4Q_GEMM_ACCUMULATE; c required).  A bfloat16 C
+    (given, or out_dtype=torch.bfloat16) takes FP4Q_GEMM_OUT_BF16."""
     opc = OPS.get(op, op)
     M, N = gemm_out_shape(opc, a, b, groups)
     if accumulate and c is None:
         raise Fp4qError("accumulate needs the C to add to")
     if c is None:
         shape = (a.batch, M, N) if a.batch > 1 else (M, N)
-        c = torch.empty(shape, dtype=torch.float32, device=a.codes.device)
-    if c.dtype != torch.float32 or c.stride(-1) != 1:
-        raise Fp4qError("C must be a row-major float32 tensor")
+        c = torch.empty(shape, dtype=out_dtype, device=a.codes.device)
+    if c.dtype not in (torch.float32, torch.bfloat16) or c.stride(-1) != 1:
+        raise Fp4qError("C must be a row-major float32 or bfloat16 tensor")
+    flags = (GEMM_ACCUMULATE if accumulate else 0) | (GEMM_OUT_BF16 if c.dtype == torch.bfloat16 else 0)
     ldc = c.stride(-2)
     cbs = c.stride(0) if c.dim() == 3 else 0
     g = None
@@ -322,9 +324,9 @@ def fp4q_gemm(op, a: QTensor, b: QTensor, c: Optional[torch.Tensor] = None,
         arr = (ctypes.c_int64 * len(groups))(*[int(v) for v in groups])
         g = _Groups(len(groups) - 1, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), 0)
     da, db = a.desc(), b.desc()
-    if accumulate:
+    if flags:
         _check(_load().fp4q_gemm_ex(opc, ctypes.byref(da), ctypes.byref(db), _ptr(c), ldc, cbs,
-                                    ctypes.byref(g) if g is not None else None, GEMM_ACCUMULATE,
+                                    ctypes.byref(g) if g is not None else None, flags,
                                     _stream_ptr(stream)), "fp4q_gemm_ex")
         return c
     _check(_load().fp4q_gemm(opc, ctypes.byref(da), ctypes.byref(db), _ptr(c), ldc, cbs,

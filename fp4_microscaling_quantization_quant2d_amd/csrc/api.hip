@@ -289,14 +289,15 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
     return fp4q_gemm_ex(op, a, b, c, ldc, c_bstride, groups, 0, hip_stream);
 }
 
-int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, int64_t ldc, int64_t c_bstride,
+int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, int64_t ldc, int64_t c_bstride,
                  const fp4q_groups* groups, int flags, void* hip_stream)
 {
     if (op != FP4Q_OP_FWD && op != FP4Q_OP_DGRAD && op != FP4Q_OP_WGRAD)
         return fail(FP4Q_EINVAL, "fp4q_gemm: op %d", op);
-    if (flags & ~FP4Q_GEMM_ACCUMULATE)
+    if (flags & ~(FP4Q_GEMM_ACCUMULATE | FP4Q_GEMM_OUT_BF16))
         return fail(FP4Q_EINVAL, "fp4q_gemm_ex: unknown flags 0x%x", flags);
     const bool accumulate = (flags & FP4Q_GEMM_ACCUMULATE) != 0;
+    const bool out_bf16 = (flags & FP4Q_GEMM_OUT_BF16) != 0;
     if (!a || !b || !c)
         return fail(FP4Q_EINVAL, "fp4q_gemm: null a, b or c");
     const bool fp8 = a->fmt == FP4Q_FMT_MXFP8_1D32;
@@ -401,7 +402,7 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c,
         if ((g.a_rows + reach) * g.lda > INT_MAX || (g.b_rows + reach) * g.ldb > INT_MAX)
             return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: an operand plane exceeds 2 GiB");
     }
-    g.c = c;
+    g.c = static_cast<float*>(c);
     g.ldc = ldc;
     g.bs_c = c_bstride;
     g.M = (int)M;
@@ -504,10 +505,13 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c,
     if (accumulate && (fp8 || groups || (oned & 1)))
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_ex: accumulation takes dense FP4 products whose A operand "
                                        "has a square-block grid");
+    if (out_bf16 && (accumulate || groups || oned))
+        return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_ex: bf16 output takes dense products (no accumulation) of "
+                                       "square-block FP4 or MXFP8 operands");
     if (fp4q::gemm_lds_bytes(fp8 ? 2 : 1, (int)kmax) > kMaxLdsBytes)
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: K %lld too large for the %s tile (max %d)", (long long)kmax,
                     fp8 ? "MXFP8" : "FP4", fp8 ? max_k(2) : max_k(1));
-    return hip_status(fp4q::launch_gemm(g, fp8 ? 2 : 1, a_st, b_st, oned, grouped_op, (int)a->batch, accumulate,
+    return hip_status(fp4q::launch_gemm(g, fp8 ? 2 : 1, a_st, b_st, oned, grouped_op, (int)a->batch, accumulate, out_bf16,
                                         static_cast<hipStream_t>(hip_stream)),
                       "fp4q_gemm");
 }

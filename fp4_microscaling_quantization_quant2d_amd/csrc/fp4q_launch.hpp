@@ -80,7 +80,7 @@ struct GemmArgs {
     const uint8_t* b;
     const uint8_t* sa;
     const uint8_t* sb;
-    float* c;
+    float* c;              // fp32 C, or bf16 C reinterpreted (out_bf16)
     int64_t lda, ldb;      // bytes per operand row
     int64_t lds_a, lds_b;  // bytes per scale-grid row
     int sh_a, sh_b;        // FP4: log2 of each operand's square scale block (5: 32x32, 6: 64x64)
@@ -109,8 +109,10 @@ enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };
 // (chunk (g, q) of rows 128g.., K-blocks 4q.. at g*lds + q*512; FP4, dense).
 // grouped_op: -1 dense/batched, else the op whose grouped wiring applies.
 // accumulate: C += A B^T (FP4, dense; oned 0 or 2 only).
+// out_bf16: C is bf16, ldc and the batch stride in bf16 elements (dense; FP4
+// with oned 0, or MXFP8).
 hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
-                       bool accumulate, hipStream_t s);
+                       bool accumulate, bool out_bf16, hipStream_t s);
 
 // Output tile of the GEMM kernel (grouped launches size their grids with it).
 int gemm_tile_m();

@@ -261,7 +261,8 @@ __device__ __forceinline__ void wait_vm_and_barrier()
 // multiplied) may read past a row's K bytes.
 // ONED: bit 0 -- A is an FP4 operand in the 1D activation layout, bit 1 -- B.
 // ACC: C += A B^T (C is read in the epilogue) instead of C = A B^T.
-template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC = false>
+// OBF: C is bf16 (each fp32 sum rounded to nearest even), ldc in bf16 elements.
+template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC = false, bool OBF = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
 {
     constexpr bool A1D = FMT == 1 && (ONED & 1), B1D = FMT == 1 && (ONED & 2);
@@ -673,6 +674,34 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // kernel to write back.  Every store instruction covers two full 128-byte
     // row segments.  Interior tiles address each store as one per-lane base
     // plus a wave-uniform row offset and a constant column offset.
+    if constexpr (OBF) {
+        // bf16 output: half the bytes of the fp32 store phase; the same
+        // rotated block order on interior tiles, bounds checks on edge tiles.
+        __bf16* ch = reinterpret_cast<__bf16*>(P.c);
+        const bool interior = m0 + kBM <= P.M && n0 + kBN <= P.N;
+        auto store_bf = [&](auto ROT) {
+            static_for<4>([&](auto B) {
+                constexpr int mi = (decltype(B)::value + decltype(ROT)::value) & 3;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const int col = n0 + wn * 128 + ni * 32 + lrow32;
+                        if (interior || (row < P.M && col < P.N))
+                            __builtin_nontemporal_store((__bf16)acc[mi][ni][r], &ch[(int64_t)row * g.ldc + col]);
+                    }
+                }
+            });
+        };
+        switch ((P.tm + P.tn) & 3) {
+        case 0: store_bf(std::integral_constant<int, 0>()); break;
+        case 1: store_bf(std::integral_constant<int, 1>()); break;
+        case 2: store_bf(std::integral_constant<int, 2>()); break;
+        default: store_bf(std::integral_constant<int, 3>()); break;
+        }
+        return;
+    }
     if (m0 + kBM <= P.M && n0 + kBN <= P.N) {
         // The store phases of all CUs coincide, and tiles otherwise write
         // the same relative rows at the same moment; for leading dimensions
@@ -765,7 +794,7 @@ __device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int&
     tn = in / rows;
 }
 
-template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC>
+template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC, bool OBF>
 __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
 {
     const int bz = blockIdx.y;
@@ -774,7 +803,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
     P.b = g.b + bz * g.bs_b;
     P.sa = g.sa + bz * g.bs_sa;
     P.sb = g.sb + bz * g.bs_sb;
-    P.c = g.c + bz * g.bs_c;
+    P.c = OBF ? reinterpret_cast<float*>(reinterpret_cast<__bf16*>(g.c) + bz * g.bs_c) : g.c + bz * g.bs_c;
     P.M = g.M;
     P.N = g.N;
     P.K = g.K;
@@ -782,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
     P.b_rows = g.b_rows;
     const int ntm = (g.M + kBM - 1) / kBM, ntn = (g.N + kBN - 1) / kBN;
     tile_of<FMT == 1 ? 4 : 8>(blockIdx.x, ntm, ntn, P.tm, P.tn);
-    gemm_tile<FMT, A_ST, B_ST, KT, ONED, ACC>(g, P);
+    gemm_tile<FMT, A_ST, B_ST, KT, ONED, ACC, OBF>(g, P);
 }
 
 // Grouped (expert) products.  Group g owns token rows [row_off[g], row_off[g+1]).
@@ -934,25 +963,39 @@ hipError_t allow_lds(F* fn, size_t bytes)
     return allow_lds_raw(reinterpret_cast<const void*>(fn), bytes);
 }
 
-template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC>
+template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC, bool OBF>
 hipError_t launch_dense_k(const GemmArgs& g, int batch, hipStream_t s)
 {
     const int ntm = (g.M + kBM - 1) / kBM, ntn = (g.N + kBN - 1) / kBN;
     const size_t lb = lds_bytes(FMT, g.K, ONED);
-    hipError_t e = allow_lds(gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED, ACC>, lb);
+    hipError_t e = allow_lds(gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED, ACC, OBF>, lb);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED, ACC>), dim3(ntm * ntn, batch), dim3(kThreads),
-                       lb, s, g);
+    hipLaunchKernelGGL((gemm_dense_kernel<FMT, A_ST, B_ST, KT, ONED, ACC, OBF>), dim3(ntm * ntn, batch),
+                       dim3(kThreads), lb, s, g);
     return hipGetLastError();
 }
 
-template <int FMT, bool A_ST, bool B_ST, int ONED = 0, bool ACC = false>
+template <int FMT, bool A_ST, bool B_ST, int ONED = 0, bool ACC = false, bool OBF = false>
 hipError_t launch_dense(const GemmArgs& g, int batch, hipStream_t s)
 {
     if (FMT == 1 && g.K % 256 == 0)
-        return launch_dense_k<FMT, A_ST, B_ST, false, ONED, ACC>(g, batch, s);
-    return launch_dense_k<FMT, A_ST, B_ST, true, ONED, ACC>(g, batch, s);
+        return launch_dense_k<FMT, A_ST, B_ST, false, ONED, ACC, OBF>(g, batch, s);
+    return launch_dense_k<FMT, A_ST, B_ST, true, ONED, ACC, OBF>(g, batch, s);
+}
+
+// bf16 C for FP4 operands with square-block grids, and for MXFP8 S = Q K^T.
+hipError_t launch_dense_obf(const GemmArgs& g, int fmt, bool a_st, bool b_st, int batch, hipStream_t s)
+{
+    if (fmt == 2)
+        return launch_dense<2, false, false, 0, false, true>(g, batch, s);
+    if (!a_st && !b_st)
+        return launch_dense<1, false, false, 0, false, true>(g, batch, s);
+    if (!a_st && b_st)
+        return launch_dense<1, false, true, 0, false, true>(g, batch, s);
+    if (a_st && b_st)
+        return launch_dense<1, true, true, 0, false, true>(g, batch, s);
+    return launch_dense<1, true, false, 0, false, true>(g, batch, s);
 }
 
 // C += A B^T for FP4 operands with 32x32 or 64x64 blocks, or a 1D-layout B
@@ -1003,8 +1046,10 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t s)
 } // namespace
 
 hipError_t launch_gemm(const GemmArgs& g, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
-                       bool accumulate, hipStream_t s)
+                       bool accumulate, bool out_bf16, hipStream_t s)
 {
+    if (out_bf16)
+        return launch_dense_obf(g, fmt, a_st, b_st, batch, s);
     if (accumulate)
         return launch_dense_acc(g, a_st, b_st, oned, batch, s);
     // 1D-layout operands (FP4, dense): the grid orientation of such an

@@ -272,7 +272,15 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
  * return FP4Q_EINVAL.
  */
 #define FP4Q_GEMM_ACCUMULATE 1
-int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, int64_t ldc,
+/*
+ * FP4Q_GEMM_OUT_BF16: C is bf16 (each fp32 result rounded to nearest even;
+ * c points to bf16, ldc and c_bstride count bf16 elements), halving the
+ * output bytes that bound the store phase.  Dense products without
+ * accumulation, of FP4 operands with square-block grids or of MXFP8
+ * operands (S = Q K^T); anything else returns FP4Q_EUNSUPPORTED.
+ */
+#define FP4Q_GEMM_OUT_BF16 2
+int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, int64_t ldc,
                  int64_t c_bstride, const fp4q_groups* groups, int flags, void* hip_stream);
 
 /*

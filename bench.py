@@ -94,8 +94,9 @@ def quant_bytes_1d(rows, cols):
 class Step:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, layers, torch, fq, block=32, x_block=None, wgrad_accumulate=False):
+    def __init__(self, layers, torch, fq, block=32, x_block=None, wgrad_accumulate=False, out_dtype=None):
         self.torch, self.fq = torch, fq
+        out_dtype = out_dtype or torch.float32  # bf16: every GEMM writes bf16 C
         # wgrad_accumulate: dW += dY^T X, as in a micro-batch after the first
         self.wgrad_acc = wgrad_accumulate
         self.layers = []
@@ -110,9 +111,9 @@ class Step:
                 d["q" + nm] = fq.alloc_fp4(a.shape[0], a.shape[1], block=x_block if nm == "X" and self.x_sep
                                            else block)
             T, K, N = L.T, L.K, L.N
-            d["Y"] = torch.empty((T, N), dtype=torch.float32, device="cuda")
-            d["dX"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
-            d["dW"] = torch.empty((N, K), dtype=torch.float32, device="cuda")
+            d["Y"] = torch.empty((T, N), dtype=out_dtype, device="cuda")
+            d["dX"] = torch.empty((T, K), dtype=out_dtype, device="cuda")
+            d["dW"] = torch.empty((N, K), dtype=out_dtype, device="cuda")
             d["shape"] = (T, K, N)
             d["name"] = L.name
             self.layers.append(d)
@@ -305,6 +306,20 @@ def side_wgrad_acc(torch, fq, wl, iters, warmup):
     return out
 
 
+def side_bf16_out(torch, fq, wl, iters, warmup):
+    """The 7B layer step with every GEMM writing bf16 C beside the fp32 step
+    (eager, per-launch events): the output write is the store phase."""
+    out = {"workload": "7b-linear-layer-step with bf16 GEMM outputs and with fp32 outputs (eager, per-launch events)"}
+    for key, dt in (("fp32", torch.float32), ("bf16", torch.bfloat16)):
+        step = Step(wl.config_7b(), torch, fq, out_dtype=dt)
+        out[key] = _eager_step(step, torch, iters, warmup)
+        del step
+        torch.cuda.empty_cache()
+    for key in ("ms_per_step", "gemm_ms"):
+        out[key + "_bf16_over_fp32"] = round(out["bf16"][key] / out["fp32"][key], 4)
+    return out
+
+
 def side_moe(torch, fq, wl, iters, warmup):
     """One step of the 30B-class MoE expert layer: per-expert 2D quantization
     (one call over the gathered, 32-aligned expert segments) and grouped
@@ -416,6 +431,14 @@ def side_attn(torch, fq, wl, iters, warmup):
                                        / 1e12, 1),
            "oproj_quant_GB/s": round((quant_bytes(T, K) + quant_bytes(N, K) + quant_bytes(T, N))
                                      / ((ms["o:quant:X"] + ms["o:quant:W"] + ms["o:quant:dY"]) / 1e3) / 1e9, 1)}
+    # S in bf16 (FP4Q_GEMM_OUT_BF16): half the bytes of the write that bounds it
+    del S, launches
+    torch.cuda.empty_cache()
+    S16 = torch.empty((B * Hh, L, L), dtype=torch.bfloat16, device="cuda")
+    s16 = _timed_launches(torch, [("S16", lambda: fq.fp4q_gemm("fwd", bq, bk, S16))], iters, warmup)["S16"]
+    out["S_bf16_ms"] = round(s16, 4)
+    out["S_bf16_TFLOP/s"] = round(2.0 * B * Hh * L * L * D / (s16 / 1e3) / 1e12, 1)
+    out["S_bf16_write_GB/s"] = round(2.0 * B * Hh * L * L / (s16 / 1e3) / 1e9, 1)
     return out
 
 
@@ -632,7 +655,7 @@ def main():
     if not args.no_side_paths:
         side = {}
         for name, fn in (("1b", side_1b), ("moe", side_moe), ("attn", side_attn), ("block64", side_block64),
-                         ("act1d", side_act1d), ("wgrad_acc", side_wgrad_acc)):
+                         ("act1d", side_act1d), ("wgrad_acc", side_wgrad_acc), ("bf16_out", side_bf16_out)):
             print("[bench] side path %s" % name, file=sys.stderr, flush=True)
             side[name] = fn(torch, fq, wl, iters=5, warmup=2)
             torch.cuda.empty_cache()

@@ -675,30 +675,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // row segments.  Interior tiles address each store as one per-lane base
     // plus a wave-uniform row offset and a constant column offset.
     if constexpr (OBF) {
-        // bf16 output: half the bytes of the fp32 store phase; the same
-        // rotated block order on interior tiles, bounds checks on edge tiles.
-        __bf16* ch = reinterpret_cast<__bf16*>(P.c);
-        const bool interior = m0 + kBM <= P.M && n0 + kBN <= P.N;
-        auto store_bf = [&](auto ROT) {
-            static_for<4>([&](auto B) {
-                constexpr int mi = (decltype(B)::value + decltype(ROT)::value) & 3;
+        // bf16 output.  A lane holds one column of each 32x32 block, so direct
+        // 2-byte stores would write half lines; instead each wave stages its
+        // 128x128 bf16 sub-tile in its 32 KB of the (now idle) operand ring
+        // and writes whole 128-byte lines with 16-byte stores.  Rows 4..7 of
+        // every 8 are XOR-shifted by 64 bytes so the two lane halves' LDS
+        // writes fall in different banks.
+        __syncthreads();  // every wave has finished reading the ring
+        uint8_t* st = lds + wave * (128 * 256);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const int col = n0 + wn * 128 + ni * 32 + lrow32;
-                        if (interior || (row < P.M && col < P.N))
-                            __builtin_nontemporal_store((__bf16)acc[mi][ni][r], &ch[(int64_t)row * g.ldc + col]);
-                    }
+                    const int row = mi * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                    const int cb = (ni * 32 + lrow32) * 2;
+                    *reinterpret_cast<__bf16*>(st + row * 256 + (cb ^ (((row >> 2) & 1) << 6))) =
+                        (__bf16)acc[mi][ni][r];
                 }
-            });
-        };
-        switch ((P.tm + P.tn) & 3) {
-        case 0: store_bf(std::integral_constant<int, 0>()); break;
-        case 1: store_bf(std::integral_constant<int, 1>()); break;
-        case 2: store_bf(std::integral_constant<int, 2>()); break;
-        default: store_bf(std::integral_constant<int, 3>()); break;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back only its own rows
+        __bf16* ch = reinterpret_cast<__bf16*>(P.c);
+        const int rbase = m0 + wm * 128, cbase = n0 + wn * 128;
+        const bool vec = m0 + kBM <= P.M && n0 + kBN <= P.N && (g.ldc & 7) == 0 &&
+                         (reinterpret_cast<uintptr_t>(P.c) & 15) == 0;
+        const int k = lane & 15;
+#pragma unroll 4
+        for (int it = 0; it < 32; ++it) {
+            const int row = it * 4 + (lane >> 4);
+            const v4u v = *reinterpret_cast<const v4u*>(st + row * 256 + ((k * 16) ^ (((row >> 2) & 1) << 6)));
+            __bf16* dst = ch + (int64_t)(rbase + row) * g.ldc + cbase + 8 * k;
+            if (vec) {
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(dst));
+            } else if (rbase + row < P.M) {
+                const __bf16* e = reinterpret_cast<const __bf16*>(&v);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (cbase + 8 * k + j < P.N)
+                        dst[j] = e[j];
+            }
         }
         return;
     }

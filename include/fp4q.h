@@ -255,7 +255,9 @@ int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
  *          batch 1: FWD  b = stacked W [n*N x K], C [T x N], group g maps
  *          rows row_off[g].. of X to expert g's rows of W; DGRAD likewise
  *          with C [T x K]; WGRAD C = stacked dW [n*N x K], each expert
- *          contracting over its own token rows.
+ *          contracting over its own token rows.  The offsets are host or
+ *          device memory (fp4q_groups.flags); with device offsets the
+ *          kernels clamp them and WGRAD's K is bounded by max_rows.
  */
 int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, int64_t ldc,
               int64_t c_bstride, const fp4q_groups* groups, void* hip_stream);
@@ -285,7 +287,7 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, 
 
 /*
  * Dequantization X ~ P * S (Sec. 2.1 of the same page) to fp32 or bf16, for
- * all three formats.
+ * every format (each plane of the 1D layout with its own grid).
  *   transposed  0: the row plane, y is rows x cols; 1 (FP4 only): the
  *               transposed plane, y is cols x rows.
  *   out_dtype   FP4Q_DT_F32 or FP4Q_DT_BF16; ldy in elements.

@@ -379,6 +379,21 @@ def side_moe(torch, fq, wl, iters, warmup):
     g_dev = sum(ms_dev.values())
     out["gemm_ms_device_offsets"] = round(g_dev, 4)
     out["gemm_device_over_host_offsets"] = round(g_dev / g_host, 4)
+    # and with bf16 outputs (FP4Q_GEMM_OUT_BF16): the expert outputs are the bound
+    del out_t
+    torch.cuda.empty_cache()
+    bf = {k: torch.empty((rows, F) if k in ("Y_up", "dX_dn") else (rows, H) if k in ("dX_up", "Y_dn")
+                         else (E * F, H) if k == "dW_up" else (E * H, F), dtype=torch.bfloat16, device="cuda")
+          for k in ("Y_up", "dX_up", "dW_up", "Y_dn", "dX_dn", "dW_dn")}
+    bf_launches = []
+    for nm, (op, a, b, c) in {"up:fwd": ("fwd", "qX", "qW_up", "Y_up"), "up:dgrad": ("dgrad", "qdY", "qW_up", "dX_up"),
+                              "up:wgrad": ("wgrad", "qdY", "qX", "dW_up"), "down:fwd": ("fwd", "qA", "qW_down", "Y_dn"),
+                              "down:dgrad": ("dgrad", "qdY_down", "qW_down", "dX_dn"),
+                              "down:wgrad": ("wgrad", "qdY_down", "qA", "dW_dn")}.items():
+        bf_launches.append((nm, lambda op=op, a=a, b=b, c=c: fq.fp4q_gemm(op, dev[a], dev[b], bf[c], groups=offs)))
+    g_bf = sum(_timed_launches(torch, bf_launches, iters, warmup).values())
+    out["gemm_ms_bf16_out"] = round(g_bf, 4)
+    out["gemm_bf16_over_fp32_out"] = round(g_bf / g_host, 4)
     return out
 
 

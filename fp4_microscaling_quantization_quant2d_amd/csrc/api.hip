@@ -505,8 +505,8 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, 
     if (accumulate && (fp8 || groups || (oned & 1)))
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_ex: accumulation takes dense FP4 products whose A operand "
                                        "has a square-block grid");
-    if (out_bf16 && (accumulate || groups || oned))
-        return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_ex: bf16 output takes dense products (no accumulation) of "
+    if (out_bf16 && (accumulate || oned))
+        return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_ex: bf16 output takes products (no accumulation) of "
                                        "square-block FP4 or MXFP8 operands");
     if (fp4q::gemm_lds_bytes(fp8 ? 2 : 1, (int)kmax) > kMaxLdsBytes)
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: K %lld too large for the %s tile (max %d)", (long long)kmax,

@@ -109,8 +109,8 @@ enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };
 // (chunk (g, q) of rows 128g.., K-blocks 4q.. at g*lds + q*512; FP4, dense).
 // grouped_op: -1 dense/batched, else the op whose grouped wiring applies.
 // accumulate: C += A B^T (FP4, dense; oned 0 or 2 only).
-// out_bf16: C is bf16, ldc and the batch stride in bf16 elements (dense; FP4
-// with oned 0, or MXFP8).
+// out_bf16: C is bf16, ldc and the batch stride in bf16 elements (FP4 with
+// oned 0, dense or grouped, or MXFP8).
 hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
                        bool accumulate, bool out_bf16, hipStream_t s);
 

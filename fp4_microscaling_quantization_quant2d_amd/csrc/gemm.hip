@@ -839,7 +839,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dense_kernel(GemmArgs g)
 // non-decreasing pairwise (a WGRAD group also to at most max_rows rows, the
 // K its LDS was sized for), so every access stays inside the operands for
 // any offsets; workgroups past the last tile exit.
-template <int OP, bool A_ST, bool B_ST, bool DEV>
+// Element `off` of C, fp32 or (OBF) bf16.
+template <bool OBF>
+__device__ __forceinline__ float* c_elem(float* c, int64_t off)
+{
+    return OBF ? reinterpret_cast<float*>(reinterpret_cast<__bf16*>(c) + off) : c + off;
+}
+
+template <int OP, bool A_ST, bool B_ST, bool DEV, bool OBF = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
 {
     const int pid = blockIdx.x;
@@ -907,7 +914,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
         P.a = g.a + (int64_t)r0 * g.lda;
         P.sa = g.sa + (int64_t)(r0 >> 5) * g.lds_a;
         P.a_rows = g.a_rows - r0;
-        P.c = g.c + (int64_t)r0 * g.ldc;
+        P.c = c_elem<OBF>(g.c, (int64_t)r0 * g.ldc);
         if (OP == kGemmFwd) {
             P.N = gn;
             P.K = g.K;
@@ -931,12 +938,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
         P.sb = g.sb + (int64_t)(r0 >> 5) * g.lds_b;
         P.a_rows = g.a_rows;
         P.b_rows = g.b_rows;
-        P.c = g.c + (int64_t)grp * gn * g.ldc;
+        P.c = c_elem<OBF>(g.c, (int64_t)grp * gn * g.ldc);
     }
     const int ntn = (P.N + kBN - 1) / kBN;
     P.tm = local / ntn;
     P.tn = local - P.tm * ntn;
-    gemm_tile<1, A_ST, B_ST, true, 0>(g, P);
+    gemm_tile<1, A_ST, B_ST, true, 0, false, OBF>(g, P);
 }
 
 // Dynamic LDS: two stage buffers plus, per operand, the tile's scale bytes
@@ -1029,7 +1036,7 @@ hipError_t launch_dense_acc(const GemmArgs& g, bool a_st, bool b_st, int oned, i
     return launch_dense<1, true, false, 0, true>(g, batch, s);
 }
 
-template <int OP, bool A_ST, bool B_ST, bool DEV>
+template <int OP, bool A_ST, bool B_ST, bool DEV, bool OBF = false>
 hipError_t launch_grouped(const GemmArgs& g, hipStream_t s)
 {
     // Host offsets: the exact tile count.  Device offsets: the bound the host
@@ -1051,10 +1058,10 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t s)
                 kmax = max(kmax, g.row_off[i + 1] - g.row_off[i]);
     }
     const size_t lb = lds_bytes(1, kmax);
-    hipError_t e = allow_lds(gemm_grouped_kernel<OP, A_ST, B_ST, DEV>, lb);
+    hipError_t e = allow_lds(gemm_grouped_kernel<OP, A_ST, B_ST, DEV, OBF>, lb);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((gemm_grouped_kernel<OP, A_ST, B_ST, DEV>), dim3(ntiles), dim3(kThreads), lb, s, g);
+    hipLaunchKernelGGL((gemm_grouped_kernel<OP, A_ST, B_ST, DEV, OBF>), dim3(ntiles), dim3(kThreads), lb, s, g);
     return hipGetLastError();
 }
 
@@ -1063,6 +1070,17 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t s)
 hipError_t launch_gemm(const GemmArgs& g, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
                        bool accumulate, bool out_bf16, hipStream_t s)
 {
+    if (out_bf16 && grouped_op >= 0) {
+        const bool dev = g.row_off_dev != nullptr;
+        if (grouped_op == kGemmFwd)
+            return dev ? launch_grouped<kGemmFwd, false, false, true, true>(g, s)
+                       : launch_grouped<kGemmFwd, false, false, false, true>(g, s);
+        if (grouped_op == kGemmDgrad)
+            return dev ? launch_grouped<kGemmDgrad, false, true, true, true>(g, s)
+                       : launch_grouped<kGemmDgrad, false, true, false, true>(g, s);
+        return dev ? launch_grouped<kGemmWgrad, true, true, true, true>(g, s)
+                   : launch_grouped<kGemmWgrad, true, true, false, true>(g, s);
+    }
     if (out_bf16)
         return launch_dense_obf(g, fmt, a_st, b_st, batch, s);
     if (accumulate)

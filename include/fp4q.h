@@ -277,9 +277,9 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
 /*
  * FP4Q_GEMM_OUT_BF16: C is bf16 (each fp32 result rounded to nearest even;
  * c points to bf16, ldc and c_bstride count bf16 elements), halving the
- * output bytes that bound the store phase.  Dense products without
- * accumulation, of FP4 operands with square-block grids or of MXFP8
- * operands (S = Q K^T); anything else returns FP4Q_EUNSUPPORTED.
+ * output bytes that bound the store phase.  Products without accumulation
+ * (dense, batched or grouped) of FP4 operands with square-block grids, or of
+ * MXFP8 operands (S = Q K^T); anything else returns FP4Q_EUNSUPPORTED.
  */
 #define FP4Q_GEMM_OUT_BF16 2
 int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, int64_t ldc,

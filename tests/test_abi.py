@@ -229,7 +229,7 @@ def test_gemm_ex_accumulate_rejects_unsupported(fp4q):
     # bf16 output: dense, no accumulation, square-block FP4 or MXFP8
     assert L.fp4q_gemm_ex(0, ctypes.byref(a), ctypes.byref(a), c, 64, 0, None, 3, None) == -2
     assert L.fp4q_gemm_ex(0, ctypes.byref(x1), ctypes.byref(a), c, 64, 0, None, 2, None) == -2
-    assert L.fp4q_gemm_ex(0, ctypes.byref(a), ctypes.byref(a), c, 64, 0, ctypes.byref(g), 2, None) == -2
+    assert L.fp4q_gemm_ex(0, ctypes.byref(x1), ctypes.byref(a), c, 64, 0, None, 2, None) == -2
     assert "bf16" in _err(fp4q)
     with pytest.raises(fp4q.Fp4qError):
         fp4q.fp4q_gemm("wgrad", fp4q.alloc_fp4(64, 64, device="cpu"), fp4q.alloc_fp4(64, 64, device="cpu"),

@@ -112,3 +112,46 @@ def test_7b_qkv_bf16_output_sampled():
         del C
         ref, bound = orc.gemm_sampled(op, d[a], d[b], ci, cj)
         check_bf16(got, ref, bound, "7B %s" % op)
+
+
+@pytest.mark.parametrize("device_offsets", [False, True])
+def test_bf16_output_grouped(device_offsets):
+    """Grouped expert products with bf16 C (host and device offsets), per
+    expert against the oracle; empty experts give a zero dW."""
+    rng = np.random.default_rng(21)
+    counts = [40, 0, 96, 7, 64, 33]
+    E, H, F = len(counts), 96, 64
+    off = np.concatenate([[0], np.cumsum([(c + 31) // 32 * 32 for c in counts])]).astype(np.int64)
+    rows = int(off[-1])
+    X = np.zeros((rows, H), np.float32)
+    dY = np.zeros((rows, F), np.float32)
+    for e, c in enumerate(counts):
+        X[off[e]:off[e] + c] = rng.standard_normal((c, H))
+        dY[off[e]:off[e] + c] = rng.standard_normal((c, F)) * 1e-3
+    W = (rng.standard_normal((E * F, H)) * 0.02).astype(np.float32)
+    ts = {"X": X, "W": W, "dY": dY}
+    q = {nm: fq.fp4q_quant2d(to_dev(t), seed=0, stream_id=STREAMS[nm]) for nm, t in ts.items()}
+    d = {}
+    for nm, t in ts.items():
+        c, _, s = orc.quant2d(t, seed=0, stream=STREAMS[nm])
+        d[nm] = orc.dequant_fp4(c, s, *t.shape)
+    groups = torch.from_numpy(off).cuda() if device_offsets else off.tolist()
+    note("grouped bf16 out, device offsets %s" % device_offsets)
+    Y = fq.fp4q_gemm("fwd", q["X"], q["W"], groups=groups, out_dtype=torch.bfloat16)
+    dX = fq.fp4q_gemm("dgrad", q["dY"], q["W"], groups=groups, out_dtype=torch.bfloat16)
+    dW = fq.fp4q_gemm("wgrad", q["dY"], q["X"], groups=groups, out_dtype=torch.bfloat16,
+                      max_group_rows=128)
+    torch.cuda.synchronize()
+    Y, dX, dW = (t.float().cpu().numpy().astype(np.float64) for t in (Y, dX, dW))
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            assert not dW[e * F:(e + 1) * F].any()
+            continue
+        We = d["W"][e * F:(e + 1) * F]
+        ref, bound = orc.gemm(orc.OP_FWD, d["X"][r0:r1], We)
+        check_bf16(Y[r0:r1], ref, bound, "fwd e%d" % e)
+        ref, bound = orc.gemm(orc.OP_DGRAD, d["dY"][r0:r1], We)
+        check_bf16(dX[r0:r1], ref, bound, "dgrad e%d" % e)
+        ref, bound = orc.gemm(orc.OP_WGRAD, d["dY"][r0:r1], d["X"][r0:r1])
+        check_bf16(dW[e * F:(e + 1) * F], ref, bound, "wgrad e%d" % e)

@@ -7,8 +7,8 @@ Forward quantizes X and W (one batch launch when both take 32x32 blocks and
 share a dtype) and runs FWD; backward quantizes dY once and runs DGRAD and
 WGRAD on the saved quantized X and W -- each tensor is quantized exactly
 once, and W's transposed plane serves DGRAD.  Every step runs in the HIP kernels; this
-module only orders the calls.  Outputs and gradients are fp32 (dX is cast to
-X's dtype for autograd).
+module only orders the calls.  Y and dW are fp32; dX has X's dtype (bf16 X:
+the kernel's bf16 output, the fp32 result rounded to nearest even).
 """
 import torch
 
@@ -37,7 +37,9 @@ class _FP4LinearFn(torch.autograd.Function):
         qdy = fp4q_quant2d(dy.contiguous(), seed=ctx.seed, stream_id=ctx.stream_base + 3)
         dx = dw = None
         if ctx.needs_input_grad[0]:
-            dx = fp4q_gemm("dgrad", qdy, qw).to(ctx.x_dtype)
+            # a bf16 X gets its gradient from the bf16 epilogue (the fp32
+            # result rounded to nearest even)
+            dx = fp4q_gemm("dgrad", qdy, qw, out_dtype=ctx.x_dtype)
         if ctx.needs_input_grad[1]:
             dw = fp4q_gemm("wgrad", qdy, qx)
         ctx.q = None

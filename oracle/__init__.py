@@ -184,12 +184,13 @@ def quant2d(x, round_mode=ROUND_SR, seed=0, stream=0, threads=None, tile_rows=No
 
 
 def quant2d_block(x, block, round_mode=ROUND_SR, seed=0, stream=0):
-    """Square block x block FP4 quantization (block 32 or 64); returns
-    (codes, codes_t, scales) with the scale grid [ceil(R/b) x ceil(C/b)]."""
+    """Square block x block FP4 quantization (block 8, 16, 32 or 64); returns
+    (codes, codes_t, scales) with the scale grid [ceil(R/b) x ceil(C/b)], R
+    and C the shape rounded up to 32 (blocks with no valid entry: byte 0)."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
     rp, cp = pad32(rows), pad32(cols)
-    nbr, nbc = -(-rows // block), -(-cols // block)
+    nbr, nbc = -(-rp // block), -(-cp // block)
     codes = np.zeros((rp, cp // 2), dtype=np.uint8)
     codes_t = np.zeros((cp, rp // 2), dtype=np.uint8)
     scales = np.zeros((nbr, nbc), dtype=np.uint8)

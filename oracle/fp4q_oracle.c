@@ -307,13 +307,14 @@ int orc_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
     return 0;
 }
 
-/* Square b x b blocks for b in {32, 64} (Sec. 3 defines the scheme for any
- * square block; Table 4 compares b = 8, 16, 32, 64).  The same definition as
- * orc_quant2d with the block side as a parameter: one scale per b x b block
- * from the amax of its valid entries, every element rounded with its own
- * random field, so the element-to-random mapping does not depend on b.
- * Scale grid [ceil(rows/b) x ld_s]; the code planes keep the 32-padded
- * shapes of orc_quant2d. */
+/* Square b x b blocks for b in {8, 16, 32, 64} (Sec. 3 defines the scheme
+ * for any square block; Table 4 compares b = 8, 16, 32, 64).  The same
+ * definition as orc_quant2d with the block side as a parameter: one scale per
+ * b x b block from the amax of its valid entries, every element rounded with
+ * its own random field, so the element-to-random mapping does not depend on
+ * b.  The code planes keep the 32-padded shapes of orc_quant2d, and the
+ * scale grid covers them: [ceil(rows_pad/b) x ld_s]; a block with no valid
+ * entry has amax 0 and byte 0. */
 int orc_quant2d_block(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                       int round_mode, uint64_t seed, uint32_t stream, int block,
                       uint8_t* codes, int64_t ld, uint8_t* codes_t, int64_t ld_t,
@@ -321,15 +322,15 @@ int orc_quant2d_block(const void* x, int dtype, int64_t rows, int64_t cols, int6
 {
     int64_t rows_pad = pad32(rows), cols_pad = pad32(cols);
     int64_t br, bc, i, j;
-    if (!x || rows <= 0 || cols <= 0 || ldx < cols || (block != 32 && block != 64))
+    if (!x || rows <= 0 || cols <= 0 || ldx < cols || (block != 8 && block != 16 && block != 32 && block != 64))
         return -1;
     if ((dtype != ORC_DT_BF16 && dtype != ORC_DT_F32) ||
         (round_mode != ORC_ROUND_SR && round_mode != ORC_ROUND_RNE))
         return -1;
-    if (ld < cols_pad / 2 || ld_t < rows_pad / 2 || ld_s < (cols + block - 1) / block)
+    if (ld < cols_pad / 2 || ld_t < rows_pad / 2 || ld_s < (cols_pad + block - 1) / block)
         return -1;
-    for (br = 0; br * block < rows; br++) {
-        for (bc = 0; bc * block < cols; bc++) {
+    for (br = 0; br * block < rows_pad; br++) {
+        for (bc = 0; bc * block < cols_pad; bc++) {
             double M = 0.0;
             int k;
             for (i = block * br; i < block * br + block && i < rows; i++) {

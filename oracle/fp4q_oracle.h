@@ -81,9 +81,10 @@ int orc_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
                 uint8_t* scales, int64_t ld_s,
                 int64_t tile_row_begin, int64_t tile_row_end);
 
-/* Square b x b blocks, b in {32, 64}: as orc_quant2d with the block side as a
- * parameter (same per-element random fields).  scales [ceil(rows/b) x ld_s],
- * ld_s >= ceil(cols/b); code planes as orc_quant2d. */
+/* Square b x b blocks, b in {8, 16, 32, 64}: as orc_quant2d with the block
+ * side as a parameter (same per-element random fields).  With R, C = rows,
+ * cols rounded up to 32: scales [ceil(R/b) x ld_s], ld_s >= ceil(C/b); blocks
+ * wholly in the padding get byte 0; code planes as orc_quant2d. */
 int orc_quant2d_block(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                       int round_mode, uint64_t seed, uint32_t stream, int block,
                       uint8_t* codes, int64_t ld, uint8_t* codes_t, int64_t ld_t,

@@ -200,3 +200,24 @@ def test_mxfp8_ragged_and_bounds(orc):
     S = 2.0 ** (np.repeat(scales.astype(np.float64), 32, axis=1)[:, :70] - 127)
     assert np.all(np.abs(x) / S <= 448)
     assert np.all(np.abs(deq - x) <= np.abs(x) * 2 ** -4 + S * 2 ** -9)
+
+
+def test_mxfp8_dequant_exact_against_torch_decode(orc):
+    """Sec. 2.1 X ~ P * S for MXFP8: every dequantized element equals, exactly,
+    torch's float8_e4m3fn decode of its byte times 2^(scale byte - 127), over
+    every finite E4M3 byte and scale bytes across the whole E8M0 range that
+    keeps the product a normal fp64 (all 254 finite scale bytes)."""
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]                     # drop the two NaN bytes
+    rows = 254
+    cols = 32 * ((len(codes) + 31) // 32)
+    c = np.zeros((rows, cols), dtype=np.uint8)
+    c[:, :len(codes)] = codes
+    for r in range(rows):                                      # vary the byte per row and group
+        c[r] = np.roll(c[r], 5 * r)
+    scales = np.tile(np.arange(254, dtype=np.uint8)[:, None], (1, cols // 32))
+    scales = (scales + np.arange(cols // 32, dtype=np.uint8)[None, :] * 37) % 254
+    deq = orc.dequant_mxfp8(c, scales.astype(np.uint8), rows, cols)
+    dec = torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = dec * np.ldexp(1.0, np.repeat(scales.astype(np.int64), 32, axis=1) - 127)
+    assert np.array_equal(deq, ref)

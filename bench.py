@@ -40,6 +40,8 @@ def parse():
                    help="time the step as eager launches instead of replays of a captured HIP graph")
     p.add_argument("--no-side-paths", action="store_true",
                    help="skip the 1B, MoE and attention measurements reported beside the 7B step")
+    p.add_argument("--side", default="",
+                   help="comma-separated side paths to run (default: all of them)")
     p.add_argument("--cpu-budget-s", type=float, default=20.0,
                    help="approximate CPU seconds for the oracle sample")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -50,31 +52,86 @@ def parse():
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_7b_step_pmc.md")
+# The sources each measured kernel is built from: a change to any of them
+# invalidates the committed counter readings.
+KERNEL_SOURCES = {"gemm": ["fp4q_launch.hpp", "gemm_kernel.hpp", "gemm_plain.hip"],
+                  "quant2d": ["fp4q_launch.hpp", "fp4q_device.hpp", "fp4q_cvt.hpp", "quant2d.hip"]}
 
 
-def source_sha256(name):
+def source_sha256(kernel):
     import hashlib
-    path = os.path.join(ROOT, "fp4_microscaling_quantization_quant2d_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "fp4_microscaling_quantization_quant2d_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def measured_traffic(kernel_source):
-    """HBM bytes per launch of the kernel built from kernel_source, from the
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` ("gemm" or "quant2d"), from the
     committed counter summary, or None when there is none or the kernel's
-    source has changed since the counters were taken."""
+    sources have changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     sha, val = None, None
     for line in open(TRAFFIC_SUMMARY):
         f = line.split()
-        if len(f) == 3 and f[0] == "source-sha256" and f[1] == kernel_source:
+        if len(f) == 3 and f[0] == "source-sha256" and f[1] == kernel:
             sha = f[2]
-        if len(f) == 3 and f[0] == "traffic-bytes-per-launch" and f[1] == kernel_source:
+        if len(f) == 3 and f[0] == "traffic-bytes-per-launch" and f[1] == kernel:
             val = float(f[2])
-    if sha is None or val is None or sha != source_sha256(kernel_source):
+    if sha is None or val is None or sha != source_sha256(kernel):
         return None
     return val
+
+
+def measured_peaks(torch, fq, step=None, reps=5):
+    """The chip's practical ceilings, measured in this process (medians of
+    `reps` timed runs):
+    - HBM: a streaming 2 GiB device-to-device copy with 16-byte accesses
+      (fp4q_probe_copy; read + written bytes over time), and torch's copy_
+      beside it;
+    - matrix cores: a sustained loop of the FP4 block-scaled MFMA
+      (fp4q_probe_mfma_fp4: 2 workgroups of 4 waves per compute unit, 8
+      independent accumulators per wave) on hashed operand words and, when a
+      step is given, on the step's own quantized codes (the matrix cores'
+      rate depends on the codes)."""
+    def timed(fn):
+        fn()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            work = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) / 1e3)
+        return work / float(np.median(t))
+
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    copy_gbps = timed(lambda: fq.fp4q_probe_copy(src, dst)) / 1e9
+    torch_gbps = timed(lambda: (dst.copy_(src), 2.0 * n)[1]) / 1e9
+    del src, dst
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg, iters = 2 * cus, 20000
+    sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    out = {"hbm_copy_GB/s": round(copy_gbps, 1), "torch_copy_GB/s": round(torch_gbps, 1),
+           "fp4_mfma_loop_hashed_TFLOP/s": round(timed(lambda: fq.fp4q_probe_mfma_fp4(iters, wg, sink)) / 1e12, 1)}
+    if step is not None:
+        planes = torch.cat([step.layers[0][k].codes.reshape(-1) for k in ("qX", "qW", "qdY")])
+        out["fp4_mfma_loop_TFLOP/s"] = round(timed(lambda: fq.fp4q_probe_mfma_fp4(iters, wg, sink, planes)) / 1e12, 1)
+        del planes
+    else:
+        out["fp4_mfma_loop_TFLOP/s"] = out["fp4_mfma_loop_hashed_TFLOP/s"]
+    out["compute_units"] = cus
+    out["how"] = ("median of %d: streaming 2 GiB device copy (fp4q_probe_copy, 16-byte accesses; 2 x bytes / time) "
+                  "and torch copy_; sustained v_mfma_scale_f32_32x32x64_f8f6f4 FP4 loop, %d workgroups x 4 waves x "
+                  "8 x %d MFMAs, on hashed words and on the first layer's quantized X, W and dY codes"
+                  % (reps, wg, iters))
+    torch.cuda.empty_cache()
+    return out
 
 
 def quant_bytes(rows, cols):
@@ -320,6 +377,59 @@ def side_bf16_out(torch, fq, wl, iters, warmup):
     return out
 
 
+def side_fused_chain(torch, fq, wl, iters, warmup):
+    """A chain of two 7B FFN projections (up 4096->11008, then down
+    11008->4096, 8192 tokens, no activation between them), one training step,
+    unfused and fused.  Unfused: the up projection's fwd writes fp32 Y and a
+    quantizer reads it back as the down projection's input, and the down
+    projection's dgrad writes fp32 dX that a quantizer turns into the up
+    projection's output gradient.  Fused: those two GEMMs quantize their
+    result in the epilogue (fp4q_gemm_quant).  Same planes, same products."""
+    up, down = wl.layer_7b(2), wl.layer_7b(3)
+    T, H, F = up.T, up.K, up.N
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    X, Wu, Wd, dYd = bf(up.X), bf(up.W), bf(down.W), bf(down.dY)
+    q = {"X": fq.alloc_fp4(T, H), "Wu": fq.alloc_fp4(F, H), "A": fq.alloc_fp4(T, F), "Wd": fq.alloc_fp4(H, F),
+         "dYd": fq.alloc_fp4(T, H), "dYu": fq.alloc_fp4(T, F)}
+    Yu = torch.empty((T, F), device="cuda")
+    Yd = torch.empty((T, H), device="cuda")
+    dXd = torch.empty((T, F), device="cuda")
+    dXu = torch.empty((T, H), device="cuda")
+    dWd = torch.empty((H, F), device="cuda")
+    dWu = torch.empty((F, H), device="cuda")
+    common_head = [("quant:X+Wu", lambda: fq.fp4q_quant2d_batch([(X, q["X"], 1), (Wu, q["Wu"], 2)])),
+                   ("quant:Wd", lambda: fq.fp4q_quant2d(Wd, q["Wd"], stream_id=5))]
+    tail_fwd = [("down:fwd", lambda: fq.fp4q_gemm("fwd", q["A"], q["Wd"], Yd)),
+                ("quant:dYd", lambda: fq.fp4q_quant2d(dYd, q["dYd"], stream_id=6))]
+    tail_bwd = [("down:wgrad", lambda: fq.fp4q_gemm("wgrad", q["dYd"], q["A"], dWd)),
+                ("up:dgrad", lambda: fq.fp4q_gemm("dgrad", q["dYu"], q["Wu"], dXu)),
+                ("up:wgrad", lambda: fq.fp4q_gemm("wgrad", q["dYu"], q["X"], dWu))]
+    unfused = (common_head
+               + [("up:fwd", lambda: fq.fp4q_gemm("fwd", q["X"], q["Wu"], Yu)),
+                  ("quant:A", lambda: fq.fp4q_quant2d(Yu, q["A"], stream_id=4))]
+               + tail_fwd
+               + [("down:dgrad", lambda: fq.fp4q_gemm("dgrad", q["dYd"], q["Wd"], dXd)),
+                  ("quant:dYu", lambda: fq.fp4q_quant2d(dXd, q["dYu"], stream_id=7))]
+               + tail_bwd)
+    fused = (common_head
+             + [("up:fwd+quant:A", lambda: fq.fp4q_gemm_quant("fwd", q["X"], q["Wu"], out=q["A"], stream_id=4))]
+             + tail_fwd
+             + [("down:dgrad+quant:dYu",
+                 lambda: fq.fp4q_gemm_quant("dgrad", q["dYd"], q["Wd"], out=q["dYu"], stream_id=7))]
+             + tail_bwd)
+    mu = _timed_launches(torch, unfused, iters, warmup)
+    mf = _timed_launches(torch, fused, iters, warmup)
+    out = {"workload": "7b FFN chain: up 4096->11008 then down 11008->4096 at 8192 tokens, one training step "
+                       "(6 GEMMs), unfused (fp32 Y / dX written, then quantized) and fused (quantize-in-epilogue); "
+                       "eager, per-launch events",
+           "unfused_ms": round(sum(mu.values()), 4), "fused_ms": round(sum(mf.values()), 4),
+           "unfused_pair_ms": {"up:fwd+quant:A": round(mu["up:fwd"] + mu["quant:A"], 4),
+                               "down:dgrad+quant:dYu": round(mu["down:dgrad"] + mu["quant:dYu"], 4)},
+           "fused_pair_ms": {k: round(mf[k], 4) for k in ("up:fwd+quant:A", "down:dgrad+quant:dYu")}}
+    out["fused_over_unfused"] = round(out["fused_ms"] / out["unfused_ms"], 4)
+    return out
+
+
 def side_moe(torch, fq, wl, iters, warmup):
     """One step of the 30B-class MoE expert layer: per-expert 2D quantization
     (one call over the gathered, 32-aligned expert segments) and grouped
@@ -457,58 +567,84 @@ def side_attn(torch, fq, wl, iters, warmup):
     return out
 
 
-def cpu_baseline(layers, budget_s):
-    """The CPU oracle, single-threaded, on a bounded sample of the same step:
-    quant2d of one 32-row band of every quantized tensor, and for every GEMM a
-    32 x 32 block of outputs computed in fp64 over the full contraction from
-    the oracle's own quantization of the bands it needs.  The step time is
-    extrapolated from the measured rates."""
+def host_threads():
+    """Host threads for the oracle: the machine's CPU share (OMP_NUM_THREADS when
+    set) and never more than the cores the process sees."""
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
+def cpu_baseline(layers, budget_s, threads=None):
+    """The CPU oracle on a bounded sample of the same step, run on `threads`
+    host threads (one oracle call per thread at a time): quant2d of 32-row
+    bands of every quantized tensor, then for every GEMM a 32 x 32 block of
+    outputs computed in fp64 over the full contraction from the oracle's own
+    quantization of the bands it needs.  Each phase is timed by wall clock
+    over all threads; the step time is extrapolated from the two rates."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle as orc
+    threads = threads or host_threads()
     rng = np.random.default_rng(0)
     tq = eq = 0.0
     tg = fg = 0.0
     total_elts = sum(L.X.size + L.W.size + L.dY.size for L in layers)
     total_flops = sum(3 * 2.0 * L.T * L.N * L.K for L in layers)
 
-    def band(a, r0):
-        a = np.ascontiguousarray(a[r0:r0 + 32])
-        t0 = time.perf_counter()
+    def band(a):
+        a = np.ascontiguousarray(a)
         c, _, s = orc.quant2d(a, seed=0, stream=1, threads=1)
-        d = orc.dequant_fp4(c, s, 32, a.shape[1])
-        return d, time.perf_counter() - t0
+        return orc.dequant_fp4(c, s, a.shape[0], a.shape[1])
+
+    def quant_task(job):
+        L, rt, rn, rk = job
+        x_b = band(L.X[rt:rt + 32])                 # X rows  [32 x K]
+        w_b = band(L.W[rn:rn + 32])                 # W rows  [32 x K]
+        dy_b = band(L.dY[rt:rt + 32])               # dY rows [32 x N]
+        wt_b = band(L.W[:, rk:rk + 32].T)           # W^T rows = W cols [32 x N]
+        dyt_b = band(L.dY[:, rn:rn + 32].T)         # dY^T rows [32 x T]
+        xt_b = band(L.X[:, rk:rk + 32].T)           # X^T rows [32 x T]
+        return (x_b, w_b, dy_b, wt_b, dyt_b, xt_b), 32 * (2 * L.K + 2 * L.N + 2 * L.T)
+
+    def gemm_task(bands):
+        x_b, w_b, dy_b, wt_b, dyt_b, xt_b = bands
+        f = 0.0
+        for op, a, b in (("fwd", x_b, w_b), ("dgrad", dy_b, np.ascontiguousarray(wt_b.T)),
+                         ("wgrad", np.ascontiguousarray(dyt_b.T), np.ascontiguousarray(xt_b.T))):
+            orc.gemm(op, a, b)
+            kk = a.shape[0] if op == "wgrad" else a.shape[1]
+            f += 2.0 * 32 * 32 * kk
+        return f
 
     deadline = time.perf_counter() + budget_s
     rounds = 0
-    while rounds == 0 or time.perf_counter() < deadline:
-        for L in layers:
-            T, K, N = L.T, L.K, L.N
-            rt, rn, rk = (int(rng.integers(0, v // 32)) * 32 for v in (T, N, K))
-            x_b, t1 = band(L.X, rt)                 # X rows  [32 x K]
-            w_b, t2 = band(L.W, rn)                 # W rows  [32 x K]
-            dy_b, t3 = band(L.dY, rt)               # dY rows [32 x N]
-            wt_b, t4 = band(L.W[:, rk:rk + 32].T, 0)     # W^T rows = W cols [32 x N]
-            dyt_b, t5 = band(L.dY[:, rn:rn + 32].T, 0)   # dY^T rows [32 x T]
-            xt_b, t6 = band(L.X[:, rk:rk + 32].T, 0)     # X^T rows [32 x T]
-            tq += t1 + t2 + t3 + t4 + t5 + t6
-            eq += 32 * (2 * K + N + N + T + T)
-            for op, a, b in (("fwd", x_b, w_b), ("dgrad", dy_b, np.ascontiguousarray(wt_b.T)),
-                             ("wgrad", np.ascontiguousarray(dyt_b.T), np.ascontiguousarray(xt_b.T))):
-                t0 = time.perf_counter()
-                orc.gemm(op, a, b)
-                tg += time.perf_counter() - t0
-                kk = a.shape[0] if op == "wgrad" else a.shape[1]
-                fg += 2.0 * 32 * 32 * kk
-        rounds += 1
+    with ThreadPoolExecutor(threads) as pool:
+        while rounds == 0 or time.perf_counter() < deadline:
+            jobs = []
+            for _ in range(max(1, threads // len(layers))):
+                for L in layers:
+                    jobs.append((L,) + tuple(int(rng.integers(0, v // 32)) * 32 for v in (L.T, L.N, L.K)))
+            t0 = time.perf_counter()
+            res = list(pool.map(quant_task, jobs))
+            tq += time.perf_counter() - t0
+            eq += sum(n for _, n in res)
+            t0 = time.perf_counter()
+            fg += sum(pool.map(gemm_task, [b for b, _ in res]))
+            tg += time.perf_counter() - t0
+            rounds += 1
     t_step = tq * total_elts / eq + tg * total_flops / fg
     return {
         "value": total_flops / t_step / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": ("%d rounds over the 4 layers: quant2d of 32-row bands (%.1f M elements, %.2f s) "
-                   "and 32x32 fp64 GEMM output blocks over the full K (%.2f GFLOP, %.2f s); "
-                   "step time extrapolated to %.0f s (quant %.2f M elt/s, GEMM %.3f GFLOP/s)"
-                   % (rounds, eq / 1e6, tq, fg / 1e9, tg, t_step, eq / tq / 1e6, fg / tg / 1e9)),
+        "sample": ("%d rounds over the %d layers on %d host threads: quant2d of 32-row bands (%.1f M "
+                   "elements, %.2f s wall) and 32x32 fp64 GEMM output blocks over the full K (%.2f GFLOP, "
+                   "%.2f s wall); step time extrapolated to %.0f s (quant %.2f M elt/s, GEMM %.3f GFLOP/s)"
+                   % (rounds, len(layers), threads, eq / 1e6, tq, fg / 1e9, tg, t_step, eq / tq / 1e6, fg / tg / 1e9)),
     }
 
 
@@ -538,6 +674,8 @@ def main():
     for w in range(args.warmup):
         step.run(seed=w)
     torch.cuda.synchronize()
+    print("[bench] measuring the copy and MFMA-loop peaks", file=sys.stderr, flush=True)
+    peaks = measured_peaks(torch, fq, step)
 
     n = len(step.launches)
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -654,23 +792,31 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_dense_kernel (MXFP4; fwd, dgrad, wgrad)",
                      "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("gemm.hip"),
+                     "measured_peak": peaks["fp4_mfma_loop_TFLOP/s"],
+                     "frac_measured": round(gemm_tflops / peaks["fp4_mfma_loop_TFLOP/s"], 4),
+                     "traffic": measured_traffic("gemm"),
                      "algorithmic_flops_per_launch": g_flops / n_g,
                      "avg_launch_us": round(g_ms / n_g * 1e3, 2),
                      "algorithmic_bytes_per_launch": step.gemm_bytes / n_g},
         "roofline_quant": {"bound": "hbm", "kernel": "quant2d_kernel (bf16 in, SR)",
                            "achieved": round(quant_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": round(quant_gbps / HBM_PEAK_GBPS, 4),
-                           "traffic": measured_traffic("quant2d.hip"),
+                           "measured_peak": peaks["hbm_copy_GB/s"],
+                           "frac_measured": round(quant_gbps / peaks["hbm_copy_GB/s"], 4),
+                           "traffic": measured_traffic("quant2d"),
                            "algorithmic_bytes_per_launch": q_bytes / n_q,
                            "avg_launch_us": round(q_ms / n_q * 1e3, 2)},
+        "measured_peaks": peaks,
         "gemm_by_op": gemm_ops,
         "per_launch_median": detail,
     }
     if not args.no_side_paths:
         side = {}
-        for name, fn in (("1b", side_1b), ("moe", side_moe), ("attn", side_attn), ("block64", side_block64),
+        for name, fn in (("1b", side_1b), ("fused_chain", side_fused_chain), ("moe", side_moe), ("attn", side_attn),
+                         ("block64", side_block64),
                          ("act1d", side_act1d), ("wgrad_acc", side_wgrad_acc), ("bf16_out", side_bf16_out)):
+            if args.side and name not in args.side.split(","):
+                continue
             print("[bench] side path %s" % name, file=sys.stderr, flush=True)
             side[name] = fn(torch, fq, wl, iters=5, warmup=2)
             torch.cuda.empty_cache()

@@ -19,13 +19,15 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["QTensor", "fp4q_quant2d", "fp4q_quant1d_mxfp8", "fp4q_gemm", "fp4q_dequant",
+__all__ = ["QTensor", "fp4q_quant2d", "fp4q_quant2d_batch", "fp4q_quant1d_mxfp8", "fp4q_gemm",
+           "fp4q_gemm_quant", "fp4q_dequant",
            "fp4q_quant2d_sizes", "alloc_fp4", "alloc_mxfp8", "library_path", "Fp4qError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp4q.so")
 
-FMT_FP4_2D32, FMT_MXFP8_1D32, FMT_FP4_2D64, FMT_FP4_1D32 = 1, 2, 3, 4
+FMT_FP4_2D32, FMT_MXFP8_1D32, FMT_FP4_2D64, FMT_FP4_1D32, FMT_FP4_2D16, FMT_FP4_2D8 = 1, 2, 3, 4, 5, 6
+_SQUARE_FMT = {32: FMT_FP4_2D32, 64: FMT_FP4_2D64, 16: FMT_FP4_2D16, 8: FMT_FP4_2D8}
 DT_BF16, DT_F32 = 1, 2
 ROUND = {"sr": 0, "rne": 1}
 OPS = {"fwd": 0, "dgrad": 1, "wgrad": 2}
@@ -88,14 +90,22 @@ def _load():
                                ctypes.c_uint32, ctypes.POINTER(_QDesc), P]
     L.fp4q_quant2d_batch.argtypes = [ctypes.c_int, ctypes.POINTER(_QItem), ctypes.c_int, ctypes.c_int,
                                      ctypes.c_uint64, P]
+    L.fp4q_quant2d_batch_ex.argtypes = [ctypes.c_int, ctypes.POINTER(_QItem), ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_uint64, P, P]
     L.fp4q_quant1d_mxfp8.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.POINTER(_QDesc), P]
     L.fp4q_gemm_ex.argtypes = [ctypes.c_int, ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc), P, I64,
                                I64, ctypes.POINTER(_Groups), ctypes.c_int, P]
     L.fp4q_gemm.argtypes = [ctypes.c_int, ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc), P, I64,
                             I64, ctypes.POINTER(_Groups), P]
+    L.fp4q_gemm_quant.argtypes = [ctypes.c_int, ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc),
+                                  ctypes.POINTER(_QDesc), ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32, P, P]
     L.fp4q_dequant.argtypes = [ctypes.POINTER(_QDesc), ctypes.c_int, ctypes.c_int, P, I64, P]
-    for fn in ("fp4q_quant2d_sizes", "fp4q_quant2d", "fp4q_quant2d_batch", "fp4q_quant1d_mxfp8",
-               "fp4q_gemm", "fp4q_gemm_ex", "fp4q_dequant"):
+    L.fp4q_probe_mfma_fp4.argtypes = [I64, ctypes.c_int, P, P, I64, P]
+    L.fp4q_probe_copy.argtypes = [P, P, I64, ctypes.c_int, P]
+    for fn in ("fp4q_quant2d_sizes", "fp4q_quant2d", "fp4q_quant2d_batch", "fp4q_quant2d_batch_ex",
+               "fp4q_quant1d_mxfp8",
+               "fp4q_gemm", "fp4q_gemm_ex", "fp4q_gemm_quant", "fp4q_dequant", "fp4q_probe_mfma_fp4",
+               "fp4q_probe_copy"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -181,10 +191,11 @@ def fp4q_quant2d_sizes(rows, cols):
 
 def alloc_fp4(rows, cols, device="cuda", transposed=True, block=32):
     """Output buffers for fp4q_quant2d with the tightest leading dimensions;
-    block 32 or 64 picks the square scale block (FMT_FP4_2D32 / FMT_FP4_2D64),
-    block "1d" the activation layout (FMT_FP4_1D32)."""
-    if block not in (32, 64, "1d"):
-        raise Fp4qError("block must be 32, 64 or '1d', got %r" % (block,))
+    block 32, 64, 16 or 8 picks the square scale block (FMT_FP4_2D32,
+    FMT_FP4_2D64, FMT_FP4_2D16, FMT_FP4_2D8), block "1d" the activation
+    layout (FMT_FP4_1D32)."""
+    if block not in (32, 64, 16, 8, "1d"):
+        raise Fp4qError("block must be 32, 64, 16, 8 or '1d', got %r" % (block,))
     R, C = _pad32(rows), _pad32(cols)
     codes = torch.empty((R, C // 2), dtype=torch.uint8, device=device)
     codes_t = torch.empty((C, R // 2), dtype=torch.uint8, device=device) if transposed else None
@@ -194,8 +205,9 @@ def alloc_fp4(rows, cols, device="cuda", transposed=True, block=32):
         scales = torch.empty((g(R), 512 * g(C)), dtype=torch.uint8, device=device)
         scales_t = torch.empty((g(C), 512 * g(R)), dtype=torch.uint8, device=device) if transposed else None
         return QTensor(FMT_FP4_1D32, rows, cols, codes, scales, codes_t, scales_t=scales_t)
-    scales = torch.empty((-(-rows // block), -(-cols // block)), dtype=torch.uint8, device=device)
-    return QTensor(FMT_FP4_2D32 if block == 32 else FMT_FP4_2D64, rows, cols, codes, scales, codes_t)
+    # the grid covers the 32-padded planes
+    scales = torch.empty((-(-R // block), -(-C // block)), dtype=torch.uint8, device=device)
+    return QTensor(_SQUARE_FMT[block], rows, cols, codes, scales, codes_t)
 
 
 def alloc_mxfp8(rows, cols, device="cuda"):
@@ -219,12 +231,16 @@ def _check_matrix(x):
 
 
 def fp4q_quant2d(x, out: Optional[QTensor] = None, round_mode="sr", seed=0, stream_id=0,
-                 stream=None, transposed=True):
-    """2D 32x32-block FP4 quantization of x (bf16/fp32, rows x cols)."""
+                 stream=None, transposed=True, seed_dev=None):
+    """2D 32x32-block FP4 quantization of x (bf16/fp32, rows x cols).
+    seed_dev: see fp4q_quant2d_batch."""
     _check_matrix(x)
     rows, cols = x.shape
     if out is None:
         out = alloc_fp4(rows, cols, x.device, transposed)
+    if seed_dev is not None:
+        return fp4q_quant2d_batch([(x, out, stream_id)], round_mode=round_mode, seed=seed, stream=stream,
+                                  seed_dev=seed_dev)[0]
     d = out.desc()
     _check(_load().fp4q_quant2d(_ptr(x), _dtype_code(x), rows, cols, x.stride(0),
                                 ROUND[round_mode], int(seed) & ((1 << 64) - 1),
@@ -233,10 +249,21 @@ def fp4q_quant2d(x, out: Optional[QTensor] = None, round_mode="sr", seed=0, stre
     return out
 
 
-def fp4q_quant2d_batch(items, round_mode="sr", seed=0, stream=None):
+def _seed_dev_ptr(seed_dev):
+    if seed_dev is None:
+        return None
+    if (not isinstance(seed_dev, torch.Tensor) or not seed_dev.is_cuda or seed_dev.numel() < 1
+            or seed_dev.dtype not in (torch.int64, torch.uint64)):
+        raise Fp4qError("seed_dev must be an int64 or uint64 CUDA tensor")
+    return _ptr(seed_dev)
+
+
+def fp4q_quant2d_batch(items, round_mode="sr", seed=0, stream=None, seed_dev=None):
     """Several fp4q_quant2d calls in one launch.  items: (x, out, stream_id)
     triples (out a QTensor from alloc_fp4, or None to allocate one), all x of
-    one dtype; returns the outputs in order."""
+    one dtype; returns the outputs in order.  seed_dev: an int64 CUDA tensor
+    whose first element the kernel adds to the Philox key when it runs
+    (fp4q_quant2d_batch_ex; for captured graphs)."""
     items = list(items)
     if not 1 <= len(items) <= QUANT2D_BATCH_MAX:
         raise Fp4qError("fp4q_quant2d_batch takes 1..%d items, got %d" % (QUANT2D_BATCH_MAX, len(items)))
@@ -259,6 +286,11 @@ def fp4q_quant2d_batch(items, round_mode="sr", seed=0, stream=None):
         arr[k].rows, arr[k].cols, arr[k].ldx = rows, cols, x.stride(0)
         arr[k].stream_id = int(stream_id) & 0xFFFFFFFF
         arr[k].out = ctypes.pointer(d)
+    if seed_dev is not None:
+        _check(_load().fp4q_quant2d_batch_ex(len(items), arr, dtype, ROUND[round_mode],
+                                             int(seed) & ((1 << 64) - 1), _seed_dev_ptr(seed_dev),
+                                             _stream_ptr(stream)), "fp4q_quant2d_batch_ex")
+        return outs
     _check(_load().fp4q_quant2d_batch(len(items), arr, dtype, ROUND[round_mode],
                                       int(seed) & ((1 << 64) - 1), _stream_ptr(stream)),
            "fp4q_quant2d_batch")
@@ -275,6 +307,23 @@ def fp4q_quant1d_mxfp8(x, out: Optional[QTensor] = None, stream=None):
     _check(_load().fp4q_quant1d_mxfp8(_ptr(x), _dtype_code(x), rows, cols, x.stride(0),
                                       ctypes.byref(d), _stream_ptr(stream)), "fp4q_quant1d_mxfp8")
     return out
+
+
+def _check_out(c, shape, device, what):
+    """A caller's output tensor must be a float32 or bfloat16 tensor on the
+    operands' device whose shape is the product's and whose rows are
+    contiguous: the C ABI sees only a pointer and a leading dimension, so
+    anything else would be written out of bounds."""
+    if not isinstance(c, torch.Tensor):
+        raise Fp4qError("%s must be a torch tensor" % what)
+    if c.dtype not in (torch.float32, torch.bfloat16):
+        raise Fp4qError("%s must be float32 or bfloat16, got %s" % (what, c.dtype))
+    if tuple(c.shape) != tuple(shape):
+        raise Fp4qError("%s has shape %s, the product needs %s" % (what, tuple(c.shape), tuple(shape)))
+    if c.stride(-1) != 1 or (c.dim() == 3 and c.stride(0) < c.shape[1] * c.stride(1)):
+        raise Fp4qError("%s must have contiguous rows and non-overlapping batch items" % what)
+    if not c.is_cuda or c.device != torch.device(device):
+        raise Fp4qError("%s must live on %s, got %s" % (what, device, c.device))
 
 
 def gemm_out_shape(op, a: QTensor, b: QTensor, groups: Optional[Sequence[int]] = None):
@@ -305,11 +354,10 @@ def fp4q_gemm(op, a: QTensor, b: QTensor, c: Optional[torch.Tensor] = None,
     M, N = gemm_out_shape(opc, a, b, groups)
     if accumulate and c is None:
         raise Fp4qError("accumulate needs the C to add to")
+    shape = (a.batch, M, N) if a.batch > 1 else (M, N)
     if c is None:
-        shape = (a.batch, M, N) if a.batch > 1 else (M, N)
         c = torch.empty(shape, dtype=out_dtype, device=a.codes.device)
-    if c.dtype not in (torch.float32, torch.bfloat16) or c.stride(-1) != 1:
-        raise Fp4qError("C must be a row-major float32 or bfloat16 tensor")
+    _check_out(c, shape, a.codes.device, "C")
     flags = (GEMM_ACCUMULATE if accumulate else 0) | (GEMM_OUT_BF16 if c.dtype == torch.bfloat16 else 0)
     ldc = c.stride(-2)
     cbs = c.stride(0) if c.dim() == 3 else 0
@@ -335,13 +383,62 @@ def fp4q_gemm(op, a: QTensor, b: QTensor, c: Optional[torch.Tensor] = None,
     return c
 
 
+def fp4q_gemm_quant(op, a: QTensor, b: QTensor, out: Optional[QTensor] = None, round_mode="sr", seed=0,
+                    stream_id=0, seed_dev=None, transposed=True, stream=None):
+    """The product of fp4q_gemm (fwd / dgrad / wgrad), quantized in the GEMM's
+    epilogue into 2D 32x32 FP4 planes instead of written as fp32: bit for bit
+    fp4q_quant2d(fp4q_gemm(op, a, b), round_mode, seed, stream_id).  Returns
+    the QTensor (allocated unless `out` is given; transposed=False skips the
+    transposed plane)."""
+    opc = OPS.get(op, op)
+    M, N = gemm_out_shape(opc, a, b)
+    if out is None:
+        out = alloc_fp4(M, N, a.codes.device, transposed)
+    da, db, do = a.desc(), b.desc(), out.desc()
+    _check(_load().fp4q_gemm_quant(opc, ctypes.byref(da), ctypes.byref(db), ctypes.byref(do),
+                                   ROUND[round_mode], int(seed) & ((1 << 64) - 1), int(stream_id) & 0xFFFFFFFF,
+                                   _seed_dev_ptr(seed_dev), _stream_ptr(stream)), "fp4q_gemm_quant")
+    return out
+
+
 def fp4q_dequant(q: QTensor, transposed=False, out_dtype=torch.float32, out=None, stream=None):
     """X ~ P * S for the row plane (rows x cols) or the transposed plane."""
     shape = (q.cols, q.rows) if transposed else (q.rows, q.cols)
     if out is None:
         out = torch.empty(shape, dtype=out_dtype, device=q.codes.device)
+    _check_out(out, shape, q.codes.device, "out")
     code = DT_F32 if out.dtype == torch.float32 else DT_BF16
     d = q.desc()
     _check(_load().fp4q_dequant(ctypes.byref(d), 1 if transposed else 0, code, _ptr(out),
                                 out.stride(0), _stream_ptr(stream)), "fp4q_dequant")
     return out
+
+
+def fp4q_probe_mfma_fp4(iters, workgroups, sink, codes=None, stream=None):
+    """Diagnostic: the sustained FP4 MFMA loop (8 * iters 32x32x64 MFMAs per
+    wave, 4 waves per workgroup) on hashed operand words, or on the words of
+    `codes` (a uint8 CUDA code plane); sink is a float32 CUDA tensor of at
+    least workgroups*256 elements.  Returns the flops enqueued."""
+    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < workgroups * 256:
+        raise Fp4qError("sink must be a float32 CUDA tensor of workgroups*256 elements")
+    if codes is not None and (codes.dtype != torch.uint8 or not codes.is_cuda or not codes.is_contiguous()):
+        raise Fp4qError("codes must be a contiguous uint8 CUDA tensor")
+    _check(_load().fp4q_probe_mfma_fp4(int(iters), int(workgroups), _ptr(sink), _ptr(codes),
+                                       0 if codes is None else codes.numel(), _stream_ptr(stream)),
+           "fp4q_probe_mfma_fp4")
+    return float(workgroups) * 4 * 8 * iters * 2.0 * 32 * 32 * 64
+
+
+def fp4q_probe_copy(src, dst, workgroups=None, stream=None):
+    """Diagnostic: streaming device copy src -> dst (contiguous CUDA tensors
+    of equal byte size, a multiple of 16).  Returns the bytes moved (read +
+    written)."""
+    n = src.numel() * src.element_size()
+    if (not src.is_cuda or not dst.is_cuda or not src.is_contiguous() or not dst.is_contiguous()
+            or dst.numel() * dst.element_size() != n):
+        raise Fp4qError("src and dst must be contiguous CUDA tensors of one byte size")
+    if workgroups is None:
+        workgroups = 8 * torch.cuda.get_device_properties(src.device).multi_processor_count
+    _check(_load().fp4q_probe_copy(_ptr(src), _ptr(dst), n, int(workgroups), _stream_ptr(stream)),
+           "fp4q_probe_copy")
+    return 2.0 * n

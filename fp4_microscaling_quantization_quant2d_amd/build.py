@@ -12,7 +12,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp4q.so")
-SOURCES = ["api.hip", "quant2d.hip", "gemm.hip", "mxfp8.hip", "dequant.hip"]
+SOURCES = ["gemm_plain.hip", "gemm_grouped.hip", "gemm_bf16.hip", "gemm_acc.hip", "gemm_1d.hip", "gemm_quant.hip",
+           "gemm_sub16.hip", "gemm_sub8.hip", "gemm.hip",
+           "api.hip", "quant2d.hip", "mxfp8.hip", "dequant.hip", "probe.hip"]
 ARCH = os.environ.get("FP4Q_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -32,9 +34,10 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 5) -> str:
+def build(verbose: bool = False, jobs: int = 0) -> str:
     """Compile every kernel for gfx950 and link libfp4q.so; returns its path."""
     os.makedirs(OBJ, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"

@@ -70,11 +70,26 @@ int check_1d_grid(const uint8_t* s, int64_t ld, int64_t width, const char* name,
     return FP4Q_OK;
 }
 
+// Side of a square-block FP4 format's scale blocks (0 for the 1D layout).
+int square_block(int fmt)
+{
+    switch (fmt) {
+    case FP4Q_FMT_FP4_2D32: return 32;
+    case FP4Q_FMT_FP4_2D64: return 64;
+    case FP4Q_FMT_FP4_2D16: return 16;
+    case FP4Q_FMT_FP4_2D8: return 8;
+    default: return 0;
+    }
+}
+
+inline int log2_block(int b) { return b == 64 ? 6 : b == 16 ? 4 : b == 8 ? 3 : 5; }
+
 int check_fp4_tensor(const fp4q_qtensor* t, const char* name, bool need_t)
 {
     if (!t)
         return fail(FP4Q_EINVAL, "%s: null descriptor", name);
-    if (t->fmt != FP4Q_FMT_FP4_2D32 && t->fmt != FP4Q_FMT_FP4_2D64 && t->fmt != FP4Q_FMT_FP4_1D32)
+    if (t->fmt != FP4Q_FMT_FP4_2D32 && t->fmt != FP4Q_FMT_FP4_2D64 && t->fmt != FP4Q_FMT_FP4_1D32 &&
+        t->fmt != FP4Q_FMT_FP4_2D16 && t->fmt != FP4Q_FMT_FP4_2D8)
         return fail(FP4Q_EINVAL, "%s: fmt %d is not an FP4 format", name, t->fmt);
     if (t->rows <= 0 || t->cols <= 0 || t->rows > kMaxDim || t->cols > kMaxDim)
         return fail(FP4Q_EINVAL, "%s: bad shape %lld x %lld", name, (long long)t->rows, (long long)t->cols);
@@ -90,10 +105,10 @@ int check_fp4_tensor(const fp4q_qtensor* t, const char* name, bool need_t)
         if (rc)
             return rc;
     } else {
-        const int64_t blk = t->fmt == FP4Q_FMT_FP4_2D64 ? 64 : 32;
-        if (t->ld_s < (t->cols + blk - 1) / blk)
-            return fail(FP4Q_EINVAL, "%s: ld_s %lld < %lld", name, (long long)t->ld_s,
-                        (long long)((t->cols + blk - 1) / blk));
+        // the grid covers the 32-padded planes: ceil(C / b) columns
+        const int64_t blk = square_block(t->fmt);
+        if (t->ld_s < (C + blk - 1) / blk)
+            return fail(FP4Q_EINVAL, "%s: ld_s %lld < %lld", name, (long long)t->ld_s, (long long)((C + blk - 1) / blk));
     }
     if (need_t || (is1d && t->codes_t)) {
         if (!t->codes_t)
@@ -134,8 +149,10 @@ int check_fp8_tensor(const fp4q_qtensor* t, const char* name)
 
 // Validates every item, then quantizes all of them in one launch.
 int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dtype, int round_mode,
-                   uint64_t seed, void* hip_stream)
+                   uint64_t seed, const uint64_t* seed_dev, void* hip_stream)
 {
+    if (seed_dev && (reinterpret_cast<uintptr_t>(seed_dev) & 7u))
+        return fail(FP4Q_EINVAL, "%s: seed_dev must be 8-byte aligned", fn);
     static_assert(FP4Q_QUANT2D_BATCH_MAX == fp4q::kQuant2dBatchMax, "batch limit");
     if (dtype != FP4Q_DT_BF16 && dtype != FP4Q_DT_F32)
         return fail(FP4Q_EINVAL, "%s: dtype %d", fn, dtype);
@@ -144,6 +161,7 @@ int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dt
     const int esz = dtype == FP4Q_DT_F32 ? 4 : 2;
     fp4q::Quant2dBatch b;
     b.n = n;
+    b.seed_dev = seed_dev;
     b.first[0] = 0;
     bool aligned = true;
     int fmt = 0;
@@ -199,6 +217,8 @@ int quant2d_launch(const char* fn, int n, const fp4q_quant2d_item* items, int dt
     return hip_status(fp4q::launch_quant2d(b, dtype == FP4Q_DT_F32, round_mode == FP4Q_ROUND_RNE, aligned,
                                            fmt == FP4Q_FMT_FP4_1D32   ? fp4q::kLayout1D
                                            : fmt == FP4Q_FMT_FP4_2D64 ? fp4q::kLayout2D64
+                                           : fmt == FP4Q_FMT_FP4_2D16 ? fp4q::kLayout2D16
+                                           : fmt == FP4Q_FMT_FP4_2D8  ? fp4q::kLayout2D8
                                                                       : fp4q::kLayout2D32,
                                            static_cast<hipStream_t>(hip_stream)),
                       fn);
@@ -237,7 +257,7 @@ int fp4q_quant2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
     it.ldx = ldx;
     it.stream_id = stream_id;
     it.out = out;
-    return quant2d_launch("fp4q_quant2d", 1, &it, dtype, round_mode, seed, hip_stream);
+    return quant2d_launch("fp4q_quant2d", 1, &it, dtype, round_mode, seed, nullptr, hip_stream);
 }
 
 int fp4q_quant2d_batch(int n, const fp4q_quant2d_item* items, int dtype, int round_mode, uint64_t seed,
@@ -247,7 +267,17 @@ int fp4q_quant2d_batch(int n, const fp4q_quant2d_item* items, int dtype, int rou
         return fail(FP4Q_EINVAL, "fp4q_quant2d_batch: n %d outside 1..%d", n, FP4Q_QUANT2D_BATCH_MAX);
     if (!items)
         return fail(FP4Q_EINVAL, "fp4q_quant2d_batch: items is null");
-    return quant2d_launch("fp4q_quant2d_batch", n, items, dtype, round_mode, seed, hip_stream);
+    return quant2d_launch("fp4q_quant2d_batch", n, items, dtype, round_mode, seed, nullptr, hip_stream);
+}
+
+int fp4q_quant2d_batch_ex(int n, const fp4q_quant2d_item* items, int dtype, int round_mode, uint64_t seed,
+                          const uint64_t* seed_dev, void* hip_stream)
+{
+    if (n < 1 || n > FP4Q_QUANT2D_BATCH_MAX)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d_batch_ex: n %d outside 1..%d", n, FP4Q_QUANT2D_BATCH_MAX);
+    if (!items)
+        return fail(FP4Q_EINVAL, "fp4q_quant2d_batch_ex: items is null");
+    return quant2d_launch("fp4q_quant2d_batch_ex", n, items, dtype, round_mode, seed, seed_dev, hip_stream);
 }
 
 int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
@@ -289,8 +319,22 @@ int fp4q_gemm(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, float* c, in
     return fp4q_gemm_ex(op, a, b, c, ldc, c_bstride, groups, 0, hip_stream);
 }
 
-int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, int64_t ldc, int64_t c_bstride,
-                 const fp4q_groups* groups, int flags, void* hip_stream)
+}  // extern "C"
+
+namespace {
+
+// The quantized output of fp4q_gemm_quant, validated against the product's
+// shape before anything is launched.
+struct QuantOut {
+    const fp4q_qtensor* out;
+    int round_mode;
+    uint64_t seed;
+    uint32_t stream_id;
+    const uint64_t* seed_dev;
+};
+
+int gemm_common(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, int64_t ldc, int64_t c_bstride,
+                const fp4q_groups* groups, int flags, const QuantOut* qo, void* hip_stream)
 {
     if (op != FP4Q_OP_FWD && op != FP4Q_OP_DGRAD && op != FP4Q_OP_WGRAD)
         return fail(FP4Q_EINVAL, "fp4q_gemm: op %d", op);
@@ -298,7 +342,7 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, 
         return fail(FP4Q_EINVAL, "fp4q_gemm_ex: unknown flags 0x%x", flags);
     const bool accumulate = (flags & FP4Q_GEMM_ACCUMULATE) != 0;
     const bool out_bf16 = (flags & FP4Q_GEMM_OUT_BF16) != 0;
-    if (!a || !b || !c)
+    if (!a || !b || (!c && !qo))
         return fail(FP4Q_EINVAL, "fp4q_gemm: null a, b or c");
     const bool fp8 = a->fmt == FP4Q_FMT_MXFP8_1D32;
     if (fp8 != (b->fmt == FP4Q_FMT_MXFP8_1D32))
@@ -366,8 +410,19 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, 
     }
     g.bs_sa = a->bstride_s;
     g.bs_sb = b->bstride_s;
-    g.sh_a = a->fmt == FP4Q_FMT_FP4_2D64 ? 6 : 5;
-    g.sh_b = b->fmt == FP4Q_FMT_FP4_2D64 ? 6 : 5;
+    g.sh_a = log2_block(square_block(a->fmt));
+    g.sh_b = log2_block(square_block(b->fmt));
+    // 16x16 / 8x8 blocks: both operands take the same block side
+    const int sub_a = fp8 ? 0 : square_block(a->fmt), sub_b = fp8 ? 0 : square_block(b->fmt);
+    const bool subblock = (sub_a > 0 && sub_a < 32) || (sub_b > 0 && sub_b < 32);
+    if (subblock) {
+        if (sub_a != sub_b)
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: 16x16 and 8x8 scale blocks need both operands in the same "
+                                           "block side (got %d and %d)", sub_a, sub_b);
+        if (groups || a->batch != 1 || qo || (flags & FP4Q_GEMM_OUT_BF16))
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: 16x16 and 8x8 scale blocks take dense products with batch 1 "
+                                           "and fp32 C (plain or accumulating)");
+    }
     // 1D-layout operands: the plane read takes its own tiled grid (scales for
     // the row plane, scales_t for the transposed plane).
     int oned = 0;
@@ -411,6 +466,44 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, 
     if (fp8 && (a->cols % 32))
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: MXFP8 K must be a multiple of 32");
 
+    if (qo) {
+        // quantize-in-epilogue: dense FP4 products of square-block operands
+        if (fp8 || groups || a->batch != 1 || oned || flags)
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_quant: dense FP4 products of square-block operands "
+                                           "with batch 1 only");
+        const fp4q_qtensor* o = qo->out;
+        if ((rc = check_fp4_tensor(o, "fp4q_gemm_quant out", false)))
+            return rc;
+        if (o->fmt != FP4Q_FMT_FP4_2D32)
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_quant: out must be FP4Q_FMT_FP4_2D32");
+        if (o->rows != M || o->cols != N || o->batch != 1)
+            return fail(FP4Q_EINVAL, "fp4q_gemm_quant: out is %lld x %lld (batch %lld), the product %lld x %lld",
+                        (long long)o->rows, (long long)o->cols, (long long)o->batch, (long long)M, (long long)N);
+        if (o->codes_t && (o->ld_t < pad32(M) / 2 || o->ld_t % 16 || !aligned16(o->codes_t)))
+            return fail(FP4Q_EINVAL, "fp4q_gemm_quant: transposed plane needs ld_t >= %lld, a multiple of 16, "
+                                     "16-byte alignment", (long long)(pad32(M) / 2));
+        if (qo->round_mode != FP4Q_ROUND_SR && qo->round_mode != FP4Q_ROUND_RNE)
+            return fail(FP4Q_EINVAL, "fp4q_gemm_quant: round_mode %d", qo->round_mode);
+        if (qo->seed_dev && (reinterpret_cast<uintptr_t>(qo->seed_dev) & 7u))
+            return fail(FP4Q_EINVAL, "fp4q_gemm_quant: seed_dev must be 8-byte aligned");
+        if (fp4q::gemm_lds_bytes(1, (int)K) > kMaxLdsBytes)
+            return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_quant: K %lld too large (max %d)", (long long)K, max_k(1));
+        g.q_codes = o->codes;
+        g.q_ld = o->ld;
+        g.q_codes_t = o->codes_t;
+        g.q_ld_t = o->ld_t;
+        g.q_scales = o->scales;
+        g.q_ld_s = o->ld_s;
+        g.q_rows_pad = (int)pad32(M);
+        g.q_cols_pad = (int)pad32(N);
+        g.q_key0 = (uint32_t)qo->seed;
+        g.q_key1 = (uint32_t)(qo->seed >> 32);
+        g.q_stream = qo->stream_id;
+        g.q_rne = qo->round_mode == FP4Q_ROUND_RNE;
+        g.q_seed_dev = qo->seed_dev;
+        return hip_status(fp4q::launch_gemm_quant(g, a_st, b_st, static_cast<hipStream_t>(hip_stream)),
+                          "fp4q_gemm_quant");
+    }
     int grouped_op = -1;
     if (!groups) {
         if (ldc < N)
@@ -502,6 +595,13 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, 
             for (int i = 0; i < g.n_groups; ++i)
                 kmax = std::max<int64_t>(kmax, g.row_off[i + 1] - g.row_off[i]);
     }
+    if (subblock) {
+        if (ldc < N)
+            return fail(FP4Q_EINVAL, "fp4q_gemm: ldc %lld < N %lld", (long long)ldc, (long long)N);
+        return hip_status(fp4q::launch_gemm_subblock(g, sub_a, a_st, b_st, accumulate,
+                                                     static_cast<hipStream_t>(hip_stream)),
+                          "fp4q_gemm");
+    }
     if (accumulate && (fp8 || groups || (oned & 1)))
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_ex: accumulation takes dense FP4 products whose A operand "
                                        "has a square-block grid");
@@ -516,6 +616,25 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, 
                       "fp4q_gemm");
 }
 
+} // namespace
+
+extern "C" {
+
+int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, int64_t ldc, int64_t c_bstride,
+                 const fp4q_groups* groups, int flags, void* hip_stream)
+{
+    return gemm_common(op, a, b, c, ldc, c_bstride, groups, flags, nullptr, hip_stream);
+}
+
+int fp4q_gemm_quant(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, const fp4q_qtensor* out, int round_mode,
+                    uint64_t seed, uint32_t stream_id, const uint64_t* seed_dev, void* hip_stream)
+{
+    if (!out)
+        return fail(FP4Q_EINVAL, "fp4q_gemm_quant: null out");
+    QuantOut qo = {out, round_mode, seed, stream_id, seed_dev};
+    return gemm_common(op, a, b, nullptr, 0, 0, nullptr, 0, &qo, hip_stream);
+}
+
 int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, int64_t ldy, void* hip_stream)
 {
     if (!q || !y)
@@ -527,11 +646,12 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
     int fmt;
     const uint8_t* scales = q->scales;
     int64_t ld_s = q->ld_s;
-    if (q->fmt == FP4Q_FMT_FP4_2D32 || q->fmt == FP4Q_FMT_FP4_2D64 || q->fmt == FP4Q_FMT_FP4_1D32) {
+    if (q->fmt == FP4Q_FMT_FP4_2D32 || q->fmt == FP4Q_FMT_FP4_2D64 || q->fmt == FP4Q_FMT_FP4_1D32 ||
+        q->fmt == FP4Q_FMT_FP4_2D16 || q->fmt == FP4Q_FMT_FP4_2D8) {
         if ((rc = check_fp4_tensor(q, "fp4q_dequant q", transposed != 0)))
             return rc;
         fmt = 1;
-        p.block_shift = q->fmt == FP4Q_FMT_FP4_2D64 ? 6 : 5;
+        p.block_shift = log2_block(square_block(q->fmt));
         p.codes = transposed ? q->codes_t : q->codes;
         p.ld = transposed ? q->ld_t : q->ld;
         p.scale_transposed = transposed ? 1 : 0;
@@ -571,6 +691,28 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
     p.ldy = ldy;
     return hip_status(fp4q::launch_dequant(p, fmt, out_dtype == FP4Q_DT_BF16, static_cast<hipStream_t>(hip_stream)),
                       "fp4q_dequant");
+}
+
+int fp4q_probe_mfma_fp4(int64_t iters, int workgroups, float* sink, const uint8_t* codes, int64_t code_bytes,
+                        void* hip_stream)
+{
+    if (iters < 1 || iters > ((int64_t)1 << 32) || workgroups < 1 || workgroups > (1 << 20) || !sink)
+        return fail(FP4Q_EINVAL, "fp4q_probe_mfma_fp4: iters in [1, 2^32], workgroups in [1, 2^20] and a sink");
+    if (codes && (code_bytes < 32 || (reinterpret_cast<uintptr_t>(codes) & 3u)))
+        return fail(FP4Q_EINVAL, "fp4q_probe_mfma_fp4: codes need >= 32 bytes and 4-byte alignment");
+    return hip_status(fp4q::launch_mfma_probe(iters, workgroups, sink, reinterpret_cast<const uint32_t*>(codes),
+                                              codes ? code_bytes / 4 : 0, static_cast<hipStream_t>(hip_stream)),
+                      "fp4q_probe_mfma_fp4");
+}
+
+int fp4q_probe_copy(const void* src, void* dst, int64_t bytes, int workgroups, void* hip_stream)
+{
+    if (!src || !dst || bytes < 16 || bytes % 16 || workgroups < 1 || workgroups > (1 << 20) ||
+        !aligned16(src) || !aligned16(dst))
+        return fail(FP4Q_EINVAL, "fp4q_probe_copy: 16-byte aligned buffers, bytes a positive multiple of 16, "
+                                 "workgroups in [1, 2^20]");
+    return hip_status(fp4q::launch_copy_probe(src, dst, bytes, workgroups, static_cast<hipStream_t>(hip_stream)),
+                      "fp4q_probe_copy");
 }
 
 }  // extern "C"

@@ -31,14 +31,17 @@ struct Quant2dBatch {
     Quant2dArgs item[kQuant2dBatchMax];
     int first[kQuant2dBatchMax + 1];
     int n;
+    // Optional device-resident seed: when set, the Philox key of every item
+    // is (key1:key0) + *seed_dev, read when the kernel runs.
+    const uint64_t* seed_dev;
 };
 
 // Regions (workgroups) of one padded matrix.
 int64_t quant2d_regions(int64_t rows_pad, int64_t cols_pad);
 
-// Scale layouts: square 32x32 or 64x64 blocks, or the 1D activation layout
-// (1x32 blocks along the rows of each plane).
-enum QuantLayout { kLayout2D32 = 0, kLayout2D64 = 1, kLayout1D = 2 };
+// Scale layouts: square 32x32, 64x64, 16x16 or 8x8 blocks, or the 1D
+// activation layout (1x32 blocks along the rows of each plane).
+enum QuantLayout { kLayout2D32 = 0, kLayout2D64 = 1, kLayout1D = 2, kLayout2D16 = 3, kLayout2D8 = 4 };
 hipError_t launch_quant2d(const Quant2dBatch& b, bool f32, bool rne, bool aligned, int layout, hipStream_t s);
 
 struct Mxfp8Args {
@@ -100,6 +103,21 @@ struct GemmArgs {
     // workgroups (an upper bound on the tiles).
     const int64_t* row_off_dev;
     int tok_rows, max_rows, tile_bound;
+    // quantize-in-epilogue (launch_gemm_quant): instead of C, the 2D 32x32
+    // FP4 planes of C -- row plane [q_rows_pad x q_ld], transposed plane
+    // [q_cols_pad x q_ld_t] (or null), scale grid [q_rows_pad/32 x q_ld_s] --
+    // with the Philox key (q_key1:q_key0) (+ *q_seed_dev when set) and stream
+    // q_stream; q_rne selects round-to-nearest-even.
+    uint8_t* q_codes;
+    int64_t q_ld;
+    uint8_t* q_codes_t;
+    int64_t q_ld_t;
+    uint8_t* q_scales;
+    int64_t q_ld_s;
+    int q_rows_pad, q_cols_pad;
+    uint32_t q_key0, q_key1, q_stream;
+    int q_rne;
+    const uint64_t* q_seed_dev;
 };
 
 enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };
@@ -113,6 +131,26 @@ enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };
 // oned 0, dense or grouped, or MXFP8).
 hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
                        bool accumulate, bool out_bf16, hipStream_t s);
+
+// Sustained FP4 MFMA loop (measured-peak probe): `workgroups` workgroups of
+// 256 threads, each wave issuing 8 * iters 32x32x64 MFMAs on hashed operand
+// words or on words taken from `codes` (n_words >= 8); sink gets one float
+// per thread.
+hipError_t launch_mfma_probe(int64_t iters, int workgroups, float* sink, const uint32_t* codes, int64_t n_words,
+                             hipStream_t s);
+// Streaming copy (measured-peak probe) of `bytes` (a multiple of 16).
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int workgroups, hipStream_t s);
+
+// Dense FP4 product (square-block operands, batch 1) whose epilogue
+// quantizes the fp32 result into 2D 32x32 FP4 planes (the q_* fields)
+// instead of writing it: bit for bit the planes launch_quant2d gives for
+// that fp32 result.
+hipError_t launch_gemm_quant(const GemmArgs& p, bool a_st, bool b_st, hipStream_t s);
+
+// Dense FP4 product (batch 1) of operands that both take 16x16 (block 16)
+// or 8x8 (block 8) scale blocks; the scale grid of an operand is
+// [rows_pad/b x lds] (or its transpose for a_st / b_st).  accumulate: C +=.
+hipError_t launch_gemm_subblock(const GemmArgs& p, int block, bool a_st, bool b_st, bool accumulate, hipStream_t s);
 
 // Output tile of the GEMM kernel (grouped launches size their grids with it).
 int gemm_tile_m();

@@ -26,9 +26,8 @@
 // diagonal block element (i, j) uses block min(i, j), half max(i, j).  Waves
 // entirely above or below the diagonal take a uniform branch and index the
 // words directly; only waves on the diagonal rearrange them per lane.
-#include "fp4q_cvt.hpp"
-#include "fp4q_device.hpp"
 #include "fp4q_launch.hpp"
+#include "quant_tile.hpp"
 
 #include <type_traits>
 
@@ -36,29 +35,10 @@ namespace fp4q {
 
 namespace {
 
+using namespace qtile;
+
 constexpr int kThreads = 256;
 constexpr int kRegion = 128;
-
-template <bool F32>
-struct Block8x8;
-
-// bf16: 8 rows x 4 dwords, dword d of row i holds columns 2d (low) and 2d+1.
-template <>
-struct Block8x8<false> {
-    uint32_t v[8][4];
-    __device__ __forceinline__ uint32_t x32(int i, int j) const
-    {
-        const uint32_t d = v[i][j >> 1];
-        return (j & 1) ? (d & 0xFFFF0000u) : (d << 16);
-    }
-};
-
-// fp32: 8 rows x 8 words.
-template <>
-struct Block8x8<true> {
-    uint32_t v[8][8];
-    __device__ __forceinline__ uint32_t x32(int i, int j) const { return v[i][j]; }
-};
 
 // Loads the lane's 8x8 block at (R0, C0).  A block fully inside an aligned
 // input takes 8 (bf16) or 16 (fp32) 16-byte loads off one base pointer; an
@@ -97,112 +77,6 @@ __device__ __forceinline__ void load_block(Block8x8<F32>& blk, const Quant2dArgs
             }
         }
     }
-}
-
-// Stochastic rounding of the lane's 8x8 block to nibbles, one converter per
-// element (seed = its 16 random bits << 16).  The random bits of element
-// (i, j) are half h of word w[a][b] of the lane's 8 Philox blocks:
-//   ROWS   (block above the diagonal):  (a, b, h) = (i, j/2, j%2)
-//   COLS   (block below the diagonal):  (a, b, h) = (j, i/2, i%2)
-//   on the diagonal block:              a = min(i, j), half max(i, j)
-// MIXED waves (those crossing the diagonal) pick among the three per lane.
-// Even columns fill the bytes of a, odd columns those of b, so row word i is
-// a | b << 4.
-enum { kRows = 0, kCols = 1, kMixed = 2 };
-
-// f(std::integral_constant<int, e>) for e = 0..3 (converter byte selects).
-template <typename F>
-__device__ __forceinline__ void static_for_sel(F&& f)
-{
-    f(std::integral_constant<int, 0>());
-    f(std::integral_constant<int, 1>());
-    f(std::integral_constant<int, 2>());
-    f(std::integral_constant<int, 3>());
-}
-
-__device__ __forceinline__ uint32_t half_seed(uint32_t rd, int h) { return h ? (rd & 0xFFFF0000u) : (rd << 16); }
-
-template <int MODE>
-__device__ __forceinline__ uint32_t seed_of(const uint32_t w[8][4], int i, int j, bool lower, bool diag)
-{
-    const uint32_t up = half_seed(w[i][j >> 1], j & 1);
-    const uint32_t lo = half_seed(w[j][i >> 1], i & 1);
-    if (MODE == kRows)
-        return up;
-    if (MODE == kCols)
-        return lo;
-    const int a = i < j ? i : j, m = i < j ? j : i;
-    const uint32_t dg = half_seed(w[a][m >> 1], m & 1);
-    return diag ? dg : (lower ? lo : up);
-}
-
-template <int SEL, bool F32>
-__device__ __forceinline__ void sr_pair(uint32_t& a, uint32_t& b, const Block8x8<F32>& blk, int i,
-                                        uint32_t seed_even, uint32_t seed_odd, float scale)
-{
-    cvt_sr_byte<SEL>(a, __uint_as_float(blk.x32(i, 2 * SEL)), seed_even, scale);
-    cvt_sr_byte<SEL>(b, __uint_as_float(blk.x32(i, 2 * SEL + 1)), seed_odd, scale);
-}
-
-template <bool F32, int MODE>
-__device__ __forceinline__ void round_sr(const Block8x8<F32>& blk, const uint32_t w[8][4], float scale,
-                                         bool lower, bool diag, uint32_t rw[8])
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t a = 0, b = 0;
-        sr_pair<0>(a, b, blk, i, seed_of<MODE>(w, i, 0, lower, diag), seed_of<MODE>(w, i, 1, lower, diag), scale);
-        sr_pair<1>(a, b, blk, i, seed_of<MODE>(w, i, 2, lower, diag), seed_of<MODE>(w, i, 3, lower, diag), scale);
-        sr_pair<2>(a, b, blk, i, seed_of<MODE>(w, i, 4, lower, diag), seed_of<MODE>(w, i, 5, lower, diag), scale);
-        sr_pair<3>(a, b, blk, i, seed_of<MODE>(w, i, 6, lower, diag), seed_of<MODE>(w, i, 7, lower, diag), scale);
-        rw[i] = a | (b << 4);
-    }
-}
-
-// Round-to-nearest-even: one converter per pair of elements.
-template <bool F32>
-__device__ __forceinline__ void round_rne(const Block8x8<F32>& blk, float scale, uint32_t rw[8])
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t a = 0;
-        if (F32) {
-            cvt_rne_f32_byte<0>(a, __uint_as_float(blk.x32(i, 0)), __uint_as_float(blk.x32(i, 1)), scale);
-            cvt_rne_f32_byte<1>(a, __uint_as_float(blk.x32(i, 2)), __uint_as_float(blk.x32(i, 3)), scale);
-            cvt_rne_f32_byte<2>(a, __uint_as_float(blk.x32(i, 4)), __uint_as_float(blk.x32(i, 5)), scale);
-            cvt_rne_f32_byte<3>(a, __uint_as_float(blk.x32(i, 6)), __uint_as_float(blk.x32(i, 7)), scale);
-        } else {
-            cvt_rne_bf16_byte<0>(a, blk.v[i][0], scale);
-            cvt_rne_bf16_byte<1>(a, blk.v[i][1], scale);
-            cvt_rne_bf16_byte<2>(a, blk.v[i][2], scale);
-            cvt_rne_bf16_byte<3>(a, blk.v[i][3], scale);
-        }
-        rw[i] = a;
-    }
-}
-
-// Largest |x| bit pattern of the lane's block (fp32 bits).
-template <bool F32>
-__device__ __forceinline__ uint32_t block_amax(const Block8x8<F32>& blk)
-{
-    if (F32) {
-        uint32_t mx = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                mx = max(mx, blk.x32(i, j) & 0x7FFFFFFFu);
-        return mx;
-    }
-    // bf16: both halves at once with packed 16-bit max over the magnitudes
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    u16x2 m = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, blk.v[i][d] & 0x7FFF7FFFu));
-    return (uint32_t)max(m.x, m.y) << 16;
 }
 
 // Position of a lane's 8x8 block inside region `region` (128x128 per
@@ -246,59 +120,23 @@ constexpr int kStageBuf = 2 * kStagePlane;
 // Scale, random bits and rounding of one lane block whose data is in blk,
 // then the stores of the workgroup's region.  Every lane reaches the
 // barrier; lanes outside the padded matrix compute nothing and their
-// staging entries are never stored.  B64: one scale per 64x64 block, which
-// is exactly one wave's region.
-template <bool F32, int RNE, bool B64>
+// staging entries are never stored.  BLK: the square block side (8, 16, 32
+// or 64; a 64x64 block is exactly one wave's region).
+template <bool F32, int RNE, int BLK>
 __device__ __forceinline__ void process(const Block8x8<F32>& blk, const Quant2dArgs& p, const LanePos& q,
                                         uint8_t* stage)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    uint32_t mx = q.active ? block_amax<F32>(blk) : 0u;
-    // Tile amax: the 16 lanes of a 32x32 tile differ in lane bits 0,1,3,4;
-    // a 64x64 block takes all 64 lanes (bits 2 and 5 as well).
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 8));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
-    if (B64) {
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
-    }
+    const uint32_t mx = square_amax<BLK>(q.active ? block_amax<F32>(blk) : 0u);
     const int R0 = q.R0, C0 = q.C0;
     uint32_t rw[8] = {};
     if (q.active) {
         const int k = truncfree_exp_e2m1(mx);
-        const float scale = e8m0_scale(k);
-        if (RNE) {
-            round_rne<F32>(blk, scale, rw);
-        } else {
-            // Philox blocks: canonical orientation (P0, Q0) with P0 <= Q0 in block units.
-            const int BR = R0 >> 3, BC = C0 >> 3;
-            const int P0 = BR <= BC ? R0 : C0;
-            const int Q0 = BR <= BC ? C0 : R0;
-            uint32_t w[8][4];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                U4 c;
-                c.x = (uint32_t)(((P0 & 31) + t) * 4 + ((Q0 & 31) >> 3));
-                c.y = (uint32_t)(P0 >> 5);
-                c.z = (uint32_t)(Q0 >> 5);
-                c.w = p.stream;
-                const U4 o = philox10(c, p.key0, p.key1);
-                w[t][0] = o.x; w[t][1] = o.y; w[t][2] = o.z; w[t][3] = o.w;
-            }
-            // Waves strictly above the diagonal draw along rows, strictly below
-            // along columns; a wave crossing the diagonal selects per lane.
-            const int WR = q.r0w >> 6, WC = q.c0w >> 6;
-            if (WR < WC)
-                round_sr<F32, kRows>(blk, w, scale, false, false, rw);
-            else if (WR > WC)
-                round_sr<F32, kCols>(blk, w, scale, true, false, rw);
-            else
-                round_sr<F32, kMixed>(blk, w, scale, BR > BC, BR == BC, rw);
+        round_lane_block<F32, RNE>(blk, k, R0, C0, q.r0w, q.c0w, p.stream, p.key0, p.key1, rw);
+        if (block_leader<BLK>(lane)) {
+            constexpr int sh = BLK == 8 ? 3 : BLK == 16 ? 4 : BLK == 32 ? 5 : 6;
+            p.scales[(int64_t)(R0 >> sh) * p.ld_s + (C0 >> sh)] = (uint8_t)(k + 127);
         }
-        if (B64 ? lane == 0 : (lane & 0x1B) == 0)   // the block's first lane
-            p.scales[(int64_t)(R0 >> (B64 ? 6 : 5)) * p.ld_s + (C0 >> (B64 ? 6 : 5))] = (uint8_t)(k + 127);
     }
 
     // Stage the row words and (after an in-register nibble transpose) the
@@ -545,19 +383,8 @@ __device__ __forceinline__ void process1d(const Block8x8<F32>& blk, const Quant2
             round_rne_1d<F32>(blk, sr, sc, both, rw, cw);
         } else {
             const int BR = R0 >> 3, BC = C0 >> 3;
-            const int P0 = BR <= BC ? R0 : C0;
-            const int Q0 = BR <= BC ? C0 : R0;
             uint32_t w[8][4];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                U4 c;
-                c.x = (uint32_t)(((P0 & 31) + t) * 4 + ((Q0 & 31) >> 3));
-                c.y = (uint32_t)(P0 >> 5);
-                c.z = (uint32_t)(Q0 >> 5);
-                c.w = p.stream;
-                const U4 o = philox10(c, p.key0, p.key1);
-                w[t][0] = o.x; w[t][1] = o.y; w[t][2] = o.z; w[t][3] = o.w;
-            }
+            philox_words(w, R0, C0, p.stream, p.key0, p.key1);
             const int WR = q.r0w >> 6, WC = q.c0w >> 6;
             if (WR < WC)
                 round_sr_1d<F32, kRows>(blk, w, sr, sc, false, false, both, rw, cw);
@@ -633,7 +460,8 @@ __device__ __forceinline__ void process1d(const Block8x8<F32>& blk, const Quant2
 // oldest-first wave priority inside a compute unit lets some workgroups
 // finish well before others.  A batch launch covers the regions of several
 // matrices, so their ramps and tails overlap.
-// LAYOUT: 0 = 32x32 blocks, 1 = 64x64 blocks, 2 = 1D activation layout.
+// LAYOUT: 0 = 32x32 blocks, 1 = 64x64 blocks, 2 = 1D activation layout,
+// 3 = 16x16 blocks, 4 = 8x8 blocks.
 template <bool F32, int RNE, bool ALIGNED, int LAYOUT>
 __global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dBatch b)
 {
@@ -641,7 +469,13 @@ __global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dBatch b)
     int i = 0;
     while (i + 1 < b.n && (int)blockIdx.x >= b.first[i + 1])
         ++i;
-    const Quant2dArgs p = b.item[i];
+    Quant2dArgs p = b.item[i];
+    if (b.seed_dev) {
+        // device-resident seed (graph replays draw fresh bits): key += *seed_dev
+        const uint64_t k = ((uint64_t)p.key1 << 32 | p.key0) + *b.seed_dev;
+        p.key0 = (uint32_t)k;
+        p.key1 = (uint32_t)(k >> 32);
+    }
     const int nbx = (p.cols_pad + kRegion - 1) / kRegion;
     Block8x8<F32> blk;
     const LanePos q = lane_pos(p, (int)blockIdx.x - b.first[i], nbx);
@@ -649,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void quant2d_kernel(Quant2dBatch b)
     if constexpr (LAYOUT == 2)
         process1d<F32, RNE>(blk, p, q, stage);
     else
-        process<F32, RNE, LAYOUT == 1>(blk, p, q, stage);
+        process<F32, RNE, LAYOUT == 1 ? 64 : LAYOUT == 3 ? 16 : LAYOUT == 4 ? 8 : 32>(blk, p, q, stage);
 }
 
 template <bool F32, int RNE, bool ALIGNED, int LAYOUT>
@@ -668,9 +502,13 @@ hipError_t launch_a(const Quant2dBatch& b, bool aligned, hipStream_t s)
 template <bool F32, int RNE>
 hipError_t launch_b(const Quant2dBatch& b, bool aligned, int layout, hipStream_t s)
 {
-    if (layout == kLayout1D)
-        return launch_a<F32, RNE, 2>(b, aligned, s);
-    return layout == kLayout2D64 ? launch_a<F32, RNE, 1>(b, aligned, s) : launch_a<F32, RNE, 0>(b, aligned, s);
+    switch (layout) {
+    case kLayout1D: return launch_a<F32, RNE, 2>(b, aligned, s);
+    case kLayout2D64: return launch_a<F32, RNE, 1>(b, aligned, s);
+    case kLayout2D16: return launch_a<F32, RNE, 3>(b, aligned, s);
+    case kLayout2D8: return launch_a<F32, RNE, 4>(b, aligned, s);
+    default: return launch_a<F32, RNE, 0>(b, aligned, s);
+    }
 }
 
 } // namespace

@@ -10,6 +10,9 @@ once, and W's transposed plane serves DGRAD.  Every step runs in the HIP kernels
 module only orders the calls.  Y and dW are fp32; dX has X's dtype (bf16 X:
 the kernel's bf16 output, the fp32 result rounded to nearest even).
 """
+import itertools
+import weakref
+
 import torch
 
 from . import alloc_fp4, fp4q_gemm, fp4q_quant2d, fp4q_quant2d_batch
@@ -42,7 +45,8 @@ class _FP4LinearFn(torch.autograd.Function):
             dx = fp4q_gemm("dgrad", qdy, qw, out_dtype=ctx.x_dtype)
         if ctx.needs_input_grad[1]:
             dw = fp4q_gemm("wgrad", qdy, qx)
-        ctx.q = None
+        # ctx.q stays: a graph kept with retain_graph=True may run backward
+        # again; autograd frees it with the graph
         return dx, dw, None, None, None
 
 
@@ -55,12 +59,31 @@ def fp4_linear(x, w, seed=0, stream_base=0, act_layout=32):
     return _FP4LinearFn.apply(x, w, seed, stream_base, act_layout)
 
 
+_layer_ids = itertools.count()
+_live_ids = weakref.WeakValueDictionary()
+
+
 class FP4Linear(torch.nn.Module):
     """Bias-free linear layer with an fp32 master weight; every call draws
-    fresh stochastic-rounding bits (the call counter is the Philox key)."""
+    fresh stochastic-rounding bits (the call counter is the Philox key).
 
-    def __init__(self, in_features, out_features, layer_id=0, act_layout=32, device="cuda"):
+    Each layer owns the Philox streams 16*layer_id + 1..3, so two layers of
+    the same shape never draw the same bits: layer_id defaults to the next
+    unused id, and an explicit id already held by a live layer is refused."""
+
+    def __init__(self, in_features, out_features, layer_id=None, act_layout=32, device="cuda"):
         super().__init__()
+        if layer_id is None:
+            layer_id = next(_layer_ids)
+            while layer_id in _live_ids:
+                layer_id = next(_layer_ids)
+        elif layer_id in _live_ids:
+            raise ValueError("FP4Linear layer_id %d is already used by a live layer; its stochastic "
+                             "rounding would repeat that layer's random bits" % layer_id)
+        if not 0 <= layer_id < (1 << 27):
+            raise ValueError("FP4Linear layer_id must be in [0, 2^27)")
+        _live_ids[layer_id] = self
+        self.layer_id = layer_id
         self.weight = torch.nn.Parameter(
             torch.randn(out_features, in_features, device=device) * (in_features ** -0.5))
         self.stream_base = 16 * layer_id

@@ -56,8 +56,11 @@ typedef enum {
     FP4Q_FMT_MXFP8_1D32 = 2, /* E4M3FN bytes, one E8M0 scale per 1x32 row group */
     FP4Q_FMT_FP4_2D64 = 3,   /* E2M1 codes, one E8M0 scale per 64x64 tile; code planes as 2D32,
                                 scale grid ceil(rows/64) x ceil(cols/64) (ld_s >= ceil(cols/64)) */
-    FP4Q_FMT_FP4_1D32 = 4    /* E2M1 codes, activation layout: one E8M0 scale per 1x32 block of
+    FP4Q_FMT_FP4_1D32 = 4,   /* E2M1 codes, activation layout: one E8M0 scale per 1x32 block of
                                 each plane's rows (layout below) */
+    FP4Q_FMT_FP4_2D16 = 5,   /* E2M1 codes, one E8M0 scale per 16x16 tile; code planes as 2D32,
+                                scale grid R/16 x C/16 over the 32-padded planes */
+    FP4Q_FMT_FP4_2D8 = 6     /* E2M1 codes, one E8M0 scale per 8x8 tile; scale grid R/8 x C/8 */
 } fp4q_fmt;
 
 /*
@@ -90,6 +93,10 @@ typedef enum {
  *   and 16-byte aligned grids; every chunk byte past the matrix is written
  *   as 0.  Code planes as for FP4_2D32.  codes_t and scales_t may both be
  *   NULL.  batch must be 1.
+ * FP4_2D64 / FP4_2D16 / FP4_2D8: the code planes of FP4_2D32 with b x b scale
+ *   blocks, b = 64, 16 or 8: scales [ceil(R/b) x ld_s], byte of tile
+ *   (r/b, c/b) at (r/b)*ld_s + c/b, ld_s >= ceil(C/b); a tile with no valid
+ *   entry (wholly in the padding) holds byte 0.
  * MXFP8_1D32 (written by fp4q_quant1d_mxfp8), with C = cols rounded up to 32:
  *   codes   [rows x ld]   one E4M3FN byte per element (padding bytes 0)
  *   scales  [rows x ld_s] E8M0 byte of group (r, c/32)
@@ -172,9 +179,10 @@ int fp4q_quant2d_sizes(int64_t rows, int64_t cols, int64_t* codes_bytes,
  *            b = max(r,c), taking half (b%8) of the 128-bit output; rounding
  *            goes up iff floor(frac * 2^16) + draw >= 2^16.  Hence
  *            quant(x^T) equals quant(x)^T bit for bit.
- *   out      fmt = FP4Q_FMT_FP4_2D32 (32x32 blocks), FP4Q_FMT_FP4_2D64
- *            (64x64 blocks, one of the block sides compared in the page's
- *            Table 4: same rule per block, same per-element random fields)
+ *   out      fmt = FP4Q_FMT_FP4_2D32 (32x32 blocks), FP4Q_FMT_FP4_2D64,
+ *            FP4Q_FMT_FP4_2D16 or FP4Q_FMT_FP4_2D8 (64x64, 16x16 or 8x8
+ *            blocks, the other block sides compared in the page's Table 4:
+ *            same rule per block, same per-element random fields)
  *            or FP4Q_FMT_FP4_1D32 (the activation layout: each plane in
  *            1x32 blocks along its rows, each element rounded once per
  *            plane with its one random field; the pages' appendix
@@ -216,6 +224,21 @@ int fp4q_quant2d_batch(int n, const fp4q_quant2d_item* items, int dtype, int rou
                        uint64_t seed, void* hip_stream);
 
 /*
+ * fp4q_quant2d_batch with a device-resident seed, for stochastic rounding
+ * inside captured HIP graphs (the abstract and Sec. 3.1 of the same page use
+ * SR to keep gradients unbiased, which needs fresh random bits every step;
+ * a seed passed by value would be frozen into the graph).
+ *   seed_dev  NULL: exactly fp4q_quant2d_batch.  Else a DEVICE pointer to one
+ *             uint64 (8-byte aligned) read by the kernel when it runs; the
+ *             Philox key is seed + *seed_dev (mod 2^64).  A caller bumps
+ *             *seed_dev between replays (for example with a small kernel
+ *             captured in the same graph).
+ * Otherwise as fp4q_quant2d_batch; a misaligned seed_dev returns FP4Q_EINVAL.
+ */
+int fp4q_quant2d_batch_ex(int n, const fp4q_quant2d_item* items, int dtype, int round_mode,
+                          uint64_t seed, const uint64_t* seed_dev, void* hip_stream);
+
+/*
  * MXFP8 quantization of the query/key projections (Sec. 3.2 of the same
  * page): E4M3FN elements, one E8M0 scale per 1x32 group along each row,
  * truncation-free (the Sec. 3.1 rule with Qp = 448), round-to-nearest-even.
@@ -234,7 +257,13 @@ int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
  *   op WGRAD: a = dY [T x N], b = X [T x K]  ->  C = dY^T X  [N x K]
  * FP4 operands may each have 32x32 or 64x64 scale blocks (a 64x64 block's
  * byte is used for both of its 32-row slabs and both of its 32-wide K
- * blocks) or the 1D activation layout (each plane read with its own tiled
+ * blocks); operands with 16x16 or 8x8 blocks must both take the same side
+ * (dense products, batch 1, fp32 C; else FP4Q_EUNSUPPORTED): the MX MFMA
+ * takes one scale per 32 K values, so each 32-K step runs as 2 (16x16) or
+ * 4 (8x8) MFMAs whose A operand keeps one sub-block of its codes (the rest
+ * zero) with that sub-block's scales -- every product exact, at 1/2 or 1/4
+ * of the matrix-core rate (contractions past 3840 for 8x8 run as chunks
+ * that accumulate in C) or the 1D activation layout (each plane read with its own tiled
  * grid: FWD reads X's row plane, WGRAD X's transposed plane; dense products
  * with batch 1 only, else FP4Q_EUNSUPPORTED); grouped products take 32x32
  * blocks only (FP4Q_EUNSUPPORTED).
@@ -286,6 +315,31 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, 
                  int64_t c_bstride, const fp4q_groups* groups, int flags, void* hip_stream);
 
 /*
+ * A GEMM whose epilogue quantizes its own result (Sec. 3 "Application to
+ * linear layers" of the same page: the output of one product -- a layer's
+ * dX, or its Y -- is an operand of the next product, and every operand is
+ * quantized once, in 32x32 blocks with the Sec. 3.1 scale and stochastic
+ * rounding).  C = op(a, b) is formed exactly as fp4q_gemm forms it, in fp32,
+ * and is never written: the epilogue writes its 2D 32x32 FP4 planes into
+ * `out` instead, bit for bit those fp4q_quant2d writes for that fp32 C
+ * (rows x cols = M x N, dtype FP4Q_DT_F32, the same round_mode, seed and
+ * stream_id).  It saves C's 4-byte store and the quantizer's 4-byte read per
+ * element.
+ *   op, a, b   as fp4q_gemm; dense FP4 products of 32x32- or 64x64-block
+ *              operands with batch 1 (else FP4Q_EUNSUPPORTED).
+ *   out        fmt FP4Q_FMT_FP4_2D32, rows = M, cols = N, batch 1; codes and
+ *              scales required, codes_t optional (NULL: row plane only);
+ *              leading dims as fp4q_quant2d requires.
+ *   round_mode, seed, stream_id   as fp4q_quant2d.
+ *   seed_dev   NULL, or a DEVICE pointer to a uint64 (8-byte aligned) added
+ *              to the Philox key when the kernel runs (as in
+ *              fp4q_quant2d_batch_ex).
+ */
+int fp4q_gemm_quant(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, const fp4q_qtensor* out,
+                    int round_mode, uint64_t seed, uint32_t stream_id, const uint64_t* seed_dev,
+                    void* hip_stream);
+
+/*
  * Dequantization X ~ P * S (Sec. 2.1 of the same page) to fp32 or bf16, for
  * every format (each plane of the 1D layout with its own grid).
  *   transposed  0: the row plane, y is rows x cols; 1 (FP4 only): the
@@ -294,6 +348,31 @@ int fp4q_gemm_ex(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, 
  */
 int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, int64_t ldy,
                  void* hip_stream);
+
+/*
+ * Diagnostics, not part of the method: the measured peaks that benchmarks
+ * report beside the nominal ones.
+ *
+ * fp4q_probe_mfma_fp4: a sustained loop of block-scaled FP4 MFMAs
+ * (v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands, the instruction of
+ * every FP4 product above).  Launches `workgroups` workgroups of 4 waves;
+ * each wave issues 8 * iters MFMAs of 2*32*32*64 flops.  The matrix cores'
+ * rate depends on the codes they multiply: codes NULL takes operand words
+ * hashed per lane; else codes (device, 4-byte aligned, code_bytes >= 32) is
+ * a code plane whose words the lanes take, so the loop runs on a
+ * workload's own codes.  sink: device array of workgroups*256 floats,
+ * written (keeps the loop alive).
+ *   iters in [1, 2^32], workgroups in [1, 2^20], else FP4Q_EINVAL.
+ *
+ * fp4q_probe_copy: a streaming device-to-device copy of `bytes` (a positive
+ * multiple of 16, both buffers 16-byte aligned, device) with 16-byte loads
+ * and stores over `workgroups` workgroups of 256 threads; its rate (read +
+ * written bytes over time) is the practical HBM ceiling of a read-once,
+ * write-once kernel.
+ */
+int fp4q_probe_mfma_fp4(int64_t iters, int workgroups, float* sink, const uint8_t* codes, int64_t code_bytes,
+                        void* hip_stream);
+int fp4q_probe_copy(const void* src, void* dst, int64_t bytes, int workgroups, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -294,3 +294,68 @@ def test_alloc_act1d_meets_the_grid_rules(fp4q):
         assert d.fmt == 4 and q.scales.shape == (-(-R // 128), 512 * -(-C // 128))
         assert q.scales_t.shape == (-(-C // 128), 512 * -(-R // 128))
         assert d.ld_s % 16 == 0 and d.ld_st % 16 == 0 and d.ld_s >= 512 * -(-C // 128)
+
+
+def test_binding_checks_outputs_before_any_launch(fp4q):
+    """The binding refuses an output the C ABI could not check (it sees only a
+    pointer and a leading dimension): wrong dtype, wrong shape or batch,
+    another device, non-contiguous rows.  Host tensors: every refusal happens
+    before anything is enqueued."""
+    import torch
+    a = fp4q.alloc_fp4(64, 96, device="cpu")
+    b = fp4q.alloc_fp4(32, 96, device="cpu")
+    cases = [
+        (torch.empty(64, 32, dtype=torch.uint8), "float32 or bfloat16"),
+        (torch.empty(64, 33), "shape"),
+        (torch.empty(2, 64, 32), "shape"),
+        (torch.empty(64, 32), "must live on"),
+        (torch.empty(32, 64).t(), "contiguous rows"),
+    ]
+    for c, msg in cases:
+        with pytest.raises(fp4q.Fp4qError, match=msg):
+            fp4q.fp4q_gemm("fwd", a, b, c=c)
+    with pytest.raises(fp4q.Fp4qError, match="accumulate"):
+        fp4q.fp4q_gemm("wgrad", a, b, accumulate=True)
+    for out, msg in ((torch.empty(64, 96, dtype=torch.uint8), "float32 or bfloat16"),
+                     (torch.empty(96, 64), "shape"), (torch.empty(64, 96), "must live on")):
+        with pytest.raises(fp4q.Fp4qError, match=msg):
+            fp4q.fp4q_dequant(a, out=out)
+    with pytest.raises(fp4q.Fp4qError, match="shape"):
+        fp4q.fp4q_dequant(a, transposed=True, out=torch.empty(64, 96))
+
+
+def test_device_seed_entry_validates(fp4q):
+    """fp4q_quant2d_batch_ex checks what fp4q_quant2d_batch checks, plus the
+    alignment of the device seed pointer."""
+    L = fp4q.lib()
+    d = _desc(fp4q)
+    it = fp4q._QItem(ctypes.c_void_p(0x10000), 64, 64, 64, 1, ctypes.pointer(d))
+    arr = (fp4q._QItem * 1)(it)
+    assert L.fp4q_quant2d_batch_ex(1, arr, 1, 0, 0, ctypes.c_void_p(0x20004), None) == -1
+    assert "aligned" in _err(fp4q)
+    assert L.fp4q_quant2d_batch_ex(0, arr, 1, 0, 0, ctypes.c_void_p(0x20000), None) == -1
+    assert L.fp4q_quant2d_batch_ex(1, arr, 7, 0, 0, ctypes.c_void_p(0x20000), None) == -1
+
+
+def test_gemm_quant_validation(fp4q):
+    """fp4q_gemm_quant takes dense FP4 products of square-block operands with
+    batch 1 and a 32x32-block output of the product's shape."""
+    L = fp4q.lib()
+    a = _desc(fp4q, rows=64, cols=64)
+    w = _desc(fp4q, rows=96, cols=64)
+    good = _desc(fp4q, rows=64, cols=96, ld=48, ld_t=32, ld_s=3)
+    seed_ok = ctypes.c_void_p(0x80000)
+    call = lambda op, x, y, o, rm=0, sd=None: L.fp4q_gemm_quant(op, ctypes.byref(x), ctypes.byref(y),
+                                                                   ctypes.byref(o) if o is not None else None,
+                                                                   rm, 0, 0, sd, None)
+    assert call(0, a, w, None) == -1
+    assert call(0, a, w, _desc(fp4q, rows=64, cols=64, ld=48, ld_s=3)) == -1      # wrong shape
+    assert "product" in _err(fp4q)
+    assert call(0, a, w, good, rm=5) == -1
+    assert call(0, a, w, good, sd=ctypes.c_void_p(0x80004)) == -1
+    f8 = _desc(fp4q, fmt=2, ld=64)
+    assert call(0, f8, f8, good) == -2
+    ab = _desc(fp4q, rows=64, cols=64, batch=2)
+    assert call(0, ab, _desc(fp4q, rows=96, cols=64, batch=2), good) == -2
+    o64 = _desc(fp4q, fmt=3, rows=64, cols=96, ld=48, ld_t=32, ld_s=2)
+    assert call(0, a, w, o64) == -2

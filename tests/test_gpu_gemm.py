@@ -75,7 +75,7 @@ def test_exact_on_grid_values():
     assert np.array_equal(C.astype(np.float64), X.astype(np.float64) @ W.astype(np.float64).T)
 
 
-def _sampled_layer_check(L, what, n_samples=3000):
+def _sampled_layer_check(L, what, n_samples=4096):
     """Full-size layer: every GPU plane vs the oracle, GEMMs at sampled outputs."""
     rng = np.random.default_rng(99)
     g, o = _quant_all(L.X, L.W, L.dY)
@@ -103,12 +103,12 @@ def test_1b_layers_sampled(i):
     _sampled_layer_check(wl.layer_1b(i), "1B layer %d" % i)
 
 
-def test_7b_qkv_sampled():
-    _sampled_layer_check(wl.layer_7b(0), "7B qkv")
-
-
-def test_7b_down_sampled():
-    _sampled_layer_check(wl.layer_7b(3), "7B down")
+@pytest.mark.parametrize("i", [0, 1, 2, 3], ids=[nm for nm, _, _ in wl.LAYERS_7B])
+def test_7b_layers_sampled(i):
+    """Every 7B layer (QKV, O, up, down): all three planes of X, W and dY
+    bit-exact at full size, and fwd / dgrad / wgrad at 4096 sampled outputs
+    plus the four corners, in the launch configuration the benchmark uses."""
+    _sampled_layer_check(wl.layer_7b(i), "7B " + wl.LAYERS_7B[i][0], n_samples=4096)
 
 
 # Grids of 512 or more 256x256 tiles (two or more per CU), one op per shape

@@ -103,3 +103,42 @@ def test_graph_replays_match_eager(streams):
                     assert torch.equal(a, b), "replay %d: %s planes differ" % (rep, k)
             else:
                 assert torch.equal(v, got[k]), "replay %d: %s differs" % (rep, k)
+
+
+def test_device_seed_draws_fresh_bits_per_replay():
+    """A quantizer captured with a device-resident seed (fp4q_quant2d_batch_ex)
+    reads the seed when the replay runs: with the seed changed between
+    replays, each replay's planes equal the oracle's for the host seed plus
+    that replay's device seed, and consecutive replays differ."""
+    import oracle as orc
+    from gpu_util import assert_planes_equal
+    L = wl.linear_layer("tiny:devseed", 200, 320, 96, 4)
+    x, w = to_dev(L.X), to_dev(L.W)
+    qx, qw = fq.alloc_fp4(*x.shape), fq.alloc_fp4(*w.shape)
+    seed_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def seq():
+        fq.fp4q_quant2d_batch([(x, qx, 5), (w, qw, 6)], seed=100, seed_dev=seed_dev)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        seq()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq()
+    prev = None
+    for dseed in (7, 8, (1 << 40) + 3, -1):
+        note("graph device seed %d" % dseed)
+        seed_dev.fill_(dseed)
+        g.replay()
+        torch.cuda.synchronize()
+        key = (100 + dseed) & ((1 << 64) - 1)
+        assert_planes_equal(qx, orc.quant2d(L.X, orc.ROUND_SR, seed=key, stream=5), "X seed %d" % dseed)
+        assert_planes_equal(qw, orc.quant2d(L.W, orc.ROUND_SR, seed=key, stream=6), "W seed %d" % dseed)
+        cur = qx.codes.clone()
+        if prev is not None:
+            assert not torch.equal(cur, prev)
+        prev = cur

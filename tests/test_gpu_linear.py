@@ -77,7 +77,7 @@ def test_toy_regression_converges(layout):
     X = torch.randn(T, K, device="cuda")
     W_star = torch.randn(N, K, device="cuda") * K ** -0.5
     Y_star = X @ W_star.t()
-    layer = fl.FP4Linear(K, N, layer_id=1, act_layout=layout)
+    layer = fl.FP4Linear(K, N, act_layout=layout)
     opt = torch.optim.Adam(layer.parameters(), lr=0.02)
     losses = []
     note("fp4 toy regression %s" % layout)
@@ -89,3 +89,22 @@ def test_toy_regression_converges(layout):
         losses.append(float(loss.detach()))
     assert all(np.isfinite(losses))
     assert np.mean(losses[-10:]) < 0.1 * losses[0], (losses[0], losses[-10:])
+
+
+def test_layers_draw_distinct_streams_and_backward_twice():
+    """Two FP4Linear layers never share Philox streams (an explicit id held
+    by a live layer is refused), and a graph kept with retain_graph=True runs
+    backward twice with the same result."""
+    a = fl.FP4Linear(64, 32)
+    b = fl.FP4Linear(64, 32)
+    assert a.stream_base != b.stream_base
+    with pytest.raises(ValueError):
+        fl.FP4Linear(64, 32, layer_id=a.layer_id)
+    x = torch.randn(96, 64, device="cuda")
+    note("fp4 linear retain_graph")
+    y = a(x)
+    y.sum().backward(retain_graph=True)
+    g1 = a.weight.grad.clone()
+    a.weight.grad = None
+    y.sum().backward()
+    assert torch.equal(g1, a.weight.grad)

@@ -72,8 +72,10 @@ def test_grouped_small_all_ops():
 
 def test_moe_config_sampled_experts():
     """30B-class MoE layer (8192 tokens, hidden 2048, 128 experts of 768,
-    top-8): up and down projections, grouped fwd/dgrad/wgrad, checked on a
-    sample of experts (first, last, largest, smallest, random)."""
+    top-8): every quantized plane of X, W_up, dY, A, W_down and dY_down
+    bit-exact against the oracle, and the up and down projections' grouped
+    fwd/dgrad/wgrad checked on a sample of experts (first, last, largest,
+    smallest, random)."""
     m = wl.config_moe()
     offs = m.row_off.tolist()
     E, H, F = m.E, m.H, m.F
@@ -87,6 +89,11 @@ def test_moe_config_sampled_experts():
         g = {"X": fq.fp4q_quant2d(to_dev(X), seed=0, stream_id=1),
              "W": fq.fp4q_quant2d(to_dev(W), seed=0, stream_id=2),
              "dY": fq.fp4q_quant2d(to_dev(dY), seed=0, stream_id=3)}
+        # every plane of the config's quantized tensors, bit for bit
+        for nm, t, sid in (("X", X, 1), ("W", W, 2), ("dY", dY, 3)):
+            note("moe %s %s planes vs the oracle (%d x %d)" % (name, nm, t.shape[0], t.shape[1]))
+            assert_planes_equal(g[nm], orc.quant2d(t, orc.ROUND_SR, seed=0, stream=sid),
+                                "moe %s %s" % (name, nm))
         note("moe %s grouped gemms" % name)
         Y = fq.fp4q_gemm("fwd", g["X"], g["W"], groups=offs)
         dX = fq.fp4q_gemm("dgrad", g["dY"], g["W"], groups=offs)

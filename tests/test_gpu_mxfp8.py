@@ -9,7 +9,7 @@ import torch
 import oracle as orc
 import fp4_microscaling_quantization_quant2d_amd as fq
 from fp4_microscaling_quantization_quant2d_amd import workloads as wl
-from gpu_util import check_gemm_tol, note, to_dev
+from gpu_util import assert_planes_equal, check_gemm_tol, note, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -109,12 +109,16 @@ def test_attention_config_sampled():
     qq = fq.fp4q_quant1d_mxfp8(to_dev(Qf))
     qk = fq.fp4q_quant1d_mxfp8(to_dev(Kf))
     rng = np.random.default_rng(7)
+    torch.cuda.synchronize()
     for q, x in ((qq, Qf), (qk, Kf)):
-        r0 = int(rng.integers(0, x.shape[0] - 512))
-        ref = orc.quant1d_mxfp8(np.ascontiguousarray(x[r0:r0 + 512]))
-        c = q.codes[r0:r0 + 512].cpu().numpy()
-        s = q.scales[r0:r0 + 512].cpu().numpy()
-        assert np.array_equal(c, ref[0]) and np.array_equal(s, ref[1])
+        # the first rows, the last rows and four random bands of 512 rows
+        n = x.shape[0]
+        starts = sorted({0, n - 512} | set(int(v) for v in rng.integers(0, n - 512, 4)))
+        for r0 in starts:
+            ref = orc.quant1d_mxfp8(np.ascontiguousarray(x[r0:r0 + 512]))
+            c = q.codes[r0:r0 + 512].cpu().numpy()
+            s = q.scales[r0:r0 + 512].cpu().numpy()
+            assert np.array_equal(c, ref[0]) and np.array_equal(s, ref[1]), "MXFP8 band at row %d" % r0
     note("attn S = QK^T batched (%d heads)" % (B * Hh))
     S = fq.fp4q_gemm("fwd", _batched_fp8(qq, B * Hh, L, D), _batched_fp8(qk, B * Hh, L, D))
     torch.cuda.synchronize()
@@ -142,9 +146,8 @@ def test_attention_config_sampled():
     o = {nm: orc.quant2d(getattr(L_o, nm), orc.ROUND_SR, seed=0, stream=i + 1)
          for i, nm in enumerate(("X", "W", "dY"))}
     for nm in g:
-        torch.cuda.synchronize()
-        assert np.array_equal(g[nm].codes.cpu().numpy(), o[nm][0])
-        assert np.array_equal(g[nm].scales.cpu().numpy(), o[nm][2])
+        # codes, the transposed plane (read by dgrad and wgrad) and scales
+        assert_planes_equal(g[nm], o[nm], "O-projection " + nm)
     deq = {nm: orc.dequant_fp4(o[nm][0], o[nm][2], *getattr(L_o, nm).shape) for nm in g}
     T, K, N = L_o.T, L_o.K, L_o.N
     for op, an, bn, (m, n) in (("fwd", "X", "W", (T, N)), ("dgrad", "dY", "W", (T, K)),

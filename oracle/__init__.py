@@ -77,6 +77,17 @@ def lib():
         L.orc_gemm_sampled.restype = ctypes.c_int
         L.orc_gemm_sampled.argtypes = [ctypes.c_int, _P, _I64, _I64, _P, _I64, _I64, _I64, _P, _P,
                                        _P, _P]
+        D = ctypes.c_double
+        L.orc_attn_fwd_rows.restype = ctypes.c_int
+        L.orc_attn_fwd_rows.argtypes = [_P, _P, _P, _I64, _I64, D, ctypes.c_int, _I64, _P, _P, _P, _P]
+        L.orc_attn_stats.restype = ctypes.c_int
+        L.orc_attn_stats.argtypes = [_P, _P, _P, _P, _I64, _I64, D, ctypes.c_int, _I64, _I64, _P, _P, _P, _P]
+        L.orc_attn_bwd_dq_rows.restype = ctypes.c_int
+        L.orc_attn_bwd_dq_rows.argtypes = [_P, _P, _P, _P, _I64, _I64, D, ctypes.c_int, _I64, _P, _P, _P, _P,
+                                           _P, _P]
+        L.orc_attn_bwd_dkdv_rows.restype = ctypes.c_int
+        L.orc_attn_bwd_dkdv_rows.argtypes = [_P, _P, _P, _P, _I64, _I64, D, ctypes.c_int, _P, _P, _P, _P, _I64,
+                                             _P, _P, _P, _P, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -319,3 +330,103 @@ def gemm_sampled(op, A, B, ci, cj):
                                   B.shape[1], len(ci), _ptr(ci), _ptr(cj), _ptr(C), _ptr(bound)),
            "gemm_sampled")
     return C, bound
+
+
+# -- attention (Sec. 3.2: MXFP8 queries and keys) ----------------------------------
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _split(n, parts):
+    parts = max(1, min(parts, n))
+    return [(n * i // parts, n * (i + 1) // parts) for i in range(parts)]
+
+
+def _threads(threads):
+    return threads or min(16, os.cpu_count() or 1)
+
+
+def attn_fwd(Q, K, V, scale, causal, rows=None, threads=None):
+    """One head: O [len(rows) x d], lse [len(rows)] (natural log) and
+    pv_abs = sum_j P_ij |V_jt|, for the selected query rows (default all).
+    Q, K are the dequantized MXFP8 values."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    L, d = Q.shape
+    rows = np.arange(L, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = len(rows)
+    O = np.zeros((n, d))
+    lse = np.zeros(n)
+    pv = np.zeros((n, d))
+
+    def run(b):
+        lo, hi = b
+        if hi <= lo:
+            return 0
+        return lib().orc_attn_fwd_rows(_ptr(Q), _ptr(K), _ptr(V), L, d, float(scale), int(causal), hi - lo,
+                                       _ptr(rows[lo:]), _ptr(O[lo:]), _ptr(lse[lo:]), _ptr(pv[lo:]))
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        for rc in ex.map(run, _split(n, _threads(threads))):
+            _check(rc, "attn_fwd")
+    return O, lse, pv
+
+
+def attn_bwd_dq(Q, K, V, dO, scale, causal, rows=None, threads=None):
+    """One head: dQ of the selected query rows and its tolerance magnitudes
+    (ds_abs_k, p_abs_k, p_k per row and feature; dvo per row)."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    L, d = Q.shape
+    rows = np.arange(L, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = len(rows)
+    dQ, a, b, c = (np.zeros((n, d)) for _ in range(4))
+    dvo = np.zeros(n)
+
+    def run(bd):
+        lo, hi = bd
+        if hi <= lo:
+            return 0
+        return lib().orc_attn_bwd_dq_rows(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), L, d, float(scale), int(causal),
+                                          hi - lo, _ptr(rows[lo:]), _ptr(dQ[lo:]), _ptr(a[lo:]), _ptr(b[lo:]),
+                                          _ptr(c[lo:]), _ptr(dvo[lo:]))
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        for rc in ex.map(run, _split(n, _threads(threads))):
+            _check(rc, "attn_bwd_dq")
+    return dQ, {"ds_abs_k": a, "p_abs_k": b, "p_k": c, "dvo": dvo}
+
+
+def attn_bwd_dkdv(Q, K, V, dO, scale, causal, rows=None, threads=None):
+    """One head: dK, dV of the selected key rows and their tolerance
+    magnitudes (ds_abs_q, p_abs_q, pd_q, p_do per row and feature)."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    L, d = Q.shape
+    rows = np.arange(L, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = len(rows)
+    mv, lv, Dv, dvo = (np.zeros(L) for _ in range(4))
+    nt = _threads(threads)
+
+    def stats(bd):
+        lo, hi = bd
+        if hi <= lo:
+            return 0
+        return lib().orc_attn_stats(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), L, d, float(scale), int(causal), lo, hi,
+                                    _ptr(mv), _ptr(lv), _ptr(Dv), _ptr(dvo))
+
+    dK, dV, a, b, c, e = (np.zeros((n, d)) for _ in range(6))
+
+    def run(bd):
+        lo, hi = bd
+        if hi <= lo:
+            return 0
+        return lib().orc_attn_bwd_dkdv_rows(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), L, d, float(scale), int(causal),
+                                            _ptr(mv), _ptr(lv), _ptr(Dv), _ptr(dvo), hi - lo, _ptr(rows[lo:]),
+                                            _ptr(dK[lo:]), _ptr(dV[lo:]), _ptr(a[lo:]), _ptr(b[lo:]), _ptr(c[lo:]),
+                                            _ptr(e[lo:]))
+
+    with ThreadPoolExecutor(nt) as ex:
+        for rc in ex.map(stats, _split(L, nt)):
+            _check(rc, "attn_stats")
+        for rc in ex.map(run, _split(n, nt)):
+            _check(rc, "attn_bwd_dkdv")
+    return dK, dV, {"ds_abs_q": a, "p_abs_q": b, "pd_q": c, "p_do": e}

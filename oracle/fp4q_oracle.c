@@ -11,6 +11,7 @@
 #include "fp4q_oracle.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <string.h>
 
@@ -570,6 +571,242 @@ int orc_gemm_sampled(int op, const double* A, int64_t a_rows, int64_t a_cols,
         if (ci[s] < 0 || ci[s] >= m || cj[s] < 0 || cj[s] >= nn)
             return -1;
         gemm_one(op, A, a_cols, B, b_cols, kk, ci[s], cj[s], &C[s], bound ? &bound[s] : NULL);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention with MXFP8 queries and keys (Sec. 3.2 "MXFP8 Attention" and    */
+/* Fig. 3: Q and K enter the score product in MXFP8; the appendix           */
+/* "Attention").  One head at a time; Q, K are the dequantized MXFP8 values */
+/* (exact in fp64), V and dO as given.  Standard scaled dot-product          */
+/* attention, written out:                                                   */
+/*   s_ij = scale * sum_d Q_id K_jd          (j <= i when causal)            */
+/*   P_ij = exp(s_ij - m_i) / l_i,  m_i = max_j s_ij,  l_i = sum_j exp(...)  */
+/*   O_i  = sum_j P_ij V_j,         lse_i = m_i + log(l_i)                   */
+/* and its gradient for a loss with dL/dO = dO:                              */
+/*   dV_j = sum_i P_ij dO_i,  dP_ij = sum_d dO_id V_jd,                      */
+/*   D_i = sum_d dO_id O_id,  dS_ij = P_ij (dP_ij - D_i),                    */
+/*   dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij Q_i.            */
+/* ------------------------------------------------------------------------ */
+
+static double attn_score(const double* Q, const double* K, int64_t d, int64_t i, int64_t j, double scale)
+{
+    double acc = 0.0;
+    int64_t t;
+    for (t = 0; t < d; t++)
+        acc += Q[i * d + t] * K[j * d + t];
+    return scale * acc;
+}
+
+/* Softmax statistics of query row i: m_i and l_i over its visible keys. */
+static void attn_row_stats(const double* Q, const double* K, int64_t L, int64_t d, double scale, int causal,
+                           int64_t i, double* m_out, double* l_out)
+{
+    int64_t j, jend = causal ? i + 1 : L;
+    double m = -INFINITY, l = 0.0;
+    for (j = 0; j < jend; j++) {
+        double sv = attn_score(Q, K, d, i, j, scale);
+        if (sv > m)
+            m = sv;
+    }
+    for (j = 0; j < jend; j++)
+        l += exp(attn_score(Q, K, d, i, j, scale) - m);
+    *m_out = m;
+    *l_out = l;
+}
+
+/* O_i = sum_j P_ij V_j and oa_i = sum_j P_ij |V_j| over keys [0, jend). */
+static void attn_row_out(const double* Q, const double* K, const double* V, int64_t d, double scale, int64_t i,
+                         int64_t jend, double m, double l, double* o, double* oa)
+{
+    int64_t j, t;
+    for (t = 0; t < d; t++) {
+        o[t] = 0.0;
+        oa[t] = 0.0;
+    }
+    for (j = 0; j < jend; j++) {
+        double pij = exp(attn_score(Q, K, d, i, j, scale) - m) / l;
+        for (t = 0; t < d; t++) {
+            o[t] += pij * V[j * d + t];
+            oa[t] += pij * fabs(V[j * d + t]);
+        }
+    }
+}
+
+int orc_attn_fwd_rows(const double* Q, const double* K, const double* V, int64_t L, int64_t d, double scale,
+                      int causal, int64_t nrows, const int64_t* rows, double* O, double* lse, double* pv_abs)
+{
+    int64_t r, j, t;
+    if (!Q || !K || !V || !rows || !O || L <= 0 || d <= 0 || nrows < 0)
+        return -1;
+    for (r = 0; r < nrows; r++) {
+        int64_t i = rows[r], jend;
+        double m, l;
+        if (i < 0 || i >= L)
+            return -1;
+        attn_row_stats(Q, K, L, d, scale, causal, i, &m, &l);
+        for (t = 0; t < d; t++) {
+            O[r * d + t] = 0.0;
+            if (pv_abs)
+                pv_abs[r * d + t] = 0.0;
+        }
+        jend = causal ? i + 1 : L;
+        for (j = 0; j < jend; j++) {
+            double pij = exp(attn_score(Q, K, d, i, j, scale) - m) / l;
+            for (t = 0; t < d; t++) {
+                O[r * d + t] += pij * V[j * d + t];
+                if (pv_abs)
+                    pv_abs[r * d + t] += pij * fabs(V[j * d + t]);
+            }
+        }
+        if (lse)
+            lse[r] = m + log(l);
+    }
+    return 0;
+}
+
+/* dQ of selected query rows (self-contained per row: P_i, dP_i and D_i are
+ * formed from the row's own softmax).  Also returns, per row and feature,
+ * the magnitudes the GPU's rounding acts on:
+ *   ds_abs_k[r][t] = scale * sum_j |dS_ij| |K_jt|
+ *   p_abs_k[r][t]  = scale * sum_j P_ij (|dP_ij| + |D_i|) |K_jt|
+ *   p_k[r][t]      = scale * sum_j P_ij |K_jt|
+ * and dvo[r] = sum_t |dO_it| * sum_j P_ij |V_jt| (the size of D's error). */
+int orc_attn_bwd_dq_rows(const double* Q, const double* K, const double* V, const double* dO, int64_t L, int64_t d,
+                         double scale, int causal, int64_t nrows, const int64_t* rows, double* dQ,
+                         double* ds_abs_k, double* p_abs_k, double* p_k, double* dvo)
+{
+    int64_t r, j, t;
+    double *orow, *oarow;
+    int rc = 0;
+    if (!Q || !K || !V || !dO || !rows || !dQ || L <= 0 || d <= 0 || nrows < 0)
+        return -1;
+    orow = (double*)malloc(2 * (size_t)d * sizeof(double));
+    if (!orow)
+        return -4;
+    oarow = orow + d;
+    for (r = 0; r < nrows; r++) {
+        int64_t i = rows[r], jend;
+        double m, l, D = 0.0, pvo = 0.0;
+        if (i < 0 || i >= L) {
+            rc = -1;
+            break;
+        }
+        attn_row_stats(Q, K, L, d, scale, causal, i, &m, &l);
+        jend = causal ? i + 1 : L;
+        /* D_i = sum_t dO_it O_it, O_i = sum_j P_ij V_j */
+        attn_row_out(Q, K, V, d, scale, i, jend, m, l, orow, oarow);
+        for (t = 0; t < d; t++) {
+            D += dO[i * d + t] * orow[t];
+            pvo += fabs(dO[i * d + t]) * oarow[t];
+        }
+        for (t = 0; t < d; t++) {
+            dQ[r * d + t] = 0.0;
+            if (ds_abs_k) {
+                ds_abs_k[r * d + t] = 0.0;
+                p_abs_k[r * d + t] = 0.0;
+                p_k[r * d + t] = 0.0;
+            }
+        }
+        for (j = 0; j < jend; j++) {
+            double pij = exp(attn_score(Q, K, d, i, j, scale) - m) / l;
+            double dp = 0.0, dsij;
+            for (t = 0; t < d; t++)
+                dp += dO[i * d + t] * V[j * d + t];
+            dsij = pij * (dp - D);
+            for (t = 0; t < d; t++) {
+                dQ[r * d + t] += scale * dsij * K[j * d + t];
+                if (ds_abs_k) {
+                    ds_abs_k[r * d + t] += scale * fabs(dsij) * fabs(K[j * d + t]);
+                    p_abs_k[r * d + t] += scale * pij * (fabs(dp) + fabs(D)) * fabs(K[j * d + t]);
+                    p_k[r * d + t] += scale * pij * fabs(K[j * d + t]);
+                }
+            }
+        }
+        if (dvo)
+            dvo[r] = pvo;
+    }
+    free(orow);
+    return rc;
+}
+
+/* Softmax statistics m_i, l_i of query rows [i0, i1), and, when dO is
+ * given, D_i = sum_t dO_it O_it and dvo_i = sum_t |dO_it| sum_j P_ij |V_jt|. */
+int orc_attn_stats(const double* Q, const double* K, const double* V, const double* dO, int64_t L, int64_t d,
+                   double scale, int causal, int64_t i0, int64_t i1, double* mv, double* lv, double* Dv, double* dvo)
+{
+    int64_t i, t;
+    double *orow, *oarow;
+    if (!Q || !K || !V || !mv || !lv || L <= 0 || d <= 0 || i0 < 0 || i1 > L || i0 > i1)
+        return -1;
+    orow = (double*)malloc(2 * (size_t)d * sizeof(double));
+    if (!orow)
+        return -4;
+    oarow = orow + d;
+    for (i = i0; i < i1; i++) {
+        int64_t jend = causal ? i + 1 : L;
+        attn_row_stats(Q, K, L, d, scale, causal, i, &mv[i], &lv[i]);
+        if (!dO)
+            continue;
+        attn_row_out(Q, K, V, d, scale, i, jend, mv[i], lv[i], orow, oarow);
+        Dv[i] = 0.0;
+        dvo[i] = 0.0;
+        for (t = 0; t < d; t++) {
+            Dv[i] += dO[i * d + t] * orow[t];
+            dvo[i] += fabs(dO[i * d + t]) * oarow[t];
+        }
+    }
+    free(orow);
+    return 0;
+}
+
+/* dK and dV of selected key rows, from every query's statistics (m, l, D and
+ * dvo of orc_attn_stats): the sums run over the queries that see key j.
+ * Magnitudes for the tolerances:
+ *   ds_abs_q[r][t] = scale * sum_i |dS_ij| |Q_it|
+ *   p_abs_q[r][t]  = scale * sum_i P_ij (|dP_ij| + |D_i|) |Q_it|
+ *   pd_q[r][t]     = scale * sum_i P_ij dvo_i |Q_it|
+ *   p_do[r][t]     = sum_i P_ij |dO_it|                 (dV's) */
+int orc_attn_bwd_dkdv_rows(const double* Q, const double* K, const double* V, const double* dO, int64_t L, int64_t d,
+                           double scale, int causal, const double* mv, const double* lv, const double* Dv,
+                           const double* dvo, int64_t nrows, const int64_t* rows, double* dK, double* dV,
+                           double* ds_abs_q, double* p_abs_q, double* pd_q, double* p_do)
+{
+    int64_t r, i, j, t;
+    if (!Q || !K || !V || !dO || !rows || !dK || !dV || !mv || !lv || !Dv || !dvo || L <= 0 || d <= 0 || nrows < 0)
+        return -1;
+    for (r = 0; r < nrows; r++) {
+        j = rows[r];
+        if (j < 0 || j >= L)
+            return -1;
+        for (t = 0; t < d; t++) {
+            dK[r * d + t] = 0.0;
+            dV[r * d + t] = 0.0;
+            if (ds_abs_q) {
+                ds_abs_q[r * d + t] = 0.0;
+                p_abs_q[r * d + t] = 0.0;
+                pd_q[r * d + t] = 0.0;
+                p_do[r * d + t] = 0.0;
+            }
+        }
+        for (i = causal ? j : 0; i < L; i++) {
+            double pij = exp(attn_score(Q, K, d, i, j, scale) - mv[i]) / lv[i];
+            double dp = 0.0, dsij;
+            for (t = 0; t < d; t++)
+                dp += dO[i * d + t] * V[j * d + t];
+            dsij = pij * (dp - Dv[i]);
+            for (t = 0; t < d; t++) {
+                dK[r * d + t] += scale * dsij * Q[i * d + t];
+                dV[r * d + t] += pij * dO[i * d + t];
+                if (ds_abs_q) {
+                    ds_abs_q[r * d + t] += scale * fabs(dsij) * fabs(Q[i * d + t]);
+                    p_abs_q[r * d + t] += scale * pij * (fabs(dp) + fabs(Dv[i])) * fabs(Q[i * d + t]);
+                    pd_q[r * d + t] += scale * pij * dvo[i] * fabs(Q[i * d + t]);
+                    p_do[r * d + t] += pij * fabs(dO[i * d + t]);
+                }
+            }
+        }
     }
     return 0;
 }

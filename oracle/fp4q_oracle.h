@@ -130,6 +130,27 @@ int orc_gemm_sampled(int op, const double* A, int64_t a_rows, int64_t a_cols,
                      int64_t n, const int64_t* ci, const int64_t* cj,
                      double* C, double* bound);
 
+/* Attention of one head with MXFP8 queries and keys (Sec. 3.2 "MXFP8
+ * Attention"): Q, K [L x d] dequantized MXFP8 values, V [L x d], scale the
+ * score factor, causal: key j visible to query i iff j <= i.  Row-major fp64.
+ * fwd_rows: O and lse (natural log) of the selected query rows, and
+ *   pv_abs = sum_j P_ij |V_jt| (may be NULL).
+ * stats: m_i, l_i (and with dO, D_i and dvo_i) of query rows [i0, i1).
+ * bwd_dq_rows / bwd_dkdv_rows: the gradient for dL/dO = dO at selected query
+ *   rows (dQ) or key rows (dK, dV; from every row's stats), with the
+ *   magnitudes the parity tolerance is built from (may be NULL as a group). */
+int orc_attn_fwd_rows(const double* Q, const double* K, const double* V, int64_t L, int64_t d, double scale,
+                      int causal, int64_t nrows, const int64_t* rows, double* O, double* lse, double* pv_abs);
+int orc_attn_stats(const double* Q, const double* K, const double* V, const double* dO, int64_t L, int64_t d,
+                   double scale, int causal, int64_t i0, int64_t i1, double* mv, double* lv, double* Dv, double* dvo);
+int orc_attn_bwd_dq_rows(const double* Q, const double* K, const double* V, const double* dO, int64_t L, int64_t d,
+                         double scale, int causal, int64_t nrows, const int64_t* rows, double* dQ,
+                         double* ds_abs_k, double* p_abs_k, double* p_k, double* dvo);
+int orc_attn_bwd_dkdv_rows(const double* Q, const double* K, const double* V, const double* dO, int64_t L, int64_t d,
+                           double scale, int causal, const double* mv, const double* lv, const double* Dv,
+                           const double* dvo, int64_t nrows, const int64_t* rows, double* dK, double* dV,
+                           double* ds_abs_q, double* p_abs_q, double* pd_q, double* p_do);
+
 #ifdef __cplusplus
 }
 #endif

@@ -304,18 +304,22 @@ def side_1b(torch, fq, wl, iters, warmup):
     return out
 
 
-def side_block64(torch, fq, wl, iters, warmup):
-    """The 7B layer step with 64x64 scale blocks beside the same step with
-    32x32 blocks, both timed eagerly with per-launch events: the block-size
-    throughput comparison of the page's Table 4, measured."""
-    out = {"workload": "7b-linear-layer-step with 64x64 and with 32x32 scale blocks (eager, per-launch events)"}
-    for b in (32, 64):
+def side_blocks(torch, fq, wl, iters, warmup):
+    """The 7B layer step with 8x8, 16x16, 32x32 and 64x64 scale blocks, each
+    timed eagerly with per-launch events: the block-size throughput comparison
+    of the page's Table 4, measured.  16x16 and 8x8 blocks split every 32-K
+    MFMA into 2 and 4 MFMAs (one per sub-block, each with its own scales)."""
+    out = {"workload": "7b-linear-layer-step with 8x8, 16x16, 32x32 and 64x64 scale blocks "
+                       "(eager, per-launch events)"}
+    for b in (32, 64, 16, 8):
         step = Step(wl.config_7b(), torch, fq, block=b)
         out["b%d" % b] = _eager_step(step, torch, iters, warmup)
         del step
         torch.cuda.empty_cache()
-    for key in ("ms_per_step", "quant_ms", "gemm_ms"):
-        out[key + "_b64_over_b32"] = round(out["b64"][key] / out["b32"][key], 4)
+    for b in (64, 16, 8):
+        for key in ("ms_per_step", "quant_ms", "gemm_ms"):
+            out["%s_b%d_over_b32" % (key, b)] = round(out["b%d" % b][key] / out["b32"][key], 4)
+        out["throughput_b%d_rel_b32" % b] = round(out["b32"]["ms_per_step"] / out["b%d" % b]["ms_per_step"], 4)
     return out
 
 
@@ -813,7 +817,7 @@ def main():
     if not args.no_side_paths:
         side = {}
         for name, fn in (("1b", side_1b), ("fused_chain", side_fused_chain), ("moe", side_moe), ("attn", side_attn),
-                         ("block64", side_block64),
+                         ("blocks", side_blocks),
                          ("act1d", side_act1d), ("wgrad_acc", side_wgrad_acc), ("bf16_out", side_bf16_out)):
             if args.side and name not in args.side.split(","):
                 continue

@@ -1300,7 +1300,13 @@ hipError_t launch_sub(const GemmArgs& g, bool accumulate, hipStream_t s)
         c.sa = g.sa + (A_ST ? (int64_t)(k0 / kB) * g.lds_a : k0 / kB);
         c.sb = g.sb + (B_ST ? (int64_t)(k0 / kB) * g.lds_b : k0 / kB);
         const bool acc = accumulate || k0 > 0;
-        const bool kt = c.K % 256 != 0;
+        // A chunk after the first starts its operands k0/2 bytes into each
+        // row while the buffer range stays a_rows * ld bytes from there, so
+        // the range would reach past the end of the planes: such chunks take
+        // the K-checked variant, whose loads past the chunk's K read as zero
+        // and never touch memory.  The first chunk's loads past its K stay
+        // inside the row or fall past the range and read as zero.
+        const bool kt = k0 > 0 || c.K % 256 != 0;
         hipError_t e = acc ? (kt ? launch_sub_k<SUB, A_ST, B_ST, true, true>(c, s)
                                  : launch_sub_k<SUB, A_ST, B_ST, false, true>(c, s))
                            : (kt ? launch_sub_k<SUB, A_ST, B_ST, true, false>(c, s)

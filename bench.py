@@ -568,6 +568,37 @@ def side_attn(torch, fq, wl, iters, warmup):
     out["S_bf16_ms"] = round(s16, 4)
     out["S_bf16_TFLOP/s"] = round(2.0 * B * Hh * L * L * D / (s16 / 1e3) / 1e12, 1)
     out["S_bf16_write_GB/s"] = round(2.0 * B * Hh * L * L / (s16 / 1e3) / 1e9, 1)
+    del S16
+    torch.cuda.empty_cache()
+    out["fused"] = side_attn_fused(torch, fq, bq, bk, qq, qk, B * Hh, L, D, iters, warmup)
+    return out
+
+
+def side_attn_fused(torch, fq, bq, bk, qq, qk, bh, L, D, iters, warmup):
+    """The fused MXFP8 attention on the same Q, K (V and dO drawn N(0,1) and
+    N(0,0.1), bf16): forward (O bf16, lse) and backward (dQ, dK, dV fp32),
+    causal and full, scores never written.  Algorithmic flops: forward
+    2 products (4 bh L^2 d), backward 5 (10 bh L^2 d: the score recompute,
+    dP, dV, dK, dQ), halved for causal."""
+    g = torch.Generator(device="cuda").manual_seed(5)
+    v = torch.randn((bh * L, D), device="cuda", generator=g).to(torch.bfloat16)
+    dout = (0.1 * torch.randn((bh * L, D), device="cuda", generator=g)).to(torch.bfloat16)
+    o = torch.empty((bh * L, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(bh * L, dtype=torch.float32, device="cuda")
+    grads = [torch.empty((bh * L, D), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = torch.empty(bh * L, dtype=torch.float32, device="cuda")
+    out = {"workload": "fused attention, MXFP8 Q and K [4, 32, 4096, 128], bf16 V and dO, O bf16, grads fp32; "
+                       "scores never written"}
+    for causal in (True, False):
+        key = "causal" if causal else "full"
+        ms = _timed_launches(torch, [
+            ("fwd", lambda: fq.fp4q_attn_fwd(qq, qk, v, bh, L, causal=causal, o=o, lse=lse)),
+            ("bwd", lambda: fq.fp4q_attn_bwd(qq, qk, v, o, lse, dout, bh, L, causal=causal, dq=grads[0], dk=grads[1],
+                                             dv=grads[2], workspace=ws))], iters, warmup)
+        f = (0.5 if causal else 1.0) * bh * L * L * D
+        out[key] = {"fwd_ms": round(ms["fwd"], 4), "bwd_ms": round(ms["bwd"], 4),
+                    "fwd_TFLOP/s": round(4 * f / (ms["fwd"] / 1e3) / 1e12, 1),
+                    "bwd_TFLOP/s": round(10 * f / (ms["bwd"] / 1e3) / 1e12, 1)}
     return out
 
 

@@ -99,12 +99,16 @@ def _load():
                             I64, ctypes.POINTER(_Groups), P]
     L.fp4q_gemm_quant.argtypes = [ctypes.c_int, ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc),
                                   ctypes.POINTER(_QDesc), ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32, P, P]
+    L.fp4q_attn_fwd.argtypes = [ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc), P, I64, P, I64, ctypes.c_int, P,
+                                I64, I64, ctypes.c_float, ctypes.c_int, P]
+    L.fp4q_attn_bwd.argtypes = [ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc), P, I64, P, I64, ctypes.c_int, P,
+                                P, I64, P, P, P, I64, P, I64, I64, ctypes.c_float, ctypes.c_int, P]
     L.fp4q_dequant.argtypes = [ctypes.POINTER(_QDesc), ctypes.c_int, ctypes.c_int, P, I64, P]
     L.fp4q_probe_mfma_fp4.argtypes = [I64, ctypes.c_int, P, P, I64, P]
     L.fp4q_probe_copy.argtypes = [P, P, I64, ctypes.c_int, P]
     for fn in ("fp4q_quant2d_sizes", "fp4q_quant2d", "fp4q_quant2d_batch", "fp4q_quant2d_batch_ex",
                "fp4q_quant1d_mxfp8",
-               "fp4q_gemm", "fp4q_gemm_ex", "fp4q_gemm_quant", "fp4q_dequant", "fp4q_probe_mfma_fp4",
+               "fp4q_gemm", "fp4q_gemm_ex", "fp4q_gemm_quant", "fp4q_attn_fwd", "fp4q_attn_bwd", "fp4q_dequant", "fp4q_probe_mfma_fp4",
                "fp4q_probe_copy"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -399,6 +403,65 @@ def fp4q_gemm_quant(op, a: QTensor, b: QTensor, out: Optional[QTensor] = None, r
                                    ROUND[round_mode], int(seed) & ((1 << 64) - 1), int(stream_id) & 0xFFFFFFFF,
                                    _seed_dev_ptr(seed_dev), _stream_ptr(stream)), "fp4q_gemm_quant")
     return out
+
+
+def _check_rows(t, rows, what, dtypes):
+    if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 2 or t.shape[0] != rows
+            or t.shape[1] != 128 or t.stride(1) != 1 or t.dtype not in dtypes):
+        raise Fp4qError("%s must be a CUDA tensor [%d x 128] with contiguous rows, dtype in %s"
+                        % (what, rows, [str(d) for d in dtypes]))
+
+
+def fp4q_attn_fwd(q: QTensor, k: QTensor, v, bh, seq_len, scale=128 ** -0.5, causal=True, out_dtype=torch.bfloat16,
+                  o=None, lse=None, stream=None):
+    """Fused attention forward with MXFP8 Q, K (from fp4q_quant1d_mxfp8 of
+    [bh*seq_len x 128] head-major rows) and bf16 V [bh*seq_len x 128]:
+    O = softmax(scale * Q K^T) V without writing the scores.  Returns (O, lse)
+    with lse the natural-log log-sum-exp per row (fp32 [bh*seq_len])."""
+    n = bh * seq_len
+    _check_rows(v, n, "v", (torch.bfloat16,))
+    if o is None:
+        o = torch.empty((n, 128), dtype=out_dtype, device=v.device)
+    _check_rows(o, n, "o", (torch.bfloat16, torch.float32))
+    if lse is None:
+        lse = torch.empty(n, dtype=torch.float32, device=v.device)
+    if lse.dtype != torch.float32 or not lse.is_cuda or lse.numel() != n or not lse.is_contiguous():
+        raise Fp4qError("lse must be a contiguous float32 CUDA tensor of bh*seq_len")
+    dq, dk = q.desc(), k.desc()
+    _check(_load().fp4q_attn_fwd(ctypes.byref(dq), ctypes.byref(dk), _ptr(v), v.stride(0), _ptr(o), o.stride(0),
+                                 DT_BF16 if o.dtype == torch.bfloat16 else DT_F32, _ptr(lse), bh, seq_len,
+                                 float(scale), 1 if causal else 0, _stream_ptr(stream)), "fp4q_attn_fwd")
+    return o, lse
+
+
+def fp4q_attn_bwd(q: QTensor, k: QTensor, v, o, lse, dout, bh, seq_len, scale=128 ** -0.5, causal=True,
+                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dQ, dK, dV), fp32 [bh*seq_len x 128], of the fused
+    attention for dL/dO = dout (bf16), from fp4q_attn_fwd's O and lse."""
+    n = bh * seq_len
+    _check_rows(v, n, "v", (torch.bfloat16,))
+    _check_rows(o, n, "o", (torch.bfloat16, torch.float32))
+    _check_rows(dout, n, "dout", (torch.bfloat16,))
+    if lse.dtype != torch.float32 or not lse.is_cuda or lse.numel() != n or not lse.is_contiguous():
+        raise Fp4qError("lse must be a contiguous float32 CUDA tensor of bh*seq_len")
+    outs = []
+    for g in (dq, dk, dv):
+        g = torch.empty((n, 128), dtype=torch.float32, device=v.device) if g is None else g
+        _check_rows(g, n, "gradient", (torch.float32,))
+        outs.append(g)
+    if len({g.stride(0) for g in outs}) != 1:
+        raise Fp4qError("dq, dk and dv must share one row stride")
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.float32, device=v.device)
+    if workspace.dtype != torch.float32 or not workspace.is_cuda or workspace.numel() < n:
+        raise Fp4qError("workspace must be a float32 CUDA tensor of bh*seq_len")
+    dqd, dkd = q.desc(), k.desc()
+    _check(_load().fp4q_attn_bwd(ctypes.byref(dqd), ctypes.byref(dkd), _ptr(v), v.stride(0), _ptr(o), o.stride(0),
+                                 DT_BF16 if o.dtype == torch.bfloat16 else DT_F32, _ptr(lse), _ptr(dout),
+                                 dout.stride(0), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), outs[0].stride(0),
+                                 _ptr(workspace), bh, seq_len, float(scale), 1 if causal else 0, _stream_ptr(stream)),
+           "fp4q_attn_bwd")
+    return tuple(outs)
 
 
 def fp4q_dequant(q: QTensor, transposed=False, out_dtype=torch.float32, out=None, stream=None):

@@ -14,7 +14,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp4q.so")
 SOURCES = ["gemm_plain.hip", "gemm_grouped.hip", "gemm_bf16.hip", "gemm_acc.hip", "gemm_1d.hip", "gemm_quant.hip",
            "gemm_sub16.hip", "gemm_sub8.hip", "gemm.hip",
-           "api.hip", "quant2d.hip", "mxfp8.hip", "dequant.hip", "probe.hip"]
+           "attn.hip", "api.hip", "quant2d.hip", "mxfp8.hip", "dequant.hip", "probe.hip"]
 ARCH = os.environ.get("FP4Q_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -693,6 +693,102 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
                       "fp4q_dequant");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the attention entry points: MXFP8 Q and K of
+// bh*seq_len rows and 128 columns, aligned for the kernels' vector accesses.
+int check_attn(const char* fn, const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, int64_t ldv,
+               const void* o, int64_t ldo, int o_dtype, const float* lse, int64_t bh, int64_t seq_len, float scale,
+               int causal, fp4q::AttnArgs& a)
+{
+    int rc;
+    if ((rc = check_fp8_tensor(q, fn)) || (rc = check_fp8_tensor(k, fn)))
+        return rc;
+    if (bh < 1 || seq_len < 1 || bh > 65535 || seq_len > (1 << 24) || bh * seq_len > ((int64_t)1 << 31))
+        return fail(FP4Q_EINVAL, "%s: bh %lld and seq_len %lld out of range", fn, (long long)bh, (long long)seq_len);
+    if (q->cols != 128 || k->cols != 128)
+        return fail(FP4Q_EUNSUPPORTED, "%s: head dimension 128 only (got %lld, %lld)", fn, (long long)q->cols,
+                    (long long)k->cols);
+    if (q->rows != bh * seq_len || k->rows != bh * seq_len || q->batch != 1 || k->batch != 1)
+        return fail(FP4Q_EINVAL, "%s: q and k need bh*seq_len rows and batch 1", fn);
+    if (q->ld_s % 4 || k->ld_s % 4 || (reinterpret_cast<uintptr_t>(q->scales) & 3u) ||
+        (reinterpret_cast<uintptr_t>(k->scales) & 3u))
+        return fail(FP4Q_EINVAL, "%s: scale grids need 4-byte aligned rows", fn);
+    if (!v || !o || !lse)
+        return fail(FP4Q_EINVAL, "%s: null v, o or lse", fn);
+    if (ldv < 128 || ldv % 8 || !aligned16(v))
+        return fail(FP4Q_EINVAL, "%s: v needs ldv >= 128, a multiple of 8, and 16-byte alignment", fn);
+    if (o_dtype != FP4Q_DT_BF16 && o_dtype != FP4Q_DT_F32)
+        return fail(FP4Q_EINVAL, "%s: o_dtype %d", fn, o_dtype);
+    if (ldo < 128 || ldo % 8 || !aligned16(o))
+        return fail(FP4Q_EINVAL, "%s: o needs ldo >= 128, a multiple of 8, and 16-byte alignment", fn);
+    if (!(scale > 0.0f) || !(scale < 1e30f))
+        return fail(FP4Q_EINVAL, "%s: scale must be positive and finite", fn);
+    if (causal != 0 && causal != 1)
+        return fail(FP4Q_EINVAL, "%s: causal must be 0 or 1", fn);
+    a = fp4q::AttnArgs{};
+    a.qc = q->codes;
+    a.ldq = q->ld;
+    a.qs = q->scales;
+    a.ldqs = q->ld_s;
+    a.kc = k->codes;
+    a.ldk = k->ld;
+    a.ks = k->scales;
+    a.ldks = k->ld_s;
+    a.v = static_cast<const uint16_t*>(v);
+    a.ldv = ldv;
+    a.o = const_cast<void*>(o);
+    a.ldo = ldo;
+    a.lse = const_cast<float*>(lse);
+    a.bh = (int)bh;
+    a.L = (int)seq_len;
+    a.scale = scale;
+    a.causal = causal;
+    a.o_bf16 = o_dtype == FP4Q_DT_BF16;
+    return FP4Q_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int fp4q_attn_fwd(const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, int64_t ldv, void* o, int64_t ldo,
+                  int o_dtype, float* lse, int64_t bh, int64_t seq_len, float scale, int causal, void* hip_stream)
+{
+    fp4q::AttnArgs a;
+    int rc = check_attn("fp4q_attn_fwd", q, k, v, ldv, o, ldo, o_dtype, lse, bh, seq_len, scale, causal, a);
+    if (rc)
+        return rc;
+    return hip_status(fp4q::launch_attn_fwd(a, static_cast<hipStream_t>(hip_stream)), "fp4q_attn_fwd");
+}
+
+int fp4q_attn_bwd(const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, int64_t ldv, const void* o,
+                  int64_t ldo, int o_dtype, const float* lse, const void* dout, int64_t lddo, float* dq, float* dk,
+                  float* dv, int64_t ldg, float* workspace, int64_t bh, int64_t seq_len, float scale, int causal,
+                  void* hip_stream)
+{
+    fp4q::AttnArgs a;
+    int rc = check_attn("fp4q_attn_bwd", q, k, v, ldv, o, ldo, o_dtype, lse, bh, seq_len, scale, causal, a);
+    if (rc)
+        return rc;
+    if (!dout || lddo < 128 || lddo % 8 || !aligned16(dout))
+        return fail(FP4Q_EINVAL, "fp4q_attn_bwd: dout needs lddo >= 128, a multiple of 8, and 16-byte alignment");
+    if (!dq || !dk || !dv || ldg < 128 || ldg % 4 || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return fail(FP4Q_EINVAL, "fp4q_attn_bwd: dq, dk, dv need ldg >= 128, a multiple of 4, 16-byte alignment");
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        return fail(FP4Q_EINVAL, "fp4q_attn_bwd: workspace of bh*seq_len floats required");
+    a.dout = static_cast<const uint16_t*>(dout);
+    a.lddo = lddo;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.ldg = ldg;
+    a.delta = workspace;
+    return hip_status(fp4q::launch_attn_bwd(a, static_cast<hipStream_t>(hip_stream)), "fp4q_attn_bwd");
+}
+
 int fp4q_probe_mfma_fp4(int64_t iters, int workgroups, float* sink, const uint8_t* codes, int64_t code_bytes,
                         void* hip_stream)
 {

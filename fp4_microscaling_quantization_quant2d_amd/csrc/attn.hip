@@ -1,0 +1,770 @@
+// Fused attention with MXFP8 queries and keys, forward and backward, for
+// gfx950.  "Stable FP4 Training via Transposition-Invariant Block
+// Quantization", Sec. 3.2 "MXFP8 Attention" and Fig. 3: Q and K enter the
+// score product in MXFP8 (E4M3, one E8M0 scale per 1x32 group along the head
+// dimension); the attention around it is standard scaled dot-product
+// attention.  The score matrix S never leaves the chip.
+//
+// Products.  An E4M3 code times its E8M0 scale is exactly a bf16 value (4
+// significant bits), so Q and K are converted to bf16 with the scale folded
+// in and every score product q_d * k_d is formed exactly by the bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16) and summed in fp32.  The probabilities P (and
+// in the backward dS) are rounded to bf16 to multiply V (dO, Q, K), which are
+// bf16 already; accumulation is fp32 throughout.
+//
+// Orientation.  The forward computes S^T = K Q^T per 32-key x 32-query
+// block, so a lane holds one query's scores in registers (keys
+// 8(r/4) + 4h + r%4 of register r, h = lane/32) and the softmax reductions
+// are register reductions plus one exchange with lane l ^ 32.  The same
+// registers are the B operand of O^T += V^T P^T once the MFMA's contraction
+// index (h, p) is mapped to key 8(2t + p/4) + 4h + p%4 of each 16-key step t
+// -- a permutation of the keys that the A operand V^T follows, read from a
+// key-pair-transposed V tile in LDS.  The backward uses the same device:
+// every product is arranged so that the operand built from a score-shaped
+// tile is the one whose contraction runs over that tile's rows.
+//
+// Head dimension 128; sequence length any (the last key and query blocks
+// are masked); full or causal.  The log-sum-exp of every query row (natural
+// log) is stored for the backward.
+#include "fp4q_launch.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
+
+namespace fp4q {
+
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;             // head dimension
+constexpr int kThreads = 256;       // 4 waves
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename F, int... I>
+__device__ __forceinline__ void sfor_impl(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void sfor(F&& f)
+{
+    sfor_impl(f, std::make_integer_sequence<int, N>());
+}
+
+// 2^(b - 127) as a float (b = 0: the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_f32(uint32_t b)
+{
+    return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// 8 E4M3 bytes times one E8M0 scale -> 8 bf16 (exact).
+__device__ __forceinline__ v8bf cvt8_e4m3(v2u raw, float scale)
+{
+    const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, false);
+    const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, true);
+    const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, false);
+    const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, true);
+    return __builtin_bit_cast(v8bf, (v4u){__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
+                                          __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3)});
+}
+
+// Two floats -> one dword of two bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
+{
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f zero16()
+{
+    v16f z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        z[r] = 0.0f;
+    return z;
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+constexpr int kFwdQ = 128;                  // queries per workgroup (32 per wave)
+constexpr int kFwdK = 64;                   // keys per step
+constexpr int kKPitch = 136;                // bytes per key row of E4M3 codes in LDS
+constexpr int kVtPitch = 144;               // bytes per d row of the key-pair-transposed V tile
+constexpr int kFwdKBytes = kFwdK * kKPitch;           // 8704
+constexpr int kFwdSBytes = kFwdK * 4;                 // 256: one scale dword per key
+constexpr int kFwdVBytes = kD * kVtPitch;             // 18432
+constexpr int kFwdBuf = kFwdKBytes + kFwdSBytes + kFwdVBytes;
+
+// Registers holding one key block on its way from memory to LDS.
+struct FwdStage {
+    v4u k[2];
+    v4u v[2][2];
+    uint32_t ks;
+};
+
+__device__ __forceinline__ void fwd_load(FwdStage& st, const AttnArgs& a, int64_t head_row, int k0)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = t + kThreads * i, key = u >> 3, c = u & 7;
+        st.k[i] = k0 + key < a.L ? *reinterpret_cast<const v4u*>(a.kc + (head_row + k0 + key) * a.ldk + 16 * c)
+                                 : (v4u){0u, 0u, 0u, 0u};
+        const int p = u & 31, dc = u >> 5;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int key2 = k0 + 2 * p + e;
+            st.v[i][e] = key2 < a.L ? *reinterpret_cast<const v4u*>(a.v + (head_row + key2) * a.ldv + 8 * dc)
+                                    : (v4u){0u, 0u, 0u, 0u};
+        }
+    }
+    st.ks = t < kFwdK && k0 + t < a.L ? *reinterpret_cast<const uint32_t*>(a.ks + (head_row + k0 + t) * a.ldks) : 0u;
+}
+
+__device__ __forceinline__ void fwd_store(const FwdStage& st, uint8_t* buf)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = t + kThreads * i, key = u >> 3, c = u & 7;
+        *reinterpret_cast<v4u*>(buf + key * kKPitch + 16 * c) = st.k[i];
+        // V^T: dword (V[2p][d], V[2p+1][d]) at row d, keys 2p..2p+1
+        const int p = u & 31, dc = u >> 5;
+        uint8_t* vt = buf + kFwdKBytes + kFwdSBytes + (8 * dc) * kVtPitch + 4 * p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = st.v[i][0][e], hi = st.v[i][1][e];
+            *reinterpret_cast<uint32_t*>(vt + (2 * e) * kVtPitch) = (lo & 0xFFFFu) | (hi << 16);
+            *reinterpret_cast<uint32_t*>(vt + (2 * e + 1) * kVtPitch) = (lo >> 16) | (hi & 0xFFFF0000u);
+        }
+    }
+    if (t < kFwdK)
+        *reinterpret_cast<uint32_t*>(buf + kFwdKBytes + 4 * t) = st.ks;
+}
+
+template <bool CAUSAL, bool OBF>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFwdBuf];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int nqb = (a.L + kFwdQ - 1) / kFwdQ;
+    const int qb = nqb - 1 - (int)blockIdx.x;  // the longest causal rows first
+    const int64_t head_row = (int64_t)blockIdx.y * a.L;
+    const int q0 = qb * kFwdQ + 32 * wave;      // the wave's first query
+    const int q = q0 + l32;                     // this lane's query
+
+    // Q of this lane's query as the B operand of S^T = K Q^T: 8 steps of d.
+    v8bf qb16[8];
+    {
+        const bool ok = q < a.L;
+        const uint32_t sc = ok ? *reinterpret_cast<const uint32_t*>(a.qs + (head_row + q) * a.ldqs) : 0u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const v2u raw = ok ? *reinterpret_cast<const v2u*>(a.qc + (head_row + q) * a.ldq + 16 * t + 8 * h)
+                               : (v2u){0u, 0u};
+            qb16[t] = cvt8_e4m3(raw, e8m0_f32((sc >> (8 * (t >> 1))) & 0xFFu));
+        }
+    }
+    v16f o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = zero16();
+    float m = -INFINITY, l = 0.0f;
+    const float c = a.scale * kLog2e;           // scores in log2 units
+
+    const int nkb_all = (a.L + kFwdK - 1) / kFwdK;
+    const int nkb = CAUSAL ? min(nkb_all, (qb * kFwdQ + kFwdQ - 1) / kFwdK + 1) : nkb_all;
+    FwdStage st;
+    fwd_load(st, a, head_row, 0);
+    fwd_store(st, lds);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const uint8_t* buf = lds + (kb & 1) * kFwdBuf;
+        const int k0 = kb * kFwdK;
+        if (kb + 1 < nkb)
+            fwd_load(st, a, head_row, k0 + kFwdK);
+
+        // S^T for the 64 keys: two 32-key sub-blocks.
+        v16f s[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int key = 32 * sb + l32;
+            const uint32_t ksc = *reinterpret_cast<const uint32_t*>(buf + kFwdKBytes + 4 * key);
+            s[sb] = zero16();
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const v2u raw = *reinterpret_cast<const v2u*>(buf + key * kKPitch + 16 * t + 8 * h);
+                s[sb] = mfma_bf16(cvt8_e4m3(raw, e8m0_f32((ksc >> (8 * (t >> 1))) & 0xFFu)), qb16[t], s[sb]);
+            }
+        }
+        // mask keys past the sequence and (causal) after the query
+        const bool edge = k0 + kFwdK > a.L || (CAUSAL && k0 + kFwdK - 1 > q0);
+        if (edge) {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (key >= a.L || (CAUSAL && key > q))
+                        s[sb][r] = -INFINITY;
+                }
+        }
+        // online softmax of this lane's query
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, s[sb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(c * (m - m_use));
+        const float cm = c * m_use;
+        float rs = 0.0f;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[sb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(c, s[sb][r], -cm));
+                rs += s[sb][r];
+            }
+        rs += __shfl_xor(rs, 32);
+        l = l * alpha + rs;
+        m = m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o[i][r] *= alpha;
+        // O^T += V^T P^T over four 16-key steps
+        const uint8_t* vt = buf + kFwdKBytes + kFwdSBytes;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int sb = t4 >> 1, tp = t4 & 1;
+            const v4u pw = {pack_bf16(s[sb][8 * tp + 0], s[sb][8 * tp + 1]), pack_bf16(s[sb][8 * tp + 2], s[sb][8 * tp + 3]),
+                            pack_bf16(s[sb][8 * tp + 4], s[sb][8 * tp + 5]), pack_bf16(s[sb][8 * tp + 6], s[sb][8 * tp + 7])};
+            const v8bf pb = __builtin_bit_cast(v8bf, pw);
+            const int kk = 32 * sb + 16 * tp + 4 * h;   // keys kk..kk+3 and kk+8..kk+11
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const uint8_t* row = vt + (32 * db + l32) * kVtPitch + 2 * kk;
+                const v2u lo = *reinterpret_cast<const v2u*>(row);
+                const v2u hi = *reinterpret_cast<const v2u*>(row + 16);
+                o[db] = mfma_bf16(__builtin_bit_cast(v8bf, (v4u){lo.x, lo.y, hi.x, hi.y}), pb, o[db]);
+            }
+        }
+        if (kb + 1 < nkb) {
+            __syncthreads();   // every wave is done with the other buffer
+            fwd_store(st, lds + ((kb + 1) & 1) * kFwdBuf);
+            __syncthreads();
+        }
+    }
+    // O = O^T / l; lse = ln(l) + scale * m
+    if (q < a.L) {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = 32 * db + 8 * g4 + 4 * h;
+                const float x0 = o[db][4 * g4] * inv, x1 = o[db][4 * g4 + 1] * inv;
+                const float x2 = o[db][4 * g4 + 2] * inv, x3 = o[db][4 * g4 + 3] * inv;
+                if (OBF) {
+                    v2u w = {pack_bf16(x0, x1), pack_bf16(x2, x3)};
+                    *reinterpret_cast<v2u*>(reinterpret_cast<__bf16*>(a.o) + (head_row + q) * a.ldo + d) = w;
+                } else {
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + (head_row + q) * a.ldo + d) =
+                        make_float4(x0, x1, x2, x3);
+                }
+            }
+        if (h == 0)
+            a.lse[head_row + q] = (__builtin_amdgcn_logf(l) + c * m) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward.  D_i = sum_d dO_id O_id first (one thread per row), then
+//   dQ kernel   (128 queries per workgroup, over key blocks of 64):
+//     S^T = K Q^T, P^T = exp2(c S^T - lse2), dP^T = V dO^T,
+//     dS^T = P^T (dP^T - D), dQ^T += K^T dS^T;
+//   dK/dV kernel (128 keys per workgroup, over query blocks of 64):
+//     S = Q K^T, P = exp2(c S - lse2), dP = dO V^T, dS = P (dP - D),
+//     dV += P^T dO, dK += dS^T Q.
+// Both recompute the scores, so no partial sums cross workgroups.
+// ---------------------------------------------------------------------------
+template <bool OBF>
+__global__ __launch_bounds__(kThreads) void attn_delta_kernel(AttnArgs a)
+{
+    const int64_t row = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (row >= (int64_t)a.bh * a.L)
+        return;
+    const uint16_t* g = a.dout + row * a.lddo;
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < kD / 8; ++c) {
+        const v4u gw = *reinterpret_cast<const v4u*>(g + 8 * c);
+        float ov[8];
+        if (OBF) {
+            const v4u ow = *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(a.o) + row * a.ldo + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ov[2 * e] = __uint_as_float(ow[e] << 16);
+                ov[2 * e + 1] = __uint_as_float(ow[e] & 0xFFFF0000u);
+            }
+        } else {
+            const float* op = reinterpret_cast<const float*>(a.o) + row * a.ldo + 8 * c;
+            const float4 x0 = *reinterpret_cast<const float4*>(op), x1 = *reinterpret_cast<const float4*>(op + 4);
+            ov[0] = x0.x; ov[1] = x0.y; ov[2] = x0.z; ov[3] = x0.w;
+            ov[4] = x1.x; ov[5] = x1.y; ov[6] = x1.z; ov[7] = x1.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = __builtin_fmaf(__uint_as_float(gw[e] << 16), ov[2 * e], acc);
+            acc = __builtin_fmaf(__uint_as_float(gw[e] & 0xFFFF0000u), ov[2 * e + 1], acc);
+        }
+    }
+    a.delta[row] = acc;
+}
+
+// Pairs of rows of a [64 x 128] tile, transposed into bf16 dwords: row d of
+// the transposed tile holds, at dword p, (X[2p][d], X[2p+1][d]).  `lo`, `hi`:
+// 8 bf16 (one d-chunk of 8) of rows 2p and 2p+1.
+__device__ __forceinline__ void store_pair_t(uint8_t* tt, int pitch, int dchunk, int p, v4u lo, v4u hi)
+{
+    uint8_t* base = tt + (8 * dchunk) * pitch + 4 * p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint32_t*>(base + (2 * e) * pitch) = (lo[e] & 0xFFFFu) | (hi[e] << 16);
+        *reinterpret_cast<uint32_t*>(base + (2 * e + 1) * pitch) = (lo[e] >> 16) | (hi[e] & 0xFFFF0000u);
+    }
+}
+
+// The 8-value A operand of a product whose contraction runs over the rows of
+// a key-pair-transposed tile: row `row`, 16-element step covering tile rows
+// [32 sb + 16 tp, +16), this lane half's permuted 8 of them.
+__device__ __forceinline__ v8bf read_pair_t(const uint8_t* tt, int pitch, int row, int sb, int tp, int h)
+{
+    const uint8_t* p = tt + row * pitch + 2 * (32 * sb + 16 * tp + 4 * h);
+    const v2u lo = *reinterpret_cast<const v2u*>(p);
+    const v2u hi = *reinterpret_cast<const v2u*>(p + 16);
+    return __builtin_bit_cast(v8bf, (v4u){lo.x, lo.y, hi.x, hi.y});
+}
+
+// Registers of a score-shaped tile (16 of them, rows 8(r/4) + 4h + r%4),
+// its 16-row step tp as the 8-value operand of the next product, in bf16.
+__device__ __forceinline__ v8bf pack_step(const v16f& x, int tp)
+{
+    const v4u w = {pack_bf16(x[8 * tp + 0], x[8 * tp + 1]), pack_bf16(x[8 * tp + 2], x[8 * tp + 3]),
+                   pack_bf16(x[8 * tp + 4], x[8 * tp + 5]), pack_bf16(x[8 * tp + 6], x[8 * tp + 7])};
+    return __builtin_bit_cast(v8bf, w);
+}
+
+// ---- dQ ----
+constexpr int kDqQ = 128;                  // queries per workgroup
+constexpr int kDqK = 64;                   // keys per step
+constexpr int kRowPitch = 272;             // bytes per row of a row-major bf16 [64 x 128] tile
+constexpr int kDqKc = kDqK * kKPitch;      // K codes
+constexpr int kDqKs = kDqK * 4;            // K scales
+constexpr int kDqV = kDqK * kRowPitch;     // V row-major bf16
+constexpr int kDqKt = kD * kVtPitch;       // K^T bf16 (key pairs)
+constexpr int kDqBuf = kDqKc + kDqKs + kDqV + kDqKt;
+
+struct DqStage {
+    v2u kc[2][2];   // K codes of keys 2p, 2p+1, 8 bytes at d-chunk dc
+    uint32_t ksb[2][2];
+    v4u v[2][2];    // V rows 2p, 2p+1, d-chunk dc (8 bf16)
+    uint32_t ks;
+};
+
+__device__ __forceinline__ void dq_load(DqStage& st, const AttnArgs& a, int64_t head_row, int k0)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = t + kThreads * i, p = u & 31, dc = u >> 5;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int key = k0 + 2 * p + e;
+            const bool ok = key < a.L;
+            st.kc[i][e] = ok ? *reinterpret_cast<const v2u*>(a.kc + (head_row + key) * a.ldk + 8 * dc) : (v2u){0u, 0u};
+            st.ksb[i][e] = ok ? a.ks[(head_row + key) * a.ldks + (dc >> 2)] : 0u;
+            st.v[i][e] = ok ? *reinterpret_cast<const v4u*>(a.v + (head_row + key) * a.ldv + 8 * dc) : (v4u){0u, 0u, 0u, 0u};
+        }
+    }
+    st.ks = t < kDqK && k0 + t < a.L ? *reinterpret_cast<const uint32_t*>(a.ks + (head_row + k0 + t) * a.ldks) : 0u;
+}
+
+__device__ __forceinline__ void dq_store(const DqStage& st, uint8_t* buf)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = t + kThreads * i, p = u & 31, dc = u >> 5;
+        v4u kb[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int key = 2 * p + e;
+            *reinterpret_cast<v2u*>(buf + key * kKPitch + 8 * dc) = st.kc[i][e];
+            *reinterpret_cast<v4u*>(buf + kDqKc + kDqKs + key * kRowPitch + 16 * dc) = st.v[i][e];
+            kb[e] = __builtin_bit_cast(v4u, cvt8_e4m3(st.kc[i][e], e8m0_f32(st.ksb[i][e])));
+        }
+        store_pair_t(buf + kDqKc + kDqKs + kDqV, kVtPitch, dc, p, kb[0], kb[1]);
+    }
+    if (t < kDqK)
+        *reinterpret_cast<uint32_t*>(buf + kDqKc + 4 * t) = st.ks;
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void attn_dq_kernel(AttnArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int nqb = (a.L + kDqQ - 1) / kDqQ;
+    const int qb = nqb - 1 - (int)blockIdx.x;
+    const int64_t head_row = (int64_t)blockIdx.y * a.L;
+    const int q0 = qb * kDqQ + 32 * wave;
+    const int q = q0 + l32;
+    const bool qok = q < a.L;
+    const float c = a.scale * kLog2e;
+
+    // this lane's query: Q (B operand of S^T = K Q^T), dO (B operand of
+    // dP^T = V dO^T), lse in log2 units, D
+    v8bf qb16[8], gb16[8];
+    {
+        const uint32_t sc = qok ? *reinterpret_cast<const uint32_t*>(a.qs + (head_row + q) * a.ldqs) : 0u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const v2u raw = qok ? *reinterpret_cast<const v2u*>(a.qc + (head_row + q) * a.ldq + 16 * t + 8 * h)
+                                : (v2u){0u, 0u};
+            qb16[t] = cvt8_e4m3(raw, e8m0_f32((sc >> (8 * (t >> 1))) & 0xFFu));
+            const v4u gw = qok ? *reinterpret_cast<const v4u*>(a.dout + (head_row + q) * a.lddo + 16 * t + 8 * h)
+                               : (v4u){0u, 0u, 0u, 0u};
+            gb16[t] = __builtin_bit_cast(v8bf, gw);
+        }
+    }
+    const float lse2 = qok ? a.lse[head_row + q] * kLog2e : 0.0f;
+    const float dlt = qok ? a.delta[head_row + q] : 0.0f;
+    v16f dq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dq[i] = zero16();
+
+    const int nkb_all = (a.L + kDqK - 1) / kDqK;
+    const int nkb = CAUSAL ? min(nkb_all, (qb * kDqQ + kDqQ - 1) / kDqK + 1) : nkb_all;
+    DqStage st;
+    dq_load(st, a, head_row, 0);
+    dq_store(st, lds);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const uint8_t* buf = lds + (kb & 1) * kDqBuf;
+        const int k0 = kb * kDqK;
+        if (kb + 1 < nkb)
+            dq_load(st, a, head_row, k0 + kDqK);
+        v16f s[2], dp[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int key = 32 * sb + l32;
+            const uint32_t ksc = *reinterpret_cast<const uint32_t*>(buf + kDqKc + 4 * key);
+            s[sb] = zero16();
+            dp[sb] = zero16();
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const v2u raw = *reinterpret_cast<const v2u*>(buf + key * kKPitch + 16 * t + 8 * h);
+                s[sb] = mfma_bf16(cvt8_e4m3(raw, e8m0_f32((ksc >> (8 * (t >> 1))) & 0xFFu)), qb16[t], s[sb]);
+                const v4u vw = *reinterpret_cast<const v4u*>(buf + kDqKc + kDqKs + key * kRowPitch + 32 * t + 16 * h);
+                dp[sb] = mfma_bf16(__builtin_bit_cast(v8bf, vw), gb16[t], dp[sb]);
+            }
+        }
+        // dS^T = P^T (dP^T - D), with P^T = 0 for keys past the sequence,
+        // (causal) after the query, and for queries past the sequence
+        const bool edge = k0 + kDqK > a.L || (CAUSAL && k0 + kDqK - 1 > q0);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(c, s[sb][r], -lse2));
+                if (edge) {
+                    const int key = k0 + 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (key >= a.L || (CAUSAL && key > q))
+                        pv = 0.0f;
+                }
+                s[sb][r] = qok ? pv * (dp[sb][r] - dlt) : 0.0f;
+            }
+        // dQ^T += K^T dS^T
+        const uint8_t* kt = buf + kDqKc + kDqKs + kDqV;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int sb = t4 >> 1, tp = t4 & 1;
+            const v8bf bds = pack_step(s[sb], tp);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                dq[db] = mfma_bf16(read_pair_t(kt, kVtPitch, 32 * db + l32, sb, tp, h), bds, dq[db]);
+        }
+        if (kb + 1 < nkb) {
+            __syncthreads();
+            dq_store(st, lds + ((kb + 1) & 1) * kDqBuf);
+            __syncthreads();
+        }
+    }
+    if (qok) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = 32 * db + 8 * g4 + 4 * h;
+                *reinterpret_cast<float4*>(a.dq + (head_row + q) * a.ldg + d) =
+                    make_float4(a.scale * dq[db][4 * g4], a.scale * dq[db][4 * g4 + 1], a.scale * dq[db][4 * g4 + 2],
+                                a.scale * dq[db][4 * g4 + 3]);
+            }
+    }
+}
+
+// ---- dK, dV ----
+constexpr int kDkK = 128;                  // keys per workgroup
+constexpr int kDkQ = 64;                   // queries per step
+constexpr int kDkQc = kDkQ * kKPitch;      // Q codes
+constexpr int kDkQs = kDkQ * 4;            // Q scales
+constexpr int kDkQt = kD * kVtPitch;       // Q^T bf16 (query pairs)
+constexpr int kDkG = kDkQ * kRowPitch;     // dO row-major
+constexpr int kDkGt = kD * kVtPitch;       // dO^T (query pairs)
+constexpr int kDkL = kDkQ * 4;             // lse (log2 units) of the queries
+constexpr int kDkDl = kDkQ * 4;            // D of the queries
+constexpr int kDkBuf = kDkQc + kDkQs + kDkQt + kDkG + kDkGt + kDkL + kDkDl;
+
+struct DkStage {
+    v2u qc[2][2];
+    uint32_t qsb[2][2];
+    v4u g[2][2];
+    uint32_t qs;
+    float ls, dl;
+};
+
+__device__ __forceinline__ void dk_load(DkStage& st, const AttnArgs& a, int64_t head_row, int i0)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = t + kThreads * i, p = u & 31, dc = u >> 5;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int qq = i0 + 2 * p + e;
+            const bool ok = qq < a.L;
+            st.qc[i][e] = ok ? *reinterpret_cast<const v2u*>(a.qc + (head_row + qq) * a.ldq + 8 * dc) : (v2u){0u, 0u};
+            st.qsb[i][e] = ok ? a.qs[(head_row + qq) * a.ldqs + (dc >> 2)] : 0u;
+            st.g[i][e] = ok ? *reinterpret_cast<const v4u*>(a.dout + (head_row + qq) * a.lddo + 8 * dc)
+                            : (v4u){0u, 0u, 0u, 0u};
+        }
+    }
+    const bool ok = t < kDkQ && i0 + t < a.L;
+    st.qs = ok ? *reinterpret_cast<const uint32_t*>(a.qs + (head_row + i0 + t) * a.ldqs) : 0u;
+    st.ls = ok ? a.lse[head_row + i0 + t] * kLog2e : 0.0f;
+    st.dl = ok ? a.delta[head_row + i0 + t] : 0.0f;
+}
+
+__device__ __forceinline__ void dk_store(const DkStage& st, uint8_t* buf)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = t + kThreads * i, p = u & 31, dc = u >> 5;
+        v4u qb[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int qq = 2 * p + e;
+            *reinterpret_cast<v2u*>(buf + qq * kKPitch + 8 * dc) = st.qc[i][e];
+            *reinterpret_cast<v4u*>(buf + kDkQc + kDkQs + kDkQt + qq * kRowPitch + 16 * dc) = st.g[i][e];
+            qb[e] = __builtin_bit_cast(v4u, cvt8_e4m3(st.qc[i][e], e8m0_f32(st.qsb[i][e])));
+        }
+        store_pair_t(buf + kDkQc + kDkQs, kVtPitch, dc, p, qb[0], qb[1]);
+        store_pair_t(buf + kDkQc + kDkQs + kDkQt + kDkG, kVtPitch, dc, p, st.g[i][0], st.g[i][1]);
+    }
+    if (t < kDkQ) {
+        *reinterpret_cast<uint32_t*>(buf + kDkQc + 4 * t) = st.qs;
+        reinterpret_cast<float*>(buf + kDkQc + kDkQs + kDkQt + kDkG + kDkGt)[t] = st.ls;
+        reinterpret_cast<float*>(buf + kDkQc + kDkQs + kDkQt + kDkG + kDkGt + kDkL)[t] = st.dl;
+    }
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void attn_dkdv_kernel(AttnArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int kb = (int)blockIdx.x;
+    const int64_t head_row = (int64_t)blockIdx.y * a.L;
+    const int j0 = kb * kDkK + 32 * wave;       // the wave's first key
+    const int j = j0 + l32;                     // this lane's key
+    const bool kok = j < a.L;
+    const float c = a.scale * kLog2e;
+
+    // this lane's key: K (B operand of S = Q K^T), V (B operand of dP = dO V^T)
+    v8bf kb16[8], vb16[8];
+    {
+        const uint32_t sc = kok ? *reinterpret_cast<const uint32_t*>(a.ks + (head_row + j) * a.ldks) : 0u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const v2u raw = kok ? *reinterpret_cast<const v2u*>(a.kc + (head_row + j) * a.ldk + 16 * t + 8 * h)
+                                : (v2u){0u, 0u};
+            kb16[t] = cvt8_e4m3(raw, e8m0_f32((sc >> (8 * (t >> 1))) & 0xFFu));
+            const v4u vw = kok ? *reinterpret_cast<const v4u*>(a.v + (head_row + j) * a.ldv + 16 * t + 8 * h)
+                               : (v4u){0u, 0u, 0u, 0u};
+            vb16[t] = __builtin_bit_cast(v8bf, vw);
+        }
+    }
+    v16f dk[4], dv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dk[i] = zero16();
+        dv[i] = zero16();
+    }
+    const int nib = (a.L + kDkQ - 1) / kDkQ;
+    const int ib0 = CAUSAL ? (kb * kDkK) / kDkQ : 0;   // the first query block that sees a key of the tile
+    DkStage st;
+    dk_load(st, a, head_row, ib0 * kDkQ);
+    dk_store(st, lds);
+    __syncthreads();
+    for (int ib = ib0; ib < nib; ++ib) {
+        const uint8_t* buf = lds + ((ib - ib0) & 1) * kDkBuf;
+        const int i0 = ib * kDkQ;
+        if (ib + 1 < nib)
+            dk_load(st, a, head_row, i0 + kDkQ);
+        const uint8_t* qt = buf + kDkQc + kDkQs;
+        const uint8_t* g = qt + kDkQt;
+        const uint8_t* gt = g + kDkG;
+        const float* lsv = reinterpret_cast<const float*>(gt + kDkGt);
+        const float* dlv = lsv + kDkQ;
+        v16f s[2], dp[2];
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+            const int qr = 32 * qs + l32;
+            const uint32_t qsc = *reinterpret_cast<const uint32_t*>(buf + kDkQc + 4 * qr);
+            s[qs] = zero16();
+            dp[qs] = zero16();
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const v2u raw = *reinterpret_cast<const v2u*>(buf + qr * kKPitch + 16 * t + 8 * h);
+                s[qs] = mfma_bf16(cvt8_e4m3(raw, e8m0_f32((qsc >> (8 * (t >> 1))) & 0xFFu)), kb16[t], s[qs]);
+                const v4u gw = *reinterpret_cast<const v4u*>(g + qr * kRowPitch + 32 * t + 16 * h);
+                dp[qs] = mfma_bf16(__builtin_bit_cast(v8bf, gw), vb16[t], dp[qs]);
+            }
+        }
+        // P = exp2(c S - lse2) and dS = P (dP - D), rows = queries
+        // 32 qs + 8(r/4) + 4h + r%4; zero past the sequence and (causal)
+        // where the key follows the query
+        const bool edge = i0 + kDkQ > a.L || (CAUSAL && i0 < j0 + 31);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int qr = 32 * qs + 8 * g4 + 4 * h;
+                const float4 l4 = *reinterpret_cast<const float4*>(lsv + qr);
+                const float4 d4 = *reinterpret_cast<const float4*>(dlv + qr);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g4 + e;
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(c, s[qs][r], -lv[e]));
+                    if (edge) {
+                        const int qq = i0 + qr + e;
+                        if (qq >= a.L || (CAUSAL && j > qq))
+                            pv = 0.0f;
+                    }
+                    s[qs][r] = pv;
+                    dp[qs][r] = pv * (dp[qs][r] - dv4[e]);
+                }
+            }
+        // dV += P^T dO, dK += dS^T Q over four 16-query steps
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int qs = t4 >> 1, tp = t4 & 1;
+            const v8bf pb = pack_step(s[qs], tp), dsb = pack_step(dp[qs], tp);
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                dv[db] = mfma_bf16(pb, read_pair_t(gt, kVtPitch, 32 * db + l32, qs, tp, h), dv[db]);
+                dk[db] = mfma_bf16(dsb, read_pair_t(qt, kVtPitch, 32 * db + l32, qs, tp, h), dk[db]);
+            }
+        }
+        if (ib + 1 < nib) {
+            __syncthreads();
+            dk_store(st, lds + ((ib + 1 - ib0) & 1) * kDkBuf);
+            __syncthreads();
+        }
+    }
+    // dV[key][d], dK[key][d]: lane holds column d = 32 db + l32, keys
+    // j0 + 8(r/4) + 4h + r%4
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key < a.L) {
+                a.dv[(head_row + key) * a.ldg + 32 * db + l32] = dv[db][r];
+                a.dk[(head_row + key) * a.ldg + 32 * db + l32] = a.scale * dk[db][r];
+            }
+        }
+}
+
+} // namespace
+
+hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s)
+{
+    const int64_t rows = (int64_t)a.bh * a.L;
+    hipLaunchKernelGGL((a.o_bf16 ? attn_delta_kernel<true> : attn_delta_kernel<false>),
+                       dim3((unsigned)((rows + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    constexpr size_t kDqLds = 2 * kDqBuf, kDkLds = 2 * kDkBuf;
+    static_assert(kDqLds <= 160 * 1024 && kDkLds <= 160 * 1024, "LDS");
+    auto raise = [](const void* fn, size_t bytes) {
+        return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    };
+    const void* dqf = a.causal ? reinterpret_cast<const void*>(attn_dq_kernel<true>)
+                               : reinterpret_cast<const void*>(attn_dq_kernel<false>);
+    const void* dkf = a.causal ? reinterpret_cast<const void*>(attn_dkdv_kernel<true>)
+                               : reinterpret_cast<const void*>(attn_dkdv_kernel<false>);
+    if ((e = raise(dqf, kDqLds)) != hipSuccess || (e = raise(dkf, kDkLds)) != hipSuccess)
+        return e;
+    const dim3 gq((a.L + kDqQ - 1) / kDqQ, a.bh), gk((a.L + kDkK - 1) / kDkK, a.bh);
+    if (a.causal) {
+        hipLaunchKernelGGL(attn_dq_kernel<true>, gq, dim3(kThreads), kDqLds, s, a);
+        hipLaunchKernelGGL(attn_dkdv_kernel<true>, gk, dim3(kThreads), kDkLds, s, a);
+    } else {
+        hipLaunchKernelGGL(attn_dq_kernel<false>, gq, dim3(kThreads), kDqLds, s, a);
+        hipLaunchKernelGGL(attn_dkdv_kernel<false>, gk, dim3(kThreads), kDkLds, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s)
+{
+    const dim3 grid((a.L + kFwdQ - 1) / kFwdQ, a.bh);
+    if (a.causal)
+        hipLaunchKernelGGL((a.o_bf16 ? attn_fwd_kernel<true, true> : attn_fwd_kernel<true, false>), grid,
+                           dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((a.o_bf16 ? attn_fwd_kernel<false, true> : attn_fwd_kernel<false, false>), grid,
+                           dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+} // namespace fp4q

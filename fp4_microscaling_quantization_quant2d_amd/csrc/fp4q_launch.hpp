@@ -132,6 +132,37 @@ enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };
 hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
                        bool accumulate, bool out_bf16, hipStream_t s);
 
+// Fused attention with MXFP8 Q and K (head dimension 128).  Rows of every
+// tensor are head-major: row (head, i) at head * L + i.
+struct AttnArgs {
+    const uint8_t* qc;   // Q E4M3 codes [bh*L x ldq]
+    int64_t ldq;
+    const uint8_t* qs;   // Q E8M0 scales [bh*L x ldqs] (4 per row)
+    int64_t ldqs;
+    const uint8_t* kc;   // K codes / scales likewise
+    int64_t ldk;
+    const uint8_t* ks;
+    int64_t ldks;
+    const uint16_t* v;   // V bf16 [bh*L x ldv]
+    int64_t ldv;
+    void* o;             // O fp32 or bf16 [bh*L x ldo] (forward output, backward input)
+    int64_t ldo;
+    float* lse;          // [bh*L] natural-log log-sum-exp of every query row
+    const uint16_t* dout;  // backward: dO bf16 [bh*L x lddo]
+    int64_t lddo;
+    float* dq;           // backward outputs fp32 [bh*L x ldg]
+    float* dk;
+    float* dv;
+    int64_t ldg;
+    float* delta;        // backward workspace [bh*L]: D_i = sum_d dO_id O_id
+    int bh, L;
+    float scale;
+    int causal, o_bf16;
+};
+
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s);
+
 // Sustained FP4 MFMA loop (measured-peak probe): `workgroups` workgroups of
 // 256 threads, each wave issuing 8 * iters 32x32x64 MFMAs on hashed operand
 // words or on words taken from `codes` (n_words >= 8); sink gets one float

@@ -340,6 +340,53 @@ int fp4q_gemm_quant(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, const 
                     void* hip_stream);
 
 /*
+ * Fused attention forward with MXFP8 queries and keys (Sec. 3.2 "MXFP8
+ * Attention" and Fig. 3 of the same page: Q and K enter the score product in
+ * MXFP8; the attention around it is standard scaled dot-product attention):
+ *   O = softmax(scale * Q K^T [+ causal mask]) V,   lse_i = ln sum_j exp(s_ij)
+ * computed in one pass without writing the scores: every product q_d k_d is
+ * formed exactly (E4M3 x E8M0 is exact in bf16) and summed in fp32, the
+ * softmax is online in fp32, and P is rounded to bf16 to multiply V.
+ *   q, k     FP4Q_FMT_MXFP8_1D32 from fp4q_quant1d_mxfp8, bh*seq_len rows of
+ *            128 (head dimension 128 only, else FP4Q_EUNSUPPORTED), rows
+ *            head-major (row h*seq_len + i), batch 1; scale grids with 4-byte
+ *            aligned rows (ld_s % 4 == 0).
+ *   v        device bf16 [bh*seq_len x ldv], ldv >= 128 and a multiple of 8,
+ *            16-byte aligned.
+ *   o        device [bh*seq_len x ldo] in o_dtype (FP4Q_DT_BF16 or
+ *            FP4Q_DT_F32), ldo >= 128 and a multiple of 8, 16-byte aligned.
+ *   lse      device fp32 [bh*seq_len]: natural-log log-sum-exp of each row's
+ *            scaled scores (needed by fp4q_attn_bwd).
+ *   scale    the score factor (1/sqrt(128) for standard attention), > 0.
+ *   causal   1: key j is visible to query i iff j <= i; 0: all keys.
+ */
+int fp4q_attn_fwd(const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, int64_t ldv, void* o, int64_t ldo,
+                  int o_dtype, float* lse, int64_t bh, int64_t seq_len, float scale, int causal, void* hip_stream);
+
+/*
+ * Fused attention backward for the forward above: the gradients of Q, K, V
+ * for dL/dO = dout, with the scores and probabilities recomputed from the
+ * MXFP8 Q and K and lse, never stored:
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_d dO_id O_id,  dS = P (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q
+ * (P, dS rounded to bf16 to multiply; products of bf16 values exact; fp32
+ * accumulation).  dQ comes from one kernel over query blocks and dK, dV from
+ * one over key blocks, so no partial sums cross workgroups.
+ *   q, k, v, o, ldo, o_dtype, lse, bh, seq_len, scale, causal  as given to
+ *            and returned by fp4q_attn_fwd.
+ *   dout     device bf16 [bh*seq_len x lddo], lddo >= 128, a multiple of 8,
+ *            16-byte aligned.
+ *   dq, dk, dv  device fp32 [bh*seq_len x ldg] outputs, ldg >= 128 and a
+ *            multiple of 4, 16-byte aligned.
+ *   workspace device fp32 scratch of bh*seq_len floats (D), caller-owned;
+ *            overwritten.
+ */
+int fp4q_attn_bwd(const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, int64_t ldv, const void* o,
+                  int64_t ldo, int o_dtype, const float* lse, const void* dout, int64_t lddo, float* dq, float* dk,
+                  float* dv, int64_t ldg, float* workspace, int64_t bh, int64_t seq_len, float scale, int causal,
+                  void* hip_stream);
+
+/*
  * Dequantization X ~ P * S (Sec. 2.1 of the same page) to fp32 or bf16, for
  * every format (each plane of the 1D layout with its own grid).
  *   transposed  0: the row plane, y is rows x cols; 1 (FP4 only): the

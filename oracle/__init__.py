@@ -87,7 +87,7 @@ def lib():
                                            _P, _P]
         L.orc_attn_bwd_dkdv_rows.restype = ctypes.c_int
         L.orc_attn_bwd_dkdv_rows.argtypes = [_P, _P, _P, _P, _I64, _I64, D, ctypes.c_int, _P, _P, _P, _P, _I64,
-                                             _P, _P, _P, _P, _P, _P, _P]
+                                             _P, _P, _P, _P, _P, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -398,7 +398,7 @@ def attn_bwd_dq(Q, K, V, dO, scale, causal, rows=None, threads=None):
 
 def attn_bwd_dkdv(Q, K, V, dO, scale, causal, rows=None, threads=None):
     """One head: dK, dV of the selected key rows and their tolerance
-    magnitudes (ds_abs_q, p_abs_q, pd_q, p_do per row and feature)."""
+    magnitudes (ds_abs_q, p_abs_q, pd_q, p_q, p_do per row and feature)."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
     L, d = Q.shape
     rows = np.arange(L, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
@@ -413,7 +413,7 @@ def attn_bwd_dkdv(Q, K, V, dO, scale, causal, rows=None, threads=None):
         return lib().orc_attn_stats(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), L, d, float(scale), int(causal), lo, hi,
                                     _ptr(mv), _ptr(lv), _ptr(Dv), _ptr(dvo))
 
-    dK, dV, a, b, c, e = (np.zeros((n, d)) for _ in range(6))
+    dK, dV, a, b, c, f, e = (np.zeros((n, d)) for _ in range(7))
 
     def run(bd):
         lo, hi = bd
@@ -422,11 +422,11 @@ def attn_bwd_dkdv(Q, K, V, dO, scale, causal, rows=None, threads=None):
         return lib().orc_attn_bwd_dkdv_rows(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), L, d, float(scale), int(causal),
                                             _ptr(mv), _ptr(lv), _ptr(Dv), _ptr(dvo), hi - lo, _ptr(rows[lo:]),
                                             _ptr(dK[lo:]), _ptr(dV[lo:]), _ptr(a[lo:]), _ptr(b[lo:]), _ptr(c[lo:]),
-                                            _ptr(e[lo:]))
+                                            _ptr(f[lo:]), _ptr(e[lo:]))
 
     with ThreadPoolExecutor(nt) as ex:
         for rc in ex.map(stats, _split(L, nt)):
             _check(rc, "attn_stats")
         for rc in ex.map(run, _split(n, nt)):
             _check(rc, "attn_bwd_dkdv")
-    return dK, dV, {"ds_abs_q": a, "p_abs_q": b, "pd_q": c, "p_do": e}
+    return dK, dV, {"ds_abs_q": a, "p_abs_q": b, "pd_q": c, "p_q": f, "p_do": e}

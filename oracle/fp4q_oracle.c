@@ -767,11 +767,12 @@ int orc_attn_stats(const double* Q, const double* K, const double* V, const doub
  *   ds_abs_q[r][t] = scale * sum_i |dS_ij| |Q_it|
  *   p_abs_q[r][t]  = scale * sum_i P_ij (|dP_ij| + |D_i|) |Q_it|
  *   pd_q[r][t]     = scale * sum_i P_ij dvo_i |Q_it|
+ *   p_q[r][t]      = scale * sum_i P_ij |Q_it|
  *   p_do[r][t]     = sum_i P_ij |dO_it|                 (dV's) */
 int orc_attn_bwd_dkdv_rows(const double* Q, const double* K, const double* V, const double* dO, int64_t L, int64_t d,
                            double scale, int causal, const double* mv, const double* lv, const double* Dv,
                            const double* dvo, int64_t nrows, const int64_t* rows, double* dK, double* dV,
-                           double* ds_abs_q, double* p_abs_q, double* pd_q, double* p_do)
+                           double* ds_abs_q, double* p_abs_q, double* pd_q, double* p_q, double* p_do)
 {
     int64_t r, i, j, t;
     if (!Q || !K || !V || !dO || !rows || !dK || !dV || !mv || !lv || !Dv || !dvo || L <= 0 || d <= 0 || nrows < 0)
@@ -787,6 +788,7 @@ int orc_attn_bwd_dkdv_rows(const double* Q, const double* K, const double* V, co
                 ds_abs_q[r * d + t] = 0.0;
                 p_abs_q[r * d + t] = 0.0;
                 pd_q[r * d + t] = 0.0;
+                p_q[r * d + t] = 0.0;
                 p_do[r * d + t] = 0.0;
             }
         }
@@ -803,6 +805,7 @@ int orc_attn_bwd_dkdv_rows(const double* Q, const double* K, const double* V, co
                     ds_abs_q[r * d + t] += scale * fabs(dsij) * fabs(Q[i * d + t]);
                     p_abs_q[r * d + t] += scale * pij * (fabs(dp) + fabs(Dv[i])) * fabs(Q[i * d + t]);
                     pd_q[r * d + t] += scale * pij * dvo[i] * fabs(Q[i * d + t]);
+                    p_q[r * d + t] += scale * pij * fabs(Q[i * d + t]);
                     p_do[r * d + t] += pij * fabs(dO[i * d + t]);
                 }
             }

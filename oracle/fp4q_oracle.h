@@ -149,7 +149,7 @@ int orc_attn_bwd_dq_rows(const double* Q, const double* K, const double* V, cons
 int orc_attn_bwd_dkdv_rows(const double* Q, const double* K, const double* V, const double* dO, int64_t L, int64_t d,
                            double scale, int causal, const double* mv, const double* lv, const double* Dv,
                            const double* dvo, int64_t nrows, const int64_t* rows, double* dK, double* dV,
-                           double* ds_abs_q, double* p_abs_q, double* pd_q, double* p_do);
+                           double* ds_abs_q, double* p_abs_q, double* pd_q, double* p_q, double* p_do);
 
 #ifdef __cplusplus
 }

@@ -359,3 +359,31 @@ def test_gemm_quant_validation(fp4q):
     assert call(0, ab, _desc(fp4q, rows=96, cols=64, batch=2), good) == -2
     o64 = _desc(fp4q, fmt=3, rows=64, cols=96, ld=48, ld_t=32, ld_s=2)
     assert call(0, a, w, o64) == -2
+
+
+def test_attention_validation(fp4q):
+    """fp4q_attn_fwd / fp4q_attn_bwd check shapes, head dimension, alignment
+    and arguments on the host before any launch."""
+    L = fp4q.lib()
+    P = ctypes.c_void_p
+    rows = 2 * 64
+    q = _desc(fp4q, fmt=2, rows=rows, cols=128, ld=128, ld_s=4)
+    v, o, lse = P(0x100000), P(0x200000), P(0x300000)
+    call = lambda qq, kk, ldv=128, ldo=128, odt=1, scale=0.088, causal=1, bh=2, n=64: L.fp4q_attn_fwd(
+        ctypes.byref(qq), ctypes.byref(kk), v, ldv, o, ldo, odt, lse, bh, n, ctypes.c_float(scale), causal, None)
+    assert call(q, _desc(fp4q, fmt=2, rows=rows, cols=64, ld=64, ld_s=2)) == -2   # head dimension 64
+    assert "128" in _err(fp4q)
+    assert call(q, q, bh=3) == -1                                                   # rows != bh*seq_len
+    assert call(q, q, ldv=100) == -1
+    assert call(q, q, ldo=130) == -1
+    assert call(q, q, odt=7) == -1
+    assert call(q, q, scale=0.0) == -1
+    assert call(q, q, causal=2) == -1
+    assert call(q, _desc(fp4q, fmt=2, rows=rows, cols=128, ld=128, ld_s=5)) == -1    # scale rows not 4-aligned
+    g = P(0x400000)
+    bwd = lambda ldg=128, ws=P(0x500000), lddo=128: L.fp4q_attn_bwd(
+        ctypes.byref(q), ctypes.byref(q), v, 128, o, 128, 1, lse, g, lddo, P(0x600000), P(0x700000), P(0x800000),
+        ldg, ws, 2, 64, ctypes.c_float(0.088), 1, None)
+    assert bwd(ws=None) == -1 and "workspace" in _err(fp4q)
+    assert bwd(ldg=130) == -1
+    assert bwd(lddo=64) == -1

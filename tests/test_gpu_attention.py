@@ -1,0 +1,216 @@
+"""GPU parity of the fused MXFP8 attention (fp4q_attn_fwd, fp4q_attn_bwd)
+with the oracle's fp64 attention on the oracle's own dequantized MXFP8 Q
+and K (Sec. 3.2 "MXFP8 Attention" of "Stable FP4 Training via
+Transposition-Invariant Block Quantization").
+
+Tolerances follow from the kernels' arithmetic (the pages fix none):
+- score products are exact and summed in fp32: a logit is off by at most
+  eps_s = 1e-5 * scale * sum_d |q_d k_d| (the GEMM bound), plus the exp2
+  instruction's and the fma's roundings (2^-21 relative);
+- P (and in the backward dS) is rounded to bf16 to multiply the next
+  operand: bf16 keeps 8 significant bits, so round-to-nearest errs by at
+  most 2^-8 of the value;
+- accumulation is fp32.
+So |O - O*| <= (2^-8 + 2 eps_s + 2^-20)(1 + 2^-7) sum_j P_ij |V_j| (+ 2^-8 |O|
+for a bf16 O), with eps_s the largest logit bound of the row, and
+|lse - lse*| <= eps_s + 2^-20 (1 + |lse|).  The gradient bounds are built the
+same way in _grad_tol."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import fp4_microscaling_quantization_quant2d_amd as fq
+from fp4_microscaling_quantization_quant2d_amd import workloads as wl
+from gpu_util import note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _heads(bh, L, seed, scale_k=1.0):
+    rng = np.random.default_rng(seed)
+    Q = wl.f32_to_bf16_bits(rng.standard_normal((bh * L, D)).astype(np.float32))
+    K = wl.f32_to_bf16_bits((rng.standard_normal((bh * L, D)) * scale_k).astype(np.float32))
+    V = wl.f32_to_bf16_bits(rng.standard_normal((bh * L, D)).astype(np.float32))
+    dO = wl.f32_to_bf16_bits((rng.standard_normal((bh * L, D)) * 0.1).astype(np.float32))
+    return Q, K, V, dO
+
+
+def _deq8(x):
+    c, s = orc.quant1d_mxfp8(x)
+    return orc.dequant_mxfp8(c, s, x.shape[0], D)
+
+
+def _logit_bound(Qd, Kd, scale, causal, rows):
+    """eps_s per row: 1e-5 * scale * max over visible keys of sum_d |q||k|."""
+    A = np.abs(Qd[rows]) @ np.abs(Kd).T
+    if causal:
+        A = np.where(np.arange(Kd.shape[0])[None, :] <= rows[:, None], A, 0.0)
+    return 1e-5 * scale * A.max(axis=1)
+
+
+def _fwd_check(O, lse, Qd, Kd, Vd, scale, causal, rows, obf, what):
+    Or, lr, pv = orc.attn_fwd(Qd, Kd, Vd, scale, causal, rows=rows)
+    eps = _logit_bound(Qd, Kd, scale, causal, rows)
+    tol = (2.0 ** -8 + 2 * eps[:, None] + 2.0 ** -20) * (1 + 2.0 ** -7) * pv
+    tol += (2.0 ** -8 if obf else 2.0 ** -22) * np.abs(Or)
+    err = np.abs(O[rows].astype(np.float64) - Or)
+    bad = err > tol
+    assert not bad.any(), "%s: O off at %s: gpu %r oracle %r tol %r" % (
+        what, np.argwhere(bad)[:3].tolist(), O[rows][bad][:3], Or[bad][:3], tol[bad][:3])
+    lerr = np.abs(lse[rows].astype(np.float64) - lr)
+    ltol = eps + 2.0 ** -20 * (1 + np.abs(lr))
+    assert np.all(lerr <= ltol), "%s: lse off by %r (tol %r)" % (what, lerr.max(), ltol[np.argmax(lerr)])
+    return float((err / np.maximum(tol, 1e-300)).max())
+
+
+def _run_fwd(Q, K, V, bh, L, scale, causal, out_dtype):
+    qq = fq.fp4q_quant1d_mxfp8(to_dev(Q))
+    qk = fq.fp4q_quant1d_mxfp8(to_dev(K))
+    O, lse = fq.fp4q_attn_fwd(qq, qk, to_dev(V), bh, L, scale=scale, causal=causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return qq, qk, O.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("L", [64, 200, 300, 513])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_forward_small(L, causal, out_dtype):
+    bh = 3
+    Q, K, V, _ = _heads(bh, L, L + 7 * causal)
+    scale = D ** -0.5
+    note("attn fwd bh=%d L=%d causal=%d %s" % (bh, L, causal, out_dtype))
+    _, _, O, lse = _run_fwd(Q, K, V, bh, L, scale, causal, out_dtype)
+    Vd = wl.bf16_bits_to_f32(V).astype(np.float64)
+    for h in range(bh):
+        sl = slice(h * L, (h + 1) * L)
+        Qd, Kd = _deq8(np.ascontiguousarray(Q[sl])), _deq8(np.ascontiguousarray(K[sl]))
+        _fwd_check(O[sl], lse[sl], Qd, Kd, Vd[sl], scale, causal, np.arange(L), out_dtype == torch.bfloat16,
+                   "head %d" % h)
+
+
+def test_forward_wide_logits():
+    """Keys scaled x8: peaked softmax rows (logits up to ~100), where a
+    wrong running max or a lost rescale shows at once."""
+    bh, L = 2, 256
+    Q, K, V, _ = _heads(bh, L, 99, scale_k=8.0)
+    note("attn fwd wide logits")
+    _, _, O, lse = _run_fwd(Q, K, V, bh, L, D ** -0.5, True, torch.float32)
+    Vd = wl.bf16_bits_to_f32(V).astype(np.float64)
+    for h in range(bh):
+        sl = slice(h * L, (h + 1) * L)
+        _fwd_check(O[sl], lse[sl], _deq8(np.ascontiguousarray(Q[sl])), _deq8(np.ascontiguousarray(K[sl])), Vd[sl],
+                   D ** -0.5, True, np.arange(L), False, "wide head %d" % h)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_attention_config_sampled(causal):
+    """The attention config: Q, K [4, 32, 4096, 128] bf16 N(0,1) to MXFP8, V
+    of the same shape; two heads checked on 256 sampled rows each (the
+    first, the last and random)."""
+    a = wl.config_attn()
+    B, H, L, _ = a.Q.shape
+    bh = B * H
+    Qf, Kf = a.Q.reshape(bh * L, D), a.K.reshape(bh * L, D)
+    V = wl.f32_to_bf16_bits(np.random.default_rng(77).standard_normal((bh * L, D)).astype(np.float32))
+    note("attn fwd config causal=%d" % causal)
+    _, _, O, lse = _run_fwd(Qf, Kf, V, bh, L, D ** -0.5, causal, torch.bfloat16)
+    rng = np.random.default_rng(3)
+    for h in (0, bh - 1):
+        sl = slice(h * L, (h + 1) * L)
+        rows = np.unique(np.concatenate([[0, L - 1], rng.integers(0, L, 254)]))
+        _fwd_check(O[sl], lse[sl], _deq8(np.ascontiguousarray(Qf[sl])), _deq8(np.ascontiguousarray(Kf[sl])),
+                   wl.bf16_bits_to_f32(V[sl]).astype(np.float64), D ** -0.5, causal, rows, True, "config head %d" % h)
+
+
+def _grad_tol(eps_s, m, which, dvo=None, do_l1=None, vmax=0.0, ref=None):
+    """Bounds on the gradients (per row and feature), from the arithmetic:
+    dS = P (dP - D) and P are rounded to bf16 to multiply (2^-8 of the
+    value, times 1.01 for the fp32 accumulation around them); P carries the
+    logit and lse errors (2 eps_s + 2^-19 relative, times |dP| + |D|); D is
+    formed from the kernel's O, itself within (2^-7 + 2 eps_s) sum_j P_ij
+    |V_jd| of O* (bf16 P, plus a bf16 O), so |dD_i| <= (2^-7 + 2 eps_s +
+    2^-18) dvo_i with dvo_i = sum_d |dO_id| sum_j P_ij |V_jd|; dP is a fp32
+    sum of exact products (<= 1e-5 |dO_i|_1 max|V|); fp32 accumulation
+    elsewhere (2^-20)."""
+    a = 2 * eps_s + 2.0 ** -19
+    r8 = 1.01 * 2.0 ** -8
+    dd = 2.0 ** -7 + 2 * eps_s + 2.0 ** -18
+    if which == "dq":
+        per_row = dd * dvo + 1e-5 * do_l1 * vmax
+        return (r8 * m["ds_abs_k"] + a[:, None] * m["p_abs_k"] + per_row[:, None] * m["p_k"]
+                + 2.0 ** -20 * np.abs(ref))
+    if which == "dk":
+        return (r8 * m["ds_abs_q"] + a * m["p_abs_q"] + dd * m["pd_q"]
+                + 1e-5 * do_l1 * vmax * m["p_q"] + 2.0 ** -20 * np.abs(ref))
+    return (r8 + a) * m["p_do"] + 2.0 ** -20 * np.abs(ref)
+
+
+def _check(got, ref, tol, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    bad = err > tol
+    assert not bad.any(), "%s off at %s: gpu %r oracle %r tol %r" % (
+        what, np.argwhere(bad)[:3].tolist(), got[bad][:3], ref[bad][:3], tol[bad][:3])
+    return float((err / np.maximum(tol, 1e-300)).max())
+
+
+def _bwd_check(Q, K, V, dO, O_gpu, grads, bh, L, scale, causal, heads, qrows, krows):
+    dq, dk, dv = (g.cpu().numpy() for g in grads)
+    for h in heads:
+        sl = slice(h * L, (h + 1) * L)
+        Qd, Kd = _deq8(np.ascontiguousarray(Q[sl])), _deq8(np.ascontiguousarray(K[sl]))
+        Vd = wl.bf16_bits_to_f32(V[sl]).astype(np.float64)
+        Gd = wl.bf16_bits_to_f32(dO[sl]).astype(np.float64)
+        vmax = np.abs(Vd).max()
+        rq = np.asarray(qrows)
+        dQr, mq = orc.attn_bwd_dq(Qd, Kd, Vd, Gd, scale, causal, rows=rq)
+        eps_q = _logit_bound(Qd, Kd, scale, causal, rq)
+        tol = _grad_tol(eps_q, mq, "dq", dvo=mq["dvo"], do_l1=np.abs(Gd[rq]).sum(axis=1), vmax=vmax, ref=dQr)
+        _check(dq[sl][rq], dQr, tol, "dQ head %d" % h)
+        rk = np.asarray(krows)
+        dKr, dVr, mk = orc.attn_bwd_dkdv(Qd, Kd, Vd, Gd, scale, causal, rows=rk)
+        eps_all = _logit_bound(Qd, Kd, scale, causal, np.arange(L)).max()
+        do_l1 = np.abs(Gd).sum(axis=1).max()
+        _check(dk[sl][rk], dKr, _grad_tol(eps_all, mk, "dk", do_l1=do_l1, vmax=vmax, ref=dKr), "dK head %d" % h)
+        _check(dv[sl][rk], dVr, _grad_tol(eps_all, mk, "dv", ref=dVr), "dV head %d" % h)
+
+
+@pytest.mark.parametrize("L", [64, 200, 300])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_backward_small(L, causal, out_dtype):
+    bh = 2
+    Q, K, V, dO = _heads(bh, L, 5 * L + causal)
+    scale = D ** -0.5
+    note("attn bwd bh=%d L=%d causal=%d %s" % (bh, L, causal, out_dtype))
+    qq = fq.fp4q_quant1d_mxfp8(to_dev(Q))
+    qk = fq.fp4q_quant1d_mxfp8(to_dev(K))
+    v, g = to_dev(V), to_dev(dO)
+    O, lse = fq.fp4q_attn_fwd(qq, qk, v, bh, L, scale=scale, causal=causal, out_dtype=out_dtype)
+    grads = fq.fp4q_attn_bwd(qq, qk, v, O, lse, g, bh, L, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    _bwd_check(Q, K, V, dO, O, grads, bh, L, scale, causal, range(bh), np.arange(L), np.arange(L))
+
+
+def test_backward_attention_config_sampled():
+    """The attention config (Q, K [4, 32, 4096, 128] to MXFP8, causal),
+    forward and backward over all 128 heads; two heads checked at 128
+    sampled query rows (dQ) and 128 sampled key rows (dK, dV)."""
+    a = wl.config_attn()
+    B, H, L, _ = a.Q.shape
+    bh = B * H
+    Qf, Kf = a.Q.reshape(bh * L, D), a.K.reshape(bh * L, D)
+    rng = np.random.default_rng(12)
+    V = wl.f32_to_bf16_bits(rng.standard_normal((bh * L, D)).astype(np.float32))
+    dO = wl.f32_to_bf16_bits((rng.standard_normal((bh * L, D)) * 0.1).astype(np.float32))
+    note("attn bwd config")
+    qq = fq.fp4q_quant1d_mxfp8(to_dev(Qf))
+    qk = fq.fp4q_quant1d_mxfp8(to_dev(Kf))
+    v, g = to_dev(V), to_dev(dO)
+    O, lse = fq.fp4q_attn_fwd(qq, qk, v, bh, L, causal=True)
+    grads = fq.fp4q_attn_bwd(qq, qk, v, O, lse, g, bh, L, causal=True)
+    torch.cuda.synchronize()
+    rows = lambda: np.unique(np.concatenate([[0, L - 1], rng.integers(0, L, 126)]))
+    _bwd_check(Qf, Kf, V, dO, O, grads, bh, L, D ** -0.5, True, (0, bh - 1), rows(), rows())

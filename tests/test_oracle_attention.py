@@ -73,6 +73,10 @@ def test_backward_matches_torch_autograd(orc, L, d, causal):
     assert np.all(mq["ds_abs_k"] >= np.abs(dQ) * (1 - 1e-12))
     assert np.all(mk["ds_abs_q"] >= np.abs(dK) * (1 - 1e-12))
     assert np.all(mk["p_do"] >= np.abs(dV) * (1 - 1e-12))
+    # p_q, p_k: the P-weighted magnitudes, against numpy
+    _, _, P = _ref_fwd(Q, K, V, scale, causal)
+    assert np.allclose(mk["p_q"], scale * P.T @ np.abs(Q), rtol=1e-12, atol=1e-14)
+    assert np.allclose(mq["p_k"], scale * P @ np.abs(K), rtol=1e-12, atol=1e-14)
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -103,12 +103,14 @@ def _load():
                                 I64, I64, ctypes.c_float, ctypes.c_int, P]
     L.fp4q_attn_bwd.argtypes = [ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc), P, I64, P, I64, ctypes.c_int, P,
                                 P, I64, P, P, P, I64, P, I64, I64, ctypes.c_float, ctypes.c_int, P]
+    L.fp4q_attn_bwd_noalloc.argtypes = [ctypes.POINTER(_QDesc), ctypes.POINTER(_QDesc), P, I64, P, I64, ctypes.c_int,
+                                        P, P, I64, P, P, P, I64, I64, I64, ctypes.c_float, ctypes.c_int, P]
     L.fp4q_dequant.argtypes = [ctypes.POINTER(_QDesc), ctypes.c_int, ctypes.c_int, P, I64, P]
     L.fp4q_probe_mfma_fp4.argtypes = [I64, ctypes.c_int, P, P, I64, P]
     L.fp4q_probe_copy.argtypes = [P, P, I64, ctypes.c_int, P]
     for fn in ("fp4q_quant2d_sizes", "fp4q_quant2d", "fp4q_quant2d_batch", "fp4q_quant2d_batch_ex",
                "fp4q_quant1d_mxfp8",
-               "fp4q_gemm", "fp4q_gemm_ex", "fp4q_gemm_quant", "fp4q_attn_fwd", "fp4q_attn_bwd", "fp4q_dequant", "fp4q_probe_mfma_fp4",
+               "fp4q_gemm", "fp4q_gemm_ex", "fp4q_gemm_quant", "fp4q_attn_fwd", "fp4q_attn_bwd", "fp4q_attn_bwd_noalloc", "fp4q_dequant", "fp4q_probe_mfma_fp4",
                "fp4q_probe_copy"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L

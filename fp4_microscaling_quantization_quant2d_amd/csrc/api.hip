@@ -789,6 +789,24 @@ int fp4q_attn_bwd(const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, i
     return hip_status(fp4q::launch_attn_bwd(a, static_cast<hipStream_t>(hip_stream)), "fp4q_attn_bwd");
 }
 
+static_assert(FP4Q_ATTN_NOALLOC_MAX_ROWS == fp4q::kAttnScratchRows, "static scratch size");
+
+int fp4q_attn_bwd_noalloc(const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, int64_t ldv, const void* o,
+                          int64_t ldo, int o_dtype, const float* lse, const void* dout, int64_t lddo, float* dq,
+                          float* dk, float* dv, int64_t ldg, int64_t bh, int64_t seq_len, float scale, int causal,
+                          void* hip_stream)
+{
+    if (bh < 1 || seq_len < 1 || bh * seq_len > fp4q::kAttnScratchRows)
+        return fail(FP4Q_EINVAL, "fp4q_attn_bwd_noalloc: bh*seq_len %lld exceeds the static scratch of %lld rows",
+                    (long long)(bh * seq_len), (long long)fp4q::kAttnScratchRows);
+    float* ws = nullptr;
+    hipError_t e = fp4q::attn_noalloc_scratch(&ws);
+    if (e != hipSuccess)
+        return hip_status(e, "fp4q_attn_bwd_noalloc: address of the static scratch");
+    return fp4q_attn_bwd(q, k, v, ldv, o, ldo, o_dtype, lse, dout, lddo, dq, dk, dv, ldg, ws, bh, seq_len, scale,
+                         causal, hip_stream);
+}
+
 int fp4q_probe_mfma_fp4(int64_t iters, int workgroups, float* sink, const uint8_t* codes, int64_t code_bytes,
                         void* hip_stream)
 {

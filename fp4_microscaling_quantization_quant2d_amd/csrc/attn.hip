@@ -30,12 +30,19 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
 namespace fp4q {
 
 namespace {
+
+// Static scratch of the allocation-free backward (fp4q_attn_bwd_noalloc):
+// D of up to kAttnScratchRows query rows.  Each GPU holds its own copy for
+// the life of the process; host code reaches it only through the address
+// hipGetSymbolAddress returns on that device (attn_noalloc_scratch).
+__device__ __align__(256) float scratch[kAttnScratchRows];
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -753,6 +760,31 @@ hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s)
         hipLaunchKernelGGL(attn_dkdv_kernel<false>, gk, dim3(kThreads), kDkLds, s, a);
     }
     return hipGetLastError();
+}
+
+hipError_t attn_noalloc_scratch(float** p)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // once per device, with that device current: the device address of
+        // this GPU's copy of the array
+        void* q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = static_cast<float*>(q);
+    }
+    *p = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s)

@@ -162,6 +162,10 @@ struct AttnArgs {
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s);
+// The allocation-free backward's scratch: a file-scope device array of
+// kAttnScratchRows floats; *p gets its address on the current device.
+constexpr int64_t kAttnScratchRows = (int64_t)1 << 20;
+hipError_t attn_noalloc_scratch(float** p);
 
 // Sustained FP4 MFMA loop (measured-peak probe): `workgroups` workgroups of
 // 256 threads, each wave issuing 8 * iters 32x32x64 MFMAs on hashed operand

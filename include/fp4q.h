@@ -387,6 +387,23 @@ int fp4q_attn_bwd(const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, i
                   void* hip_stream);
 
 /*
+ * fp4q_attn_bwd without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): D lives in a static device array of
+ * FP4Q_ATTN_NOALLOC_MAX_ROWS floats (4 MiB) that each GPU holds for the life
+ * of the process.  bh*seq_len above that limit returns FP4Q_EINVAL.  The
+ * call allocates and frees nothing.  Every call on one GPU shares that GPU's
+ * array (D is fully rewritten by each call before it is read), so calls that
+ * overlap on one GPU -- on different streams, unordered -- race.  Otherwise
+ * exactly fp4q_attn_bwd.
+ */
+#define FP4Q_ATTN_NOALLOC_MAX_ROWS (1 << 20)
+int fp4q_attn_bwd_noalloc(const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, int64_t ldv, const void* o,
+                          int64_t ldo, int o_dtype, const float* lse, const void* dout, int64_t lddo, float* dq,
+                          float* dk, float* dv, int64_t ldg, int64_t bh, int64_t seq_len, float scale, int causal,
+                          void* hip_stream);
+
+/*
  * Dequantization X ~ P * S (Sec. 2.1 of the same page) to fp32 or bf16, for
  * every format (each plane of the 1D layout with its own grid).
  *   transposed  0: the row plane, y is rows x cols; 1 (FP4 only): the

@@ -706,7 +706,8 @@ int check_attn(const char* fn, const fp4q_qtensor* q, const fp4q_qtensor* k, con
     int rc;
     if ((rc = check_fp8_tensor(q, fn)) || (rc = check_fp8_tensor(k, fn)))
         return rc;
-    if (bh < 1 || seq_len < 1 || bh > 65535 || seq_len > (1 << 24) || bh * seq_len > ((int64_t)1 << 31))
+    // grids: heads along x, 64-row blocks along y (at most 65535)
+    if (bh < 1 || seq_len < 1 || bh > 65535 || seq_len > (1 << 21) || bh * seq_len > ((int64_t)1 << 31))
         return fail(FP4Q_EINVAL, "%s: bh %lld and seq_len %lld out of range", fn, (long long)bh, (long long)seq_len);
     if (q->cols != 128 || k->cols != 128)
         return fail(FP4Q_EUNSUPPORTED, "%s: head dimension 128 only (got %lld, %lld)", fn, (long long)q->cols,

@@ -170,9 +170,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFwdBuf];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, h = lane >> 5;
+    // blockIdx.x: head, blockIdx.y: query block, the last (longest causal
+    // rows) first -- the dispatcher walks x fastest, so every head's long
+    // blocks start before any short one
     const int nqb = (a.L + kFwdQ - 1) / kFwdQ;
-    const int qb = nqb - 1 - (int)blockIdx.x;  // the longest causal rows first
-    const int64_t head_row = (int64_t)blockIdx.y * a.L;
+    const int qb = nqb - 1 - (int)blockIdx.y;
+    const int64_t head_row = (int64_t)blockIdx.x * a.L;
     const int q0 = qb * kFwdQ + 32 * wave;      // the wave's first query
     const int q = q0 + l32;                     // this lane's query
 
@@ -445,8 +448,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dq_kernel(AttnArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     const int nqb = (a.L + kDqQ - 1) / kDqQ;
-    const int qb = nqb - 1 - (int)blockIdx.x;
-    const int64_t head_row = (int64_t)blockIdx.y * a.L;
+    const int qb = nqb - 1 - (int)blockIdx.y;   // as in the forward: long blocks first
+    const int64_t head_row = (int64_t)blockIdx.x * a.L;
     const int q0 = qb * kDqQ + 32 * wave;
     const int q = q0 + l32;
     const bool qok = q < a.L;
@@ -616,8 +619,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_kernel(AttnArgs a)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, h = lane >> 5;
-    const int kb = (int)blockIdx.x;
-    const int64_t head_row = (int64_t)blockIdx.y * a.L;
+    const int kb = (int)blockIdx.y;             // causal: the first key blocks see the most queries
+    const int64_t head_row = (int64_t)blockIdx.x * a.L;
     const int j0 = kb * kDkK + 32 * wave;       // the wave's first key
     const int j = j0 + l32;                     // this lane's key
     const bool kok = j < a.L;
@@ -751,7 +754,7 @@ hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s)
                                : reinterpret_cast<const void*>(attn_dkdv_kernel<false>);
     if ((e = raise(dqf, kDqLds)) != hipSuccess || (e = raise(dkf, kDkLds)) != hipSuccess)
         return e;
-    const dim3 gq((a.L + kDqQ - 1) / kDqQ, a.bh), gk((a.L + kDkK - 1) / kDkK, a.bh);
+    const dim3 gq(a.bh, (a.L + kDqQ - 1) / kDqQ), gk(a.bh, (a.L + kDkK - 1) / kDkK);
     if (a.causal) {
         hipLaunchKernelGGL(attn_dq_kernel<true>, gq, dim3(kThreads), kDqLds, s, a);
         hipLaunchKernelGGL(attn_dkdv_kernel<true>, gk, dim3(kThreads), kDkLds, s, a);
@@ -789,7 +792,7 @@ hipError_t attn_noalloc_scratch(float** p)
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s)
 {
-    const dim3 grid((a.L + kFwdQ - 1) / kFwdQ, a.bh);
+    const dim3 grid(a.bh, (a.L + kFwdQ - 1) / kFwdQ);
     if (a.causal)
         hipLaunchKernelGGL((a.o_bf16 ? attn_fwd_kernel<true, true> : attn_fwd_kernel<true, false>), grid,
                            dim3(kThreads), 0, s, a);

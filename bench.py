@@ -54,8 +54,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_7b_step_pmc.md")
 # The sources each measured kernel is built from: a change to any of them
 # invalidates the committed counter readings.
-KERNEL_SOURCES = {"gemm": ["fp4q_launch.hpp", "gemm_kernel.hpp", "gemm_plain.hip"],
-                  "quant2d": ["fp4q_launch.hpp", "fp4q_device.hpp", "fp4q_cvt.hpp", "quant2d.hip"]}
+KERNEL_SOURCES = {"gemm": ["fp4q_launch.hpp", "fp4q_device.hpp", "fp4q_cvt.hpp", "quant_tile.hpp", "gemm_kernel.hpp",
+                           "gemm_plain.hip"],
+                  "quant2d": ["fp4q_launch.hpp", "fp4q_device.hpp", "fp4q_cvt.hpp", "quant_tile.hpp", "quant2d.hip"]}
 
 
 def source_sha256(kernel):
@@ -246,15 +247,48 @@ class Step:
         main.wait_stream(side)
 
 
+_HEAD = {}
+
+
+def gpu_head_start(torch, fq, ms):
+    """Keep the GPU busy for about `ms` milliseconds with a sustained MFMA
+    loop (fp4q_probe_mfma_fp4) before timed launches, so that the host
+    enqueues them ahead of the GPU: each per-launch event pair then brackets
+    GPU time only, never a host launch gap."""
+    if not _HEAD:
+        wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+        sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+        fq.fp4q_probe_mfma_fp4(100, wg, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fq.fp4q_probe_mfma_fp4(2000, wg, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        _HEAD.update(wg=wg, sink=sink, ms_per_iter=e0.elapsed_time(e1) / 2000)
+    iters = max(1, int(min(ms, 2000.0) / _HEAD["ms_per_iter"]))
+    fq.fp4q_probe_mfma_fp4(iters, _HEAD["wg"], _HEAD["sink"])
+
+
+def _enqueue_ms(torch, fn, reps):
+    """Host milliseconds to enqueue `fn` once (mean over `reps` calls, no
+    synchronization inside), then wait for the GPU."""
+    w0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    h = (time.perf_counter() - w0) * 1e3 / max(1, reps)
+    torch.cuda.synchronize()
+    return h
+
+
 def _timed_launches(torch, launches, iters, warmup):
     """Median ms per launch of a list of (name, fn) run in order; inputs are
-    resident, each launch bracketed by events on the current stream."""
-    for _ in range(warmup):
-        for _, fn in launches:
-            fn()
-    torch.cuda.synchronize()
+    resident, each launch bracketed by events on the current stream, with the
+    GPU given a head start over the host."""
+    import fp4_microscaling_quantization_quant2d_amd as fq
+    host_ms = _enqueue_ms(torch, lambda: [fn() for _, fn in launches], max(1, warmup))
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
           for _ in range(iters)]
+    gpu_head_start(torch, fq, 2.0 + 1.5 * host_ms * iters)
     for it in range(iters):
         for (s, e), (_, fn) in zip(ev[it], launches):
             s.record()
@@ -281,11 +315,11 @@ def _eager_step(step, torch, iters, warmup, keep_launches=False):
     """Median per-launch times of a Step run eagerly, and their totals by kind."""
     work = {nm: w for _, nm, w in step.launches}
     kinds = {nm: kind for kind, nm, _ in step.launches}
-    for it in range(warmup):
-        step.run(seed=it)
-    torch.cuda.synchronize()
+    seeds = iter(range(10 ** 6))
+    host_ms = _enqueue_ms(torch, lambda: step.run(seed=next(seeds)), max(1, warmup))
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in step.launches] for _ in range(iters)]
+    gpu_head_start(torch, step.fq, 2.0 + 1.5 * host_ms * iters)
     for it in range(iters):
         step.run(seed=100 + it, events=ev[it])
     torch.cuda.synchronize()
@@ -706,9 +740,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     print("[bench] warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
-    for w in range(args.warmup):
-        step.run(seed=w)
-    torch.cuda.synchronize()
+    seeds = iter(range(args.warmup))
+    host_ms = _enqueue_ms(torch, lambda: step.run(seed=next(seeds)), args.warmup) if args.warmup else 5.0
     print("[bench] measuring the copy and MFMA-loop peaks", file=sys.stderr, flush=True)
     peaks = measured_peaks(torch, fq, step)
 
@@ -718,6 +751,9 @@ def main():
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    # the GPU starts behind the host, so every launch's events bracket GPU
+    # time only (host enqueue time per step: host_ms)
+    gpu_head_start(torch, fq, 2.0 + 1.5 * host_ms * args.steps)
     wall0 = time.perf_counter()
     t_start.record()
     for s in range(args.steps):
@@ -804,6 +840,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_eager": round(ms_step_eager, 4),
+        "host_enqueue_ms_per_step": round(host_ms, 3),
         "ms_per_step_graph_one_stream": None if ms_step_one_stream is None else round(ms_step_one_stream, 4),
         "step_timing": ("hip-graph replay, wgrad on a second stream" if graph is not None
                         else "eager launches"),

@@ -608,7 +608,12 @@ int gemm_common(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, void* c, i
     if (out_bf16 && (accumulate || oned))
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm_ex: bf16 output takes products (no accumulation) of "
                                        "square-block FP4 or MXFP8 operands");
-    if (fp4q::gemm_lds_bytes(fp8 ? 2 : 1, (int)kmax) > kMaxLdsBytes)
+    // Dense FP4 products with a square-block A (and no bf16 output) take any
+    // K: the launcher splits a long contraction into accumulating chunks.
+    const bool chunked = !fp8 && grouped_op < 0 && !out_bf16 && (oned & 1) == 0 && K > fp4q::kDenseKChunk;
+    if (chunked && fp4q::gemm_lds_bytes(1, fp4q::kDenseKChunk) > kMaxLdsBytes)
+        return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: K chunk does not fit the FP4 tile");
+    if (!chunked && fp4q::gemm_lds_bytes(fp8 ? 2 : 1, (int)kmax) > kMaxLdsBytes)
         return fail(FP4Q_EUNSUPPORTED, "fp4q_gemm: K %lld too large for the %s tile (max %d)", (long long)kmax,
                     fp8 ? "MXFP8" : "FP4", fp8 ? max_k(2) : max_k(1));
     return hip_status(fp4q::launch_gemm(g, fp8 ? 2 : 1, a_st, b_st, oned, grouped_op, (int)a->batch, accumulate, out_bf16,

@@ -129,6 +129,9 @@ enum GemmKind { kGemmFwd = 0, kGemmDgrad = 1, kGemmWgrad = 2 };
 // accumulate: C += A B^T (FP4, dense; oned 0 or 2 only).
 // out_bf16: C is bf16, ldc and the batch stride in bf16 elements (FP4 with
 // oned 0, dense or grouped, or MXFP8).
+// Dense FP4 products (no bf16 output, A with a square-block grid) with K
+// above kDenseKChunk run as accumulating chunks of kDenseKChunk.
+constexpr int kDenseKChunk = 65024;
 hipError_t launch_gemm(const GemmArgs& p, int fmt, bool a_st, bool b_st, int oned, int grouped_op, int batch,
                        bool accumulate, bool out_bf16, hipStream_t s);
 

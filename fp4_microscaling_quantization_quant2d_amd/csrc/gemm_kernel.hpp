@@ -1218,10 +1218,13 @@ hipError_t launch_dense_k(const GemmArgs& g, int batch, hipStream_t s)
     return hipGetLastError();
 }
 
+// force_kt: take the K-checked variant even for K % 256 == 0 (a launch over
+// one chunk of a longer contraction, whose operand bases start inside the
+// planes, so the buffer range no longer ends at the planes' end).
 template <int FMT, bool A_ST, bool B_ST, int ONED = 0, bool ACC = false, bool OBF = false>
-hipError_t launch_dense(const GemmArgs& g, int batch, hipStream_t s)
+hipError_t launch_dense(const GemmArgs& g, int batch, hipStream_t s, bool force_kt = false)
 {
-    if (FMT == 1 && g.K % 256 == 0)
+    if (FMT == 1 && g.K % 256 == 0 && !force_kt)
         return launch_dense_k<FMT, A_ST, B_ST, false, ONED, ACC, OBF>(g, batch, s);
     return launch_dense_k<FMT, A_ST, B_ST, true, ONED, ACC, OBF>(g, batch, s);
 }
@@ -1334,10 +1337,13 @@ hipError_t launch_sub_any(const GemmArgs& g, bool a_st, bool b_st, bool accumula
 // Launchers of the kernel families, one translation unit each (they compile
 // in parallel): plain products, bf16 output, accumulation, 1D-layout
 // operands and grouped products.  launch_gemm (gemm.hip) picks one.
-hipError_t launch_gemm_plain(const GemmArgs& g, int fmt, bool a_st, bool b_st, int batch, hipStream_t s);
+hipError_t launch_gemm_plain(const GemmArgs& g, int fmt, bool a_st, bool b_st, int batch, hipStream_t s,
+                             bool force_kt = false);
 hipError_t launch_gemm_obf(const GemmArgs& g, int fmt, bool a_st, bool b_st, int batch, hipStream_t s);
-hipError_t launch_gemm_acc(const GemmArgs& g, bool a_st, bool b_st, int oned, int batch, hipStream_t s);
-hipError_t launch_gemm_1d(const GemmArgs& g, bool a_st, bool b_st, int oned, int batch, hipStream_t s);
+hipError_t launch_gemm_acc(const GemmArgs& g, bool a_st, bool b_st, int oned, int batch, hipStream_t s,
+                           bool force_kt = false);
+hipError_t launch_gemm_1d(const GemmArgs& g, bool a_st, bool b_st, int oned, int batch, hipStream_t s,
+                          bool force_kt = false);
 hipError_t launch_gemm_grouped(const GemmArgs& g, int op, bool out_bf16, hipStream_t s);
 hipError_t launch_gemm_sub16(const GemmArgs& g, bool a_st, bool b_st, bool accumulate, hipStream_t s);
 hipError_t launch_gemm_sub8(const GemmArgs& g, bool a_st, bool b_st, bool accumulate, hipStream_t s);

@@ -274,7 +274,12 @@ int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
  * sum only by fp32 accumulation rounding, as for FP4.
  *   K      the tile keeps the scale bytes of its whole K range on chip:
  *          K (per group for grouped DGRAD / WGRAD) is at most 65152 for
- *          FP4 and 1664 for MXFP8, else FP4Q_EUNSUPPORTED.
+ *          FP4 and 1664 for MXFP8, else FP4Q_EUNSUPPORTED -- except for
+ *          dense FP4 products whose A has a square-block grid and whose C
+ *          is fp32 (every op with 2D operands, and WGRAD with X in the 1D
+ *          layout): a longer K runs as chunks of 65024 contraction values,
+ *          every chunk after the first adding into C (so C is summed in
+ *          fp32 once per chunk).
  *   size   each operand plane read (rows padded to 32, plus 256 rows of
  *          reach) times its leading dimension must stay below 2 GiB, else
  *          FP4Q_EUNSUPPORTED.

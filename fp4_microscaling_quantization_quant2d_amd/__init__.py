@@ -108,10 +108,11 @@ def _load():
     L.fp4q_dequant.argtypes = [ctypes.POINTER(_QDesc), ctypes.c_int, ctypes.c_int, P, I64, P]
     L.fp4q_probe_mfma_fp4.argtypes = [I64, ctypes.c_int, P, P, I64, P]
     L.fp4q_probe_copy.argtypes = [P, P, I64, ctypes.c_int, P]
+    L.fp4q_probe_mfma_fp8.argtypes = [P, P, P, P, P, P]
     for fn in ("fp4q_quant2d_sizes", "fp4q_quant2d", "fp4q_quant2d_batch", "fp4q_quant2d_batch_ex",
                "fp4q_quant1d_mxfp8",
                "fp4q_gemm", "fp4q_gemm_ex", "fp4q_gemm_quant", "fp4q_attn_fwd", "fp4q_attn_bwd", "fp4q_attn_bwd_noalloc", "fp4q_dequant", "fp4q_probe_mfma_fp4",
-               "fp4q_probe_copy"):
+               "fp4q_probe_copy", "fp4q_probe_mfma_fp8"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -492,6 +493,19 @@ def fp4q_probe_mfma_fp4(iters, workgroups, sink, codes=None, stream=None):
                                        0 if codes is None else codes.numel(), _stream_ptr(stream)),
            "fp4q_probe_mfma_fp4")
     return float(workgroups) * 4 * 8 * iters * 2.0 * 32 * 32 * 64
+
+
+def fp4q_probe_mfma_fp8(a, b, sa, sb, stream=None):
+    """Diagnostic: one block-scaled FP8 MFMA, C [32 x 32] fp32 = A B^T for E4M3
+    bytes a, b [32 x 64] and E8M0 bytes sa, sb [32 x 2] (contiguous uint8 CUDA
+    tensors)."""
+    for t, shape in ((a, (32, 64)), (b, (32, 64)), (sa, (32, 2)), (sb, (32, 2))):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise Fp4qError("fp4q_probe_mfma_fp8: contiguous uint8 CUDA tensors a, b [32 x 64], sa, sb [32 x 2]")
+    c = torch.empty((32, 32), dtype=torch.float32, device=a.device)
+    _check(_load().fp4q_probe_mfma_fp8(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), _ptr(c), _stream_ptr(stream)),
+           "fp4q_probe_mfma_fp8")
+    return c
 
 
 def fp4q_probe_copy(src, dst, workgroups=None, stream=None):

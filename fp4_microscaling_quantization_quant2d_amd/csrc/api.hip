@@ -835,4 +835,14 @@ int fp4q_probe_copy(const void* src, void* dst, int64_t bytes, int workgroups, v
                       "fp4q_probe_copy");
 }
 
+int fp4q_probe_mfma_fp8(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb, float* c,
+                        void* hip_stream)
+{
+    if (!a || !b || !sa || !sb || !c || (reinterpret_cast<uintptr_t>(a) & 3u) ||
+        (reinterpret_cast<uintptr_t>(b) & 3u))
+        return fail(FP4Q_EINVAL, "fp4q_probe_mfma_fp8: non-null buffers, a and b 4-byte aligned");
+    return hip_status(fp4q::launch_mfma_fp8_block(a, b, sa, sb, c, static_cast<hipStream_t>(hip_stream)),
+                      "fp4q_probe_mfma_fp8");
+}
+
 }  // extern "C"

@@ -112,4 +112,45 @@ hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int work
     return hipGetLastError();
 }
 
+namespace {
+
+// One block-scaled FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 A and B)
+// on a 32x64 A, a 32x64 B and their E8M0 scales (one per row and 32 K
+// values): C[32 x 32] = A B^T.  One wave; lane l holds row (column) l % 32
+// of A (B): registers 0-3 K values 16 (l / 32) .. +16 and registers 4-7 K
+// values 32 + 16 (l / 32) .. +16, so K-block j (K 32 j .. +32) is registers
+// 4j .. 4j+3 of both lane halves, and lane half j supplies K-block j's scale
+// byte.  Accumulator register r of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4]
+// [l % 32].
+__global__ __launch_bounds__(64) void mfma_fp8_block_kernel(const uint8_t* a, const uint8_t* b, const uint8_t* sa,
+                                                            const uint8_t* sb, float* c)
+{
+    const int l = threadIdx.x, row = l & 31, kh = l >> 5;
+    v8i va, vb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int k = (i >> 2) * 32 + kh * 16 + 4 * (i & 3);
+        va[i] = *reinterpret_cast<const int*>(a + row * 64 + k);
+        vb[i] = *reinterpret_cast<const int*>(b + row * 64 + k);
+    }
+    v16f acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        acc[r] = 0.0f;
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 0, 0, 0, (int)sa[row * 2 + kh], 0,
+                                                          (int)sb[row * 2 + kh]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        c[(8 * (r >> 2) + 4 * kh + (r & 3)) * 32 + row] = acc[r];
+}
+
+} // namespace
+
+hipError_t launch_mfma_fp8_block(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb, float* c,
+                                 hipStream_t s)
+{
+    hipLaunchKernelGGL(mfma_fp8_block_kernel, dim3(1), dim3(64), 0, s, a, b, sa, sb, c);
+    return hipGetLastError();
+}
+
 } // namespace fp4q

@@ -439,10 +439,21 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
  * and stores over `workgroups` workgroups of 256 threads; its rate (read +
  * written bytes over time) is the practical HBM ceiling of a read-once,
  * write-once kernel.
+ *
+ * fp4q_probe_mfma_fp8: ONE block-scaled FP8 MFMA (the same instruction with
+ * E4M3 operands), C = A B^T for a [32 x 64] and b [32 x 64] E4M3 bytes
+ * (row-major, device, 4-byte aligned), sa / sb [32 x 2] E8M0 bytes (one per
+ * row and 32 K values, device) and c [32 x 32] fp32 (row-major, device).  It
+ * exposes the instruction's own arithmetic, which rounds inside its dot
+ * product, so callers can compare it with the exact product; the MXFP8
+ * products above (Sec. 3.2 of the same page) form every product exactly
+ * instead.  Null or misaligned buffers: FP4Q_EINVAL.
  */
 int fp4q_probe_mfma_fp4(int64_t iters, int workgroups, float* sink, const uint8_t* codes, int64_t code_bytes,
                         void* hip_stream);
 int fp4q_probe_copy(const void* src, void* dst, int64_t bytes, int workgroups, void* hip_stream);
+int fp4q_probe_mfma_fp8(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb, float* c,
+                        void* hip_stream);
 
 #ifdef __cplusplus
 }

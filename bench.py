@@ -415,6 +415,56 @@ def side_bf16_out(torch, fq, wl, iters, warmup):
     return out
 
 
+def side_quant_cold(torch, fq, wl, iters, warmup):
+    """The quantizer alone on each tensor of the 7B step, every launch
+    preceded (outside its events) by a read of 1 GiB that evicts the 256 MB
+    MALL and the L2s without leaving dirty lines, so the input comes from HBM
+    ("cold"); and the same launches without the eviction ("warm": the input
+    may sit in the MALL).  Also "cold_dirty": a 1 GiB write before every
+    launch, whose dirty lines the launch then has to write back (the state a
+    GEMM's output leaves).  Median per launch; GB/s of algorithmic bytes
+    (3.001 B per bf16 element)."""
+    evict = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    out = {"workload": "quant2d (bf16, SR, 32x32) of each of the 12 tensors of the 7b-linear-layer-step, alone; "
+                       "cold: a 1 GiB read before every launch; cold_dirty: a 1 GiB write"}
+    modes = ("cold", "warm", "cold_dirty")
+    tot = {m: [0.0, 0.0] for m in modes}
+    for L in wl.config_7b():
+        for nm in ("X", "W", "dY"):
+            a = getattr(L, nm)
+            x = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+            q = fq.alloc_fp4(a.shape[0], a.shape[1])
+            nbytes = quant_bytes(a.shape[0], a.shape[1])
+            res = {}
+            for mode in modes:
+                t = []
+                for it in range(warmup + iters):
+                    if mode == "cold":
+                        evict.sum()
+                    elif mode == "cold_dirty":
+                        evict.fill_(float(it))
+                    else:
+                        gpu_head_start(torch, fq, 0.5)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fq.fp4q_quant2d(x, out=q, seed=it, stream_id=1)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    if it >= warmup:
+                        t.append(e0.elapsed_time(e1))
+                ms = float(np.median(t))
+                res[mode] = ms
+                tot[mode][0] += ms
+                tot[mode][1] += nbytes
+            out["%s:%s %dx%d" % (L.name, nm, a.shape[0], a.shape[1])] = {
+                m + "_GB/s": round(nbytes / (res[m] / 1e3) / 1e9, 1) for m in modes}
+            del x, q
+    for mode in modes:
+        out["all_%s_GB/s" % mode] = round(tot[mode][1] / (tot[mode][0] / 1e3) / 1e9, 1)
+    del evict
+    return out
+
+
 def side_fused_chain(torch, fq, wl, iters, warmup):
     """A chain of two 7B FFN projections (up 4096->11008, then down
     11008->4096, 8192 tokens, no activation between them), one training step,
@@ -884,8 +934,8 @@ def main():
     }
     if not args.no_side_paths:
         side = {}
-        for name, fn in (("1b", side_1b), ("fused_chain", side_fused_chain), ("moe", side_moe), ("attn", side_attn),
-                         ("blocks", side_blocks),
+        for name, fn in (("1b", side_1b), ("quant_cold", side_quant_cold), ("fused_chain", side_fused_chain),
+                         ("moe", side_moe), ("attn", side_attn), ("blocks", side_blocks),
                          ("act1d", side_act1d), ("wgrad_acc", side_wgrad_acc), ("bf16_out", side_bf16_out)):
             if args.side and name not in args.side.split(","):
                 continue

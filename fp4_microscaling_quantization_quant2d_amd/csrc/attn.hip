@@ -105,23 +105,55 @@ __device__ __forceinline__ v16f zero16()
     return z;
 }
 
+// Pair-transposed tiles.  A [64 x 128] bf16 tile X (rows: keys or queries)
+// is stored transposed with row pairs packed: row d of the stored tile holds
+// the dwords (X[2p][d], X[2p+1][d]).  Within each group of 16 rows (8 pairs)
+// the pairs are ordered so that the 8 rows one MFMA lane half contracts over
+// in a 16-row step -- rows 4h .. 4h+3 and 8+4h .. 8+4h+3 of the group, the
+// order in which a score tile's registers hold them -- are 16 contiguous
+// bytes: pair q of a group goes to dword slot q with bits 1 and 2 swapped.
+// One 16-byte read per operand then, and at a 144-byte row pitch the 16
+// lanes of a read cycle hit distinct banks.
+__device__ __forceinline__ int pair_slot(int p)
+{
+    return (p & ~7) | (p & 1) | ((p & 2) << 1) | ((p & 4) >> 1);
+}
+
+// `lo`, `hi`: 8 bf16 (d-chunk `dchunk` of 8) of rows 2p and 2p+1.
+__device__ __forceinline__ void store_pair_t(uint8_t* tt, int pitch, int dchunk, int p, v4u lo, v4u hi)
+{
+    uint8_t* base = tt + (8 * dchunk) * pitch + 4 * pair_slot(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint32_t*>(base + (2 * e) * pitch) = (lo[e] & 0xFFFFu) | (hi[e] << 16);
+        *reinterpret_cast<uint32_t*>(base + (2 * e + 1) * pitch) = (lo[e] >> 16) | (hi[e] & 0xFFFF0000u);
+    }
+}
+
+// The 8-value A operand of a product whose contraction runs over the rows of
+// a pair-transposed tile: stored row `row`, the 16-row step covering tile
+// rows [32 sb + 16 tp, +16), this lane half's 8 of them.
+__device__ __forceinline__ v8bf read_pair_t(const uint8_t* tt, int pitch, int row, int sb, int tp, int h)
+{
+    return *reinterpret_cast<const v8bf*>(tt + row * pitch + 2 * (32 * sb + 16 * tp) + 16 * h);
+}
+
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
 constexpr int kFwdQ = 128;                  // queries per workgroup (32 per wave)
 constexpr int kFwdK = 64;                   // keys per step
-constexpr int kKPitch = 136;                // bytes per key row of E4M3 codes in LDS
+constexpr int kKbPitch = 272;               // bytes per key row of the bf16 K tile (68 dwords: conflict-free)
 constexpr int kVtPitch = 144;               // bytes per d row of the key-pair-transposed V tile
-constexpr int kFwdKBytes = kFwdK * kKPitch;           // 8704
-constexpr int kFwdSBytes = kFwdK * 4;                 // 256: one scale dword per key
+constexpr int kFwdKBytes = kFwdK * kKbPitch;          // 17408
 constexpr int kFwdVBytes = kD * kVtPitch;             // 18432
-constexpr int kFwdBuf = kFwdKBytes + kFwdSBytes + kFwdVBytes;
+constexpr int kFwdBuf = kFwdKBytes + kFwdVBytes;      // 35840; two buffers, two workgroups per CU
 
 // Registers holding one key block on its way from memory to LDS.
 struct FwdStage {
-    v4u k[2];
+    v4u k[2];         // 16 E4M3 codes of one key
+    uint32_t ks[2];   // that key's scale dword (4 E8M0 bytes)
     v4u v[2][2];
-    uint32_t ks;
 };
 
 __device__ __forceinline__ void fwd_load(FwdStage& st, const AttnArgs& a, int64_t head_row, int k0)
@@ -130,8 +162,10 @@ __device__ __forceinline__ void fwd_load(FwdStage& st, const AttnArgs& a, int64_
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int u = t + kThreads * i, key = u >> 3, c = u & 7;
-        st.k[i] = k0 + key < a.L ? *reinterpret_cast<const v4u*>(a.kc + (head_row + k0 + key) * a.ldk + 16 * c)
-                                 : (v4u){0u, 0u, 0u, 0u};
+        const bool ok = k0 + key < a.L;
+        st.k[i] = ok ? *reinterpret_cast<const v4u*>(a.kc + (head_row + k0 + key) * a.ldk + 16 * c)
+                     : (v4u){0u, 0u, 0u, 0u};
+        st.ks[i] = ok ? *reinterpret_cast<const uint32_t*>(a.ks + (head_row + k0 + key) * a.ldks) : 0u;
         const int p = u & 31, dc = u >> 5;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -140,34 +174,31 @@ __device__ __forceinline__ void fwd_load(FwdStage& st, const AttnArgs& a, int64_
                                     : (v4u){0u, 0u, 0u, 0u};
         }
     }
-    st.ks = t < kFwdK && k0 + t < a.L ? *reinterpret_cast<const uint32_t*>(a.ks + (head_row + k0 + t) * a.ldks) : 0u;
 }
 
+// K is converted to bf16 here, once per block for the whole workgroup (each
+// code times its group's E8M0 scale, exact), so the waves read MFMA operands
+// straight from LDS.
 __device__ __forceinline__ void fwd_store(const FwdStage& st, uint8_t* buf)
 {
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int u = t + kThreads * i, key = u >> 3, c = u & 7;
-        *reinterpret_cast<v4u*>(buf + key * kKPitch + 16 * c) = st.k[i];
-        // V^T: dword (V[2p][d], V[2p+1][d]) at row d, keys 2p..2p+1
+        const float sc = e8m0_f32((st.ks[i] >> (8 * (c >> 1))) & 0xFFu);
+        uint8_t* kr = buf + key * kKbPitch + 32 * c;
+        *reinterpret_cast<v8bf*>(kr) = cvt8_e4m3((v2u){st.k[i].x, st.k[i].y}, sc);
+        *reinterpret_cast<v8bf*>(kr + 16) = cvt8_e4m3((v2u){st.k[i].z, st.k[i].w}, sc);
+        // V^T, key pairs packed (keys 2p, 2p+1 of d-chunk dc)
         const int p = u & 31, dc = u >> 5;
-        uint8_t* vt = buf + kFwdKBytes + kFwdSBytes + (8 * dc) * kVtPitch + 4 * p;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = st.v[i][0][e], hi = st.v[i][1][e];
-            *reinterpret_cast<uint32_t*>(vt + (2 * e) * kVtPitch) = (lo & 0xFFFFu) | (hi << 16);
-            *reinterpret_cast<uint32_t*>(vt + (2 * e + 1) * kVtPitch) = (lo >> 16) | (hi & 0xFFFF0000u);
-        }
+        store_pair_t(buf + kFwdKBytes, kVtPitch, dc, p, st.v[i][0], st.v[i][1]);
     }
-    if (t < kFwdK)
-        *reinterpret_cast<uint32_t*>(buf + kFwdKBytes + 4 * t) = st.ks;
 }
 
 template <bool CAUSAL, bool OBF>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFwdBuf];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     // blockIdx.x: head, blockIdx.y: query block, the last (longest causal
@@ -210,18 +241,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
         if (kb + 1 < nkb)
             fwd_load(st, a, head_row, k0 + kFwdK);
 
-        // S^T for the 64 keys: two 32-key sub-blocks.
+    // S^T for the 64 keys: two 32-key sub-blocks.
         v16f s[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-            const int key = 32 * sb + l32;
-            const uint32_t ksc = *reinterpret_cast<const uint32_t*>(buf + kFwdKBytes + 4 * key);
+            const uint8_t* kr = buf + (32 * sb + l32) * kKbPitch + 16 * h;
             s[sb] = zero16();
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const v2u raw = *reinterpret_cast<const v2u*>(buf + key * kKPitch + 16 * t + 8 * h);
-                s[sb] = mfma_bf16(cvt8_e4m3(raw, e8m0_f32((ksc >> (8 * (t >> 1))) & 0xFFu)), qb16[t], s[sb]);
-            }
+            for (int t = 0; t < 8; ++t)
+                s[sb] = mfma_bf16(*reinterpret_cast<const v8bf*>(kr + 32 * t), qb16[t], s[sb]);
         }
         // mask keys past the sequence and (causal) after the query
         const bool edge = k0 + kFwdK > a.L || (CAUSAL && k0 + kFwdK - 1 > q0);
@@ -243,9 +271,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
             for (int r = 0; r < 16; ++r)
                 mx = fmaxf(mx, s[sb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
+        // Lazy rescaling: the reference m moves only when this block's max
+        // passes it by more than 8 in log2 units (or m is still -inf; both
+        // -inf gives NaN, no move), so P = exp2(c s - c m) stays below 2^8,
+        // and O and l are rescaled only when some row of the wave moved.
+        const bool grow = c * (mx - m) > 8.0f;
+        const float m_new = grow ? mx : m;
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(c * (m - m_use));
         const float cm = c * m_use;
         float rs = 0.0f;
 #pragma unroll
@@ -256,29 +288,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
                 rs += s[sb][r];
             }
         rs += __shfl_xor(rs, 32);
-        l = l * alpha + rs;
+        if (__any(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(c * (m - m_use)) : 1.0f;
+            l *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    o[i][r] *= alpha;
+        }
+        l += rs;
         m = m_new;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                o[i][r] *= alpha;
         // O^T += V^T P^T over four 16-key steps
-        const uint8_t* vt = buf + kFwdKBytes + kFwdSBytes;
+        const uint8_t* vt = buf + kFwdKBytes;
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
             const int sb = t4 >> 1, tp = t4 & 1;
             const v4u pw = {pack_bf16(s[sb][8 * tp + 0], s[sb][8 * tp + 1]), pack_bf16(s[sb][8 * tp + 2], s[sb][8 * tp + 3]),
                             pack_bf16(s[sb][8 * tp + 4], s[sb][8 * tp + 5]), pack_bf16(s[sb][8 * tp + 6], s[sb][8 * tp + 7])};
             const v8bf pb = __builtin_bit_cast(v8bf, pw);
-            const int kk = 32 * sb + 16 * tp + 4 * h;   // keys kk..kk+3 and kk+8..kk+11
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const uint8_t* row = vt + (32 * db + l32) * kVtPitch + 2 * kk;
-                const v2u lo = *reinterpret_cast<const v2u*>(row);
-                const v2u hi = *reinterpret_cast<const v2u*>(row + 16);
-                o[db] = mfma_bf16(__builtin_bit_cast(v8bf, (v4u){lo.x, lo.y, hi.x, hi.y}), pb, o[db]);
-            }
+            for (int db = 0; db < 4; ++db)
+                o[db] = mfma_bf16(read_pair_t(vt, kVtPitch, 32 * db + l32, sb, tp, h), pb, o[db]);
         }
         if (kb + 1 < nkb) {
             __syncthreads();   // every wave is done with the other buffer
@@ -353,30 +384,6 @@ __global__ __launch_bounds__(kThreads) void attn_delta_kernel(AttnArgs a)
     a.delta[row] = acc;
 }
 
-// Pairs of rows of a [64 x 128] tile, transposed into bf16 dwords: row d of
-// the transposed tile holds, at dword p, (X[2p][d], X[2p+1][d]).  `lo`, `hi`:
-// 8 bf16 (one d-chunk of 8) of rows 2p and 2p+1.
-__device__ __forceinline__ void store_pair_t(uint8_t* tt, int pitch, int dchunk, int p, v4u lo, v4u hi)
-{
-    uint8_t* base = tt + (8 * dchunk) * pitch + 4 * p;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint32_t*>(base + (2 * e) * pitch) = (lo[e] & 0xFFFFu) | (hi[e] << 16);
-        *reinterpret_cast<uint32_t*>(base + (2 * e + 1) * pitch) = (lo[e] >> 16) | (hi[e] & 0xFFFF0000u);
-    }
-}
-
-// The 8-value A operand of a product whose contraction runs over the rows of
-// a key-pair-transposed tile: row `row`, 16-element step covering tile rows
-// [32 sb + 16 tp, +16), this lane half's permuted 8 of them.
-__device__ __forceinline__ v8bf read_pair_t(const uint8_t* tt, int pitch, int row, int sb, int tp, int h)
-{
-    const uint8_t* p = tt + row * pitch + 2 * (32 * sb + 16 * tp + 4 * h);
-    const v2u lo = *reinterpret_cast<const v2u*>(p);
-    const v2u hi = *reinterpret_cast<const v2u*>(p + 16);
-    return __builtin_bit_cast(v8bf, (v4u){lo.x, lo.y, hi.x, hi.y});
-}
-
 // Registers of a score-shaped tile (16 of them, rows 8(r/4) + 4h + r%4),
 // its 16-row step tp as the 8-value operand of the next product, in bf16.
 __device__ __forceinline__ v8bf pack_step(const v16f& x, int tp)
@@ -390,17 +397,15 @@ __device__ __forceinline__ v8bf pack_step(const v16f& x, int tp)
 constexpr int kDqQ = 128;                  // queries per workgroup
 constexpr int kDqK = 64;                   // keys per step
 constexpr int kRowPitch = 272;             // bytes per row of a row-major bf16 [64 x 128] tile
-constexpr int kDqKc = kDqK * kKPitch;      // K codes
-constexpr int kDqKs = kDqK * 4;            // K scales
+constexpr int kDqKb = kDqK * kRowPitch;    // K row-major bf16 (converted once per block)
 constexpr int kDqV = kDqK * kRowPitch;     // V row-major bf16
 constexpr int kDqKt = kD * kVtPitch;       // K^T bf16 (key pairs)
-constexpr int kDqBuf = kDqKc + kDqKs + kDqV + kDqKt;
+constexpr int kDqBuf = kDqKb + kDqV + kDqKt;
 
 struct DqStage {
     v2u kc[2][2];   // K codes of keys 2p, 2p+1, 8 bytes at d-chunk dc
     uint32_t ksb[2][2];
     v4u v[2][2];    // V rows 2p, 2p+1, d-chunk dc (8 bf16)
-    uint32_t ks;
 };
 
 __device__ __forceinline__ void dq_load(DqStage& st, const AttnArgs& a, int64_t head_row, int k0)
@@ -418,7 +423,6 @@ __device__ __forceinline__ void dq_load(DqStage& st, const AttnArgs& a, int64_t 
             st.v[i][e] = ok ? *reinterpret_cast<const v4u*>(a.v + (head_row + key) * a.ldv + 8 * dc) : (v4u){0u, 0u, 0u, 0u};
         }
     }
-    st.ks = t < kDqK && k0 + t < a.L ? *reinterpret_cast<const uint32_t*>(a.ks + (head_row + k0 + t) * a.ldks) : 0u;
 }
 
 __device__ __forceinline__ void dq_store(const DqStage& st, uint8_t* buf)
@@ -431,14 +435,12 @@ __device__ __forceinline__ void dq_store(const DqStage& st, uint8_t* buf)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int key = 2 * p + e;
-            *reinterpret_cast<v2u*>(buf + key * kKPitch + 8 * dc) = st.kc[i][e];
-            *reinterpret_cast<v4u*>(buf + kDqKc + kDqKs + key * kRowPitch + 16 * dc) = st.v[i][e];
             kb[e] = __builtin_bit_cast(v4u, cvt8_e4m3(st.kc[i][e], e8m0_f32(st.ksb[i][e])));
+            *reinterpret_cast<v4u*>(buf + key * kRowPitch + 16 * dc) = kb[e];
+            *reinterpret_cast<v4u*>(buf + kDqKb + key * kRowPitch + 16 * dc) = st.v[i][e];
         }
-        store_pair_t(buf + kDqKc + kDqKs + kDqV, kVtPitch, dc, p, kb[0], kb[1]);
+        store_pair_t(buf + kDqKb + kDqV, kVtPitch, dc, p, kb[0], kb[1]);
     }
-    if (t < kDqK)
-        *reinterpret_cast<uint32_t*>(buf + kDqKc + 4 * t) = st.ks;
 }
 
 template <bool CAUSAL>
@@ -492,15 +494,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dq_kernel(AttnArgs a)
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int key = 32 * sb + l32;
-            const uint32_t ksc = *reinterpret_cast<const uint32_t*>(buf + kDqKc + 4 * key);
             s[sb] = zero16();
             dp[sb] = zero16();
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const v2u raw = *reinterpret_cast<const v2u*>(buf + key * kKPitch + 16 * t + 8 * h);
-                s[sb] = mfma_bf16(cvt8_e4m3(raw, e8m0_f32((ksc >> (8 * (t >> 1))) & 0xFFu)), qb16[t], s[sb]);
-                const v4u vw = *reinterpret_cast<const v4u*>(buf + kDqKc + kDqKs + key * kRowPitch + 32 * t + 16 * h);
-                dp[sb] = mfma_bf16(__builtin_bit_cast(v8bf, vw), gb16[t], dp[sb]);
+                const v8bf kw = *reinterpret_cast<const v8bf*>(buf + key * kRowPitch + 32 * t + 16 * h);
+                s[sb] = mfma_bf16(kw, qb16[t], s[sb]);
+                const v8bf vw = *reinterpret_cast<const v8bf*>(buf + kDqKb + key * kRowPitch + 32 * t + 16 * h);
+                dp[sb] = mfma_bf16(vw, gb16[t], dp[sb]);
             }
         }
         // dS^T = P^T (dP^T - D), with P^T = 0 for keys past the sequence,
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dq_kernel(AttnArgs a)
                 s[sb][r] = qok ? pv * (dp[sb][r] - dlt) : 0.0f;
             }
         // dQ^T += K^T dS^T
-        const uint8_t* kt = buf + kDqKc + kDqKs + kDqV;
+        const uint8_t* kt = buf + kDqKb + kDqV;
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
             const int sb = t4 >> 1, tp = t4 & 1;
@@ -550,20 +551,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dq_kernel(AttnArgs a)
 // ---- dK, dV ----
 constexpr int kDkK = 128;                  // keys per workgroup
 constexpr int kDkQ = 64;                   // queries per step
-constexpr int kDkQc = kDkQ * kKPitch;      // Q codes
-constexpr int kDkQs = kDkQ * 4;            // Q scales
+constexpr int kDkQb = kDkQ * kRowPitch;    // Q row-major bf16 (converted once per block)
 constexpr int kDkQt = kD * kVtPitch;       // Q^T bf16 (query pairs)
 constexpr int kDkG = kDkQ * kRowPitch;     // dO row-major
 constexpr int kDkGt = kD * kVtPitch;       // dO^T (query pairs)
 constexpr int kDkL = kDkQ * 4;             // lse (log2 units) of the queries
 constexpr int kDkDl = kDkQ * 4;            // D of the queries
-constexpr int kDkBuf = kDkQc + kDkQs + kDkQt + kDkG + kDkGt + kDkL + kDkDl;
+constexpr int kDkBuf = kDkQb + kDkQt + kDkG + kDkGt + kDkL + kDkDl;
 
 struct DkStage {
     v2u qc[2][2];
     uint32_t qsb[2][2];
     v4u g[2][2];
-    uint32_t qs;
     float ls, dl;
 };
 
@@ -584,7 +583,6 @@ __device__ __forceinline__ void dk_load(DkStage& st, const AttnArgs& a, int64_t 
         }
     }
     const bool ok = t < kDkQ && i0 + t < a.L;
-    st.qs = ok ? *reinterpret_cast<const uint32_t*>(a.qs + (head_row + i0 + t) * a.ldqs) : 0u;
     st.ls = ok ? a.lse[head_row + i0 + t] * kLog2e : 0.0f;
     st.dl = ok ? a.delta[head_row + i0 + t] : 0.0f;
 }
@@ -599,17 +597,16 @@ __device__ __forceinline__ void dk_store(const DkStage& st, uint8_t* buf)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int qq = 2 * p + e;
-            *reinterpret_cast<v2u*>(buf + qq * kKPitch + 8 * dc) = st.qc[i][e];
-            *reinterpret_cast<v4u*>(buf + kDkQc + kDkQs + kDkQt + qq * kRowPitch + 16 * dc) = st.g[i][e];
             qb[e] = __builtin_bit_cast(v4u, cvt8_e4m3(st.qc[i][e], e8m0_f32(st.qsb[i][e])));
+            *reinterpret_cast<v4u*>(buf + qq * kRowPitch + 16 * dc) = qb[e];
+            *reinterpret_cast<v4u*>(buf + kDkQb + kDkQt + qq * kRowPitch + 16 * dc) = st.g[i][e];
         }
-        store_pair_t(buf + kDkQc + kDkQs, kVtPitch, dc, p, qb[0], qb[1]);
-        store_pair_t(buf + kDkQc + kDkQs + kDkQt + kDkG, kVtPitch, dc, p, st.g[i][0], st.g[i][1]);
+        store_pair_t(buf + kDkQb, kVtPitch, dc, p, qb[0], qb[1]);
+        store_pair_t(buf + kDkQb + kDkQt + kDkG, kVtPitch, dc, p, st.g[i][0], st.g[i][1]);
     }
     if (t < kDkQ) {
-        *reinterpret_cast<uint32_t*>(buf + kDkQc + 4 * t) = st.qs;
-        reinterpret_cast<float*>(buf + kDkQc + kDkQs + kDkQt + kDkG + kDkGt)[t] = st.ls;
-        reinterpret_cast<float*>(buf + kDkQc + kDkQs + kDkQt + kDkG + kDkGt + kDkL)[t] = st.dl;
+        reinterpret_cast<float*>(buf + kDkQb + kDkQt + kDkG + kDkGt)[t] = st.ls;
+        reinterpret_cast<float*>(buf + kDkQb + kDkQt + kDkG + kDkGt + kDkL)[t] = st.dl;
     }
 }
 
@@ -657,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_kernel(AttnArgs a)
         const int i0 = ib * kDkQ;
         if (ib + 1 < nib)
             dk_load(st, a, head_row, i0 + kDkQ);
-        const uint8_t* qt = buf + kDkQc + kDkQs;
+        const uint8_t* qt = buf + kDkQb;
         const uint8_t* g = qt + kDkQt;
         const uint8_t* gt = g + kDkG;
         const float* lsv = reinterpret_cast<const float*>(gt + kDkGt);
@@ -666,13 +663,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_kernel(AttnArgs a)
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
             const int qr = 32 * qs + l32;
-            const uint32_t qsc = *reinterpret_cast<const uint32_t*>(buf + kDkQc + 4 * qr);
             s[qs] = zero16();
             dp[qs] = zero16();
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const v2u raw = *reinterpret_cast<const v2u*>(buf + qr * kKPitch + 16 * t + 8 * h);
-                s[qs] = mfma_bf16(cvt8_e4m3(raw, e8m0_f32((qsc >> (8 * (t >> 1))) & 0xFFu)), kb16[t], s[qs]);
+                const v8bf qw = *reinterpret_cast<const v8bf*>(buf + qr * kRowPitch + 32 * t + 16 * h);
+                s[qs] = mfma_bf16(qw, kb16[t], s[qs]);
                 const v4u gw = *reinterpret_cast<const v4u*>(g + qr * kRowPitch + 32 * t + 16 * h);
                 dp[qs] = mfma_bf16(__builtin_bit_cast(v8bf, gw), vb16[t], dp[qs]);
             }
@@ -792,13 +788,16 @@ hipError_t attn_noalloc_scratch(float** p)
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s)
 {
+    constexpr size_t kFwdLds = 2 * kFwdBuf;
+    static_assert(2 * kFwdLds <= 160 * 1024, "two forward workgroups per CU");
     const dim3 grid(a.bh, (a.L + kFwdQ - 1) / kFwdQ);
-    if (a.causal)
-        hipLaunchKernelGGL((a.o_bf16 ? attn_fwd_kernel<true, true> : attn_fwd_kernel<true, false>), grid,
-                           dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((a.o_bf16 ? attn_fwd_kernel<false, true> : attn_fwd_kernel<false, false>), grid,
-                           dim3(kThreads), 0, s, a);
+    auto fn = a.causal ? (a.o_bf16 ? attn_fwd_kernel<true, true> : attn_fwd_kernel<true, false>)
+                       : (a.o_bf16 ? attn_fwd_kernel<false, true> : attn_fwd_kernel<false, false>);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kFwdLds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(fn, grid, dim3(kThreads), kFwdLds, s, a);
     return hipGetLastError();
 }
 

@@ -734,6 +734,11 @@ int check_attn(const char* fn, const fp4q_qtensor* q, const fp4q_qtensor* k, con
         return fail(FP4Q_EINVAL, "%s: scale must be positive and finite", fn);
     if (causal != 0 && causal != 1)
         return fail(FP4Q_EINVAL, "%s: causal must be 0 or 1", fn);
+    // the kernels address a head's rows with 32-bit element offsets
+    const int64_t kHeadSlice = (int64_t)1 << 31;
+    if (seq_len * q->ld >= kHeadSlice || seq_len * k->ld >= kHeadSlice || seq_len * q->ld_s >= kHeadSlice ||
+        seq_len * k->ld_s >= kHeadSlice || seq_len * ldv >= kHeadSlice || seq_len * ldo >= kHeadSlice)
+        return fail(FP4Q_EINVAL, "%s: seq_len x leading dimension must stay below 2^31 elements per head", fn);
     a = fp4q::AttnArgs{};
     a.qc = q->codes;
     a.ldq = q->ld;
@@ -783,6 +788,8 @@ int fp4q_attn_bwd(const fp4q_qtensor* q, const fp4q_qtensor* k, const void* v, i
         return fail(FP4Q_EINVAL, "fp4q_attn_bwd: dout needs lddo >= 128, a multiple of 8, and 16-byte alignment");
     if (!dq || !dk || !dv || ldg < 128 || ldg % 4 || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return fail(FP4Q_EINVAL, "fp4q_attn_bwd: dq, dk, dv need ldg >= 128, a multiple of 4, 16-byte alignment");
+    if (seq_len * lddo >= ((int64_t)1 << 31) || seq_len * ldg >= ((int64_t)1 << 31))
+        return fail(FP4Q_EINVAL, "fp4q_attn_bwd: seq_len x leading dimension must stay below 2^31 elements per head");
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 3u))
         return fail(FP4Q_EINVAL, "fp4q_attn_bwd: workspace of bh*seq_len floats required");
     a.dout = static_cast<const uint16_t*>(dout);

@@ -67,6 +67,16 @@ __device__ __forceinline__ void sfor(F&& f)
     sfor_impl(f, std::make_integer_sequence<int, N>());
 }
 
+// Element `col` of row `row` of a head's slice: the head's base is uniform
+// (scalar registers) and the rest a 32-bit offset, which the loads take as a
+// vector offset on a scalar base (the host keeps every head's slice of
+// every tensor below 2 GiB).
+template <typename T>
+__device__ __forceinline__ const T* head_at(const T* base, int64_t head_row, int64_t ld, int row, int col)
+{
+    return base + head_row * ld + (uint32_t)(row * (uint32_t)ld + col);
+}
+
 // 2^(b - 127) as a float (b = 0: the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_f32(uint32_t b)
 {
@@ -163,14 +173,14 @@ __device__ __forceinline__ void fwd_load(FwdStage& st, const AttnArgs& a, int64_
     for (int i = 0; i < 2; ++i) {
         const int u = t + kThreads * i, key = u >> 3, c = u & 7;
         const bool ok = k0 + key < a.L;
-        st.k[i] = ok ? *reinterpret_cast<const v4u*>(a.kc + (head_row + k0 + key) * a.ldk + 16 * c)
+        st.k[i] = ok ? *reinterpret_cast<const v4u*>(head_at(a.kc, head_row, a.ldk, k0 + key, 16 * c))
                      : (v4u){0u, 0u, 0u, 0u};
-        st.ks[i] = ok ? *reinterpret_cast<const uint32_t*>(a.ks + (head_row + k0 + key) * a.ldks) : 0u;
+        st.ks[i] = ok ? *reinterpret_cast<const uint32_t*>(head_at(a.ks, head_row, a.ldks, k0 + key, 0)) : 0u;
         const int p = u & 31, dc = u >> 5;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int key2 = k0 + 2 * p + e;
-            st.v[i][e] = key2 < a.L ? *reinterpret_cast<const v4u*>(a.v + (head_row + key2) * a.ldv + 8 * dc)
+            st.v[i][e] = key2 < a.L ? *reinterpret_cast<const v4u*>(head_at(a.v, head_row, a.ldv, key2, 8 * dc))
                                     : (v4u){0u, 0u, 0u, 0u};
         }
     }
@@ -418,9 +428,11 @@ __device__ __forceinline__ void dq_load(DqStage& st, const AttnArgs& a, int64_t 
         for (int e = 0; e < 2; ++e) {
             const int key = k0 + 2 * p + e;
             const bool ok = key < a.L;
-            st.kc[i][e] = ok ? *reinterpret_cast<const v2u*>(a.kc + (head_row + key) * a.ldk + 8 * dc) : (v2u){0u, 0u};
-            st.ksb[i][e] = ok ? a.ks[(head_row + key) * a.ldks + (dc >> 2)] : 0u;
-            st.v[i][e] = ok ? *reinterpret_cast<const v4u*>(a.v + (head_row + key) * a.ldv + 8 * dc) : (v4u){0u, 0u, 0u, 0u};
+            st.kc[i][e] = ok ? *reinterpret_cast<const v2u*>(head_at(a.kc, head_row, a.ldk, key, 8 * dc))
+                             : (v2u){0u, 0u};
+            st.ksb[i][e] = ok ? *head_at(a.ks, head_row, a.ldks, key, dc >> 2) : 0u;
+            st.v[i][e] = ok ? *reinterpret_cast<const v4u*>(head_at(a.v, head_row, a.ldv, key, 8 * dc))
+                            : (v4u){0u, 0u, 0u, 0u};
         }
     }
 }
@@ -444,7 +456,7 @@ __device__ __forceinline__ void dq_store(const DqStage& st, uint8_t* buf)
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_dq_kernel(AttnArgs a)
+__global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(AttnArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -479,59 +491,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dq_kernel(AttnArgs a)
     for (int i = 0; i < 4; ++i)
         dq[i] = zero16();
 
+    // One LDS buffer: the next key block is loaded into registers during a
+    // step and stored between the step's two barriers.  Two workgroups per
+    // CU (two waves per SIMD) hide each other's latencies.
     const int nkb_all = (a.L + kDqK - 1) / kDqK;
     const int nkb = CAUSAL ? min(nkb_all, (qb * kDqQ + kDqQ - 1) / kDqK + 1) : nkb_all;
+    const uint8_t* buf = lds;
+    const uint8_t* kt = buf + kDqKb + kDqV;
     DqStage st;
     dq_load(st, a, head_row, 0);
     dq_store(st, lds);
     __syncthreads();
     for (int kb = 0; kb < nkb; ++kb) {
-        const uint8_t* buf = lds + (kb & 1) * kDqBuf;
         const int k0 = kb * kDqK;
         if (kb + 1 < nkb)
             dq_load(st, a, head_row, k0 + kDqK);
-        v16f s[2], dp[2];
+        const bool edge = k0 + kDqK > a.L || (CAUSAL && k0 + kDqK - 1 > q0);
+        // one 32-key half at a time: S^T, dP^T, dS^T = P^T (dP^T - D) with
+        // P^T = 0 for keys past the sequence, (causal) after the query, and
+        // for queries past the sequence; then dQ^T += K^T dS^T
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int key = 32 * sb + l32;
-            s[sb] = zero16();
-            dp[sb] = zero16();
+            v16f sv = zero16(), dp = zero16();
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const v8bf kw = *reinterpret_cast<const v8bf*>(buf + key * kRowPitch + 32 * t + 16 * h);
-                s[sb] = mfma_bf16(kw, qb16[t], s[sb]);
+                sv = mfma_bf16(kw, qb16[t], sv);
                 const v8bf vw = *reinterpret_cast<const v8bf*>(buf + kDqKb + key * kRowPitch + 32 * t + 16 * h);
-                dp[sb] = mfma_bf16(vw, gb16[t], dp[sb]);
+                dp = mfma_bf16(vw, gb16[t], dp);
             }
-        }
-        // dS^T = P^T (dP^T - D), with P^T = 0 for keys past the sequence,
-        // (causal) after the query, and for queries past the sequence
-        const bool edge = k0 + kDqK > a.L || (CAUSAL && k0 + kDqK - 1 > q0);
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(c, s[sb][r], -lse2));
+                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(c, sv[r], -lse2));
                 if (edge) {
-                    const int key = k0 + 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (key >= a.L || (CAUSAL && key > q))
+                    const int kk = k0 + 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (kk >= a.L || (CAUSAL && kk > q))
                         pv = 0.0f;
                 }
-                s[sb][r] = qok ? pv * (dp[sb][r] - dlt) : 0.0f;
+                sv[r] = qok ? pv * (dp[r] - dlt) : 0.0f;
             }
-        // dQ^T += K^T dS^T
-        const uint8_t* kt = buf + kDqKb + kDqV;
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-            const int sb = t4 >> 1, tp = t4 & 1;
-            const v8bf bds = pack_step(s[sb], tp);
+            for (int tp = 0; tp < 2; ++tp) {
+                const v8bf bds = pack_step(sv, tp);
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-                dq[db] = mfma_bf16(read_pair_t(kt, kVtPitch, 32 * db + l32, sb, tp, h), bds, dq[db]);
+                for (int db = 0; db < 4; ++db)
+                    dq[db] = mfma_bf16(read_pair_t(kt, kVtPitch, 32 * db + l32, sb, tp, h), bds, dq[db]);
+            }
         }
         if (kb + 1 < nkb) {
-            __syncthreads();
-            dq_store(st, lds + ((kb + 1) & 1) * kDqBuf);
+            __syncthreads();   // every wave is done with the buffer
+            dq_store(st, lds);
             __syncthreads();
         }
     }
@@ -561,7 +571,7 @@ constexpr int kDkBuf = kDkQb + kDkQt + kDkG + kDkGt + kDkL + kDkDl;
 
 struct DkStage {
     v2u qc[2][2];
-    uint32_t qsb[2][2];
+    uint32_t qsb;     // the four E8M0 bytes of qc, byte 2i + e
     v4u g[2][2];
     float ls, dl;
 };
@@ -576,9 +586,11 @@ __device__ __forceinline__ void dk_load(DkStage& st, const AttnArgs& a, int64_t 
         for (int e = 0; e < 2; ++e) {
             const int qq = i0 + 2 * p + e;
             const bool ok = qq < a.L;
-            st.qc[i][e] = ok ? *reinterpret_cast<const v2u*>(a.qc + (head_row + qq) * a.ldq + 8 * dc) : (v2u){0u, 0u};
-            st.qsb[i][e] = ok ? a.qs[(head_row + qq) * a.ldqs + (dc >> 2)] : 0u;
-            st.g[i][e] = ok ? *reinterpret_cast<const v4u*>(a.dout + (head_row + qq) * a.lddo + 8 * dc)
+            st.qc[i][e] = ok ? *reinterpret_cast<const v2u*>(head_at(a.qc, head_row, a.ldq, qq, 8 * dc))
+                             : (v2u){0u, 0u};
+            const uint32_t sb = ok ? *head_at(a.qs, head_row, a.ldqs, qq, dc >> 2) : 0u;
+            st.qsb = (i | e) ? st.qsb | (sb << (8 * (2 * i + e))) : sb;
+            st.g[i][e] = ok ? *reinterpret_cast<const v4u*>(head_at(a.dout, head_row, a.lddo, qq, 8 * dc))
                             : (v4u){0u, 0u, 0u, 0u};
         }
     }
@@ -597,7 +609,7 @@ __device__ __forceinline__ void dk_store(const DkStage& st, uint8_t* buf)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int qq = 2 * p + e;
-            qb[e] = __builtin_bit_cast(v4u, cvt8_e4m3(st.qc[i][e], e8m0_f32(st.qsb[i][e])));
+            qb[e] = __builtin_bit_cast(v4u, cvt8_e4m3(st.qc[i][e], e8m0_f32((st.qsb >> (8 * (2 * i + e))) & 0xFFu)));
             *reinterpret_cast<v4u*>(buf + qq * kRowPitch + 16 * dc) = qb[e];
             *reinterpret_cast<v4u*>(buf + kDkQb + kDkQt + qq * kRowPitch + 16 * dc) = st.g[i][e];
         }
@@ -610,8 +622,10 @@ __device__ __forceinline__ void dk_store(const DkStage& st, uint8_t* buf)
     }
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_dkdv_kernel(AttnArgs a)
+// DV: dV += P^T dO (needs S only); else dK += dS^T Q (needs S and dP).  Two
+// kernels rather than one, so each fits two waves per SIMD; both recompute S.
+template <bool CAUSAL, bool DV>
+__global__ __launch_bounds__(kThreads, 2) void attn_dkdv_kernel(AttnArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -624,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_kernel(AttnArgs a)
     const float c = a.scale * kLog2e;
 
     // this lane's key: K (B operand of S = Q K^T), V (B operand of dP = dO V^T)
-    v8bf kb16[8], vb16[8];
+    v8bf kb16[8], vb16[DV ? 1 : 8];
     {
         const uint32_t sc = kok ? *reinterpret_cast<const uint32_t*>(a.ks + (head_row + j) * a.ldks) : 0u;
 #pragma unroll
@@ -632,100 +646,108 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_kernel(AttnArgs a)
             const v2u raw = kok ? *reinterpret_cast<const v2u*>(a.kc + (head_row + j) * a.ldk + 16 * t + 8 * h)
                                 : (v2u){0u, 0u};
             kb16[t] = cvt8_e4m3(raw, e8m0_f32((sc >> (8 * (t >> 1))) & 0xFFu));
-            const v4u vw = kok ? *reinterpret_cast<const v4u*>(a.v + (head_row + j) * a.ldv + 16 * t + 8 * h)
-                               : (v4u){0u, 0u, 0u, 0u};
-            vb16[t] = __builtin_bit_cast(v8bf, vw);
+            if constexpr (!DV) {
+                const v4u vw = kok ? *reinterpret_cast<const v4u*>(a.v + (head_row + j) * a.ldv + 16 * t + 8 * h)
+                                   : (v4u){0u, 0u, 0u, 0u};
+                vb16[t] = __builtin_bit_cast(v8bf, vw);
+            }
         }
     }
-    v16f dk[4], dv[4];
+    v16f acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        dk[i] = zero16();
-        dv[i] = zero16();
-    }
+    for (int i = 0; i < 4; ++i)
+        acc[i] = zero16();
+    // One LDS buffer (see the dQ kernel), two workgroups per CU.
     const int nib = (a.L + kDkQ - 1) / kDkQ;
     const int ib0 = CAUSAL ? (kb * kDkK) / kDkQ : 0;   // the first query block that sees a key of the tile
+    const uint8_t* buf = lds;
+    const uint8_t* qt = buf + kDkQb;
+    const uint8_t* g = qt + kDkQt;
+    const uint8_t* gt = g + kDkG;
+    const float* lsv = reinterpret_cast<const float*>(gt + kDkGt);
+    const float* dlv = lsv + kDkQ;
     DkStage st;
     dk_load(st, a, head_row, ib0 * kDkQ);
     dk_store(st, lds);
     __syncthreads();
     for (int ib = ib0; ib < nib; ++ib) {
-        const uint8_t* buf = lds + ((ib - ib0) & 1) * kDkBuf;
         const int i0 = ib * kDkQ;
-        if (ib + 1 < nib)
+        if (DV && ib + 1 < nib)
             dk_load(st, a, head_row, i0 + kDkQ);
-        const uint8_t* qt = buf + kDkQb;
-        const uint8_t* g = qt + kDkQt;
-        const uint8_t* gt = g + kDkG;
-        const float* lsv = reinterpret_cast<const float*>(gt + kDkGt);
-        const float* dlv = lsv + kDkQ;
-        v16f s[2], dp[2];
+        // rows = queries 32 qs + 8(r/4) + 4h + r%4; zero past the sequence
+        // and (causal) where the key follows the query
+        const bool edge = i0 + kDkQ > a.L || (CAUSAL && i0 < j0 + 31);
+        // one 32-query half at a time: S = Q K^T, P = exp2(c S - lse2),
+        // then dV += P^T dO, or dP = dO V^T, dS = P (dP - D), dK += dS^T Q,
+        // over the half's two 16-query steps
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
-            const int qr = 32 * qs + l32;
-            s[qs] = zero16();
-            dp[qs] = zero16();
+            // the dK kernel's loads of the next query block go out with the
+            // second half, so their registers are live for half a step (the
+            // dV kernel has the registers to issue them at the top)
+            if (!DV && qs == 1 && ib + 1 < nib)
+                dk_load(st, a, head_row, i0 + kDkQ);
+            const int qr0 = 32 * qs + l32;
+            v16f sv = zero16(), dp = zero16();
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const v8bf qw = *reinterpret_cast<const v8bf*>(buf + qr * kRowPitch + 32 * t + 16 * h);
-                s[qs] = mfma_bf16(qw, kb16[t], s[qs]);
-                const v4u gw = *reinterpret_cast<const v4u*>(g + qr * kRowPitch + 32 * t + 16 * h);
-                dp[qs] = mfma_bf16(__builtin_bit_cast(v8bf, gw), vb16[t], dp[qs]);
+                const v8bf qw = *reinterpret_cast<const v8bf*>(buf + qr0 * kRowPitch + 32 * t + 16 * h);
+                sv = mfma_bf16(qw, kb16[t], sv);
+                if constexpr (!DV) {
+                    const v8bf gw = *reinterpret_cast<const v8bf*>(g + qr0 * kRowPitch + 32 * t + 16 * h);
+                    dp = mfma_bf16(gw, vb16[t], dp);
+                }
             }
-        }
-        // P = exp2(c S - lse2) and dS = P (dP - D), rows = queries
-        // 32 qs + 8(r/4) + 4h + r%4; zero past the sequence and (causal)
-        // where the key follows the query
-        const bool edge = i0 + kDkQ > a.L || (CAUSAL && i0 < j0 + 31);
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int qr = 32 * qs + 8 * g4 + 4 * h;
                 const float4 l4 = *reinterpret_cast<const float4*>(lsv + qr);
-                const float4 d4 = *reinterpret_cast<const float4*>(dlv + qr);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                float dv4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (!DV) {
+                    const float4 d4 = *reinterpret_cast<const float4*>(dlv + qr);
+                    dv4[0] = d4.x; dv4[1] = d4.y; dv4[2] = d4.z; dv4[3] = d4.w;
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g4 + e;
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(c, s[qs][r], -lv[e]));
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(c, sv[r], -lv[e]));
                     if (edge) {
                         const int qq = i0 + qr + e;
                         if (qq >= a.L || (CAUSAL && j > qq))
                             pv = 0.0f;
                     }
-                    s[qs][r] = pv;
-                    dp[qs][r] = pv * (dp[qs][r] - dv4[e]);
+                    if constexpr (DV)
+                        sv[r] = pv;
+                    else
+                        sv[r] = pv * (dp[r] - dv4[e]);
                 }
             }
-        // dV += P^T dO, dK += dS^T Q over four 16-query steps
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-            const int qs = t4 >> 1, tp = t4 & 1;
-            const v8bf pb = pack_step(s[qs], tp), dsb = pack_step(dp[qs], tp);
+            for (int tp = 0; tp < 2; ++tp) {
+                const v8bf ob = pack_step(sv, tp);
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                dv[db] = mfma_bf16(pb, read_pair_t(gt, kVtPitch, 32 * db + l32, qs, tp, h), dv[db]);
-                dk[db] = mfma_bf16(dsb, read_pair_t(qt, kVtPitch, 32 * db + l32, qs, tp, h), dk[db]);
+                for (int db = 0; db < 4; ++db)
+                    acc[db] = mfma_bf16(ob, read_pair_t(DV ? gt : qt, kVtPitch, 32 * db + l32, qs, tp, h), acc[db]);
             }
         }
         if (ib + 1 < nib) {
-            __syncthreads();
-            dk_store(st, lds + ((ib + 1 - ib0) & 1) * kDkBuf);
+            __syncthreads();   // every wave is done with the buffer
+            dk_store(st, lds);
             __syncthreads();
         }
     }
-    // dV[key][d], dK[key][d]: lane holds column d = 32 db + l32, keys
+    // dV[key][d] or dK[key][d]: lane holds column d = 32 db + l32, keys
     // j0 + 8(r/4) + 4h + r%4
+    float* out = DV ? a.dv : a.dk;
+    const float mul = DV ? 1.0f : a.scale;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key < a.L) {
-                a.dv[(head_row + key) * a.ldg + 32 * db + l32] = dv[db][r];
-                a.dk[(head_row + key) * a.ldg + 32 * db + l32] = a.scale * dk[db][r];
-            }
+            if (key < a.L)
+                out[(head_row + key) * a.ldg + 32 * db + l32] = mul * acc[db][r];
         }
 }
 
@@ -739,24 +761,29 @@ hipError_t launch_attn_bwd(const AttnArgs& a, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    constexpr size_t kDqLds = 2 * kDqBuf, kDkLds = 2 * kDkBuf;
-    static_assert(kDqLds <= 160 * 1024 && kDkLds <= 160 * 1024, "LDS");
+    constexpr size_t kDqLds = kDqBuf, kDkLds = kDkBuf;
+    static_assert(2 * kDqLds <= 160 * 1024 && 2 * kDkLds <= 160 * 1024, "two workgroups per CU");
     auto raise = [](const void* fn, size_t bytes) {
         return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     };
     const void* dqf = a.causal ? reinterpret_cast<const void*>(attn_dq_kernel<true>)
                                : reinterpret_cast<const void*>(attn_dq_kernel<false>);
-    const void* dkf = a.causal ? reinterpret_cast<const void*>(attn_dkdv_kernel<true>)
-                               : reinterpret_cast<const void*>(attn_dkdv_kernel<false>);
-    if ((e = raise(dqf, kDqLds)) != hipSuccess || (e = raise(dkf, kDkLds)) != hipSuccess)
+    const void* dvf = a.causal ? reinterpret_cast<const void*>(attn_dkdv_kernel<true, true>)
+                               : reinterpret_cast<const void*>(attn_dkdv_kernel<false, true>);
+    const void* dkf = a.causal ? reinterpret_cast<const void*>(attn_dkdv_kernel<true, false>)
+                               : reinterpret_cast<const void*>(attn_dkdv_kernel<false, false>);
+    if ((e = raise(dqf, kDqLds)) != hipSuccess || (e = raise(dvf, kDkLds)) != hipSuccess ||
+        (e = raise(dkf, kDkLds)) != hipSuccess)
         return e;
     const dim3 gq(a.bh, (a.L + kDqQ - 1) / kDqQ), gk(a.bh, (a.L + kDkK - 1) / kDkK);
     if (a.causal) {
         hipLaunchKernelGGL(attn_dq_kernel<true>, gq, dim3(kThreads), kDqLds, s, a);
-        hipLaunchKernelGGL(attn_dkdv_kernel<true>, gk, dim3(kThreads), kDkLds, s, a);
+        hipLaunchKernelGGL((attn_dkdv_kernel<true, true>), gk, dim3(kThreads), kDkLds, s, a);
+        hipLaunchKernelGGL((attn_dkdv_kernel<true, false>), gk, dim3(kThreads), kDkLds, s, a);
     } else {
         hipLaunchKernelGGL(attn_dq_kernel<false>, gq, dim3(kThreads), kDqLds, s, a);
-        hipLaunchKernelGGL(attn_dkdv_kernel<false>, gk, dim3(kThreads), kDkLds, s, a);
+        hipLaunchKernelGGL((attn_dkdv_kernel<false, true>), gk, dim3(kThreads), kDkLds, s, a);
+        hipLaunchKernelGGL((attn_dkdv_kernel<false, false>), gk, dim3(kThreads), kDkLds, s, a);
     }
     return hipGetLastError();
 }

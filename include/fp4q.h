@@ -362,7 +362,9 @@ int fp4q_gemm_quant(int op, const fp4q_qtensor* a, const fp4q_qtensor* b, const 
  *            FP4Q_DT_F32), ldo >= 128 and a multiple of 8, 16-byte aligned.
  *   lse      device fp32 [bh*seq_len]: natural-log log-sum-exp of each row's
  *            scaled scores (needed by fp4q_attn_bwd).
- *   bh, seq_len  heads (1..65535) and rows per head (1..2^21).
+ *   bh, seq_len  heads (1..65535) and rows per head (1..2^21); every
+ *            head's slice of every tensor, seq_len x its leading dimension,
+ *            stays below 2^31 elements (else FP4Q_EINVAL).
  *   scale    the score factor (1/sqrt(128) for standard attention), > 0.
  *   causal   1: key j is visible to query i iff j <= i; 0: all keys.
  */

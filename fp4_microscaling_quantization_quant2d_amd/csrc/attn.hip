@@ -599,6 +599,9 @@ __device__ __forceinline__ void dk_load(DkStage& st, const AttnArgs& a, int64_t 
     st.dl = ok ? a.delta[head_row + i0 + t] : 0.0f;
 }
 
+// The dV kernel reads Q (rows) and dO^T (pairs); the dK kernel Q (rows),
+// Q^T (pairs), dO (rows) and D.  Each stores only its own tiles.
+template <bool DV>
 __device__ __forceinline__ void dk_store(const DkStage& st, uint8_t* buf)
 {
     const int t = threadIdx.x;
@@ -611,14 +614,18 @@ __device__ __forceinline__ void dk_store(const DkStage& st, uint8_t* buf)
             const int qq = 2 * p + e;
             qb[e] = __builtin_bit_cast(v4u, cvt8_e4m3(st.qc[i][e], e8m0_f32((st.qsb >> (8 * (2 * i + e))) & 0xFFu)));
             *reinterpret_cast<v4u*>(buf + qq * kRowPitch + 16 * dc) = qb[e];
-            *reinterpret_cast<v4u*>(buf + kDkQb + kDkQt + qq * kRowPitch + 16 * dc) = st.g[i][e];
+            if constexpr (!DV)
+                *reinterpret_cast<v4u*>(buf + kDkQb + kDkQt + qq * kRowPitch + 16 * dc) = st.g[i][e];
         }
-        store_pair_t(buf + kDkQb, kVtPitch, dc, p, qb[0], qb[1]);
-        store_pair_t(buf + kDkQb + kDkQt + kDkG, kVtPitch, dc, p, st.g[i][0], st.g[i][1]);
+        if constexpr (DV)
+            store_pair_t(buf + kDkQb + kDkQt + kDkG, kVtPitch, dc, p, st.g[i][0], st.g[i][1]);
+        else
+            store_pair_t(buf + kDkQb, kVtPitch, dc, p, qb[0], qb[1]);
     }
     if (t < kDkQ) {
         reinterpret_cast<float*>(buf + kDkQb + kDkQt + kDkG + kDkGt)[t] = st.ls;
-        reinterpret_cast<float*>(buf + kDkQb + kDkQt + kDkG + kDkGt + kDkL)[t] = st.dl;
+        if constexpr (!DV)
+            reinterpret_cast<float*>(buf + kDkQb + kDkQt + kDkG + kDkGt + kDkL)[t] = st.dl;
     }
 }
 
@@ -668,7 +675,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dkdv_kernel(AttnArgs a)
     const float* dlv = lsv + kDkQ;
     DkStage st;
     dk_load(st, a, head_row, ib0 * kDkQ);
-    dk_store(st, lds);
+    dk_store<DV>(st, lds);
     __syncthreads();
     for (int ib = ib0; ib < nib; ++ib) {
         const int i0 = ib * kDkQ;
@@ -733,7 +740,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dkdv_kernel(AttnArgs a)
         }
         if (ib + 1 < nib) {
             __syncthreads();   // every wave is done with the buffer
-            dk_store(st, lds);
+            dk_store<DV>(st, lds);
             __syncthreads();
         }
     }

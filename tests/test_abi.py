@@ -387,3 +387,23 @@ def test_attention_validation(fp4q):
     assert bwd(ws=None) == -1 and "workspace" in _err(fp4q)
     assert bwd(ldg=130) == -1
     assert bwd(lddo=64) == -1
+    # every head's slice of every tensor stays below 2^31 elements
+    big = _desc(fp4q, fmt=2, rows=1 << 21, cols=128, ld=128, ld_s=4)
+    assert call(big, big, bh=1, n=1 << 21, ldv=1024) == -1 and "2^31" in _err(fp4q)
+    assert call(big, big, bh=1, n=1 << 21, ldo=1024) == -1 and "2^31" in _err(fp4q)
+
+
+def test_fp8_mfma_probe_validation(fp4q):
+    """The FP8 MFMA probe refuses null or misaligned buffers (ABI) and
+    wrong shapes or host tensors (binding) before any launch."""
+    import torch
+    L = fp4q.lib()
+    P = ctypes.c_void_p
+    assert L.fp4q_probe_mfma_fp8(None, P(0x1000), P(0x2000), P(0x3000), P(0x4000), None) == -1
+    assert L.fp4q_probe_mfma_fp8(P(0x1001), P(0x1000), P(0x2000), P(0x3000), P(0x4000), None) == -1
+    a = torch.zeros((32, 64), dtype=torch.uint8)
+    s = torch.zeros((32, 2), dtype=torch.uint8)
+    with pytest.raises(fp4q.Fp4qError):
+        fp4q.fp4q_probe_mfma_fp8(a, a, s, s)                  # host tensors
+    with pytest.raises(fp4q.Fp4qError):
+        fp4q.fp4q_probe_mfma_fp8(a[:, :32], a, s, s)          # wrong shape

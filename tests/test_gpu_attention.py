@@ -214,3 +214,30 @@ def test_backward_attention_config_sampled():
     torch.cuda.synchronize()
     rows = lambda: np.unique(np.concatenate([[0, L - 1], rng.integers(0, L, 126)]))
     _bwd_check(Qf, Kf, V, dO, O, grads, bh, L, D ** -0.5, True, (0, bh - 1), rows(), rows())
+
+
+@pytest.mark.parametrize("L", [1, 2, 33])
+@pytest.mark.parametrize("causal", [False, True])
+def test_degenerate_lengths(L, causal):
+    """Sequences shorter than one 64-key block (one key: O = V, and the
+    gradients of Q and K vanish up to rounding), five heads, forward and
+    backward against the oracle."""
+    bh = 5
+    Q, K, V, dO = _heads(bh, L, 11 * L + causal)
+    scale = D ** -0.5
+    note("attn degenerate bh=%d L=%d causal=%d" % (bh, L, causal))
+    qq = fq.fp4q_quant1d_mxfp8(to_dev(Q))
+    qk = fq.fp4q_quant1d_mxfp8(to_dev(K))
+    v, g = to_dev(V), to_dev(dO)
+    O, lse = fq.fp4q_attn_fwd(qq, qk, v, bh, L, scale=scale, causal=causal, out_dtype=torch.float32)
+    grads = fq.fp4q_attn_bwd(qq, qk, v, O, lse, g, bh, L, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    On, lsen = O.cpu().numpy(), lse.cpu().numpy()
+    Vd = wl.bf16_bits_to_f32(V).astype(np.float64)
+    for h in range(bh):
+        sl = slice(h * L, (h + 1) * L)
+        _fwd_check(On[sl], lsen[sl], _deq8(np.ascontiguousarray(Q[sl])), _deq8(np.ascontiguousarray(K[sl])),
+                   Vd[sl], scale, causal, np.arange(L), False, "L=%d head %d" % (L, h))
+    if L == 1:
+        assert np.allclose(On, Vd, rtol=2.0 ** -20, atol=0.0)
+    _bwd_check(Q, K, V, dO, O, grads, bh, L, scale, causal, range(bh), np.arange(L), np.arange(L))

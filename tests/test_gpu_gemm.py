@@ -51,7 +51,7 @@ def test_tiny_all_ops():
 
 
 @pytest.mark.parametrize("T,K,N", [(100, 200, 72), (32, 32, 32), (33, 65, 97), (512, 640, 384),
-                                   (260, 300, 520), (64, 1056, 96)])
+                                   (260, 300, 520), (64, 1056, 96), (1, 1, 1), (1, 70, 3), (3, 1, 257)])
 def test_ragged_and_multi_tile(T, K, N):
     L = wl.linear_layer("tiny:ragged", T, K, N, T * 7 + K)
     _layer_full_check(L.X, L.W, L.dY, "%dx%dx%d" % (T, K, N))

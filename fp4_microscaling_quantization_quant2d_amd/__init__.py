@@ -109,10 +109,11 @@ def _load():
     L.fp4q_probe_mfma_fp4.argtypes = [I64, ctypes.c_int, P, P, I64, P]
     L.fp4q_probe_copy.argtypes = [P, P, I64, ctypes.c_int, P]
     L.fp4q_probe_mfma_fp8.argtypes = [P, P, P, P, P, P]
+    L.fp4q_probe_stream.argtypes = [P, P, I64, ctypes.c_int, ctypes.c_int, P]
     for fn in ("fp4q_quant2d_sizes", "fp4q_quant2d", "fp4q_quant2d_batch", "fp4q_quant2d_batch_ex",
                "fp4q_quant1d_mxfp8",
                "fp4q_gemm", "fp4q_gemm_ex", "fp4q_gemm_quant", "fp4q_attn_fwd", "fp4q_attn_bwd", "fp4q_attn_bwd_noalloc", "fp4q_dequant", "fp4q_probe_mfma_fp4",
-               "fp4q_probe_copy", "fp4q_probe_mfma_fp8"):
+               "fp4q_probe_copy", "fp4q_probe_mfma_fp8", "fp4q_probe_stream"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -506,6 +507,19 @@ def fp4q_probe_mfma_fp8(a, b, sa, sb, stream=None):
     _check(_load().fp4q_probe_mfma_fp8(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), _ptr(c), _stream_ptr(stream)),
            "fp4q_probe_mfma_fp8")
     return c
+
+
+def fp4q_probe_stream(src, dst, nread, workgroups, stream=None):
+    """Diagnostic: a stream of `nread` read streams and one write stream;
+    src holds nread * dst's bytes (contiguous CUDA tensors, dst a multiple of
+    16 bytes).  Returns the bytes moved (read + written)."""
+    n = dst.numel() * dst.element_size()
+    if (not src.is_cuda or not dst.is_cuda or not src.is_contiguous() or not dst.is_contiguous()
+            or src.numel() * src.element_size() < nread * n):
+        raise Fp4qError("src must hold nread times dst's bytes; both contiguous CUDA tensors")
+    _check(_load().fp4q_probe_stream(_ptr(src), _ptr(dst), n, int(nread), int(workgroups), _stream_ptr(stream)),
+           "fp4q_probe_stream")
+    return (nread + 1.0) * n
 
 
 def fp4q_probe_copy(src, dst, workgroups=None, stream=None):

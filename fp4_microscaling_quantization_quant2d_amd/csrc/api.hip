@@ -842,6 +842,17 @@ int fp4q_probe_copy(const void* src, void* dst, int64_t bytes, int workgroups, v
                       "fp4q_probe_copy");
 }
 
+int fp4q_probe_stream(const void* src, void* dst, int64_t bytes, int nread, int workgroups, void* hip_stream)
+{
+    if (!src || !dst || bytes < 16 || bytes % 16 || nread < 1 || nread > 4 || workgroups < 1 ||
+        workgroups > (1 << 20) || !aligned16(src) || !aligned16(dst))
+        return fail(FP4Q_EINVAL, "fp4q_probe_stream: 16-byte aligned buffers, bytes a positive multiple of 16, "
+                                 "nread in [1, 4], workgroups in [1, 2^20]");
+    return hip_status(fp4q::launch_stream_probe(src, dst, bytes, nread, workgroups,
+                                                static_cast<hipStream_t>(hip_stream)),
+                      "fp4q_probe_stream");
+}
+
 int fp4q_probe_mfma_fp8(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb, float* c,
                         void* hip_stream)
 {

@@ -178,6 +178,7 @@ hipError_t launch_mfma_probe(int64_t iters, int workgroups, float* sink, const u
                              hipStream_t s);
 // Streaming copy (measured-peak probe) of `bytes` (a multiple of 16).
 hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int workgroups, hipStream_t s);
+hipError_t launch_stream_probe(const void* src, void* dst, int64_t bytes, int nread, int workgroups, hipStream_t s);
 hipError_t launch_mfma_fp8_block(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb, float* c,
                                  hipStream_t s);
 

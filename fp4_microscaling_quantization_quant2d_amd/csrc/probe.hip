@@ -114,6 +114,38 @@ hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int work
 
 namespace {
 
+// A stream with a given read:write mix: every 16-byte word of dst is the
+// xor of the words at the same index in `nread` consecutive source streams
+// of n16 words each (a grid-stride loop, one word per thread per step).
+// nread = 2 is the quantizer's mix (2 bytes of bf16 read per byte of codes
+// written).
+__global__ __launch_bounds__(256) void stream_probe_kernel(const uint4* src, uint4* dst, int64_t n16, int nread)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
+        uint4 x = src[i];
+        for (int r = 1; r < nread; ++r) {
+            const uint4 y = src[i + r * n16];
+            x.x ^= y.x;
+            x.y ^= y.y;
+            x.z ^= y.z;
+            x.w ^= y.w;
+        }
+        dst[i] = x;
+    }
+}
+
+} // namespace
+
+hipError_t launch_stream_probe(const void* src, void* dst, int64_t bytes, int nread, int workgroups, hipStream_t s)
+{
+    hipLaunchKernelGGL(stream_probe_kernel, dim3(workgroups), dim3(256), 0, s, static_cast<const uint4*>(src),
+                       static_cast<uint4*>(dst), bytes / 16, nread);
+    return hipGetLastError();
+}
+
+namespace {
+
 // One block-scaled FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 A and B)
 // on a 32x64 A, a 32x64 B and their E8M0 scales (one per row and 32 K
 // values): C[32 x 32] = A B^T.  One wave; lane l holds row (column) l % 32

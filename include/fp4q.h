@@ -442,6 +442,14 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
  * written bytes over time) is the practical HBM ceiling of a read-once,
  * write-once kernel.
  *
+ * fp4q_probe_stream: a streaming kernel with `nread` (1..4) read streams and
+ * one write stream: dst (bytes, device, 16-byte aligned) receives, word by
+ * word, the xor of the words at the same index of nread consecutive source
+ * streams of `bytes` each (src holds nread*bytes).  A grid-stride loop of
+ * one 16-byte word per thread over `workgroups` workgroups of 256 threads.
+ * nread = 2 is the quantizer's traffic mix (two bytes read per byte
+ * written): its rate is that kernel's practical HBM ceiling.
+ *
  * fp4q_probe_mfma_fp8: ONE block-scaled FP8 MFMA (the same instruction with
  * E4M3 operands), C = A B^T for a [32 x 64] and b [32 x 64] E4M3 bytes
  * (row-major, device, 4-byte aligned), sa / sb [32 x 2] E8M0 bytes (one per
@@ -454,6 +462,7 @@ int fp4q_dequant(const fp4q_qtensor* q, int transposed, int out_dtype, void* y, 
 int fp4q_probe_mfma_fp4(int64_t iters, int workgroups, float* sink, const uint8_t* codes, int64_t code_bytes,
                         void* hip_stream);
 int fp4q_probe_copy(const void* src, void* dst, int64_t bytes, int workgroups, void* hip_stream);
+int fp4q_probe_stream(const void* src, void* dst, int64_t bytes, int nread, int workgroups, void* hip_stream);
 int fp4q_probe_mfma_fp8(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb, float* c,
                         void* hip_stream);
 

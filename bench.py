@@ -935,7 +935,7 @@ def main():
                            "achieved": round(quant_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": round(quant_gbps / HBM_PEAK_GBPS, 4),
                            "measured_peak": peaks["hbm_read2_write1_GB/s"],
-                           "measured_peak_kind": "2:1 read:write stream (the quantizer's mix)",
+                           "measured_peak_kind": "2:1 read:write stream (the quantizer's mix), 3 GiB",
                            "frac_measured": round(quant_gbps / peaks["hbm_read2_write1_GB/s"], 4),
                            "traffic": measured_traffic("quant2d"),
                            "algorithmic_bytes_per_launch": q_bytes / n_q,

@@ -569,11 +569,14 @@ constexpr int kDkL = kDkQ * 4;             // lse (log2 units) of the queries
 constexpr int kDkDl = kDkQ * 4;            // D of the queries
 constexpr int kDkBuf = kDkQb + kDkQt + kDkG + kDkGt + kDkL + kDkDl;
 
+// Raw loaded words only: arithmetic on a loaded value here would make the
+// compiler wait for that load (and, loads completing in order, for every
+// load before it) at once, instead of at the LDS store a step later.
 struct DkStage {
     v2u qc[2][2];
-    uint32_t qsb;     // the four E8M0 bytes of qc, byte 2i + e
+    uint32_t qs[2];   // the scale dwords (4 E8M0 bytes) of query rows 2p and 2p+1
     v4u g[2][2];
-    float ls, dl;
+    float ls, dl;     // lse (natural log) and D of query t
 };
 
 __device__ __forceinline__ void dk_load(DkStage& st, const AttnArgs& a, int64_t head_row, int i0)
@@ -588,14 +591,14 @@ __device__ __forceinline__ void dk_load(DkStage& st, const AttnArgs& a, int64_t 
             const bool ok = qq < a.L;
             st.qc[i][e] = ok ? *reinterpret_cast<const v2u*>(head_at(a.qc, head_row, a.ldq, qq, 8 * dc))
                              : (v2u){0u, 0u};
-            const uint32_t sb = ok ? *head_at(a.qs, head_row, a.ldqs, qq, dc >> 2) : 0u;
-            st.qsb = (i | e) ? st.qsb | (sb << (8 * (2 * i + e))) : sb;
+            if (i == 0)   // the same rows for i = 1
+                st.qs[e] = ok ? *reinterpret_cast<const uint32_t*>(head_at(a.qs, head_row, a.ldqs, qq, 0)) : 0u;
             st.g[i][e] = ok ? *reinterpret_cast<const v4u*>(head_at(a.dout, head_row, a.lddo, qq, 8 * dc))
                             : (v4u){0u, 0u, 0u, 0u};
         }
     }
     const bool ok = t < kDkQ && i0 + t < a.L;
-    st.ls = ok ? a.lse[head_row + i0 + t] * kLog2e : 0.0f;
+    st.ls = ok ? a.lse[head_row + i0 + t] : 0.0f;
     st.dl = ok ? a.delta[head_row + i0 + t] : 0.0f;
 }
 
@@ -612,7 +615,7 @@ __device__ __forceinline__ void dk_store(const DkStage& st, uint8_t* buf)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int qq = 2 * p + e;
-            qb[e] = __builtin_bit_cast(v4u, cvt8_e4m3(st.qc[i][e], e8m0_f32((st.qsb >> (8 * (2 * i + e))) & 0xFFu)));
+            qb[e] = __builtin_bit_cast(v4u, cvt8_e4m3(st.qc[i][e], e8m0_f32((st.qs[e] >> (8 * (dc >> 2))) & 0xFFu)));
             *reinterpret_cast<v4u*>(buf + qq * kRowPitch + 16 * dc) = qb[e];
             if constexpr (!DV)
                 *reinterpret_cast<v4u*>(buf + kDkQb + kDkQt + qq * kRowPitch + 16 * dc) = st.g[i][e];
@@ -623,7 +626,7 @@ __device__ __forceinline__ void dk_store(const DkStage& st, uint8_t* buf)
             store_pair_t(buf + kDkQb, kVtPitch, dc, p, qb[0], qb[1]);
     }
     if (t < kDkQ) {
-        reinterpret_cast<float*>(buf + kDkQb + kDkQt + kDkG + kDkGt)[t] = st.ls;
+        reinterpret_cast<float*>(buf + kDkQb + kDkQt + kDkG + kDkGt)[t] = st.ls * kLog2e;
         if constexpr (!DV)
             reinterpret_cast<float*>(buf + kDkQb + kDkQt + kDkG + kDkGt + kDkL)[t] = st.dl;
     }

@@ -295,7 +295,8 @@ int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
     if (out->rows != rows || out->cols != cols || out->batch != 1)
         return fail(FP4Q_EINVAL, "fp4q_quant1d_mxfp8: out shape/batch mismatch");
     const int esz = dtype == FP4Q_DT_F32 ? 4 : 2;
-    if (rows * (pad32(cols) / 32) >= (int64_t)UINT_MAX * 256)
+    // 4 (bf16) or 8 (fp32) work-items per 1x32 group; a launch holds fewer than 2^32.
+    if (rows * (pad32(cols) / 32) * (esz == 4 ? 8 : 4) >= ((int64_t)1 << 32))
         return fail(FP4Q_EINVAL, "fp4q_quant1d_mxfp8: too many groups for one launch");
     fp4q::Mxfp8Args p;
     p.x = x;

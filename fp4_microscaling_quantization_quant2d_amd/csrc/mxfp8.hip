@@ -3,9 +3,14 @@
 // one E8M0 scale per 1x32 group along each row, truncation-free (the Sec. 3.1
 // rule with Qp = 448, Qn = -448), round-to-nearest-even.
 //
-// One lane per 1x32 group: it reads 64 contiguous bytes (bf16) with four
-// 16-byte loads, so a wave streams 4 KB; the group amax, the exponent and the
-// 32 conversions stay in registers; 32 code bytes and one scale byte go out.
+// A 1x32 group is spread over consecutive lanes that each read 16 contiguous
+// bytes (4 lanes of 8 bf16 values, or 8 lanes of 4 fp32 values), so every
+// load instruction of a wave reads 1 KB of whole cache lines.  The group
+// amax is a max over those lanes (xor shuffles); each lane converts its own
+// values on the gfx950 FP8 converters (two values per instruction, the block
+// scale as their divisor) and writes their code bytes, and the group's first
+// lane writes the scale byte.
+#include "fp4q_cvt.hpp"
 #include "fp4q_device.hpp"
 #include "fp4q_launch.hpp"
 
@@ -15,112 +20,114 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// |x| * 2^-k rounded to nearest-even E4M3FN, magnitude code 0..126.
-// x32: fp32 bits of x; the scaled value is at most 448 by construction.
-__device__ __forceinline__ uint32_t e4m3_code(uint32_t x32, int k)
+// E4M3FN (OCP FP8) conversions: v_cvt_scalef32_pk_fp8_{bf16,f32} divide two
+// values by the float scale, round them to nearest (ties to even) and write
+// the two code bytes (first value in the low byte) into word HI of the
+// destination, keeping the other word, which the wrappers tie.  The
+// quantizer only converts values whose magnitude after scaling is at most
+// 448, so saturation never applies.  Checked on MI355X against the software
+// rounding rule for every finite bf16 pattern at every block exponent.
+
+// Word HI of acc <- E4M3 codes of the two bf16 halves of d (low half -> low byte).
+template <int HI>
+__device__ __forceinline__ void cvt8_rne_bf16_word(uint32_t& acc, uint32_t d, float scale)
 {
-    const uint32_t a = x32 & 0x7FFFFFFFu;
-    int E = (int)(a >> 23);
-    uint32_t m24 = (a & 0x7FFFFFu) | 0x800000u;
-    if (E == 0) {
-        if (a == 0)
-            return 0;
-        const int lz = __builtin_clz(a) - 8;   // normalize a subnormal input
-        m24 = a << lz;
-        E = 1 - lz;
-    }
-    const int Ev = E - k;                      // biased exponent of v = |x| * 2^-k
-    if (Ev >= 121) {                           // v >= 2^-6: normal E4M3, 3 mantissa bits
-        uint32_t T = m24 >> 20;
-        const uint32_t rem = m24 & 0xFFFFFu;
-        T += (rem > 0x80000u || (rem == 0x80000u && (T & 1u))) ? 1u : 0u;
-        int e = Ev - 120;
-        if (T == 16u) {
-            T = 8u;
-            ++e;
-        }
-        return ((uint32_t)e << 3) | (T & 7u);
-    }
-    // subnormal E4M3: multiples of 2^-9, code = RNE(v * 2^9)
-    const int s = imin(141 - Ev, 31);
-    const uint32_t T = m24 >> s;
-    const uint32_t rem = m24 & ((1u << s) - 1u);
-    const uint32_t half = 1u << (s - 1);
-    return T + ((rem > half || (rem == half && (T & 1u))) ? 1u : 0u);
+    if constexpr (HI == 0)
+        asm("v_cvt_scalef32_pk_fp8_bf16 %0, %1, %2" : "+v"(acc) : "v"(d), "v"(scale));
+    else
+        asm("v_cvt_scalef32_pk_fp8_bf16 %0, %1, %2 op_sel:[0,0,1]" : "+v"(acc) : "v"(d), "v"(scale));
 }
+
+// Word HI of acc <- E4M3 codes of x0 (low byte) and x1 (high byte).
+template <int HI>
+__device__ __forceinline__ void cvt8_rne_f32_word(uint32_t& acc, float x0, float x1, float scale)
+{
+    if constexpr (HI == 0)
+        asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %3" : "+v"(acc) : "v"(x0), "v"(x1), "v"(scale));
+    else
+        asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]"
+            : "+v"(acc) : "v"(x0), "v"(x1), "v"(scale));
+}
+
+// Lanes per 1x32 group: 16 bytes of input each.
+template <bool F32>
+constexpr int lanes_per_group() { return F32 ? 8 : 4; }
 
 template <bool F32, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void mxfp8_kernel(Mxfp8Args p)
 {
-    const int groups = p.cols_pad >> 5;
-    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (gid >= p.rows * groups)
-        return;
-    const int64_t r = gid / groups;
-    const int g = (int)(gid - r * groups);
-    const int c0 = g * 32;
-    const int esz = F32 ? 4 : 2;
-    const char* row = static_cast<const char*>(p.x) + r * p.ldx * esz;
+    constexpr int LPG = lanes_per_group<F32>();
+    constexpr int esz = F32 ? 4 : 2;
+    const uint32_t groups = (uint32_t)(p.cols_pad >> 5);
+    // fewer than 2^32 work-items per launch (checked by the caller)
+    const uint32_t t = blockIdx.x * (uint32_t)kThreads + threadIdx.x;
+    const uint32_t gid = t / LPG;
+    const int sub = (int)(t % LPG);
+    const bool live = (int64_t)gid < p.rows * groups;
+    const uint32_t r = live ? gid / groups : 0u;
+    const int g = live ? (int)(gid - r * groups) : 0;
+    const int c0 = g * 32 + sub * (32 / LPG);
 
-    uint32_t v[32];
-    if (ALIGNED && c0 + 32 <= p.cols) {
-        const uint4* src = reinterpret_cast<const uint4*>(row + (int64_t)c0 * esz);
-        if (F32) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint4 t = src[q];
-                v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
-            }
+    // the lane's 16 input bytes: 8 bf16 (two per word) or 4 fp32
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (live) {
+        const char* row = static_cast<const char*>(p.x) + (int64_t)r * p.ldx * esz;
+        if (ALIGNED && c0 + 32 / LPG <= p.cols) {
+            const uint4 v = *reinterpret_cast<const uint4*>(row + (int64_t)c0 * esz);
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 t = src[q];
-                const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    v[8 * q + 2 * d] = w[d] << 16;
-                    v[8 * q + 2 * d + 1] = w[d] & 0xFFFF0000u;
-                }
+            for (int j = 0; j < 32 / LPG; ++j) {
+                const int c = c0 + j;
+                if (c >= p.cols)
+                    continue;
+                if (F32)
+                    w[j] = reinterpret_cast<const uint32_t*>(row)[c];
+                else
+                    w[j >> 1] |= (uint32_t)reinterpret_cast<const uint16_t*>(row)[c] << (16 * (j & 1));
             }
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const int c = c0 + j;
-            uint32_t x = 0;
-            if (c < p.cols)
-                x = F32 ? reinterpret_cast<const uint32_t*>(row)[c]
-                        : (uint32_t)reinterpret_cast<const uint16_t*>(row)[c] << 16;
-            v[j] = x;
-        }
     }
+    // |x| as fp32 bits (bf16: the high half of the fp32 pattern)
     uint32_t mx = 0;
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-        mx = max(mx, v[j] & 0x7FFFFFFFu);
-    const int k = truncfree_exp_e4m3(mx);
-    uint32_t out[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t x = v[4 * q + b];
-            const uint32_t byte = e4m3_code(x, k) | ((x >> 24) & 0x80u);
-            w |= byte << (8 * b);
-        }
-        out[q] = w;
+    for (int d = 0; d < 4; ++d) {
+        if (F32)
+            mx = max(mx, w[d] & 0x7FFFFFFFu);
+        else
+            mx = max(mx, max((w[d] << 16) & 0x7FFFFFFFu, w[d] & 0x7FFF0000u));
     }
-    uint4* dst = reinterpret_cast<uint4*>(p.codes + r * p.ld + c0);
-    dst[0] = uint4{out[0], out[1], out[2], out[3]};
-    dst[1] = uint4{out[4], out[5], out[6], out[7]};
-    p.scales[r * p.ld_s + g] = (uint8_t)(k + 127);
+    // Every lane takes part in the shuffles; the group's lanes are
+    // consecutive within the wave.
+#pragma unroll
+    for (int o = 1; o < LPG; o <<= 1)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    if (!live)
+        return;
+    const int k = truncfree_exp_e4m3(mx);
+    const float scale = e8m0_scale(k);
+    uint8_t* dst = p.codes + (int64_t)r * p.ld + c0;
+    if constexpr (F32) {
+        uint32_t o = 0;
+        cvt8_rne_f32_word<0>(o, __uint_as_float(w[0]), __uint_as_float(w[1]), scale);
+        cvt8_rne_f32_word<1>(o, __uint_as_float(w[2]), __uint_as_float(w[3]), scale);
+        *reinterpret_cast<uint32_t*>(dst) = o;
+    } else {
+        uint32_t o0 = 0, o1 = 0;
+        cvt8_rne_bf16_word<0>(o0, w[0], scale);
+        cvt8_rne_bf16_word<1>(o0, w[1], scale);
+        cvt8_rne_bf16_word<0>(o1, w[2], scale);
+        cvt8_rne_bf16_word<1>(o1, w[3], scale);
+        *reinterpret_cast<uint2*>(dst) = uint2{o0, o1};
+    }
+    if (sub == 0)
+        p.scales[(int64_t)r * p.ld_s + g] = (uint8_t)(k + 127);
 }
 
 template <bool F32>
 hipError_t launch_f(const Mxfp8Args& p, bool aligned, hipStream_t s)
 {
-    const int64_t n = p.rows * (p.cols_pad >> 5);
+    const int64_t n = p.rows * (p.cols_pad >> 5) * lanes_per_group<F32>();
     const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
     if (aligned)
         hipLaunchKernelGGL((mxfp8_kernel<F32, true>), grid, dim3(kThreads), 0, s, p);

@@ -53,6 +53,67 @@ def test_mxfp8_special_values():
         _check_fp8(fq.fp4q_quant1d_mxfp8(to_dev(xx)), orc.quant1d_mxfp8(xx), 8)
 
 
+def _e4m3_values():
+    """The 127 non-negative finite E4M3FN magnitudes, code order (0 .. 448)."""
+    return torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_mxfp8_every_bf16_pattern_every_exponent():
+    """Every finite bf16 value x at every block exponent k it can have: for
+    each k (-127 .. 120) a group's first element 448 * 2^k (the largest
+    bf16 value of that exponent; the largest finite bf16 for k = 120) sets
+    the amax, and the other 31 elements run through every bf16 pattern of
+    either sign whose magnitude is at most it.  The codes (the rounding of
+    x * 2^-k to E4M3, ties to even, subnormals included) and the scale bytes
+    are compared bit for bit with the oracle."""
+    rows = []
+    for k in range(-127, 121):
+        a_bits = 0x7F7F if k == 120 else ((135 + k) << 7) | 0x60
+        mags = np.arange(a_bits + 1, dtype=np.uint32)
+        pats = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+        n = -(-len(pats) // 31)
+        body = np.zeros(n * 31, np.uint16)
+        body[:len(pats)] = pats
+        blk = np.empty((n, 32), np.uint16)
+        blk[:, 0] = a_bits
+        blk[:, 1:] = body.reshape(n, 31)
+        rows.append(blk)
+    x = np.ascontiguousarray(np.concatenate(rows))   # one group per row
+    note("mxfp8 every bf16 pattern x every exponent: %d rows x %d" % x.shape)
+    q = fq.fp4q_quant1d_mxfp8(to_dev(x))
+    _check_fp8(q, orc.quant1d_mxfp8(x), x.shape[0])
+
+
+def test_mxfp8_f32_ties_and_neighbours():
+    """fp32 inputs at sampled block exponents: every midpoint between two
+    adjacent E4M3 magnitudes (normal and subnormal), the fp32 values one ulp
+    either side of it, and hashed fp32 patterns below the group's amax,
+    scaled by 2^k, both signs."""
+    vals = _e4m3_values()
+    mid = (vals[:-1] + vals[1:]) / 2.0
+    rng = np.random.default_rng(5)
+    groups = []
+    for k in list(range(-127, -110)) + list(range(-20, 21)) + list(range(100, 121)):
+        A = np.float32(448.0 * 2.0 ** k) if k < 120 else np.float32(3.0e38)
+        with np.errstate(over="ignore"):   # midpoints past the fp32 range drop out below
+            m = (mid * 2.0 ** k).astype(np.float32)
+        m = m[(m > 0) & (m <= A)]
+        cand = np.concatenate([m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(np.inf))])
+        h = (rng.integers(0, int(A.view(np.uint32)) + 1, 4 * 31, dtype=np.int64)).astype(np.uint32).view(np.float32)
+        cand = np.concatenate([cand[(cand <= A) & np.isfinite(cand)], h])
+        cand = np.concatenate([cand, -cand])
+        n = -(-len(cand) // 31)
+        body = np.zeros(n * 31, np.float32)
+        body[:len(cand)] = cand
+        blk = np.empty((n, 32), np.float32)
+        blk[:, 0] = A
+        blk[:, 1:] = body.reshape(n, 31)
+        groups.append(blk)
+    x = np.ascontiguousarray(np.concatenate(groups))
+    note("mxfp8 f32 ties: %d rows" % x.shape[0])
+    _check_fp8(fq.fp4q_quant1d_mxfp8(to_dev(x)), orc.quant1d_mxfp8(x), x.shape[0])
+
+
 def _batched_fp8(q, B, L, D):
     """View a [B*L x D] MXFP8 quantization as a batch of B [L x D] matrices."""
     ld, lds = q.codes.shape[1], q.scales.shape[1]

@@ -244,6 +244,8 @@ int fp4q_quant2d_batch_ex(int n, const fp4q_quant2d_item* items, int dtype, int 
  * truncation-free (the Sec. 3.1 rule with Qp = 448), round-to-nearest-even.
  *   x    device, rows x cols, leading dim ldx elements (bf16 or f32).
  *   out  fmt = FP4Q_FMT_MXFP8_1D32, codes and scales set, batch 1.
+ * One launch handles fewer than 2^32 / 4 (bf16) or 2^32 / 8 (f32) groups of
+ * 32; more returns FP4Q_EINVAL.
  */
 int fp4q_quant1d_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                        const fp4q_qtensor* out, void* hip_stream);

@@ -274,7 +274,7 @@ def test_dequant_and_mxfp8_reject_bad_arguments(fp4q):
     bad = _desc(fp4q, fmt=2, ld=48)
     assert L.fp4q_quant1d_mxfp8(ctypes.c_void_p(0x10000), 1, 64, 64, 64, ctypes.byref(bad), None) == -1
     # 4 (bf16) or 8 (f32) work-items per group of 32: 2^30 groups of bf16, or
-    # 2^29 of f32, exceed one launch; 2^30 - 1 bf16 groups do not reach it
+    # 2^29 of f32, reach 2^32 work-items, more than one launch holds
     for dt, rows in ((1, 1 << 30), (2, 1 << 29)):
         big = _desc(fp4q, fmt=2, rows=rows, cols=32, ld=32, ld_s=1)
         assert L.fp4q_quant1d_mxfp8(ctypes.c_void_p(0x10000), dt, rows, 32, 32, ctypes.byref(big), None) == -1

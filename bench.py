@@ -54,9 +54,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_7b_step_pmc.md")
 # The sources each measured kernel is built from: a change to any of them
 # invalidates the committed counter readings.
-KERNEL_SOURCES = {"gemm": ["fp4q_launch.hpp", "fp4q_device.hpp", "fp4q_cvt.hpp", "quant_tile.hpp", "gemm_kernel.hpp",
-                           "gemm_plain.hip"],
-                  "quant2d": ["fp4q_launch.hpp", "fp4q_device.hpp", "fp4q_cvt.hpp", "quant_tile.hpp", "quant2d.hip"]}
+KERNEL_SOURCES = {"gemm": ["fp4q_launch.hpp", "fp4q_device.hpp", "fp4q_cvt.hpp", "lane_ops.hpp", "quant_tile.hpp",
+                           "gemm_kernel.hpp", "gemm_plain.hip"],
+                  "quant2d": ["fp4q_launch.hpp", "fp4q_device.hpp", "fp4q_cvt.hpp", "lane_ops.hpp", "quant_tile.hpp",
+                              "quant2d.hip"]}
 
 
 def source_sha256(kernel):

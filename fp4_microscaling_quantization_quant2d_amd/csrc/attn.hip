@@ -27,6 +27,7 @@
 // are masked); full or causal.  The log-sum-exp of every query row (natural
 // log) is stored for the backward.
 #include "fp4q_launch.hpp"
+#include "lane_ops.hpp"
 
 #include <hip/hip_runtime.h>
 
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mx = fmaxf(mx, s[sb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmax_xor32(mx);
         // Lazy rescaling: the reference m moves only when this block's max
         // passes it by more than 8 in log2 units (or m is still -inf; both
         // -inf gives NaN, no move), so P = exp2(c s - c m) stays below 2^8,
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
                 s[sb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(c, s[sb][r], -cm));
                 rs += s[sb][r];
             }
-        rs += __shfl_xor(rs, 32);
+        rs = fadd_xor32(rs);
         if (__any(grow)) {
             const float alpha = grow ? __builtin_amdgcn_exp2f(c * (m - m_use)) : 1.0f;
             l *= alpha;

@@ -6,13 +6,14 @@
 // A 1x32 group is spread over consecutive lanes that each read 16 contiguous
 // bytes (4 lanes of 8 bf16 values, or 8 lanes of 4 fp32 values), so every
 // load instruction of a wave reads 1 KB of whole cache lines.  The group
-// amax is a max over those lanes (xor shuffles); each lane converts its own
+// amax is a max over those lanes (DPP / swizzle exchanges); each lane converts its own
 // values on the gfx950 FP8 converters (two values per instruction, the block
 // scale as their divisor) and writes their code bytes, and the group's first
 // lane writes the scale byte.
 #include "fp4q_cvt.hpp"
 #include "fp4q_device.hpp"
 #include "fp4q_launch.hpp"
+#include "lane_ops.hpp"
 
 namespace fp4q {
 
@@ -99,9 +100,10 @@ __global__ __launch_bounds__(kThreads) void mxfp8_kernel(Mxfp8Args p)
     }
     // Every lane takes part in the shuffles; the group's lanes are
     // consecutive within the wave.
-#pragma unroll
-    for (int o = 1; o < LPG; o <<= 1)
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    mx = max_xor<1>(mx);
+    mx = max_xor<2>(mx);
+    if constexpr (LPG == 8)
+        mx = max_xor<4>(mx);
     if (!live)
         return;
     const int k = truncfree_exp_e4m3(mx);

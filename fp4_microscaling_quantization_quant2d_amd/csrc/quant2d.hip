@@ -12,7 +12,7 @@
 //   lane      = one 8x8 block: lane = bc + 8*br, rows 8br.., cols 8bc..
 // A lane loads its block with 16-byte loads (a wave's load instruction reads
 // 8 rows x 128 contiguous bytes), reduces |x| to a tile amax over the 16
-// lanes of its tile with cross-lane xor shuffles, derives the E8M0 byte,
+// lanes of its tile with DPP and ds_swizzle exchanges, derives the E8M0 byte,
 // draws 8 Philox blocks and rounds its 64 elements with the hardware FP4
 // converters (scale folded in; one per element for stochastic rounding, one
 // per pair for round-to-nearest-even), which write the nibbles straight into

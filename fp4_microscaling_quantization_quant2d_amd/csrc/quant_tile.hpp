@@ -23,6 +23,7 @@
 
 #include "fp4q_cvt.hpp"
 #include "fp4q_device.hpp"
+#include "lane_ops.hpp"
 
 #include <type_traits>
 
@@ -163,17 +164,17 @@ template <int BLK>
 __device__ __forceinline__ uint32_t square_amax(uint32_t mx)
 {
     static_assert(BLK == 8 || BLK == 16 || BLK == 32 || BLK == 64, "block side");
-    if (BLK >= 16)
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
-    if (BLK >= 32)
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
-    if (BLK >= 16)
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 8));
-    if (BLK >= 32)
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
-    if (BLK == 64) {
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+    if constexpr (BLK >= 16)
+        mx = max_xor<1>(mx);
+    if constexpr (BLK >= 32)
+        mx = max_xor<2>(mx);
+    if constexpr (BLK >= 16)
+        mx = max_xor<8>(mx);
+    if constexpr (BLK >= 32)
+        mx = max_xor<16>(mx);
+    if constexpr (BLK == 64) {
+        mx = max_xor<4>(mx);
+        mx = max_xor<32>(mx);
     }
     return mx;
 }

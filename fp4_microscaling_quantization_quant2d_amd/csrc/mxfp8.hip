@@ -6,10 +6,10 @@
 // A 1x32 group is spread over consecutive lanes that each read 16 contiguous
 // bytes (4 lanes of 8 bf16 values, or 8 lanes of 4 fp32 values), so every
 // load instruction of a wave reads 1 KB of whole cache lines.  The group
-// amax is a max over those lanes (DPP / swizzle exchanges); each lane converts its own
-// values on the gfx950 FP8 converters (two values per instruction, the block
-// scale as their divisor) and writes their code bytes, and the group's first
-// lane writes the scale byte.
+// amax is a max over those lanes (DPP and ds_swizzle exchanges).  Each lane
+// converts its own values on the gfx950 FP8 converters (two values per
+// instruction, the block scale as their divisor) and writes their code
+// bytes; the group's first lane writes the scale byte.
 #include "fp4q_cvt.hpp"
 #include "fp4q_device.hpp"
 #include "fp4q_launch.hpp"
@@ -26,8 +26,8 @@ constexpr int kThreads = 256;
 // the two code bytes (first value in the low byte) into word HI of the
 // destination, keeping the other word, which the wrappers tie.  The
 // quantizer only converts values whose magnitude after scaling is at most
-// 448, so saturation never applies.  Checked on MI355X against the software
-// rounding rule for every finite bf16 pattern at every block exponent.
+// 448, so saturation never applies.  Checked on MI355X against the oracle's
+// round-to-nearest-even for every finite bf16 pattern at every block exponent.
 
 // Word HI of acc <- E4M3 codes of the two bf16 halves of d (low half -> low byte).
 template <int HI>

@@ -586,6 +586,41 @@ def side_moe(torch, fq, wl, iters, warmup):
             op, dev[a], dev[b], out_t[c], groups=dev_off, max_group_rows=max_rows)))
     ms_dev = _timed_launches(torch, dev_launches, iters, warmup)
     g_host = sum(v for n, v in ms.items() if kinds[n] == "gemm")
+    # The whole step with each projection's wgrad on a second stream beside
+    # its dgrad (both read only the quantized dY; dgrad feeds the layer
+    # below, wgrad only the optimizer), against the same launches in order
+    # on one stream.  The grouped products are bound by their fp32 stores,
+    # and tiles of the two mix on the compute units.
+    fns = dict(launches)
+    side = torch.cuda.Stream()
+
+    def step_one():
+        for _, fn in launches:
+            fn()
+
+    def step_two():
+        main = torch.cuda.current_stream()
+        for proj, qs in (("up", ("X", "W_up", "dY")), ("down", ("A", "W_down", "dY_down"))):
+            for nm in qs:
+                fns["quant:" + nm]()
+            fns[proj + ":fwd"]()
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                fns[proj + ":wgrad"]()
+            fns[proj + ":dgrad"]()
+        main.wait_stream(side)
+
+    for nm, step in (("ms_per_step_one_stream", step_one), ("ms_per_step_two_streams", step_two)):
+        host_ms = _enqueue_ms(torch, step, max(1, warmup))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gpu_head_start(torch, fq, 2.0 + 1.5 * host_ms * iters)
+        e0.record()
+        for _ in range(iters):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        out[nm] = round(e0.elapsed_time(e1) / iters, 4)
+    out["two_streams_over_one"] = round(out["ms_per_step_two_streams"] / out["ms_per_step_one_stream"], 4)
     g_dev = sum(ms_dev.values())
     out["gemm_ms_device_offsets"] = round(g_dev, 4)
     out["gemm_device_over_host_offsets"] = round(g_dev / g_host, 4)

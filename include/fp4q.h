@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
     FP4Q_OK = 0,
     FP4Q_EINVAL = -1,       /* bad argument: null pointer, shape, alignment, leading dim */
-    FP4Q_EUNSUPPORTED = -2, /* valid request this build does not implement */
+    FP4Q_EUNSUPPORTED = -2, /* valid request the library does not implement */
     FP4Q_EHIP = -3          /* the HIP runtime rejected a launch */
 } fp4q_status;
 

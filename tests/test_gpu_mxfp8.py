@@ -36,6 +36,24 @@ def test_mxfp8_quant_bit_exact(shape, dtype):
     _check_fp8(q, orc.quant1d_mxfp8(x), shape[0])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("col0,cols", [(0, 96), (8, 96), (3, 77)])
+def test_mxfp8_quant_strided_rows(dtype, col0, cols):
+    """x a column window of a wider matrix (leading dimension 200 or 201
+    elements): rows whose 16-byte lane loads stay aligned (col0 0 or 8 with
+    an aligned pitch) and rows that take the element-wise path."""
+    rng = np.random.default_rng(col0 * 100 + cols)
+    pitch = 200 if col0 != 3 else 201
+    full = (rng.standard_normal((45, pitch)) * np.exp(rng.uniform(-8, 8, (45, 1)))).astype(np.float32)
+    if dtype == "bf16":
+        full = wl.f32_to_bf16_bits(full)
+    x = np.ascontiguousarray(full[:, col0:col0 + cols])
+    dev = to_dev(full)[:, col0:col0 + cols]
+    assert dev.stride(0) == pitch
+    note("mxfp8 strided %s col0=%d cols=%d" % (dtype, col0, cols))
+    _check_fp8(fq.fp4q_quant1d_mxfp8(dev), orc.quant1d_mxfp8(x), 45)
+
+
 def test_mxfp8_special_values():
     rng = np.random.default_rng(1)
     x = np.zeros((8, 128), np.float32)

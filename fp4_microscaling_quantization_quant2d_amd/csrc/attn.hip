@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
                 o[db] = mfma_bf16(read_pair_t(vt, kVtPitch, 32 * db + l32, sb, tp, h), pb, o[db]);
         }
         if (kb + 1 < nkb) {
-            __syncthreads();   // every wave is done with the other buffer
+            // every wave left the other buffer at the previous step's barrier
             fwd_store(st, lds + ((kb + 1) & 1) * kFwdBuf);
             __syncthreads();
         }

@@ -311,6 +311,21 @@ def _timed_launches(torch, launches, iters, warmup):
     return {nm: float(np.median(per[:, j])) for j, (nm, _) in enumerate(launches)}
 
 
+def _whole_step_ms(torch, fq, step, iters, warmup):
+    """Milliseconds per call of `step` (a function enqueueing one whole step),
+    timed between two events on the current stream over `iters` calls, with
+    the GPU given a head start over the host."""
+    host_ms = _enqueue_ms(torch, step, max(1, warmup))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gpu_head_start(torch, fq, 2.0 + 1.5 * host_ms * iters)
+    e0.record()
+    for _ in range(iters):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
 def _summary(ms, work, kinds):
     """Totals over launches of one kind: ms and rate (GB/s for quantizers, TFLOP/s for GEMMs)."""
     out = {"ms_per_step": round(sum(ms.values()), 4)}
@@ -346,7 +361,17 @@ def _eager_step(step, torch, iters, warmup, keep_launches=False):
 def side_1b(torch, fq, wl, iters, warmup):
     """The 1B-class layer step (up 2048->8192 and down 8192->2048 at 4096 tokens)."""
     out = {"workload": "1b-linear-layer-step: tokens 4096, hidden 2048, FFN 8192 (up, down)"}
-    out.update(_eager_step(Step(wl.config_1b(), torch, fq), torch, iters, warmup))
+    step = Step(wl.config_1b(), torch, fq)
+    out.update(_eager_step(step, torch, iters, warmup))
+    # The whole step on one stream, and with each layer's wgrad on a second
+    # stream beside its dgrad (the 7B step's schedule): two of the six
+    # products, 4096x2048 outputs over K = 8192, have 128 tiles, half the
+    # compute units, and the other half can run the wgrad beside them.
+    side = torch.cuda.Stream()
+    out["ms_per_step_one_stream"] = round(_whole_step_ms(torch, fq, lambda: step.run(seed=7), iters, warmup), 4)
+    out["ms_per_step_two_streams"] = round(
+        _whole_step_ms(torch, fq, lambda: step.run_two_streams(7, side), iters, warmup), 4)
+    out["two_streams_over_one"] = round(out["ms_per_step_two_streams"] / out["ms_per_step_one_stream"], 4)
     return out
 
 
@@ -611,15 +636,7 @@ def side_moe(torch, fq, wl, iters, warmup):
         main.wait_stream(side)
 
     for nm, step in (("ms_per_step_one_stream", step_one), ("ms_per_step_two_streams", step_two)):
-        host_ms = _enqueue_ms(torch, step, max(1, warmup))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        gpu_head_start(torch, fq, 2.0 + 1.5 * host_ms * iters)
-        e0.record()
-        for _ in range(iters):
-            step()
-        e1.record()
-        torch.cuda.synchronize()
-        out[nm] = round(e0.elapsed_time(e1) / iters, 4)
+        out[nm] = round(_whole_step_ms(torch, fq, step, iters, warmup), 4)
     out["two_streams_over_one"] = round(out["ms_per_step_two_streams"] / out["ms_per_step_one_stream"], 4)
     g_dev = sum(ms_dev.values())
     out["gemm_ms_device_offsets"] = round(g_dev, 4)

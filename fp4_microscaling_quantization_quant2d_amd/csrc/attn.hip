@@ -78,6 +78,20 @@ __device__ __forceinline__ const T* head_at(const T* base, int64_t head_row, int
     return base + head_row * ld + (uint32_t)(row * (uint32_t)ld + col);
 }
 
+// A buffer resource over rows [r0, L) of one head's slice of a row-major
+// tensor (ld elements per row): a load at a row past the sequence lies past
+// the resource and reads as zero, so the next-block loads need no masks, and
+// their per-lane offsets do not change from block to block.  Needs
+// r0 < L; the extent fits 32 bits because a head's slice of every operand is
+// below 2^31 elements (checked at the entry points).
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, int64_t head_row, int64_t ld, int r0, int L)
+{
+    const uint32_t bytes = (uint32_t)(L - r0) * (uint32_t)ld * (uint32_t)sizeof(T);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(head_at(base, head_row, ld, r0, 0)), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
 // 2^(b - 127) as a float (b = 0: the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_f32(uint32_t b)
 {
@@ -167,23 +181,41 @@ struct FwdStage {
     v4u v[2][2];
 };
 
-__device__ __forceinline__ void fwd_load(FwdStage& st, const AttnArgs& a, int64_t head_row, int k0)
+// Per-lane byte offsets of the next-block loads inside a block (the same
+// for every block).
+struct FwdOff {
+    uint32_t k[2], ks[2], v[2][2];
+};
+
+__device__ __forceinline__ FwdOff fwd_offsets(const AttnArgs& a)
 {
     const int t = threadIdx.x;
+    FwdOff o;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int u = t + kThreads * i, key = u >> 3, c = u & 7;
-        const bool ok = k0 + key < a.L;
-        st.k[i] = ok ? *reinterpret_cast<const v4u*>(head_at(a.kc, head_row, a.ldk, k0 + key, 16 * c))
-                     : (v4u){0u, 0u, 0u, 0u};
-        st.ks[i] = ok ? *reinterpret_cast<const uint32_t*>(head_at(a.ks, head_row, a.ldks, k0 + key, 0)) : 0u;
+        o.k[i] = (uint32_t)(key * a.ldk + 16 * c);
+        o.ks[i] = (uint32_t)(key * a.ldks);
         const int p = u & 31, dc = u >> 5;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int key2 = k0 + 2 * p + e;
-            st.v[i][e] = key2 < a.L ? *reinterpret_cast<const v4u*>(head_at(a.v, head_row, a.ldv, key2, 8 * dc))
-                                    : (v4u){0u, 0u, 0u, 0u};
-        }
+        for (int e = 0; e < 2; ++e)
+            o.v[i][e] = (uint32_t)(((2 * p + e) * a.ldv + 8 * dc) * 2);
+    }
+    return o;
+}
+
+__device__ __forceinline__ void fwd_load(FwdStage& st, const AttnArgs& a, const FwdOff& o, int64_t head_row, int k0)
+{
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.kc, head_row, a.ldk, k0, a.L);
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.ks, head_row, a.ldks, k0, a.L);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(a.v, head_row, a.ldv, k0, a.L);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.k[i], 0, 0);
+        st.ks[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)o.ks[i], 0, 0);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            st.v[i][e] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o.v[i][e], 0, 0);
     }
 }
 
@@ -243,14 +275,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a)
     const int nkb_all = (a.L + kFwdK - 1) / kFwdK;
     const int nkb = CAUSAL ? min(nkb_all, (qb * kFwdQ + kFwdQ - 1) / kFwdK + 1) : nkb_all;
     FwdStage st;
-    fwd_load(st, a, head_row, 0);
+    const FwdOff fo = fwd_offsets(a);
+    fwd_load(st, a, fo, head_row, 0);
     fwd_store(st, lds);
     __syncthreads();
     for (int kb = 0; kb < nkb; ++kb) {
         const uint8_t* buf = lds + (kb & 1) * kFwdBuf;
         const int k0 = kb * kFwdK;
         if (kb + 1 < nkb)
-            fwd_load(st, a, head_row, k0 + kFwdK);
+            fwd_load(st, a, fo, head_row, k0 + kFwdK);
 
     // S^T for the 64 keys: two 32-key sub-blocks.
         v16f s[2];
@@ -419,23 +452,40 @@ struct DqStage {
     v4u v[2][2];    // V rows 2p, 2p+1, d-chunk dc (8 bf16)
 };
 
-__device__ __forceinline__ void dq_load(DqStage& st, const AttnArgs& a, int64_t head_row, int k0)
+// Per-lane byte offsets of the next-block loads inside a block, for keys
+// 2p + e; the second half of the threads' columns (i = 1) lies 64 bytes
+// (codes), 2 bytes (scales) and 128 bytes (V) further on.
+struct DqOff {
+    uint32_t kc[2], ks[2], v[2];
+};
+
+__device__ __forceinline__ DqOff dq_offsets(const AttnArgs& a)
 {
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, p = t & 31, dc = t >> 5;
+    DqOff o;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = t + kThreads * i, p = u & 31, dc = u >> 5;
+    for (int e = 0; e < 2; ++e) {
+        const int key = 2 * p + e;
+        o.kc[e] = (uint32_t)(key * a.ldk + 8 * dc);
+        o.ks[e] = (uint32_t)(key * a.ldks + (dc >> 2));
+        o.v[e] = (uint32_t)((key * a.ldv + 8 * dc) * 2);
+    }
+    return o;
+}
+
+__device__ __forceinline__ void dq_load(DqStage& st, const AttnArgs& a, const DqOff& o, int64_t head_row, int k0)
+{
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.kc, head_row, a.ldk, k0, a.L);
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.ks, head_row, a.ldks, k0, a.L);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(a.v, head_row, a.ldv, k0, a.L);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int key = k0 + 2 * p + e;
-            const bool ok = key < a.L;
-            st.kc[i][e] = ok ? *reinterpret_cast<const v2u*>(head_at(a.kc, head_row, a.ldk, key, 8 * dc))
-                             : (v2u){0u, 0u};
-            st.ksb[i][e] = ok ? *head_at(a.ks, head_row, a.ldks, key, dc >> 2) : 0u;
-            st.v[i][e] = ok ? *reinterpret_cast<const v4u*>(head_at(a.v, head_row, a.ldv, key, 8 * dc))
-                            : (v4u){0u, 0u, 0u, 0u};
+            st.kc[i][e] = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)(o.kc[e] + 64 * i), 0, 0);
+            st.ksb[i][e] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(o.ks[e] + 2 * i), 0, 0);
+            st.v[i][e] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(o.v[e] + 128 * i), 0, 0);
         }
-    }
 }
 
 __device__ __forceinline__ void dq_store(const DqStage& st, uint8_t* buf)
@@ -500,13 +550,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_kernel(AttnArgs a)
     const uint8_t* buf = lds;
     const uint8_t* kt = buf + kDqKb + kDqV;
     DqStage st;
-    dq_load(st, a, head_row, 0);
+    const DqOff qo = dq_offsets(a);
+    dq_load(st, a, qo, head_row, 0);
     dq_store(st, lds);
     __syncthreads();
     for (int kb = 0; kb < nkb; ++kb) {
         const int k0 = kb * kDqK;
         if (kb + 1 < nkb)
-            dq_load(st, a, head_row, k0 + kDqK);
+            dq_load(st, a, qo, head_row, k0 + kDqK);
         const bool edge = k0 + kDqK > a.L || (CAUSAL && k0 + kDqK - 1 > q0);
         // one 32-key half at a time: S^T, dP^T, dS^T = P^T (dP^T - D) with
         // P^T = 0 for keys past the sequence, (causal) after the query, and
@@ -580,27 +631,46 @@ struct DkStage {
     float ls, dl;     // lse (natural log) and D of query t
 };
 
-__device__ __forceinline__ void dk_load(DkStage& st, const AttnArgs& a, int64_t head_row, int i0)
+// Per-lane byte offsets of the next-block loads inside a block, for queries
+// 2p + e; the second half of the threads' columns (i = 1) lies 64 bytes
+// (codes) and 128 bytes (dO) further on.
+struct DkOff {
+    uint32_t qc[2], qs[2], g[2];
+};
+
+__device__ __forceinline__ DkOff dk_offsets(const AttnArgs& a)
+{
+    const int t = threadIdx.x, p = t & 31, dc = t >> 5;
+    DkOff o;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int q = 2 * p + e;
+        o.qc[e] = (uint32_t)(q * a.ldq + 8 * dc);
+        o.qs[e] = (uint32_t)(q * a.ldqs);
+        o.g[e] = (uint32_t)((q * a.lddo + 8 * dc) * 2);
+    }
+    return o;
+}
+
+__device__ __forceinline__ void dk_load(DkStage& st, const AttnArgs& a, const DkOff& o, int64_t head_row, int i0)
 {
     const int t = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(a.qc, head_row, a.ldq, i0, a.L);
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.qs, head_row, a.ldqs, i0, a.L);
+    const __amdgpu_buffer_rsrc_t rg = rows_rsrc(a.dout, head_row, a.lddo, i0, a.L);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = t + kThreads * i, p = u & 31, dc = u >> 5;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int qq = i0 + 2 * p + e;
-            const bool ok = qq < a.L;
-            st.qc[i][e] = ok ? *reinterpret_cast<const v2u*>(head_at(a.qc, head_row, a.ldq, qq, 8 * dc))
-                             : (v2u){0u, 0u};
+            st.qc[i][e] = __builtin_amdgcn_raw_buffer_load_b64(rq, (int)(o.qc[e] + 64 * i), 0, 0);
             if (i == 0)   // the same rows for i = 1
-                st.qs[e] = ok ? *reinterpret_cast<const uint32_t*>(head_at(a.qs, head_row, a.ldqs, qq, 0)) : 0u;
-            st.g[i][e] = ok ? *reinterpret_cast<const v4u*>(head_at(a.dout, head_row, a.lddo, qq, 8 * dc))
-                            : (v4u){0u, 0u, 0u, 0u};
+                st.qs[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)o.qs[e], 0, 0);
+            st.g[i][e] = __builtin_amdgcn_raw_buffer_load_b128(rg, (int)(o.g[e] + 128 * i), 0, 0);
         }
-    }
-    const bool ok = t < kDkQ && i0 + t < a.L;
-    st.ls = ok ? a.lse[head_row + i0 + t] : 0.0f;
-    st.dl = ok ? a.delta[head_row + i0 + t] : 0.0f;
+    const __amdgpu_buffer_rsrc_t rl = rows_rsrc(a.lse, head_row, 1, i0, a.L);
+    const __amdgpu_buffer_rsrc_t rd = rows_rsrc(a.delta, head_row, 1, i0, a.L);
+    st.ls = __uint_as_float(t < kDkQ ? __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * t, 0, 0) : 0u);
+    st.dl = __uint_as_float(t < kDkQ ? __builtin_amdgcn_raw_buffer_load_b32(rd, 4 * t, 0, 0) : 0u);
 }
 
 // The dV kernel reads Q (rows) and dO^T (pairs); the dK kernel Q (rows),
@@ -678,13 +748,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dkdv_kernel(AttnArgs a)
     const float* lsv = reinterpret_cast<const float*>(gt + kDkGt);
     const float* dlv = lsv + kDkQ;
     DkStage st;
-    dk_load(st, a, head_row, ib0 * kDkQ);
+    const DkOff ko = dk_offsets(a);
+    dk_load(st, a, ko, head_row, ib0 * kDkQ);
     dk_store<DV>(st, lds);
     __syncthreads();
     for (int ib = ib0; ib < nib; ++ib) {
         const int i0 = ib * kDkQ;
         if (DV && ib + 1 < nib)
-            dk_load(st, a, head_row, i0 + kDkQ);
+            dk_load(st, a, ko, head_row, i0 + kDkQ);
         // rows = queries 32 qs + 8(r/4) + 4h + r%4; zero past the sequence
         // and (causal) where the key follows the query
         const bool edge = i0 + kDkQ > a.L || (CAUSAL && i0 < j0 + 31);
@@ -697,7 +768,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dkdv_kernel(AttnArgs a)
             // second half, so their registers are live for half a step (the
             // dV kernel has the registers to issue them at the top)
             if (!DV && qs == 1 && ib + 1 < nib)
-                dk_load(st, a, head_row, i0 + kDkQ);
+                dk_load(st, a, ko, head_row, i0 + kDkQ);
             const int qr0 = 32 * qs + l32;
             v16f sv = zero16(), dp = zero16();
 #pragma unroll

@@ -241,3 +241,57 @@ def test_degenerate_lengths(L, causal):
     if L == 1:
         assert np.allclose(On, Vd, rtol=2.0 ** -20, atol=0.0)
     _bwd_check(Q, K, V, dO, O, grads, bh, L, scale, causal, range(bh), np.arange(L), np.arange(L))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_strided_operands_match_contiguous(causal):
+    """Every operand at a row pitch wider than its 128 columns and at a
+    column offset (Q, K, V, dO as column slices of wider bf16 matrices, as a
+    fused QKV projection lays them out; codes, scales, O and the gradients in
+    wider buffers): the outputs are bit-identical to the run on contiguous
+    operands, and nothing outside the slices is written.  L = 200 leaves a
+    ragged last block, so the loads past the sequence are exercised with
+    pitches wider than a row."""
+    bh, L = 3, 200
+    n = bh * L
+    Q, K, V, dO = _heads(bh, L, 91 + causal)
+    note("attn strided bh=%d L=%d causal=%d" % (bh, L, causal))
+    qd, kd, vd, gd = to_dev(Q), to_dev(K), to_dev(V), to_dev(dO)
+    qq, qk = fq.fp4q_quant1d_mxfp8(qd), fq.fp4q_quant1d_mxfp8(kd)
+    O, lse = fq.fp4q_attn_fwd(qq, qk, vd, bh, L, causal=causal, out_dtype=torch.float32)
+    ref = fq.fp4q_attn_bwd(qq, qk, vd, O, lse, gd, bh, L, causal=causal)
+
+    x = torch.zeros((n, 400), dtype=torch.bfloat16, device="cuda")
+    x[:, 0:128], x[:, 136:264], x[:, 264:392] = qd, kd, vd
+    gbig = torch.zeros((n, 256), dtype=torch.bfloat16, device="cuda")
+    gbig[:, 128:256] = gd
+    sentinel = 0xA5
+
+    def qslice():
+        codes = torch.full((n, 192), sentinel, dtype=torch.uint8, device="cuda")
+        scales = torch.full((n, 12), sentinel, dtype=torch.uint8, device="cuda")
+        return codes, scales, fq.QTensor(fq.FMT_MXFP8_1D32, n, 128, codes[:, 32:160], scales[:, 4:8])
+
+    cq, sq, qq2 = qslice()
+    ck, sk, qk2 = qslice()
+    fq.fp4q_quant1d_mxfp8(x[:, 0:128], qq2)
+    fq.fp4q_quant1d_mxfp8(x[:, 136:264], qk2)
+    obig = torch.full((n, 136), -7.0, dtype=torch.float32, device="cuda")
+    o2 = obig[:, 8:136]
+    lse2 = torch.empty(n, dtype=torch.float32, device="cuda")
+    fq.fp4q_attn_fwd(qq2, qk2, x[:, 264:392], bh, L, causal=causal, o=o2, lse=lse2)
+    gb = [torch.full((n, 132), -7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+    fq.fp4q_attn_bwd(qq2, qk2, x[:, 264:392], o2, lse2, gbig[:, 128:256], bh, L, causal=causal,
+                     dq=gb[0][:, 4:132], dk=gb[1][:, 4:132], dv=gb[2][:, 4:132])
+    torch.cuda.synchronize()
+
+    for a, b in ((qq.codes, qq2.codes), (qq.scales, qq2.scales), (qk.codes, qk2.codes), (qk.scales, qk2.scales)):
+        assert torch.equal(a, b)
+    for buf, lo, hi in ((cq, 32, 160), (ck, 32, 160), (sq, 4, 8), (sk, 4, 8)):
+        assert bool((buf[:, :lo] == sentinel).all()) and bool((buf[:, hi:] == sentinel).all())
+    assert torch.equal(O.view(torch.int32), o2.contiguous().view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    assert bool((obig[:, :8] == -7.0).all())
+    for r, big in zip(ref, gb):
+        assert torch.equal(r.view(torch.int32), big[:, 4:132].contiguous().view(torch.int32))
+        assert bool((big[:, :4] == -7.0).all())

@@ -322,8 +322,11 @@ __device__ __forceinline__ void wait_vm_and_barrier()
 // QEP: the epilogue quantizes C into 2D 32x32 FP4 planes (the q_* fields of
 // GemmArgs) instead of writing C.
 // SUB: operands in (32/SUB)x(32/SUB) blocks (2: 16x16, 4: 8x8; FP4, dense).
+// MSKIP: a wave skips the MFMAs of its 32-row blocks that lie wholly past
+// row M (their sums are never stored), so the last, mostly empty row tile
+// of an expert segment costs the MFMA time of its valid blocks only.
 template <int FMT, bool A_ST, bool B_ST, bool KT, int ONED, bool ACC = false, bool OBF = false, bool QEP = false,
-          int SUB = 1>
+          int SUB = 1, bool MSKIP = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
 {
     constexpr bool A1D = FMT == 1 && (ONED & 1), B1D = FMT == 1 && (ONED & 2);
@@ -417,6 +420,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     // Load k (0..15) of pair p into slot p%2: instruction k/2 of operand A
     // (k even) or B (k odd).
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // LDS addresses in scalar registers
+    // MSKIP: 32-row blocks of this wave holding at least one row below M (0..4)
+    const int nmi_s = __builtin_amdgcn_readfirstlane(min(4, max(0, (P.M - m0 - (wave_s >> 1) * 128 + 31) >> 5)));
     auto issue_load = [&](int p, int k) {
         // a pair's 1D scale loads go out just before its first data load, so
         // every wait that covers the pair's data covers them as well
@@ -603,6 +608,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
             });
             return;
         }
+        if constexpr (MSKIP)
+            if (mi >= nmi_s)
+                return;
         const int ssa = (int)(mi >> 1 ? C.sa.y : C.sa.x);
         static_for<4>([&](auto NI) {
             constexpr int ni = decltype(NI)::value;
@@ -1163,7 +1171,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
     const int ntn = (P.N + kBN - 1) / kBN;
     P.tm = local / ntn;
     P.tn = local - P.tm * ntn;
-    gemm_tile<1, A_ST, B_ST, true, 0, false, OBF>(g, P);
+    gemm_tile<1, A_ST, B_ST, true, 0, false, OBF, false, 1, OP != kGemmWgrad>(g, P);
 }
 
 // Dynamic LDS: two stage buffers plus, per operand, the tile's scale bytes

@@ -116,3 +116,52 @@ def test_moe_config_sampled_experts():
                 ref, bd = orc.gemm_sampled(op, a, b, i, j)
                 gv = got[torch.from_numpy(i + base).cuda(), torch.from_numpy(j).cuda()].cpu().numpy()
                 check_gemm_tol(gv, ref, bd, "moe %s %s expert %d" % (name, op, e))
+
+
+def test_grouped_every_tail_block_count():
+    """Experts whose last row tile holds 1 to 8 valid 32-row blocks (some of
+    them ragged inside the last block), over one, two and three row tiles:
+    grouped fwd and dgrad (whose waves skip the MFMAs of blocks past an
+    expert's last row) and wgrad within the parity bound of the oracle, and
+    the device-offset launch identical to the host-offset one."""
+    rng = np.random.default_rng(31)
+    counts = [27, 64, 96, 123, 160, 192, 224, 256, 300, 480, 545, 767]
+    E, H, F = len(counts), 160, 128
+    padded = [(c + 31) // 32 * 32 for c in counts]
+    off = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+    rows = int(off[-1])
+    X = np.zeros((rows, H), np.float32)
+    dY = np.zeros((rows, F), np.float32)
+    for e, c in enumerate(counts):
+        X[off[e]:off[e] + c] = rng.standard_normal((c, H))
+        dY[off[e]:off[e] + c] = rng.standard_normal((c, F)) * 1e-3
+    W = (rng.standard_normal((E * F, H)) * 0.02).astype(np.float32)
+    bf = wl.f32_to_bf16_bits
+    X, W, dY = bf(X), bf(W), bf(dY)
+    g = {nm: fq.fp4q_quant2d(to_dev(t), seed=0, stream_id=i + 1) for i, (nm, t) in
+         enumerate((("X", X), ("W", W), ("dY", dY)))}
+    o = {nm: orc.quant2d(t, orc.ROUND_SR, seed=0, stream=i + 1) for i, (nm, t) in
+         enumerate((("X", X), ("W", W), ("dY", dY)))}
+    Xd = orc.dequant_fp4(o["X"][0], o["X"][2], *X.shape)
+    Wd = orc.dequant_fp4(o["W"][0], o["W"][2], *W.shape)
+    dYd = orc.dequant_fp4(o["dY"][0], o["dY"][2], *dY.shape)
+    offs = off.tolist()
+    note("moe tail block counts: host offsets")
+    out = {op: fq.fp4q_gemm(op, g[a], g[b], groups=offs)
+           for op, a, b in (("fwd", "X", "W"), ("dgrad", "dY", "W"), ("wgrad", "dY", "X"))}
+    note("moe tail block counts: device offsets")
+    dev = {op: fq.fp4q_gemm(op, g[a], g[b], groups=torch.from_numpy(off).cuda(), max_group_rows=max(padded))
+           for op, a, b in (("fwd", "X", "W"), ("dgrad", "dY", "W"), ("wgrad", "dY", "X"))}
+    torch.cuda.synchronize()
+    for op in out:
+        assert torch.equal(out[op], dev[op]), op
+    Y, dX, dW = (out[k].cpu().numpy() for k in ("fwd", "dgrad", "wgrad"))
+    for e in range(E):
+        r0, r1 = offs[e], offs[e + 1]
+        We = Wd[e * F:(e + 1) * F]
+        ref, b = orc.gemm("fwd", Xd[r0:r1], We)
+        check_gemm_tol(Y[r0:r1], ref, b, "fwd expert %d (%d rows)" % (e, counts[e]))
+        ref, b = orc.gemm("dgrad", dYd[r0:r1], We)
+        check_gemm_tol(dX[r0:r1], ref, b, "dgrad expert %d (%d rows)" % (e, counts[e]))
+        ref, b = orc.gemm("wgrad", dYd[r0:r1], Xd[r0:r1])
+        check_gemm_tol(dW[e * F:(e + 1) * F], ref, b, "wgrad expert %d (%d rows)" % (e, counts[e]))

@@ -810,9 +810,10 @@ int fp4q_attn_bwd_noalloc(const fp4q_qtensor* q, const fp4q_qtensor* k, const vo
                           float* dk, float* dv, int64_t ldg, int64_t bh, int64_t seq_len, float scale, int causal,
                           void* hip_stream)
 {
-    if (bh < 1 || seq_len < 1 || bh * seq_len > fp4q::kAttnScratchRows)
-        return fail(FP4Q_EINVAL, "fp4q_attn_bwd_noalloc: bh*seq_len %lld exceeds the static scratch of %lld rows",
-                    (long long)(bh * seq_len), (long long)fp4q::kAttnScratchRows);
+    // bh * seq_len is formed only once both factors are known small enough
+    if (bh < 1 || seq_len < 1 || bh > fp4q::kAttnScratchRows || seq_len > fp4q::kAttnScratchRows / bh)
+        return fail(FP4Q_EINVAL, "fp4q_attn_bwd_noalloc: bh %lld x seq_len %lld rows exceed the static scratch of "
+                    "%lld rows", (long long)bh, (long long)seq_len, (long long)fp4q::kAttnScratchRows);
     float* ws = nullptr;
     hipError_t e = fp4q::attn_noalloc_scratch(&ws);
     if (e != hipSuccess)

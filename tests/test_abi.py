@@ -393,6 +393,15 @@ def test_attention_validation(fp4q):
     assert bwd(ws=None) == -1 and "workspace" in _err(fp4q)
     assert bwd(ldg=130) == -1
     assert bwd(lddo=64) == -1
+    # the allocation-free backward checks its static scratch bound first,
+    # without forming a product that could wrap
+    na = lambda bh, n: L.fp4q_attn_bwd_noalloc(
+        ctypes.byref(q), ctypes.byref(q), v, 128, o, 128, 1, lse, g, 128, P(0x600000), P(0x700000), P(0x800000),
+        128, bh, n, ctypes.c_float(0.088), 1, None)
+    assert na(2, (1 << 19) + 1) == -1 and "static scratch" in _err(fp4q)
+    assert na(1 << 40, 1 << 40) == -1 and "static scratch" in _err(fp4q)
+    assert na((1 << 62) + 1, 4) == -1 and "static scratch" in _err(fp4q)
+    assert na(0, 64) == -1 and na(2, 0) == -1
     # every head's slice of every tensor stays below 2^31 elements
     big = _desc(fp4q, fmt=2, rows=1 << 21, cols=128, ld=128, ld_s=4)
     assert call(big, big, bh=1, n=1 << 21, ldv=1024) == -1 and "2^31" in _err(fp4q)

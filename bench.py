@@ -187,6 +187,11 @@ class Step:
             d["shape"] = (T, K, N)
             d["name"] = L.name
             self.layers.append(d)
+        # None: the quantizers take the host seed alone.  A 1-element int64
+        # CUDA tensor: its value is added to the Philox key when each
+        # quantizer runs (the captured graphs advance it once per replay, so
+        # every replayed step draws fresh stochastic-rounding bits).
+        self.seed_dev = None
         self.launches = []   # (kind, name, work) in launch order
         self.gemm_bytes = 0  # algorithmic HBM bytes of the step's GEMMs: FP4 operands, scales, fp32 C
         for d in self.layers:
@@ -210,7 +215,7 @@ class Step:
     def quant_xw(self, i, d, seed):
         """The layer's activations and weights, quantized in one batch launch."""
         self.fq.fp4q_quant2d_batch([(d["X"], d["qX"], 16 * i + 1), (d["W"], d["qW"], 16 * i + 2)],
-                                   seed=seed)
+                                   seed=seed, seed_dev=self.seed_dev)
 
     def run(self, seed, events=None):
         """Enqueue one step; with events, record one (start, end) pair per launch."""
@@ -228,13 +233,16 @@ class Step:
 
         for i, d in enumerate(self.layers):
             if self.x_sep:
-                timed(lambda: fq.fp4q_quant2d(d["X"], d["qX"], seed=seed, stream_id=16 * i + 1))
-                timed(lambda: fq.fp4q_quant2d(d["W"], d["qW"], seed=seed, stream_id=16 * i + 2))
+                timed(lambda: fq.fp4q_quant2d(d["X"], d["qX"], seed=seed, stream_id=16 * i + 1,
+                                              seed_dev=self.seed_dev))
+                timed(lambda: fq.fp4q_quant2d(d["W"], d["qW"], seed=seed, stream_id=16 * i + 2,
+                                              seed_dev=self.seed_dev))
             else:
                 timed(lambda: self.quant_xw(i, d, seed))
             timed(lambda: fq.fp4q_gemm("fwd", d["qX"], d["qW"], d["Y"]))
         for i, d in reversed(list(enumerate(self.layers))):
-            timed(lambda: fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3))
+            timed(lambda: fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3,
+                                          seed_dev=self.seed_dev))
             timed(lambda: fq.fp4q_gemm("dgrad", d["qdY"], d["qW"], d["dX"]))
             timed(lambda: fq.fp4q_gemm("wgrad", d["qdY"], d["qX"], d["dW"], accumulate=self.wgrad_acc))
 
@@ -251,7 +259,7 @@ class Step:
             self.quant_xw(i, d, seed)
             fq.fp4q_gemm("fwd", d["qX"], d["qW"], d["Y"])
         for i, d in reversed(list(enumerate(self.layers))):
-            fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3)
+            fq.fp4q_quant2d(d["dY"], d["qdY"], seed=seed, stream_id=16 * i + 3, seed_dev=self.seed_dev)
             side.wait_stream(main)
             fq.fp4q_gemm("dgrad", d["qdY"], d["qW"], d["dX"])
             with torch.cuda.stream(side):
@@ -881,16 +889,25 @@ def main():
     per = np.array([[s.elapsed_time(e) for (s, e) in events[k]] for k in range(args.steps)])  # ms
     ms_step_eager = ms_step
 
-    # Whole-step time: the step's launches captured once in a HIP graph (one
-    # fixed seed) and replayed K times between two events, so launch gaps and
-    # the per-launch events above do not count.  The captured step runs each
+    # Whole-step time: the step's launches captured once in a HIP graph and
+    # replayed K times between two events, so launch gaps and the per-launch
+    # events above do not count.  The captured step's quantizers read a
+    # device-resident seed that the step itself advances at its end (one
+    # small add kernel inside the timed replays), so each replay draws fresh
+    # stochastic-rounding bits, as a training loop replaying the graph must.  The captured step runs each
     # layer's wgrad on a second stream (run_two_streams); the same launches
     # captured on one stream are timed too.  Per-kernel rates come from the
     # eager pass.
     graph = None
     ms_step_one_stream = None
 
-    def graph_ms(schedule):
+    step.seed_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def graph_ms(run_step):
+        def schedule():
+            run_step()
+            step.seed_dev.add_(1)
+
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
@@ -968,6 +985,9 @@ def main():
         "ms_per_step_graph_two_streams": None if ms_step_two_streams is None else round(ms_step_two_streams, 4),
         "step_timing": ("hip-graph replay, the faster of two schedules: " + schedule if graph is not None
                         else "eager launches"),
+        "sr_seed": ("host seed 7 plus a device-resident counter that every replayed step advances "
+                    "(fresh stochastic-rounding bits per step)" if graph is not None
+                    else "host seed 1000 + step index"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -142,3 +142,67 @@ def test_device_seed_draws_fresh_bits_per_replay():
         if prev is not None:
             assert not torch.equal(cur, prev)
         prev = cur
+
+
+def test_bench_graph_advances_device_seed():
+    """The bench's captured step (wgrad on a second stream) with its
+    quantizers on a device-resident seed that the graph advances at the end
+    of every replay: replay r leaves exactly the planes and products of an
+    eager step run with host seed 7 + r, and consecutive replays differ."""
+    import importlib.util
+    import pathlib
+    spec = importlib.util.spec_from_file_location("bench_mod", pathlib.Path(__file__).parent.parent / "bench.py")
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    layers = [wl.linear_layer("tiny:seedgraph", 320, 448, 288, 1), wl.linear_layer("tiny:seedgraph", 320, 288, 96, 2)]
+    step = bench.Step(layers, torch, fq)
+    keys, outs = ("qX", "qW", "qdY"), ("Y", "dX", "dW")
+
+    def snapshot():
+        torch.cuda.synchronize()
+        snap = {}
+        for i, d in enumerate(step.layers):
+            for k in keys:
+                snap[(i, k)] = (d[k].codes.clone(), d[k].codes_t.clone(), d[k].scales.clone())
+            for k in outs:
+                snap[(i, k)] = d[k].clone()
+        return snap
+
+    refs = []
+    for r in range(3):
+        step.run(seed=7 + r)
+        refs.append(snapshot())
+    step.seed_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+
+    def captured():
+        step.run_two_streams(7, side)
+        step.seed_dev.add_(1)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        captured()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note("bench graph with device seed: capture")
+    with torch.cuda.graph(g):
+        captured()
+    step.seed_dev.zero_()
+    prev = None
+    for r in range(3):
+        torch.cuda.synchronize()
+        note("bench graph with device seed: replay %d" % r)
+        g.replay()
+        got = snapshot()
+        for k, v in refs[r].items():
+            if isinstance(v, tuple):
+                for a, b in zip(v, got[k]):
+                    assert torch.equal(a, b), "replay %d: layer %d %s planes differ" % (r, k[0], k[1])
+            else:
+                assert torch.equal(v, got[k]), "replay %d: layer %d %s differs" % (r, k[0], k[1])
+        if prev is not None:
+            assert not torch.equal(prev, got[(0, "qX")][0]), "replay %d drew the same bits as the last" % r
+        prev = got[(0, "qX")][0]
+    assert int(step.seed_dev.item()) == 3

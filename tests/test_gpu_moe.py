@@ -165,3 +165,57 @@ def test_grouped_every_tail_block_count():
         check_gemm_tol(dX[r0:r1], ref, b, "dgrad expert %d (%d rows)" % (e, counts[e]))
         ref, b = orc.gemm("wgrad", dYd[r0:r1], Xd[r0:r1])
         check_gemm_tol(dW[e * F:(e + 1) * F], ref, b, "wgrad expert %d (%d rows)" % (e, counts[e]))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_grouped_random_routings(case):
+    """Seeded random expert layouts (empty, ragged and multi-tile experts,
+    hidden and expert widths of several 32-multiples): grouped fwd, dgrad and
+    wgrad within the parity bound of the oracle for every expert, host and
+    device offsets identical."""
+    rng = np.random.default_rng(1000 + case)
+    E = int(rng.integers(2, 9))
+    H = 32 * int(rng.integers(1, 12))
+    F = 32 * int(rng.integers(1, 12))
+    counts = [int(c) for c in rng.integers(0, 700, size=E)]
+    counts[int(rng.integers(0, E))] = 0
+    padded = [(c + 31) // 32 * 32 for c in counts]
+    off = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+    rows = max(int(off[-1]), 32)
+    X = np.zeros((rows, H), np.float32)
+    dY = np.zeros((rows, F), np.float32)
+    for e, c in enumerate(counts):
+        X[off[e]:off[e] + c] = rng.standard_normal((c, H))
+        dY[off[e]:off[e] + c] = rng.standard_normal((c, F)) * 1e-3
+    W = (rng.standard_normal((E * F, H)) * 0.02).astype(np.float32)
+    bf = wl.f32_to_bf16_bits
+    X, W, dY = bf(X), bf(W), bf(dY)
+    g = {nm: fq.fp4q_quant2d(to_dev(t), seed=case, stream_id=i + 1) for i, (nm, t) in
+         enumerate((("X", X), ("W", W), ("dY", dY)))}
+    o = {nm: orc.quant2d(t, orc.ROUND_SR, seed=case, stream=i + 1) for i, (nm, t) in
+         enumerate((("X", X), ("W", W), ("dY", dY)))}
+    Xd = orc.dequant_fp4(o["X"][0], o["X"][2], *X.shape)
+    Wd = orc.dequant_fp4(o["W"][0], o["W"][2], *W.shape)
+    dYd = orc.dequant_fp4(o["dY"][0], o["dY"][2], *dY.shape)
+    offs = off.tolist()
+    note("moe random routing %d: E=%d H=%d F=%d counts=%s" % (case, E, H, F, counts))
+    ops = (("fwd", "X", "W"), ("dgrad", "dY", "W"), ("wgrad", "dY", "X"))
+    out = {op: fq.fp4q_gemm(op, g[a], g[b], groups=offs) for op, a, b in ops}
+    dev = {op: fq.fp4q_gemm(op, g[a], g[b], groups=torch.from_numpy(off).cuda(),
+                            max_group_rows=max(max(padded), 32)) for op, a, b in ops}
+    torch.cuda.synchronize()
+    for op in out:
+        assert torch.equal(out[op], dev[op]), op
+    Y, dX, dW = (out[k].cpu().numpy() for k in ("fwd", "dgrad", "wgrad"))
+    for e in range(E):
+        r0, r1 = offs[e], offs[e + 1]
+        if r1 == r0:
+            assert not dW[e * F:(e + 1) * F].any()
+            continue
+        We = Wd[e * F:(e + 1) * F]
+        ref, b = orc.gemm("fwd", Xd[r0:r1], We)
+        check_gemm_tol(Y[r0:r1], ref, b, "case %d fwd expert %d" % (case, e))
+        ref, b = orc.gemm("dgrad", dYd[r0:r1], We)
+        check_gemm_tol(dX[r0:r1], ref, b, "case %d dgrad expert %d" % (case, e))
+        ref, b = orc.gemm("wgrad", dYd[r0:r1], Xd[r0:r1])
+        check_gemm_tol(dW[e * F:(e + 1) * F], ref, b, "case %d wgrad expert %d" % (case, e))

@@ -602,6 +602,7 @@ def side_moe(torch, fq, wl, iters, warmup):
     out = {"workload": "30b-moe-expert-layer-step: 8192 tokens, top-8 of 128 experts, hidden 2048, FFN 768; "
                        "%d gathered rows (32-aligned segments); flops counted on the gathered rows" % rows}
     out.update(_summary(ms, work, kinds))
+    out["per_launch_ms"] = {n: round(v, 4) for n, v in ms.items()}
     # The same grouped GEMMs with the offsets in device memory (routing that
     # never visits the host): the grid is a bound and every workgroup builds
     # the tile table itself.

@@ -976,6 +976,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Problem& P)
     }
 }
 
+// Workgroup `id` of a 1-D grid runs on XCD id % 8.  Tile xcd_tile(id, n)
+// gives XCD x the contiguous tile range [x*q + min(x, r), ..) of n = 8q + r
+// tiles (a bijection on [0, n)), so consecutive tiles, which share operand
+// panels (a band of one product, an expert's tiles), meet in one XCD's L2.
+__device__ __forceinline__ int xcd_tile(int id, int n)
+{
+    const int x = id & 7, q = n >> 3, r = n & 7;
+    return x * q + min(x, r) + (id >> 3);
+}
+
 // Tile order: each XCD (dispatch id mod 8) receives a contiguous range of
 // tile ids; inside it tiles are M-grouped in bands of BAND tile rows.  FP4
 // takes 4 (1% faster on the 7B step than 8 or 2; 16 slower), the batched
@@ -985,8 +995,7 @@ __device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int&
 {
     constexpr int kBandRows = BAND;
     const int nt = ntm * ntn;
-    if ((nt & 7) == 0)
-        pid = (pid & 7) * (nt >> 3) + (pid >> 3);
+    pid = xcd_tile(pid, nt);
     const int band = kBandRows * ntn;
     const int first = (pid / band) * kBandRows;
     const int rows = min(ntm - first, kBandRows);
@@ -1077,7 +1086,7 @@ __device__ __forceinline__ float* c_elem(float* c, int64_t off)
 template <int OP, bool A_ST, bool B_ST, bool DEV, bool OBF = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
 {
-    const int pid = blockIdx.x;
+    int pid = blockIdx.x;
     int grp, r0, r1, local;
     const int ntn_g = ((OP == kGemmFwd ? g.group_n : g.N) + kBN - 1) / kBN;
     if constexpr (DEV) {
@@ -1108,6 +1117,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
         }
         if (pid >= incl[n - 1])
             return;  // uniform over the workgroup
+        pid = xcd_tile(pid, incl[n - 1]);
         int lo = 0, hi = n - 1;  // first group whose inclusive count exceeds pid
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
@@ -1122,6 +1132,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_kernel(GemmArgs g)
         local = pid - (grp ? incl[grp - 1] : 0);
         __syncthreads();  // the tile reuses this LDS
     } else {
+        pid = xcd_tile(pid, g.tile_start[g.n_groups]);  // the grid holds exactly these tiles
         int lo = 0, hi = g.n_groups;  // find grp with tile_start[grp] <= pid < tile_start[grp+1]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
